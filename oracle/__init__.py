@@ -1,0 +1,15 @@
+"""Plain CPU oracle of the KV-cache compression hot path (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the HIP implementation in
+``sparse_decode_amd`` and never imports it.
+"""
+from .ref import (  # noqa: F401
+    build,
+    cache_bytes,
+    decode,
+    gather,
+    score_window,
+    select_topk,
+    set_threads,
+)

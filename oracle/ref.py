@@ -1,0 +1,175 @@
+"""ctypes binding of the plain C oracle ``kvc_oracle.c`` (test infrastructure only).
+
+Every function takes and returns numpy arrays on the host.  Floating-point inputs
+are float32 arrays; bf16 data is passed after an exact widening to float32 by the
+caller.  The C file states, step by step, what each function computes and which
+page section it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvc_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "libkvc_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compiles the oracle with gcc (plain -O2, OpenMP, no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-fvisibility=hidden",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            I = ctypes.c_int
+            lib.kvo_cache_bytes.restype = ctypes.c_uint64
+            lib.kvo_cache_bytes.argtypes = [ctypes.c_int64] * 5
+            lib.kvo_set_threads.restype = I
+            lib.kvo_set_threads.argtypes = [I]
+            lib.kvo_score_window.restype = None
+            lib.kvo_score_window.argtypes = [I, I, P, I, I, I, P, P, I, I, I, I, ctypes.c_double, P, P, P]
+            lib.kvo_select_topk.restype = None
+            lib.kvo_select_topk.argtypes = [I, I, I, P, P, I, I, I, P, P]
+            lib.kvo_gather.restype = None
+            lib.kvo_gather.argtypes = [I, I, I, I, P, P, P, P, I, P, P]
+            lib.kvo_decode.restype = None
+            lib.kvo_decode.argtypes = [I, I, I, I, P, P, P, P, I, ctypes.c_double, P, P]
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError("oracle expects float32 input, got %s" % a.dtype)
+    return a
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def set_threads(n: int = 0) -> int:
+    return int(_load().kvo_set_threads(int(n)))
+
+
+def cache_bytes(L: int, S: int, n_kv: int, d_h: int, b: int) -> int:
+    """Tutorial, "MHA et GQA": 2 * L * S * n_kv * d_h * b bytes per sequence."""
+    return int(_load().kvo_cache_bytes(L, S, n_kv, d_h, b))
+
+
+def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=None, pool=1,
+                 scale=None, want_raw64=False):
+    """Window saliency + candidate-region max pool (FastKV 2.A; Tutorial,
+    "Compresser un cache existant").
+
+    q_win [B][n_h][w][d_h] float32, k [B][n_kv][s_max][d_h] float32.
+    Returns (raw, pooled) float32 [B][n_kv][s_max] (and raw64 float64 if asked).
+    """
+    q_win = _f32(q_win)
+    k = _f32(k)
+    B, n_h, w_, d_h = q_win.shape
+    Bk, n_kv, s_max, d_k = k.shape
+    assert w_ == w and Bk == B and d_k == d_h and n_h % n_kv == 0
+    if n_keep is None:
+        n_keep = w
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    sl = _i32(seq_lens)
+    raw = np.zeros((B, n_kv, s_max), np.float32)
+    pooled = np.zeros((B, n_kv, s_max), np.float32)
+    raw64 = np.zeros((B, n_kv, s_max), np.float64) if want_raw64 else None
+    _load().kvo_score_window(B, s_max, _ptr(sl), n_h, n_kv, d_h, _ptr(q_win), _ptr(k), int(w),
+                             int(bool(window_in_cache)), int(n_keep), int(pool), float(scale),
+                             _ptr(raw64), _ptr(raw), _ptr(pooled))
+    if want_raw64:
+        return raw, pooled, raw64
+    return raw, pooled
+
+
+def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False):
+    """Per-head top-k (score desc, index asc) + trailing n_keep tokens, ascending.
+
+    scores [B][H][s_max] float32.  Returns (idx int32 [B][H_out][k+n_keep], count int32 [B][H_out]).
+    """
+    scores = _f32(scores)
+    B, H, s_max = scores.shape
+    H_out = 1 if shared_heads else H
+    cap = k + n_keep
+    idx = np.empty((B, H_out, cap), np.int32)
+    count = np.empty((B, H_out), np.int32)
+    sl = _i32(seq_lens)
+    _load().kvo_select_topk(B, H, s_max, _ptr(sl), _ptr(scores), int(k), int(n_keep),
+                            int(bool(shared_heads)), _ptr(idx), _ptr(count))
+    return idx, count
+
+
+def gather(src, idx, count, *, src_pos=None, dst=None):
+    """Compacting gather of rows; src [B][heads][s_max][...] any dtype.
+
+    Returns (dst [B][heads][cap][...], pos_out [B][heads][cap]).  Rows past count
+    keep what ``dst`` held (zeros when it is not given); their pos_out is -1.
+    """
+    src = np.ascontiguousarray(src)
+    B, heads, s_max = src.shape[:3]
+    row_shape = src.shape[3:]
+    row_bytes = int(np.prod(row_shape, dtype=np.int64)) * src.itemsize
+    idx = _i32(idx)
+    count = _i32(count)
+    cap = idx.shape[-1]
+    if dst is None:
+        dst = np.zeros((B, heads, cap) + row_shape, src.dtype)
+    else:
+        dst = np.ascontiguousarray(dst).copy()
+    pos = np.empty((B, heads, cap), np.int32)
+    sp = _i32(src_pos)
+    _load().kvo_gather(B, heads, s_max, row_bytes, _ptr(src), _ptr(sp), _ptr(idx), _ptr(count),
+                       cap, _ptr(dst), _ptr(pos))
+    return dst, pos
+
+
+def decode(q, kc, vc, count, *, scale=None):
+    """GQA decode attention over the compacted cache, in double.
+
+    q [B][n_h][d_h], kc/vc [B][n_kv][cap][d_h] float32, count [B][n_kv].
+    Returns (out float64 [B][n_h][d_h], lse float64 [B][n_h]).
+    """
+    q = _f32(q)
+    kc = _f32(kc)
+    vc = _f32(vc)
+    B, n_h, d_h = q.shape
+    _, n_kv, cap, _ = kc.shape
+    assert n_h % n_kv == 0
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    count = _i32(count)
+    out = np.zeros((B, n_h, d_h), np.float64)
+    lse = np.zeros((B, n_h), np.float64)
+    _load().kvo_decode(B, n_h, n_kv, d_h, _ptr(q), _ptr(kc), _ptr(vc), _ptr(count), int(cap),
+                       float(scale), _ptr(out), _ptr(lse))
+    return out, lse

@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test ties one part of the oracle to a value the pages print, a closed form,
+an invariant, a library routine on a special case, or brute force on tiny inputs,
+so that a dropped term, a wrong sign or index, or a transposed operand anywhere in
+the oracle fails at least one of them.
+"""
+import dataclasses
+import itertools
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from sparse_decode_amd import synth
+
+
+# ----------------------------------------------------------------------------------
+# Worked example printed on the page (Tutorial, "MHA et GQA")
+# ----------------------------------------------------------------------------------
+def test_cache_bytes_worked_example(golden_dir):
+    with open(os.path.join(golden_dir, "cache_size_worked_example.json")) as f:
+        gold = json.load(f)
+    for c in gold["cases"]:
+        got = c["sequences"] * oracle.cache_bytes(c["L"], c["S"], c["n_kv"], c["d_h"], c["b"])
+        assert got == c["bytes"], c["what"]
+    # 512 MiB and 2 GiB as the page states them
+    assert oracle.cache_bytes(32, 4096, 8, 128, 2) == 512 * 2**20
+    # GQA shrinks the cache by n_kv / n_h relative to MHA
+    assert oracle.cache_bytes(32, 4096, 8, 128, 2) * 4 == oracle.cache_bytes(32, 4096, 32, 128, 2)
+
+
+def _rand(shape, seed, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------
+# Softmax rows sum to one: the window score sums to (number of rows that see a key)
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("n_h,n_kv,w,wic", [(4, 2, 8, True), (8, 1, 4, True), (4, 4, 3, False), (6, 2, 1, False)])
+def test_score_rows_sum_to_one(n_h, n_kv, w, wic):
+    B, S, d = 2, 97, 16
+    q = _rand((B, n_h, w, d), 1)
+    k = _rand((B, n_kv, S, d), 2)
+    sl = np.array([97, 40], np.int32)
+    raw, pooled, raw64 = oracle.score_window(q, k, w, seq_lens=sl, window_in_cache=wic, n_keep=w,
+                                             pool=3, want_raw64=True)
+    r = n_h // n_kv
+    for b in range(B):
+        for g in range(n_kv):
+            assert abs(raw64[b, g].sum() - r * w) < 1e-11
+            assert np.all(raw64[b, g, sl[b]:] == 0.0)
+    # one row: exactly a softmax
+    raw1, _, raw64_1 = oracle.score_window(q[:, :1, :1], k[:, :1], 1, window_in_cache=False, n_keep=1,
+                                           pool=1, want_raw64=True)
+    assert abs(raw64_1[0, 0].sum() - 1.0) < 1e-13
+
+
+def test_score_row_with_no_visible_key_adds_nothing():
+    # S_b < w with the window in the cache: rows i < w - S_b see no key.
+    q = _rand((1, 2, 8, 4), 3)
+    k = _rand((1, 1, 16, 4), 4)
+    _, _, raw64 = oracle.score_window(q, k, 8, seq_lens=np.array([5], np.int32), n_keep=8, pool=1,
+                                      want_raw64=True)
+    assert abs(raw64[0, 0].sum() - 2 * 5) < 1e-12   # rows i = 3..7 of both heads see >= 1 key
+
+
+# ----------------------------------------------------------------------------------
+# Closed form with identical keys: every visible logit of a row is equal, so row i
+# gives 1/(S - w + i + 1) to each key it sees (causal alignment, Tutorial section
+# "Quand la reutilisation est-elle exacte ?").
+# ----------------------------------------------------------------------------------
+def _uniform_key_closed_form(S, w, r, t, top_left=False):
+    tot = Fraction(0)
+    for i in range(w):
+        last = i if top_left else S - w + i
+        if t <= last:
+            tot += Fraction(1, last + 1)
+    return r * tot
+
+
+def test_uniform_keys_closed_form_and_ties():
+    wl = synth.WORKLOADS[1]
+    S, w, r, d = wl.s_max, wl.w, wl.group, wl.d_h
+    q = _rand((1, wl.n_h, w, d), 5)
+    row = _rand((d,), 6)
+    k = np.broadcast_to(row, (1, wl.n_kv, S, d)).copy()
+    raw, pooled, raw64 = oracle.score_window(q, k, w, n_keep=wl.n_keep, pool=wl.pool, want_raw64=True)
+    # printed value for the tiny shape: r * (H_S - H_{S-w}) = 0.0634344...
+    assert abs(raw64[0, 0, 0] - 0.06343443427670455) < 1e-15
+    for t in [0, 1, 200, S - w - 1, S - w, S - w + 1, S - 2, S - 1]:
+        want = float(_uniform_key_closed_form(S, w, r, t))
+        assert abs(raw64[0, 0, t] - want) <= 1e-14 * want, t
+        # a top-left aligned mask would give a different value (the pin sees the mask)
+        naive = float(_uniform_key_closed_form(S, w, r, t, top_left=True))
+        assert abs(naive - want) > 1e-6 * want or t >= S - w
+    # all candidates tie -> the lowest indices win, then the window
+    idx, count = oracle.select_topk(pooled, wl.k, wl.n_keep)
+    want = list(range(wl.k)) + list(range(S - wl.n_keep, S))
+    for g in range(wl.n_kv):
+        assert count[0, g] == wl.k + wl.n_keep
+        assert idx[0, g].tolist() == want
+
+
+# ----------------------------------------------------------------------------------
+# Brute force at 50 decimal digits on tiny inputs
+# ----------------------------------------------------------------------------------
+getcontext().prec = 50
+
+
+def _dec_score(q, k, S, w, wic, scale):
+    """p_t = 1 / sum_u exp(x_u - x_t): the softmax written another way."""
+    n_h, d = q.shape[0], q.shape[-1]
+    n_kv = k.shape[0]
+    r = n_h // n_kv
+    sc = Decimal(scale)
+    raw = [[Decimal(0)] * S for _ in range(n_kv)]
+    for h in range(n_h):
+        g = h // r
+        for i in range(w):
+            last = S - w + i if wic else S - 1
+            last = min(last, S - 1)
+            if last < 0:
+                continue
+            xs = [sc * sum(Decimal(float(q[h, i, e])) * Decimal(float(k[g, t, e])) for e in range(d))
+                  for t in range(last + 1)]
+            for t in range(last + 1):
+                raw[g][t] += 1 / sum((xu - xs[t]).exp() for xu in xs)
+    return raw
+
+
+def _brute_select(scores, k, n_keep, S):
+    C = max(0, S - n_keep)
+    k_eff = min(k, C)
+    best = None
+    for sub in itertools.combinations(range(C), k_eff):
+        key = sorted((-scores[t], t) for t in sub)
+        if best is None or key < best[0]:
+            best = (key, sub)
+    return sorted(best[1]) + list(range(C, S))
+
+
+@pytest.mark.parametrize("seed,n_h,n_kv,S,w,wic,k,pool", [
+    (11, 2, 1, 10, 3, True, 3, 3),
+    (12, 2, 2, 9, 2, True, 4, 3),
+    (13, 3, 1, 8, 1, False, 2, 1),
+    (14, 4, 2, 11, 3, True, 3, 5),
+])
+def test_bruteforce_tiny(seed, n_h, n_kv, S, w, wic, k, pool):
+    d = 3
+    q = _rand((1, n_h, w, d), seed, 2.0)
+    kk = _rand((1, n_kv, S, d), seed + 100, 2.0)
+    scale = 1 / math.sqrt(d)
+    raw, pooled, raw64 = oracle.score_window(q, kk, w, window_in_cache=wic, n_keep=w, pool=pool,
+                                             scale=scale, want_raw64=True)
+    dec = _dec_score(q[0], kk[0], S, w, wic, scale)
+    for g in range(n_kv):
+        for t in range(S):
+            assert abs(raw64[0, g, t] - float(dec[g][t])) <= 1e-14 * max(1.0, float(dec[g][t]))
+            assert raw[0, g, t] == np.float32(float(dec[g][t]))
+        C = S - w
+        for t in range(S):
+            if t < C:
+                lo, hi = max(0, t - pool // 2), min(C - 1, t + pool // 2)
+                want = max(raw[0, g, lo:hi + 1])
+            else:
+                want = raw[0, g, t]
+            assert pooled[0, g, t] == want
+    idx, count = oracle.select_topk(pooled, k, w)
+    for g in range(n_kv):
+        want = _brute_select([float(x) for x in pooled[0, g]], k, w, S)
+        assert count[0, g] == len(want)
+        assert idx[0, g, :len(want)].tolist() == want
+    # decode by the direct formula
+    qd = _rand((1, n_h, d), seed + 200)
+    cnt = np.array([[5] * n_kv], np.int32)
+    vv = _rand((1, n_kv, 5, d), seed + 300)
+    kc = kk[:, :, :5].copy()
+    out, lse = oracle.decode(qd, kc, vv, cnt, scale=scale)
+    r = n_h // n_kv
+    for h in range(n_h):
+        g = h // r
+        ys = [Decimal(scale) * sum(Decimal(float(qd[0, h, e])) * Decimal(float(kc[0, g, t, e])) for e in range(d))
+              for t in range(5)]
+        Z = sum(y.exp() for y in ys)
+        for e in range(d):
+            want = sum(y.exp() / Z * Decimal(float(vv[0, g, t, e])) for t, y in enumerate(ys))
+            assert abs(out[0, h, e] - float(want)) < 1e-14
+        assert abs(lse[0, h] - float(Z.ln())) < 1e-14
+
+
+# ----------------------------------------------------------------------------------
+# Special cases that reduce to library routines (torch CPU, float64)
+# ----------------------------------------------------------------------------------
+def _torch_raw(q, k, w, S, wic, scale, gqa_map="block"):
+    qt = torch.from_numpy(q).double()[0]          # [n_h][w][d]
+    kt = torch.from_numpy(k).double()[0, :, :S]   # [n_kv][S][d]
+    n_h, n_kv = qt.shape[0], kt.shape[0]
+    r = n_h // n_kv
+    if gqa_map == "block":
+        kh = kt.repeat_interleave(r, dim=0)       # head h reads KV head h // r
+    else:
+        kh = kt.repeat(r, 1, 1)                   # a wrong map: head h reads h % n_kv
+    logits = torch.matmul(qt, kh.transpose(1, 2)) * scale
+    if wic:
+        vis = torch.ones(w, S, dtype=torch.bool).tril(diagonal=S - w)
+        logits = logits.masked_fill(~vis, float("-inf"))
+    p = torch.softmax(logits, dim=-1)             # [n_h][w][S]
+    if gqa_map == "block":
+        return p.reshape(n_kv, r * w, S).sum(1)
+    return p.reshape(r, n_kv, w, S).sum((0, 2))
+
+
+@pytest.mark.parametrize("n_h,n_kv,wic", [(8, 2, True), (4, 4, True), (4, 1, False)])
+def test_torch_crosscheck(n_h, n_kv, wic):
+    S, w, d, pool, k_bud = 300, 8, 32, 7, 40
+    q = _rand((1, n_h, w, d), 21)
+    kk = _rand((1, n_kv, S, d), 22)
+    scale = 1 / math.sqrt(d)
+    raw, pooled, raw64 = oracle.score_window(q, kk, w, window_in_cache=wic, n_keep=w, pool=pool,
+                                             want_raw64=True)
+    ref = _torch_raw(q, kk, w, S, wic, scale)
+    assert torch.allclose(torch.from_numpy(raw64[0]), ref, rtol=1e-12, atol=1e-15)
+    if 1 < n_kv < n_h:   # the pin would catch a wrong query-head -> KV-head map
+        wrong = _torch_raw(q, kk, w, S, wic, scale, gqa_map="mod")
+        assert not torch.allclose(torch.from_numpy(raw64[0]), wrong, rtol=1e-6)
+    C = S - w
+    rt = torch.from_numpy(raw[0]).double()
+    mp = F.max_pool1d(rt[:, :C].unsqueeze(0), kernel_size=pool, stride=1, padding=pool // 2)[0]
+    assert torch.equal(mp.float(), torch.from_numpy(pooled[0, :, :C]))
+    assert np.array_equal(pooled[0, :, C:], raw[0, :, C:])
+    idx, count = oracle.select_topk(pooled, k_bud, w)
+    for g in range(n_kv):
+        order = torch.sort(torch.from_numpy(pooled[0, g, :C]), descending=True, stable=True).indices
+        want = sorted(order[:k_bud].tolist()) + list(range(C, S))
+        assert idx[0, g].tolist() == want and count[0, g] == k_bud + w
+    # decode over the compacted cache == attention over the full cache with a keep mask
+    v = _rand((1, n_kv, S, d), 23)
+    qd = _rand((1, n_h, d), 24)
+    kc, _ = oracle.gather(kk, idx, count)
+    vc, _ = oracle.gather(v, idx, count)
+    out, lse = oracle.decode(qd, kc, vc, count)
+    r = n_h // n_kv
+    keep = torch.zeros(n_kv, S, dtype=torch.bool)
+    for g in range(n_kv):
+        keep[g, torch.from_numpy(idx[0, g].astype(np.int64))] = True
+    Kf = torch.from_numpy(kk[0]).double().repeat_interleave(r, 0)
+    Vf = torch.from_numpy(v[0]).double().repeat_interleave(r, 0)
+    ref_out = F.scaled_dot_product_attention(torch.from_numpy(qd[0]).double()[:, None, :], Kf, Vf,
+                                             attn_mask=keep.repeat_interleave(r, 0)[:, None, :])[:, 0]
+    assert torch.allclose(torch.from_numpy(out[0]), ref_out, rtol=1e-12, atol=1e-13)
+
+
+def test_shared_heads_sum_in_float_head_order():
+    rng = np.random.default_rng(31)
+    B, H, S = 2, 5, 64
+    sc = rng.random((B, H, S)).astype(np.float32)
+    idx, count = oracle.select_topk(sc, 10, 4, shared_heads=True)
+    for b in range(B):
+        s = np.zeros(S, np.float32)
+        for g in range(H):
+            s = (s + sc[b, g]).astype(np.float32)
+        order = sorted(range(S - 4), key=lambda t: (-s[t], t))[:10]
+        assert idx[b, 0].tolist() == sorted(order) + list(range(S - 4, S))
+        assert count[b, 0] == 14
+
+
+# ----------------------------------------------------------------------------------
+# Dense equivalence: a budget covering every candidate gives plain attention
+# ----------------------------------------------------------------------------------
+def test_dense_equivalence():
+    n_h, n_kv, S, d, w = 8, 2, 200, 16, 4
+    q = _rand((1, n_h, w, d), 41)
+    kk = _rand((1, n_kv, S, d), 42)
+    v = _rand((1, n_kv, S, d), 43)
+    qd = _rand((1, n_h, d), 44)
+    _, pooled = oracle.score_window(q, kk, w, n_keep=w, pool=7)
+    idx, count = oracle.select_topk(pooled, S, w)      # k >= S - n_keep
+    assert np.all(count == S)
+    assert np.array_equal(idx[0, :, :S], np.tile(np.arange(S), (n_kv, 1)))
+    kc, _ = oracle.gather(kk, idx, count)
+    vc, _ = oracle.gather(v, idx, count)
+    out, lse = oracle.decode(qd, kc, vc, count)
+    r = n_h // n_kv
+    for h in range(n_h):
+        g = h // r
+        y = kk[0, g].astype(np.float64) @ qd[0, h].astype(np.float64) / math.sqrt(d)
+        p = np.exp(y - y.max())
+        want = (p / p.sum()) @ v[0, g].astype(np.float64)
+        assert np.allclose(out[0, h], want, rtol=1e-12, atol=1e-13)
+        assert abs(lse[0, h] - (y.max() + math.log(p.sum()))) < 1e-12
+
+
+# ----------------------------------------------------------------------------------
+# Invariants of selection and gather
+# ----------------------------------------------------------------------------------
+def test_select_gather_invariants():
+    rng = np.random.default_rng(51)
+    B, H, s_max = 3, 4, 500
+    sc = (rng.integers(0, 20, (B, H, s_max)) / 7.0).astype(np.float32)   # many exact ties
+    sl = np.array([500, 37, 3], np.int32)
+    k, n_keep = 60, 16
+    idx, count = oracle.select_topk(sc, k, n_keep, seq_lens=sl)
+    src_pos = rng.permutation(10_000)[: B * s_max].reshape(B, s_max).astype(np.int32)
+    rows = rng.integers(0, 2**16, (B, H, s_max, 8)).astype(np.uint16)
+    dst, pos = oracle.gather(rows, idx, count, src_pos=src_pos)
+    for b in range(B):
+        S = int(sl[b])
+        C = max(0, S - n_keep)
+        for h in range(H):
+            n = int(count[b, h])
+            assert n == min(k, C) + (S - C)
+            sel = idx[b, h, :n]
+            assert np.all(np.diff(sel) > 0) and sel.min(initial=0) >= 0 and sel.max(initial=0) < max(S, 1)
+            assert set(range(C, S)) <= set(sel.tolist())
+            assert np.all(idx[b, h, n:] == -1)
+            # every selected candidate beats (or ties with a higher index than) every unselected one
+            chosen = [t for t in sel if t < C]
+            rest = sorted(set(range(C)) - set(chosen))
+            if chosen and rest:
+                worst = min((-(-sc[b, h, t]), -t) for t in chosen)
+                best_rest = max((sc[b, h, t], -t) for t in rest)
+                assert worst > best_rest
+            assert np.array_equal(pos[b, h, :n], src_pos[b, sel])
+            assert np.all(pos[b, h, n:] == -1)
+            assert np.array_equal(dst[b, h, :n], rows[b, h, sel])
+            assert np.all(dst[b, h, n:] == 0)
+
+
+def test_select_degenerate_cases():
+    sc = np.random.default_rng(61).random((1, 2, 50)).astype(np.float32)
+    # n_keep >= S_b: everything kept, no candidate
+    idx, count = oracle.select_topk(sc, 10, 8, seq_lens=np.array([5], np.int32))
+    assert count.tolist() == [[5, 5]] and idx[0, 0, :5].tolist() == list(range(5))
+    # k = 0: only the window
+    idx, count = oracle.select_topk(sc, 0, 8)
+    assert count.tolist() == [[8, 8]] and idx[0, 1].tolist() == list(range(42, 50))
+    # S_b = 0: nothing
+    idx, count = oracle.select_topk(sc, 10, 8, seq_lens=np.array([0], np.int32))
+    assert count.tolist() == [[0, 0]] and np.all(idx == -1)
+
+
+# ----------------------------------------------------------------------------------
+# Planted heavy hitters are always selected
+# ----------------------------------------------------------------------------------
+def test_planted_heavy_hitters_tiny():
+    wl = synth.WORKLOADS[1]
+    for layer in range(6):
+        inp = synth.layer_inputs(wl, layer=layer)
+        q = synth.to_host_f32(inp["q_win"])
+        k = synth.to_host_f32(inp["k"])
+        _, pooled = oracle.score_window(q, k, wl.w, n_keep=wl.n_keep, pool=wl.pool)
+        idx, count = oracle.select_topk(pooled, wl.k, wl.n_keep)
+        planted = set(inp["planted"][0].tolist())
+        assert len(planted) == 8
+        for g in range(wl.n_kv):
+            assert planted <= set(idx[0, g, : count[0, g]].tolist()), (layer, g)
+
+
+def test_planted_heavy_hitters_bf16_shape():
+    wl = dataclasses.replace(synth.WORKLOADS[2], s_max=6144, k=256)
+    inp = synth.layer_inputs(wl, layer=3)
+    q = synth.to_host_f32(inp["q_win"])
+    k = synth.to_host_f32(inp["k"])
+    planted = set(inp["planted"][0].tolist())
+    assert len(planted) == math.ceil(0.01 * 6144)
+    for pool in (1, 7):
+        _, pooled = oracle.score_window(q, k, wl.w, n_keep=wl.n_keep, pool=pool)
+        idx, count = oracle.select_topk(pooled, wl.k, wl.n_keep)
+        for g in range(wl.n_kv):
+            sel = set(idx[0, g, : count[0, g]].tolist())
+            if pool == 1 or len(planted) * pool <= wl.k:
+                assert planted <= sel, (pool, g)
+            else:
+                assert len(planted & sel) >= wl.k // pool
+
+
+# ----------------------------------------------------------------------------------
+# Decode closed forms
+# ----------------------------------------------------------------------------------
+def test_decode_closed_forms():
+    n_h, n_kv, cap, d = 4, 2, 9, 8
+    q = _rand((1, n_h, d), 71)
+    kc = _rand((1, n_kv, cap, d), 72)
+    vc = _rand((1, n_kv, cap, d), 73)
+    # one token: the output is that V row
+    out, lse = oracle.decode(q, kc, vc, np.array([[1, 1]], np.int32))
+    for h in range(n_h):
+        assert np.allclose(out[0, h], vc[0, h // 2, 0], rtol=0, atol=1e-15)
+        assert abs(lse[0, h] - np.dot(q[0, h].astype(np.float64), kc[0, h // 2, 0]) / math.sqrt(d)) < 1e-12
+    # identical keys, or q = 0: the mean of the V rows
+    same = np.broadcast_to(kc[:, :, :1], kc.shape).copy()
+    out, _ = oracle.decode(q, same, vc, np.array([[6, 9]], np.int32))
+    assert np.allclose(out[0, 0], vc[0, 0, :6].astype(np.float64).mean(0), atol=1e-14)
+    assert np.allclose(out[0, 3], vc[0, 1, :9].astype(np.float64).mean(0), atol=1e-14)
+    out, _ = oracle.decode(np.zeros_like(q), kc, vc, np.array([[9, 9]], np.int32))
+    assert np.allclose(out[0, 2], vc[0, 1].astype(np.float64).mean(0), atol=1e-14)
+    # count 0: output 0, lse -inf
+    out, lse = oracle.decode(q, kc, vc, np.array([[0, 3]], np.int32))
+    assert np.all(out[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
+    # MQA (one KV head) reduces to textbook attention per head
+    out, _ = oracle.decode(q, kc[:, :1], vc[:, :1], np.array([[cap]], np.int32))
+    for h in range(n_h):
+        y = kc[0, 0].astype(np.float64) @ q[0, h].astype(np.float64) / math.sqrt(d)
+        p = np.exp(y - y.max())
+        assert np.allclose(out[0, h], (p / p.sum()) @ vc[0, 0].astype(np.float64), atol=1e-14)
