@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-cache compression hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: for every
+layer of the workload, window scoring -> per-KV-head top-k -> compacting gather ->
+GQA decode attention over the compacted cache.  The default workload is the
+Llama-3-8B-shaped cache (32 layers, S = 32768, 32 query / 8 KV heads, d_h = 128,
+bf16, w = 32, pool 7, k = 2048 + 32 kept) with every layer's K/V resident in HBM.
+
+Prints one JSON line.  `value` is whole-step algorithmic HBM traffic per second
+(GB/s); the per-step breakdown, the decode-attention GB/s over the compacted cache,
+the roofline of the dominant call and the CPU-oracle baseline ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "compacted decode-attn HBM GB/s + score/select/gather µs per layer, % roofline"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_32k")
+    ap.add_argument("--layers", type=int, default=0, help="0: all layers of the workload")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (for scaling PMC byte counters)")
+    return ap.parse_args()
+
+
+def layer_bytes(wl, S, cap):
+    """Algorithmic bytes per layer and step (what the method itself must move)."""
+    b = wl.elem_bytes
+    units = wl.batch * wl.n_kv
+    R = wl.group * wl.w
+    r = wl.group
+    score = units * (S * wl.d_h * b + R * wl.d_h * b + 2 * 4 * S)          # K once, Q, raw + pooled out
+    select = units * ((S - wl.n_keep) * 4 + cap * 4 + 4)                    # pooled in, idx + count out
+    gather = units * (2 * 2 * cap * wl.d_h * b + 4 * cap + 4 * cap)         # K,V rows read+write, idx, pos
+    decode = units * (2 * cap * wl.d_h * b + 2 * r * wl.d_h * b + 4)        # Kc,Vc once, q in, out
+    flops_score = units * 2 * R * S * wl.d_h                                # one Q K^T
+    return dict(score=score, select=select, gather=gather, decode=decode, flops_score=flops_score)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU mode "
+              "(requested --gpus %d)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import oracle
+    from sparse_decode_amd import kvc, synth
+    from sparse_decode_amd.pipeline import LayerPath
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvc.lib()
+    wl = synth.by_name(args.workload)
+    L = args.layers or wl.layers
+    dev = torch.device("cuda")
+    print("[bench] generating %s: %d layers" % (wl.name, L), file=sys.stderr, flush=True)
+    layers = []
+    for l in range(L):
+        inp = synth.layer_inputs(wl, l, device=dev)
+        inp["seq_lens_dev"] = torch.from_numpy(inp["seq_lens"]).to(dev)
+        layers.append(inp)
+    torch.cuda.synchronize()
+    path = LayerPath(wl, device=dev)        # one set of output buffers, reused by every layer
+    S, cap = wl.s_max, path.cap
+    mean_S = float(np.mean(layers[0]["seq_lens"]))
+    by = layer_bytes(wl, mean_S, cap)
+    step_bytes = L * (by["score"] + by["select"] + by["gather"] + by["decode"])
+
+    def one_step():
+        for inp in layers:
+            path.run(inp["q_win"], inp["k"], inp["v"], inp["q_dec"], inp["seq_lens_dev"])
+
+    # ---------------------------------------------------------------- timed region 1: whole steps
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        one_step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print("[bench] %d steps: %.3f ms/step (wall %.3f s)" % (args.steps, ms_per_step, wall), file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- timed region 2: per-call events
+    names = ("score", "select", "gather", "decode")
+    acc = {n: 0.0 for n in names}
+    n_ev = 0
+    for rep in range(args.steps):
+        evs = []
+        for inp in layers:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e[0].record()
+            path.score(inp["q_win"], inp["k"], inp["seq_lens_dev"])
+            e[1].record()
+            path.select(inp["seq_lens_dev"])
+            e[2].record()
+            path.gather(inp["k"], inp["v"])
+            e[3].record()
+            path.decode(inp["q_dec"])
+            e[4].record()
+            evs.append(e)
+        torch.cuda.synchronize()
+        for e in evs:
+            for i, n in enumerate(names):
+                acc[n] += e[i].elapsed_time(e[i + 1])
+        n_ev += len(evs)
+    us = {n: 1000.0 * acc[n] / n_ev for n in names}
+
+    # ---------------------------------------------------------------- decode-only loop over all layers
+    # A decode step of the model reads every layer's compacted cache in turn; give each
+    # layer its own compacted buffers so the working set is the model's, not one layer's.
+    kcs = []
+    for inp in layers:
+        path.score(inp["q_win"], inp["k"], inp["seq_lens_dev"])
+        path.select(inp["seq_lens_dev"])
+        path.gather(inp["k"], inp["v"])
+        kcs.append((path.kc.clone(), path.vc.clone(), path.count.clone(), inp["q_dec"]))
+    torch.cuda.synchronize()
+    for _ in range(2):
+        for kc, vc, cnt, q in kcs:
+            kvc.decode_attn(q, kc, vc, cnt, out=path.out, lse=path.lse, ws=path.ws_decode)
+    torch.cuda.synchronize()
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(args.steps):
+        for kc, vc, cnt, q in kcs:
+            kvc.decode_attn(q, kc, vc, cnt, out=path.out, lse=path.lse, ws=path.ws_decode)
+    d1.record()
+    torch.cuda.synchronize()
+    decode_only_us = 1000.0 * d0.elapsed_time(d1) / (args.steps * L)
+    del kcs
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        bcp = torch.empty_like(a)
+        bcp.copy_(a)
+        torch.cuda.synchronize()
+        del a, bcp
+
+    # ---------------------------------------------------------------- CPU oracle baseline (sampled)
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = oracle.set_threads(0)
+        t_cpu, done = 0.0, 0
+        for inp in layers:
+            q = synth.to_host_f32(inp["q_win"])
+            k = synth.to_host_f32(inp["k"])
+            v = synth.to_host_f32(inp["v"])
+            qd = synth.to_host_f32(inp["q_dec"])
+            sl = inp["seq_lens"]
+            c0 = time.perf_counter()
+            _, pooled = oracle.score_window(q, k, wl.w, seq_lens=sl, window_in_cache=wl.window_in_cache,
+                                            n_keep=wl.n_keep, pool=wl.pool)
+            idx, cnt = oracle.select_topk(pooled, wl.k, wl.n_keep, seq_lens=sl)
+            kc, _ = oracle.gather(k, idx, cnt)
+            vc, _ = oracle.gather(v, idx, cnt)
+            oracle.decode(qd, kc, vc, cnt)
+            t_cpu += time.perf_counter() - c0
+            done += 1
+            if t_cpu >= args.cpu_seconds:
+                break
+        lb = by["score"] + by["select"] + by["gather"] + by["decode"]
+        cpu = {"value": round(done * lb / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": "%d of %d layers of %s, all four steps, plain fp64 C oracle (OpenMP), %.1f s" % (
+                   done, L, wl.name, t_cpu),
+               "ms_per_layer": round(1000.0 * t_cpu / done, 2)}
+
+    gbps = {n: by[n] / (us[n] * 1e-6) / 1e9 for n in names}
+    dominant = max(names, key=lambda n: us[n])
+    roof = {"bound": "hbm", "achieved": round(gbps[dominant], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "kvc_%s (one call)" % (
+                {"score": "score_window", "select": "select_topk", "gather": "gather_compact",
+                 "decode": "decode_attn"}[dominant]),
+            "bytes_per_launch": int(by[dominant]), "us_per_launch": round(us[dominant], 3)}
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    decode_only_gbps = by["decode"] / (decode_only_us * 1e-6) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V with planted heavy hitters; no model weights)",
+        "config": {"workload": wl.name, "layers": L, "batch": wl.batch, "seq_len": S, "n_h": wl.n_h,
+                   "n_kv": wl.n_kv, "d_h": wl.d_h, "w": wl.w, "pool": wl.pool, "k": wl.k, "n_keep": wl.n_keep},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_layer_us": {n: round(us[n], 3) for n in names},
+        "per_layer_GBps": {n: round(gbps[n], 1) for n in names},
+        "per_layer_hbm_frac": {n: round(gbps[n] / HBM_PEAK_GBPS, 4) for n in names},
+        "decode_attn_GBps_all_layers": round(decode_only_gbps, 1),
+        "decode_attn_us_all_layers": round(decode_only_us, 3),
+        "score_mfma_frac_algorithmic": round(by["flops_score"] / (us["score"] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "wall_s_timed_region": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

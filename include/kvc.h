@@ -1,0 +1,215 @@
+/*
+ * kvc.h -- C ABI of the MI355X (gfx950) KV-cache compression hot path.
+ *
+ * Four steps shared by observation-window KV eviction (SnapKV-style), FastKV's
+ * token-selective propagation and per-step KV retrieval (FreeKV):
+ *
+ *   kvc_score_window    saliency of every cached token from the attention of the
+ *                       last w queries, summed over the window and over the query
+ *                       heads of each GQA group, then max-pooled in 1-D
+ *   kvc_select_topk     per-KV-head top-k under a retention budget, plus the
+ *                       trailing window, lower index first on equal scores
+ *   kvc_gather_compact  copy of the kept rows into a compacted cache that keeps
+ *                       the original positions
+ *   kvc_decode_attn     GQA decode attention of one query per head over the
+ *                       compacted cache
+ *
+ * Pages these calls follow (cited by title and section):
+ *   [FastKV]   "FastKV: Decoupling of Context Reduction and KV Cache Compression for
+ *              Prefill-Decoding Acceleration", section 2.A (saliency from the recent
+ *              window's attention; the selected tokens and the sliding-window tokens
+ *              propagate) and section 2.B (TSP rate and KV retention rate are two
+ *              independent budgets).
+ *   [Tutorial] "Variantes de l'attention et compression du cache KV", sections
+ *              "MHA et GQA" (L, S, n_h, n_kv, d_h, b; query heads sharing a KV head),
+ *              "Quand la reutilisation est-elle exacte ?" (causal alignment of rows
+ *              appended after S cached tokens; keep original positions after
+ *              eviction) and "Compresser un cache existant" (observation-window
+ *              scoring, keep a subset of past keys and values).
+ *   [FreeKV]   "FreeKV: Boosting KV Cache Retrieval for Efficient LLM Inference",
+ *              technical summary section 2.A (select a subset with the current
+ *              query, then attend over it, at every decode step).
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates no memory; scratch space is the caller's `ws` buffer, sized by the
+ *     matching *_workspace() query.  Workspaces need no initialisation and may be
+ *     reused freely between calls that are ordered on one stream.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Nothing blocks the host.  Calls sharing a workspace must
+ *     be ordered on one stream.
+ *   - Layouts are head-major, contiguous, row-major, exactly as written below.
+ *     bf16 means the 16-bit bfloat format stored as uint16 bit patterns.
+ *   - Every precondition that the host can check is checked before any HIP call;
+ *     on failure the call returns KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED or
+ *     KVC_ERR_WORKSPACE and launches nothing.  A failed launch returns KVC_ERR_HIP.
+ *   - Device-resident sequence lengths are a caller contract: kernels clamp each
+ *     to [0, s_max].
+ *   - No C++ exception crosses this interface.  The library keeps no state
+ *     between calls apart from a cache of device attributes.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_ERR_INVALID_ARG = 1,  /* a null pointer, a size out of range, inconsistent shapes */
+    KVC_ERR_UNSUPPORTED = 2,  /* a valid shape or dtype this build has no kernel for      */
+    KVC_ERR_WORKSPACE = 3,    /* ws is NULL or smaller than the *_workspace() size         */
+    KVC_ERR_HIP = 4           /* the HIP runtime reported an error (no device, launch)    */
+} kvc_status;
+
+typedef enum kvc_dtype {
+    KVC_F32 = 0,              /* 4-byte IEEE float                                        */
+    KVC_BF16 = 1              /* 2-byte bfloat16 (uint16 bit patterns), fp32 arithmetic   */
+} kvc_dtype;
+
+/*
+ * Problem dimensions (Tutorial, "MHA et GQA": S cached tokens, n_h query heads,
+ * n_kv KV heads, head width d_h, b bytes per element).  Layers are not a
+ * dimension: call once per layer, or fold independent layers into `batch`.
+ */
+typedef struct kvc_dims {
+    int32_t batch;            /* B >= 1 sequences (or sequence-layer pairs)                 */
+    int32_t s_max;            /* S >= 1: token capacity, the leading token dim of K/V/scores */
+    const int32_t *seq_lens;  /* device int32[B] cached lengths S_b; NULL: every S_b = s_max */
+    int32_t n_h;              /* query heads, a multiple of n_kv                             */
+    int32_t n_kv;             /* KV heads; query head h reads KV head h / (n_h / n_kv)       */
+    int32_t d_h;              /* head width: 64 or 128                                       */
+    int32_t dtype;            /* kvc_dtype of Q, K, V and the decode output                  */
+} kvc_dims;
+
+/* kvc_select_topk flag: one selection per sequence from the float sum of the
+ * pooled scores over all KV heads, added in head order (FastKV 2.A: the tokens
+ * chosen at the propagation layer are the same for every head). */
+#define KVC_SELECT_SHARED_HEADS 1
+
+/* kvc_score_window flag: use the portable VALU kernels (any R, d_h, dtype) instead
+ * of the bf16 MFMA kernels.  Results agree to the same tolerance; meant for tests. */
+#define KVC_SCORE_GENERIC 1
+
+int32_t kvc_abi_version(void);
+const char *kvc_status_str(kvc_status status);
+
+/*
+ * kvc_score_window -- observation-window saliency (FastKV 2.A; Tutorial,
+ * "Compresser un cache existant"), R = (n_h/n_kv) * w rows per KV head.
+ *
+ * For sequence b and KV head g, with r = n_h/n_kv, every query head h in
+ * [g*r, g*r + r) and every window row i < w:
+ *   x[h,i,t] = scale * <q_win[b][h][i], k[b][g][t]>            for visible t < S_b
+ *   raw[b][g][t] = sum over (h, i) of exp(x[h,i,t] - M[h,i]) / L[h,i]
+ * with M, L the max and the sum of exp(x - M) over the visible t of that row.
+ * Visibility (Tutorial, "Quand la reutilisation est-elle exacte ?"): when
+ * window_in_cache != 0 the window rows are the last w cached tokens, so row i sees
+ * t <= S_b - w + i; otherwise (a new query that is not in the cache) every
+ * t < S_b is visible.  A row that sees no key adds nothing.
+ * Pooling over the candidate region C = [0, max(0, S_b - n_keep)):
+ *   pooled[b][g][t] = max of raw[b][g][u] over u in [t - p/2, t + p/2] intersect C, t in C
+ *   pooled[b][g][t] = raw[b][g][t] for t in [max(0, S_b - n_keep), S_b)
+ *   raw and pooled are 0 for t in [S_b, s_max).
+ *
+ * q_win      [B][n_h][w][d_h] dtype      window queries
+ * k          [B][n_kv][s_max][d_h] dtype  keys
+ * w          1 <= w <= 1024, and (n_h/n_kv)*w <= 1024
+ * pool_kernel odd, 1 <= p <= 63 (1: no pooling)
+ * scale      > 0; 0 means 1/sqrt(d_h)
+ * raw        [B][n_kv][s_max] float, written (required)
+ * pooled     [B][n_kv][s_max] float, written (required)
+ * flags      0 or KVC_SCORE_GENERIC
+ * Arithmetic: fp32 logits (bf16 products are exact), fp32 exp2-based softmax with
+ * the row sums accumulated per lane and merged in double; raw agrees with a
+ * double-precision evaluation to about 1e-6 relative.  Probabilities below the
+ * fp32 normal range are flushed to zero.
+ */
+size_t kvc_score_window_workspace(const kvc_dims *dims, int32_t w, int32_t flags);
+kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void *k, int32_t w,
+                            int32_t window_in_cache, int32_t n_keep, int32_t pool_kernel,
+                            float scale, float *raw, float *pooled, int32_t flags,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kvc_select_topk -- per-KV-head selection under the retention budget (FastKV 2.B),
+ * plus the always-kept trailing tokens (FastKV 2.A), in ascending original order.
+ *
+ * For each unit (b, g) (or b alone with KVC_SELECT_SHARED_HEADS, score = float sum
+ * over g in head order), with C = max(0, S_b - n_keep) candidates [0, C):
+ *   k_eff = min(k, C); the first k_eff candidates in the total order
+ *   (score descending, index ascending) are selected;
+ *   idx[0 .. k_eff) = those indices ascending; idx[k_eff ..) = C, C+1, ..., S_b - 1;
+ *   count = k_eff + (S_b - C); idx entries past count are -1.
+ *
+ * scores [B][n_kv][s_max] float (the pooled output of kvc_score_window); must not
+ *        hold NaN; -0.0 and +0.0 are equal
+ * k, n_keep  >= 0, cap = k + n_keep >= 1
+ * idx    [B][H][k + n_keep] int32, H = n_kv, or 1 with KVC_SELECT_SHARED_HEADS
+ * count  [B][H] int32
+ * The result is unique (ties are ordered by index) and bit-reproducible.
+ */
+size_t kvc_select_topk_workspace(const kvc_dims *dims, int32_t k, int32_t n_keep, int32_t flags);
+kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores, int32_t k, int32_t n_keep,
+                           int32_t flags, int32_t *idx, int32_t *count,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kvc_gather_compact -- compacted cache that keeps original positions (Tutorial,
+ * "Quand la reutilisation est-elle exacte ?"; FreeKV 2.B on keeping the GPU copy in
+ * one layout).  A byte copy: any row type works.
+ *
+ * For unit u = (b, h), h < heads, and j < count[b][h'] (clamped to [0, cap]):
+ *   dst0[b][h][j] = src0[b][h][idx[b][h'][j]]    (row_bytes bytes)
+ *   dst1[b][h][j] = src1[b][h][idx[b][h'][j]]    (when src1/dst1 are given)
+ *   pos_out[b][h][j] = src_pos[b][idx[b][h'][j]]  (idx itself when src_pos is NULL)
+ * where h' = h when idx_heads == heads and h' = 0 when idx_heads == 1 (one list
+ * shared by every head).  Rows j >= count are not written; their pos_out is -1.
+ * An index outside [0, s_max) copies nothing and gets pos_out -1.
+ *
+ * src0, src1   [B][heads][s_max][row_bytes]; src1 may be NULL (then dst1 must be NULL)
+ * src_pos      [B][s_max] int32 or NULL
+ * idx          [B][idx_heads][cap] int32; count [B][idx_heads] int32
+ * dst0, dst1   [B][heads][cap][row_bytes]
+ * pos_out      [B][heads][cap] int32 or NULL
+ * row_bytes    a multiple of 16; row_bytes/16 a power of two or a multiple of 256;
+ *              every row pointer 16-byte aligned
+ */
+kvc_status kvc_gather_compact(int32_t batch, int32_t heads, int32_t s_max, int32_t row_bytes,
+                              const void *src0, const void *src1, const int32_t *src_pos,
+                              const int32_t *idx, const int32_t *count, int32_t idx_heads,
+                              int32_t cap, void *dst0, void *dst1, int32_t *pos_out, void *stream);
+
+/*
+ * kvc_decode_attn -- GQA decode attention over the compacted cache (FreeKV 2.A:
+ * attend over the selected subset; Tutorial, "MHA et GQA").
+ *
+ * For each (b, h), g = h / (n_h/n_kv), n = count[b][g] clamped to [0, cap]:
+ *   y_t = scale * <q[b][h], kc[b][g][t]>, t < n
+ *   out[b][h] = sum_t softmax(y)_t * vc[b][g][t]     (count 0: zeros)
+ *   lse[b][h] = max_t y_t + log(sum_t exp(y_t - max_t y_t))   (count 0: -inf)
+ *
+ * dims       batch, n_h, n_kv, d_h and dtype are used (s_max and seq_lens are not)
+ * q          [B][n_h][d_h] dtype
+ * kc, vc     [B][n_kv][cap][d_h] dtype
+ * count      [B][n_kv] int32
+ * out        [B][n_h][d_h] dtype (bf16: round to nearest even)
+ * lse        [B][n_h] float or NULL
+ * Splits over t are merged in a fixed order: results are bit-reproducible.
+ */
+size_t kvc_decode_attn_workspace(const kvc_dims *dims, int32_t cap);
+kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const void *kc, const void *vc,
+                           const int32_t *count, int32_t cap, float scale, void *out, float *lse,
+                           void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,117 @@
+// gather.hip -- compacting gather of kept cache rows that keeps their original
+// positions (Tutorial "Variantes de l'attention et compression du cache KV",
+// section "Quand la reutilisation est-elle exacte ?": keep the original position
+// indices after eviction).
+//
+// Pure data movement, bound by HBM bandwidth: every kept row is read once and
+// written once with 16-byte vector accesses.  A row of d_h = 128 bf16 is 256 B =
+// 16 lanes; a 4096-wide hidden-state row is 8 KiB = 512 lanes.  Each thread keeps
+// several independent 16-byte loads in flight before it stores.
+#include "kvc_device.h"
+#include "kvc_launch.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kGatherThreads = 256;
+constexpr int kGatherUnroll = 4;
+
+// Work-group (blockIdx.x, blockIdx.y) copies rows [blockIdx.x * rows_per_block, ...)
+// of unit blockIdx.y = b * heads + h.  tpr threads share one row (a power of two
+// <= 256); a row wider than 256 vectors is walked in strides of 256.
+__global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
+    const u32x4 *__restrict__ src0, const u32x4 *__restrict__ src1,
+    const int32_t *__restrict__ src_pos, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ count, int heads, int idx_heads, int s_max, int vpr, int tpr_log2,
+    int cap, int rows_per_block, u32x4 *__restrict__ dst0, u32x4 *__restrict__ dst1,
+    int32_t *__restrict__ pos_out)
+{
+    const int unit = blockIdx.y;
+    const int b = unit / heads;
+    const int h = unit - b * heads;
+    const int list = b * idx_heads + (idx_heads == 1 ? 0 : h);
+    int n = count[list];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    const int r0 = blockIdx.x * rows_per_block;
+    int r1 = r0 + rows_per_block;
+    r1 = r1 > cap ? cap : r1;
+    const int32_t *lidx = idx + (size_t)list * cap;
+
+    if (pos_out) {
+        for (int j = r0 + threadIdx.x; j < r1; j += kGatherThreads) {
+            int p = -1;
+            if (j < n) {
+                const int t = lidx[j];
+                if (t >= 0 && t < s_max) p = src_pos ? src_pos[(size_t)b * s_max + t] : t;
+            }
+            pos_out[(size_t)unit * cap + j] = p;
+        }
+    }
+    const int rend = r1 < n ? r1 : n;
+    if (rend <= r0) return;
+
+    const int tpr = 1 << tpr_log2;
+    const int rows_per_iter = kGatherThreads >> tpr_log2;
+    const int sub = threadIdx.x >> tpr_log2;          // row offset within one iteration
+    const int col0 = threadIdx.x & (tpr - 1);
+    const size_t src_unit = (size_t)unit * s_max * vpr;
+    const size_t dst_unit = (size_t)unit * cap * vpr;
+
+    for (int j0 = r0 + sub; j0 < rend; j0 += rows_per_iter * kGatherUnroll) {
+        int t[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int j = j0 + u * rows_per_iter;
+            int tt = j < rend ? lidx[j] : -1;
+            t[u] = (tt >= 0 && tt < s_max) ? tt : -1;
+        }
+        for (int c = col0; c < vpr; c += tpr) {
+            u32x4 a[kGatherUnroll], bb[kGatherUnroll];
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                if (t[u] >= 0) {
+                    a[u] = ld_stream(src0 + src_unit + (size_t)t[u] * vpr + c);
+                    if (src1) bb[u] = ld_stream(src1 + src_unit + (size_t)t[u] * vpr + c);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                if (t[u] >= 0) {
+                    const size_t o = dst_unit + (size_t)(j0 + u * rows_per_iter) * vpr + c;
+                    dst0[o] = a[u];
+                    if (src1) dst1[o] = bb[u];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather(int batch, int heads, int s_max, int row_bytes, const void *src0,
+                         const void *src1, const int32_t *src_pos, const int32_t *idx,
+                         const int32_t *count, int idx_heads, int cap, void *dst0, void *dst1,
+                         int32_t *pos_out, const DeviceInfo &dev, hipStream_t stream)
+{
+    const int vpr = row_bytes / 16;
+    int tpr_log2 = 0;
+    while ((1 << (tpr_log2 + 1)) <= vpr && (1 << (tpr_log2 + 1)) <= kGatherThreads) ++tpr_log2;
+    const int rows_per_iter = kGatherThreads >> tpr_log2;
+    const long units = (long)batch * heads;
+    // Enough work-groups to cover every CU several times; at least one full
+    // unrolled iteration of rows per group.
+    const long want_blocks = 4L * dev.cus;
+    long rpb = (long)cap * units / (want_blocks > 0 ? want_blocks : 1);
+    const long min_rows = (long)rows_per_iter * kGatherUnroll;
+    if (rpb < min_rows) rpb = min_rows;
+    rpb = ((rpb + min_rows - 1) / min_rows) * min_rows;
+    if (rpb > cap) rpb = cap;
+    if (rpb < 1) rpb = 1;
+    dim3 grid((unsigned)((cap + rpb - 1) / rpb), (unsigned)units);
+    hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(kGatherThreads), 0, stream,
+                       (const u32x4 *)src0, (const u32x4 *)src1, src_pos, idx, count, heads, idx_heads,
+                       s_max, vpr, tpr_log2, cap, (int)rpb, (u32x4 *)dst0, (u32x4 *)dst1, pos_out);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,82 @@
+// kvc_device.h -- device-side helpers shared by the gfx950 kernels of the KV-cache
+// compression path: bf16 conversion, 64-lane shuffles and work-group scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int kWave = 64;
+
+// Native 16-byte vector (HIP's uint4 is a struct; clang builtins want a vector type).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load hinted as streamed once (non-temporal).
+__device__ __forceinline__ u32x4 ld_stream(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+
+// bf16 <-> fp32.  Widening is exact (the bf16 bits are the high half of the float).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round to nearest, ties to even; a NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+__device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+__device__ __forceinline__ int clamp_len(const int32_t *seq_lens, int b, int s_max)
+{
+    int s = seq_lens ? seq_lens[b] : s_max;
+    return s < 0 ? 0 : (s > s_max ? s_max : s);
+}
+
+// Inclusive prefix sum across one 64-lane wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Exclusive prefix sum across the work-group (blockDim.x a multiple of 64, at most
+// 1024).  `scratch` holds at least 17 ints of LDS.  Returns the exclusive prefix and
+// writes the group total to *total.  Contains barriers: call from every thread.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *total)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    int inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) scratch[wid] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < nw; ++i) {
+            int t = scratch[i];
+            scratch[i] = run;
+            run += t;
+        }
+        scratch[16] = run;
+    }
+    __syncthreads();
+    int res = scratch[wid] + inc - v;
+    *total = scratch[16];
+    __syncthreads();
+    return res;
+}
+
+}  // namespace kvc

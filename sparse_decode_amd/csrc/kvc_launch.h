@@ -1,0 +1,61 @@
+// kvc_launch.h -- host-side launchers of the gfx950 kernels.  Arguments reaching
+// these functions have been validated by the C ABI layer (kvc_api.hip); each
+// launcher only sizes grids and enqueues kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvc {
+
+struct DeviceInfo {
+    int cus = 256;              // compute units
+    int max_lds_per_block = 65536;
+};
+// Attributes of the current device (cached per device ordinal).
+hipError_t device_info(DeviceInfo *out);
+
+// ---- gather -------------------------------------------------------------------------
+hipError_t launch_gather(int batch, int heads, int s_max, int row_bytes, const void *src0,
+                         const void *src1, const int32_t *src_pos, const int32_t *idx,
+                         const int32_t *count, int idx_heads, int cap, void *dst0, void *dst1,
+                         int32_t *pos_out, const DeviceInfo &dev, hipStream_t stream);
+
+// ---- decode -------------------------------------------------------------------------
+struct DecodePlan {
+    int n_splits = 1;
+    int split_tokens = 0;
+    int head_chunk = 1;        // query heads handled per work-group
+    int head_chunks = 1;
+    size_t ws_bytes = 0;
+};
+DecodePlan plan_decode(int batch, int n_h, int n_kv, int d_h, int cap, int cus);
+hipError_t launch_decode(int batch, int n_h, int n_kv, int d_h, bool bf16, const void *q,
+                         const void *kc, const void *vc, const int32_t *count, int cap, float scale,
+                         void *out, float *lse, void *ws, const DecodePlan &plan, hipStream_t stream);
+
+// ---- select -------------------------------------------------------------------------
+size_t select_ws_bytes(int batch, int n_kv, int s_max, bool shared);
+hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
+                         int k, int n_keep, bool shared, int32_t *idx, int32_t *count, void *ws,
+                         const DeviceInfo &dev, hipStream_t stream);
+
+// ---- score --------------------------------------------------------------------------
+struct ScorePlan {
+    bool mfma = false;
+    int R = 0;                 // rows per KV head: (n_h / n_kv) * w
+    int tiles_per_wave = 1;    // MFMA path: 32-token tiles per wave per chunk
+    int chunk_tokens = 0;      // MFMA path: tokens per work-group
+    int n_chunks = 0;
+    int group_units = 0;       // KV-head units per pass-1/pass-2 launch pair
+    size_t ws_bytes = 0;
+};
+ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16, int w,
+                     bool generic, int cus);
+hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, int n_kv, int d_h,
+                        bool bf16, const void *q_win, const void *k, int w, bool window_in_cache,
+                        int n_keep, int pool, float scale, float *raw, float *pooled, void *ws,
+                        const ScorePlan &plan, hipStream_t stream);
+
+}  // namespace kvc

@@ -1,0 +1,244 @@
+"""Thin ctypes binding of ``libkvc.so`` (include/kvc.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module only turns
+torch tensors into device pointers, allocates outputs and workspaces when the
+caller does not pass them, and raises on a non-OK status.  There is no fallback:
+if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libkvc.so")
+
+KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(5)
+KVC_F32, KVC_BF16 = 0, 1
+KVC_SELECT_SHARED_HEADS = 1
+KVC_SCORE_GENERIC = 1
+
+EXPORTED = (
+    "kvc_abi_version", "kvc_status_str",
+    "kvc_score_window_workspace", "kvc_score_window",
+    "kvc_select_topk_workspace", "kvc_select_topk",
+    "kvc_gather_compact",
+    "kvc_decode_attn_workspace", "kvc_decode_attn",
+)
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("s_max", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+                ("n_h", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("d_h", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_str(status), status))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """Loads libkvc.so and declares its signatures; raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libkvc.so is not built (%s); run __graft_entry__.build() first" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            P, I, Z, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+            D = ctypes.POINTER(Dims)
+            sig = {
+                "kvc_abi_version": (I, []),
+                "kvc_status_str": (ctypes.c_char_p, [I]),
+                "kvc_score_window_workspace": (Z, [D, I, I]),
+                "kvc_score_window": (I, [D, P, P, I, I, I, I, F, P, P, I, P, Z, P]),
+                "kvc_select_topk_workspace": (Z, [D, I, I, I]),
+                "kvc_select_topk": (I, [D, P, I, I, I, P, P, P, Z, P]),
+                "kvc_gather_compact": (I, [I, I, I, I, P, P, P, P, P, I, I, P, P, P, P]),
+                "kvc_decode_attn_workspace": (Z, [D, I]),
+                "kvc_decode_attn": (I, [D, P, P, P, P, I, F, P, P, P, Z, P]),
+            }
+            for name, (res, args) in sig.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().kvc_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != KVC_OK:
+        raise KvcError(status, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KVC_BF16
+    if t.dtype == torch.float32:
+        return KVC_F32
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _seq_lens(seq_lens, device):
+    if seq_lens is None:
+        return None
+    if isinstance(seq_lens, torch.Tensor) and seq_lens.is_cuda:
+        if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be a contiguous int32 device tensor")
+        return seq_lens
+    return torch.as_tensor(seq_lens, dtype=torch.int32).to(device)
+
+
+def make_dims(batch, s_max, n_h, n_kv, d_h, dtype_code, seq_lens=None) -> Dims:
+    return Dims(int(batch), int(s_max), _ptr(seq_lens), int(n_h), int(n_kv), int(d_h), int(dtype_code))
+
+
+# ------------------------------------------------------------------------------- score
+
+def score_window_workspace(dims: Dims, w: int, flags: int = 0) -> int:
+    return int(lib().kvc_score_window_workspace(ctypes.byref(dims), int(w), int(flags)))
+
+
+def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=None, pool=1, scale=0.0,
+                 generic=False, raw=None, pooled=None, ws=None, stream=None):
+    """kvc_score_window: q_win [B][n_h][w][d_h], k [B][n_kv][s_max][d_h] -> (raw, pooled) fp32."""
+    _dev(q_win, "q_win")
+    _dev(k, "k")
+    B, n_h, w_, d_h = q_win.shape
+    _, n_kv, s_max, _ = k.shape
+    if w_ != w or k.dtype != q_win.dtype:
+        raise ValueError("q_win/k shapes or dtypes disagree")
+    sl = _seq_lens(seq_lens, k.device)
+    dims = make_dims(B, s_max, n_h, n_kv, d_h, _dtype_code(k), sl)
+    flags = KVC_SCORE_GENERIC if generic else 0
+    if n_keep is None:
+        n_keep = w
+    if raw is None:
+        raw = torch.empty((B, n_kv, s_max), dtype=torch.float32, device=k.device)
+    if pooled is None:
+        pooled = torch.empty((B, n_kv, s_max), dtype=torch.float32, device=k.device)
+    need = score_window_workspace(dims, w, flags)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+    st = lib().kvc_score_window(ctypes.byref(dims), _ptr(q_win), _ptr(k), int(w), int(bool(window_in_cache)),
+                                int(n_keep), int(pool), float(scale), _ptr(raw), _ptr(pooled), flags,
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kvc_score_window")
+    return raw, pooled
+
+
+# ------------------------------------------------------------------------------ select
+
+def select_topk_workspace(dims: Dims, k: int, n_keep: int, flags: int = 0) -> int:
+    return int(lib().kvc_select_topk_workspace(ctypes.byref(dims), int(k), int(n_keep), int(flags)))
+
+
+def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=None, count=None, ws=None,
+                stream=None):
+    """kvc_select_topk: scores [B][n_kv][s_max] fp32 -> (idx [B][H][k+n_keep], count [B][H]) int32."""
+    _dev(scores, "scores")
+    if scores.dtype != torch.float32:
+        raise TypeError("scores must be float32")
+    B, n_kv, s_max = scores.shape
+    sl = _seq_lens(seq_lens, scores.device)
+    dims = make_dims(B, s_max, n_kv, n_kv, 128, KVC_F32, sl)
+    flags = KVC_SELECT_SHARED_HEADS if shared_heads else 0
+    H = 1 if shared_heads else n_kv
+    cap = k + n_keep
+    if idx is None:
+        idx = torch.empty((B, H, cap), dtype=torch.int32, device=scores.device)
+    if count is None:
+        count = torch.empty((B, H), dtype=torch.int32, device=scores.device)
+    need = select_topk_workspace(dims, k, n_keep, flags)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    st = lib().kvc_select_topk(ctypes.byref(dims), _ptr(scores), int(k), int(n_keep), flags, _ptr(idx),
+                               _ptr(count), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream))
+    _check(st, "kvc_select_topk")
+    return idx, count
+
+
+# ------------------------------------------------------------------------------ gather
+
+def gather_compact(src0, idx, count, *, src1=None, src_pos=None, dst0=None, dst1=None, pos_out=None,
+                   want_pos=True, stream=None):
+    """kvc_gather_compact: src [B][heads][s_max][...] -> dst [B][heads][cap][...] (+ pos_out)."""
+    _dev(src0, "src0")
+    _dev(idx, "idx")
+    _dev(count, "count")
+    B, heads, s_max = src0.shape[:3]
+    row_shape = tuple(src0.shape[3:])
+    row_bytes = src0.element_size()
+    for s in row_shape:
+        row_bytes *= s
+    idx_heads, cap = idx.shape[1], idx.shape[2]
+    if dst0 is None:
+        dst0 = torch.empty((B, heads, cap) + row_shape, dtype=src0.dtype, device=src0.device)
+    if src1 is not None and dst1 is None:
+        dst1 = torch.empty_like(dst0)
+    if want_pos and pos_out is None:
+        pos_out = torch.empty((B, heads, cap), dtype=torch.int32, device=src0.device)
+    st = lib().kvc_gather_compact(int(B), int(heads), int(s_max), int(row_bytes), _ptr(src0), _ptr(src1),
+                                  _ptr(src_pos), _ptr(idx), _ptr(count), int(idx_heads), int(cap), _ptr(dst0),
+                                  _ptr(dst1), _ptr(pos_out), _stream(stream))
+    _check(st, "kvc_gather_compact")
+    return dst0, dst1, pos_out
+
+
+# ------------------------------------------------------------------------------ decode
+
+def decode_attn_workspace(dims: Dims, cap: int) -> int:
+    return int(lib().kvc_decode_attn_workspace(ctypes.byref(dims), int(cap)))
+
+
+def decode_attn(q, kc, vc, count, *, scale=0.0, out=None, lse=None, want_lse=True, ws=None, stream=None):
+    """kvc_decode_attn: q [B][n_h][d_h], kc/vc [B][n_kv][cap][d_h] -> (out [B][n_h][d_h], lse [B][n_h])."""
+    for t, nm in ((q, "q"), (kc, "kc"), (vc, "vc"), (count, "count")):
+        _dev(t, nm)
+    B, n_h, d_h = q.shape
+    _, n_kv, cap, _ = kc.shape
+    dims = make_dims(B, 1, n_h, n_kv, d_h, _dtype_code(q))
+    if out is None:
+        out = torch.empty((B, n_h, d_h), dtype=q.dtype, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, n_h), dtype=torch.float32, device=q.device)
+    need = decode_attn_workspace(dims, cap)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib().kvc_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(kc), _ptr(vc), _ptr(count), int(cap),
+                               float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream))
+    _check(st, "kvc_decode_attn")
+    return out, lse

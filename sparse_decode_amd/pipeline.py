@@ -1,0 +1,97 @@
+"""Per-layer driver of the four-step path: preallocated buffers plus the call
+sequence score -> select -> gather -> decode through the C ABI binding.
+
+This is host-side orchestration only (no arithmetic of its own): it is what a
+serving loop would do after prefill (FastKV section 2.B: one retention budget per
+layer; Tutorial "Variantes de l'attention et compression du cache KV", section
+"Compresser un cache existant") or at every decode step of a retrieval method
+(FreeKV technical summary section 2.A).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import kvc
+from .synth import Workload
+
+
+class LayerPath:
+    """Buffers for one layer shape; `run` enqueues the four steps on the current stream."""
+
+    def __init__(self, wl: Workload, device="cuda", s_max: int | None = None, batch: int | None = None,
+                 k: int | None = None):
+        self.wl = wl
+        self.B = wl.batch if batch is None else batch
+        self.S = wl.s_max if s_max is None else s_max
+        self.k = wl.k if k is None else k
+        self.cap = self.k + wl.n_keep
+        dev = torch.device(device)
+        B, S, nkv, nh, d = self.B, self.S, wl.n_kv, wl.n_h, wl.d_h
+        dt = wl.torch_dtype
+        self.raw = torch.empty((B, nkv, S), dtype=torch.float32, device=dev)
+        self.pooled = torch.empty((B, nkv, S), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((B, nkv, self.cap), dtype=torch.int32, device=dev)
+        self.count = torch.empty((B, nkv), dtype=torch.int32, device=dev)
+        self.kc = torch.empty((B, nkv, self.cap, d), dtype=dt, device=dev)
+        self.vc = torch.empty((B, nkv, self.cap, d), dtype=dt, device=dev)
+        self.pos = torch.empty((B, nkv, self.cap), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, nh, d), dtype=dt, device=dev)
+        self.lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
+        code = kvc.KVC_BF16 if wl.dtype == "bf16" else kvc.KVC_F32
+        dims = kvc.make_dims(B, S, nh, nkv, d, code)
+        self.ws_score = torch.empty(max(256, kvc.score_window_workspace(dims, wl.w)), dtype=torch.uint8, device=dev)
+        self.ws_decode = torch.empty(max(256, kvc.decode_attn_workspace(dims, self.cap)), dtype=torch.uint8,
+                                     device=dev)
+
+    def score(self, q_win, k, seq_lens=None):
+        wl = self.wl
+        return kvc.score_window(q_win, k, wl.w, seq_lens=seq_lens, window_in_cache=wl.window_in_cache,
+                                n_keep=wl.n_keep, pool=wl.pool, raw=self.raw, pooled=self.pooled,
+                                ws=self.ws_score)
+
+    def select(self, seq_lens=None):
+        return kvc.select_topk(self.pooled, self.k, self.wl.n_keep, seq_lens=seq_lens, idx=self.idx,
+                               count=self.count)
+
+    def gather(self, k, v, src_pos=None):
+        return kvc.gather_compact(k, self.idx, self.count, src1=v, src_pos=src_pos, dst0=self.kc, dst1=self.vc,
+                                  pos_out=self.pos)
+
+    def decode(self, q_dec):
+        return kvc.decode_attn(q_dec, self.kc, self.vc, self.count, out=self.out, lse=self.lse,
+                               ws=self.ws_decode)
+
+    def run(self, q_win, k, v, q_dec, seq_lens=None, src_pos=None):
+        self.score(q_win, k, seq_lens)
+        self.select(seq_lens)
+        self.gather(k, v, src_pos)
+        self.decode(q_dec)
+        return self.out
+
+
+class TspStep:
+    """FastKV section 2.A token-selective propagation at one layer: one selection per
+    sequence from the head-summed window scores, then the gather of those tokens'
+    hidden states (the sliding-window tokens always propagate)."""
+
+    def __init__(self, wl: Workload, k_tsp: int, device="cuda", s_max: int | None = None):
+        self.wl = wl
+        self.S = wl.s_max if s_max is None else s_max
+        self.k = k_tsp
+        self.cap = k_tsp + wl.n_keep
+        dev = torch.device(device)
+        B = wl.batch
+        self.idx = torch.empty((B, 1, self.cap), dtype=torch.int32, device=dev)
+        self.count = torch.empty((B, 1), dtype=torch.int32, device=dev)
+        self.hidden_out = torch.empty((B, 1, self.cap, wl.hidden), dtype=wl.torch_dtype, device=dev)
+        self.pos = torch.empty((B, 1, self.cap), dtype=torch.int32, device=dev)
+        dims = kvc.make_dims(B, self.S, wl.n_kv, wl.n_kv, wl.d_h, kvc.KVC_F32)
+        need = kvc.select_topk_workspace(dims, self.k, wl.n_keep, kvc.KVC_SELECT_SHARED_HEADS)
+        self.ws = torch.empty(max(256, need), dtype=torch.uint8, device=dev)
+
+    def run(self, pooled, hidden, seq_lens=None):
+        kvc.select_topk(pooled, self.k, self.wl.n_keep, seq_lens=seq_lens, shared_heads=True, idx=self.idx,
+                        count=self.count, ws=self.ws)
+        h = hidden.view(hidden.shape[0], 1, hidden.shape[1], hidden.shape[2])
+        kvc.gather_compact(h, self.idx, self.count, dst0=self.hidden_out, pos_out=self.pos)
+        return self.hidden_out, self.pos

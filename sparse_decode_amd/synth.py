@@ -17,6 +17,10 @@ section 4; none of those suites is used, these synthetic shapes stand in):
 3. ``ctx_128k``       as 2 with S=131072, 0.5% planted, k=ceil(1% of S)=1311 (+32).
 4. ``ragged_b16``     batch 16, S_b ~ U{4096..16384}, 32/8 heads, bf16, one new query
                       per step (not in the cache), n_keep=32, pool 7, k=512, 64 steps.
+                      Each head's query is (3 m + z_t) / sqrt(10): a persistent N(0,1)
+                      component m plus fresh noise z_t, so adjacent steps have cosine
+                      ~0.9 (FreeKV technical summary 2.A observes > 0.9); planted keys
+                      lie along the unit mean of the group's persistent components.
 5. ``mha_tsp``        batch 2, n_h=n_kv=32, S=65536, bf16, w=32, pool 7; at layer 16 the
                       top ceil(20%) tokens by window score (+32) keep their hidden
                       states [S][4096]; every layer keeps k=1024 (+32) for decode.
@@ -29,7 +33,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-STREAM_QWIN, STREAM_K, STREAM_V, STREAM_QDEC, STREAM_HIDDEN = 0, 1, 2, 3, 4
+STREAM_QWIN, STREAM_K, STREAM_V, STREAM_QDEC, STREAM_HIDDEN, STREAM_QMEAN = 0, 1, 2, 3, 4, 5
 
 
 @dataclass(frozen=True)
@@ -51,7 +55,8 @@ class Workload:
     hh_frac: float = 0.0        # planted heavy hitters as a fraction of S_b (ceil)
     hh_count: int = 0           # or an absolute count
     hh_mag: float = 4.0         # magnitude in units of sqrt(d_h)
-    hh_dir: str = "random"      # "random" per (layer, KV head) or "window_mean"
+    hh_dir: str = "random"      # "random" per (layer, KV head), "window_mean" or "query_mean"
+    query_mode: str = "iid"     # "iid", or "persistent" (per-step queries share a component)
     ragged: tuple | None = None  # (lo, hi) inclusive range of S_b
     steps: int = 1
     tsp_layer: int | None = None
@@ -84,7 +89,7 @@ WORKLOADS = {
     3: Workload(3, "ctx_128k", 1, 32, 131072, 32, 8, 128, "bf16", 32, True, 32, 7, 1311,
                 hh_frac=0.005),
     4: Workload(4, "ragged_b16", 16, 1, 16384, 32, 8, 128, "bf16", 1, False, 32, 7, 512,
-                hh_frac=0.01, ragged=(4096, 16384), steps=64),
+                hh_frac=0.01, hh_dir="query_mean", query_mode="persistent", ragged=(4096, 16384), steps=64),
     5: Workload(5, "mha_tsp", 2, 32, 65536, 32, 32, 128, "bf16", 32, True, 32, 7, 1024,
                 hh_frac=0.01, tsp_layer=16, tsp_rate=0.2, hidden=4096),
 }
@@ -158,6 +163,9 @@ def layer_inputs(wl: Workload, layer: int = 0, device="cpu", step: int = 0, s_ma
         q_dec = _randn((B, nh, d), seed_for(wl.cfg_id, layer, STREAM_QDEC), device)
     else:
         q_win = _randn((B, nh, wl.w, d), seed_for(wl.cfg_id, layer, STREAM_QDEC, step), device)
+        if wl.query_mode == "persistent":
+            qm = _randn((B, nh, d), seed_for(wl.cfg_id, layer, STREAM_QMEAN), device)
+            q_win = (3.0 * qm[:, :, None, :] + q_win) / math.sqrt(10.0)
         q_dec = q_win[:, :, -1, :].clone()
     k = _randn((B, nkv, S, d), seed_for(wl.cfg_id, layer, STREAM_K), device)
     v = _randn((B, nkv, S, d), seed_for(wl.cfg_id, layer, STREAM_V), device)
@@ -170,6 +178,9 @@ def layer_inputs(wl: Workload, layer: int = 0, device="cpu", step: int = 0, s_ma
         if wl.hh_dir == "window_mean":
             r = wl.group
             m = q_win[b].reshape(nkv, r * wl.w, d).mean(dim=1)
+            dirs = m / m.norm(dim=1, keepdim=True)
+        elif wl.hh_dir == "query_mean":
+            m = qm[b].reshape(nkv, wl.group, d).mean(dim=1)
             dirs = m / m.norm(dim=1, keepdim=True)
         else:
             dirs = torch.from_numpy(_unit_dirs(wl, layer, nkv, d)).to(device=device, dtype=torch.float32)

@@ -1,0 +1,167 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared symbol,
+and rejects every invalid argument before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from sparse_decode_amd import kvc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+BAD = 0x1000  # a non-null, 16-byte aligned address that is never dereferenced on these paths
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = kvc.lib()
+    declared = _declared()
+    assert set(declared) == set(kvc.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert kvc.lib().kvc_abi_version() == 1
+    seen = set()
+    for s in range(5):
+        txt = kvc.status_str(s)
+        assert txt and txt not in seen
+        seen.add(txt)
+    assert kvc.status_str(99) == "unknown status"
+
+
+def _dims(**kw):
+    base = dict(batch=1, s_max=1024, n_h=32, n_kv=8, d_h=128, dtype_code=kvc.KVC_BF16)
+    base.update(kw)
+    return kvc.make_dims(base["batch"], base["s_max"], base["n_h"], base["n_kv"], base["d_h"], base["dtype_code"])
+
+
+def _score(dims, w=32, **kw):
+    a = dict(q=BAD, k=BAD, wic=1, n_keep=32, pool=7, scale=0.0, raw=BAD, pooled=BAD, flags=0, ws=BAD,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return kvc.lib().kvc_score_window(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], w,
+                                      a["wic"], a["n_keep"], a["pool"], a["scale"], a["raw"], a["pooled"],
+                                      a["flags"], a["ws"], a["ws_bytes"], None)
+
+
+def test_score_rejects_invalid_arguments():
+    E, U, W = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_UNSUPPORTED, kvc.KVC_ERR_WORKSPACE
+    assert _score(None) == E
+    assert _score(_dims(batch=0)) == E
+    assert _score(_dims(s_max=0)) == E
+    assert _score(_dims(n_h=30)) == E            # n_h % n_kv != 0
+    assert _score(_dims(dtype_code=7)) == E
+    assert _score(_dims(d_h=96)) == U
+    assert _score(_dims(), w=0) == E
+    assert _score(_dims(), w=2048) == E
+    assert _score(_dims(), q=None) == E
+    assert _score(_dims(), raw=None) == E
+    assert _score(_dims(), pooled=None) == E
+    assert _score(_dims(), pool=4) == E          # even pool kernel
+    assert _score(_dims(), pool=0) == E
+    assert _score(_dims(), n_keep=-1) == E
+    assert _score(_dims(), scale=-1.0) == E
+    assert _score(_dims(), scale=float("nan")) == E
+    assert _score(_dims(), flags=4) == E
+    assert _score(_dims(), k=BAD + 4) == E       # misaligned
+    assert _score(_dims(), ws=None) == W
+    need = kvc.score_window_workspace(_dims(), 32)
+    assert need > 0
+    assert _score(_dims(), ws_bytes=need - 1) == W
+
+
+def test_workspace_queries():
+    d = _dims()
+    assert kvc.score_window_workspace(_dims(batch=0), 32) == 0
+    small = kvc.score_window_workspace(_dims(s_max=4096), 32)
+    big = kvc.score_window_workspace(_dims(s_max=131072), 32)
+    assert 0 < small <= big
+    gen = kvc.score_window_workspace(_dims(s_max=4096), 32, kvc.KVC_SCORE_GENERIC)
+    assert gen >= 32 * 4 * 4096 * 4 * 8     # stored logits
+    assert kvc.select_topk_workspace(d, 64, 16) == 0
+    assert kvc.select_topk_workspace(d, 64, 16, kvc.KVC_SELECT_SHARED_HEADS) >= 1024 * 4
+    assert kvc.select_topk_workspace(d, -1, 16) == 0
+    assert kvc.decode_attn_workspace(d, 2080) > 0
+    assert kvc.decode_attn_workspace(d, 2080) <= kvc.decode_attn_workspace(d, 8192)
+    assert kvc.decode_attn_workspace(d, 0) == 0
+
+
+def _select(dims, k=64, n_keep=16, flags=0, scores=BAD, idx=BAD, count=BAD, ws=None, ws_bytes=0):
+    return kvc.lib().kvc_select_topk(ctypes.byref(dims) if dims is not None else None, scores, k, n_keep, flags,
+                                     idx, count, ws, ws_bytes, None)
+
+
+def test_select_rejects_invalid_arguments():
+    E, W = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_WORKSPACE
+    assert _select(None) == E
+    assert _select(_dims(batch=0)) == E
+    assert _select(_dims(), k=-1) == E
+    assert _select(_dims(), k=0, n_keep=0) == E
+    assert _select(_dims(), flags=2) == E
+    assert _select(_dims(), scores=None) == E
+    assert _select(_dims(), idx=None) == E
+    assert _select(_dims(), count=None) == E
+    assert _select(_dims(), flags=kvc.KVC_SELECT_SHARED_HEADS) == W
+
+
+def _gather(**kw):
+    a = dict(batch=1, heads=8, s_max=1024, row_bytes=256, src0=BAD, src1=BAD, src_pos=None, idx=BAD, count=BAD,
+             idx_heads=8, cap=80, dst0=BAD, dst1=BAD, pos=BAD)
+    a.update(kw)
+    return kvc.lib().kvc_gather_compact(a["batch"], a["heads"], a["s_max"], a["row_bytes"], a["src0"], a["src1"],
+                                        a["src_pos"], a["idx"], a["count"], a["idx_heads"], a["cap"], a["dst0"],
+                                        a["dst1"], a["pos"], None)
+
+
+def test_gather_rejects_invalid_arguments():
+    E, U = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_UNSUPPORTED
+    assert _gather(batch=0) == E
+    assert _gather(cap=0) == E
+    assert _gather(idx_heads=3) == E
+    assert _gather(src0=None) == E
+    assert _gather(idx=None) == E
+    assert _gather(dst1=None) == E              # src1 given without dst1
+    assert _gather(row_bytes=8) == E
+    assert _gather(row_bytes=24) == U           # not a multiple of 16
+    assert _gather(row_bytes=48) == U           # 3 vectors: neither a power of two nor a multiple of 256
+    assert _gather(src0=BAD + 8) == U           # misaligned
+
+
+def _decode(dims, cap=80, **kw):
+    a = dict(q=BAD, kc=BAD, vc=BAD, count=BAD, scale=0.0, out=BAD, lse=None, ws=BAD, ws_bytes=1 << 40)
+    a.update(kw)
+    return kvc.lib().kvc_decode_attn(ctypes.byref(dims) if dims is not None else None, a["q"], a["kc"], a["vc"],
+                                     a["count"], cap, a["scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_rejects_invalid_arguments():
+    E, U, W = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_UNSUPPORTED, kvc.KVC_ERR_WORKSPACE
+    assert _decode(None) == E
+    assert _decode(_dims(n_kv=5)) == E
+    assert _decode(_dims(d_h=80)) == U
+    assert _decode(_dims(), cap=0) == E
+    assert _decode(_dims(), q=None) == E
+    assert _decode(_dims(), out=None) == E
+    assert _decode(_dims(), scale=-2.0) == E
+    assert _decode(_dims(), vc=BAD + 2) == E
+    assert _decode(_dims(), ws=None) == W
+    assert _decode(_dims(), ws_bytes=16) == W
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the error path of a host without a GPU")
+def test_valid_call_without_gpu_reports_hip_error():
+    # every argument passes validation, so the call reaches the HIP runtime, which has no device
+    assert _gather() == kvc.KVC_ERR_HIP
+    assert _select(_dims()) == kvc.KVC_ERR_HIP
+    assert _decode(_dims()) == kvc.KVC_ERR_HIP
+    assert _score(_dims()) == kvc.KVC_ERR_HIP

@@ -1,0 +1,267 @@
+"""Kernel-level GPU parity: each HIP kernel against the CPU oracle on the same seeded
+inputs, at sizes that span several tiles and a ragged tail, plus edge cases."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_decode_amd import kvc, synth
+from _parity import (assert_decode_close, assert_scores_close, check_selection, host)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kvc.lib()
+    yield
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _randn(shape, seed, dtype=torch.bfloat16):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=DEV, dtype=torch.float32).to(dtype).contiguous()
+
+
+# ===================================================================================== gather
+
+@pytest.mark.parametrize("dtype,d,heads,idx_heads,s_max,cap", [
+    (torch.bfloat16, 128, 8, 8, 3000, 700),
+    (torch.float32, 64, 2, 2, 512, 80),
+    (torch.bfloat16, 64, 4, 1, 1000, 300),
+    (torch.bfloat16, 4096, 1, 1, 2000, 600),       # hidden-state rows of 8 KiB
+])
+def test_gather_bitexact(dtype, d, heads, idx_heads, s_max, cap):
+    _say("gather", dtype, d, heads, idx_heads, s_max, cap)
+    B = 3
+    rng = np.random.default_rng(7)
+    src0 = _randn((B, heads, s_max, d), 1, dtype)
+    src1 = _randn((B, heads, s_max, d), 2, dtype)
+    idx = np.full((B, idx_heads, cap), -1, np.int32)
+    count = np.zeros((B, idx_heads), np.int32)
+    counts = [cap, 0, 1, cap // 2, 37]
+    for b in range(B):
+        for h in range(idx_heads):
+            n = counts[(b * idx_heads + h) % len(counts)]
+            idx[b, h, :n] = np.sort(rng.choice(s_max, n, replace=False))
+            count[b, h] = n
+    idx[0, 0, 5] = s_max + 3          # out of range: copies nothing, pos -1
+    src_pos = rng.permutation(10 * s_max)[: B * s_max].reshape(B, s_max).astype(np.int32)
+    sentinel = torch.full((B, heads, cap, d), 7.0, dtype=dtype, device=DEV)
+    d0, d1, pos = kvc.gather_compact(src0, torch.from_numpy(idx).to(DEV), torch.from_numpy(count).to(DEV),
+                                     src1=src1, src_pos=torch.from_numpy(src_pos).to(DEV),
+                                     dst0=sentinel.clone(), dst1=sentinel.clone())
+    torch.cuda.synchronize()
+    for src, dst in ((src0, d0), (src1, d1)):
+        s_np = src.view(torch.int16).cpu().numpy() if dtype == torch.bfloat16 else src.view(torch.int32).cpu().numpy()
+        base = sentinel.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+        src_b = np.broadcast_to(s_np, s_np.shape)
+        if idx_heads == 1:
+            idx_full = np.repeat(idx, heads, axis=1)
+            cnt_full = np.repeat(count, heads, axis=1)
+        else:
+            idx_full, cnt_full = idx, count
+        ref, ref_pos = oracle.gather(src_b, np.where((idx_full >= 0) & (idx_full < s_max), idx_full, 0), cnt_full,
+                                     src_pos=src_pos, dst=base)
+        # the out-of-range index leaves its row untouched and gets pos -1
+        ref[0, :heads if idx_heads == 1 else 1, 5] = base[0, :heads if idx_heads == 1 else 1, 5]
+        ref_pos[0, :heads if idx_heads == 1 else 1, 5] = -1
+        got = dst.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+        assert np.array_equal(got, ref)
+        assert np.array_equal(host(pos), ref_pos)
+
+
+# ===================================================================================== decode
+
+@pytest.mark.parametrize("dtype,d,n_h,n_kv,cap", [
+    (torch.bfloat16, 128, 32, 8, 2080),
+    (torch.bfloat16, 128, 32, 32, 1056),     # MHA
+    (torch.bfloat16, 128, 32, 1, 300),       # MQA: 32 heads per KV head, 4 head chunks
+    (torch.bfloat16, 64, 12, 4, 517),        # group of 3
+    (torch.float32, 64, 4, 2, 80),
+    (torch.float32, 128, 8, 2, 999),
+])
+def test_decode_vs_oracle(dtype, d, n_h, n_kv, cap):
+    _say("decode", dtype, d, n_h, n_kv, cap)
+    B = 2
+    q = _randn((B, n_h, d), 11, dtype)
+    kc = _randn((B, n_kv, cap, d), 12, dtype)
+    vc = _randn((B, n_kv, cap, d), 13, dtype)
+    row0 = [cap, 1] + [cap - 7 * i for i in range(max(0, n_kv - 2))]
+    row1 = [0] + [max(0, cap // (i + 1)) for i in range(max(0, n_kv - 1))]
+    cnt = np.array([row0[:n_kv], row1[:n_kv]], np.int32)
+    out, lse = kvc.decode_attn(q, kc, vc, torch.from_numpy(cnt).to(DEV))
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(host(q), host(kc), host(vc), cnt)
+    bf16 = dtype == torch.bfloat16
+    assert_decode_close(out, ref, bf16)
+    g = host(lse)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(g), fin)
+    assert np.allclose(g[fin], ref_lse[fin], rtol=1e-5, atol=1e-5)
+    assert np.all(host(out)[~fin] == 0)
+    # bit-reproducible
+    out2, lse2 = kvc.decode_attn(q, kc, vc, torch.from_numpy(cnt).to(DEV))
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_decode_closed_forms():
+    _say("decode closed forms")
+    n_h, n_kv, cap, d = 8, 2, 64, 128
+    q = _randn((1, n_h, d), 21)
+    kc = _randn((1, n_kv, cap, d), 22)
+    vc = _randn((1, n_kv, cap, d), 23)
+    one = torch.tensor([[1, 1]], dtype=torch.int32, device=DEV)
+    out, _ = kvc.decode_attn(q, kc, vc, one)
+    # one token: the output is that V row, exactly (p = 1, bf16 round trip is exact)
+    for h in range(n_h):
+        assert torch.equal(out[0, h], vc[0, h // 4, 0])
+    same = kc[:, :, :1].expand(1, n_kv, cap, d).contiguous()
+    full = torch.tensor([[cap, cap]], dtype=torch.int32, device=DEV)
+    out, _ = kvc.decode_attn(q, same, vc, full)
+    mean = vc.float().mean(2)
+    assert torch.allclose(out.float()[0, 0], mean[0, 0], atol=2e-2, rtol=1e-2)
+
+
+# ===================================================================================== select
+
+def _select_case(scores_np, seq_lens, k, n_keep, shared=False):
+    sc = torch.from_numpy(scores_np).to(DEV)
+    idx, cnt = kvc.select_topk(sc, k, n_keep, seq_lens=seq_lens, shared_heads=shared)
+    torch.cuda.synchronize()
+    ri, rc = oracle.select_topk(scores_np, k, n_keep, seq_lens=seq_lens, shared_heads=shared)
+    assert np.array_equal(host(cnt), rc)
+    assert np.array_equal(host(idx), ri)
+
+
+@pytest.mark.parametrize("s_max", [100, 4096, 32768, 65536])
+def test_select_bitexact_with_ties(s_max):
+    _say("select ties", s_max)
+    rng = np.random.default_rng(s_max)
+    B, H = 2, 8
+    sc = (rng.integers(0, 50, (B, H, s_max)) / 37.0).astype(np.float32)   # many exact ties
+    sl = np.array([s_max, max(1, s_max * 2 // 3 + 5)], np.int32)
+    for k in (1, 17, s_max // 16, s_max // 2, s_max):
+        for n_keep in (0, 32):
+            if k + n_keep < 1:
+                continue
+            _select_case(sc, sl, k, n_keep)
+
+
+@pytest.mark.parametrize("s_max", [4096, 131072])
+def test_select_bitexact_continuous(s_max):
+    _say("select continuous", s_max)
+    rng = np.random.default_rng(3)
+    sc = rng.random((1, 8, s_max)).astype(np.float32) ** 4
+    sc[0, 0, 1000:1100] = 0.5                     # a tie wall
+    sc[0, 1] = 0.25                               # all equal
+    sc[0, 2, ::7] = 0.0
+    sl = np.array([s_max], np.int32)
+    for k in (1311, 2048, 7):
+        _select_case(sc, sl, k, 32)
+
+
+def test_select_shared_heads_and_degenerate():
+    _say("select shared")
+    rng = np.random.default_rng(5)
+    B, H, s_max = 2, 32, 65536
+    sc = rng.random((B, H, s_max)).astype(np.float32) * 1e-3
+    _select_case(sc, np.array([s_max, s_max], np.int32), 13108, 32, shared=True)
+    small = rng.random((3, 2, 64)).astype(np.float32)
+    _select_case(small, np.array([0, 5, 64], np.int32), 10, 8)     # S_b = 0, S_b < n_keep
+    _select_case(small, np.array([64, 64, 64], np.int32), 0, 8)    # k = 0
+    neg = (rng.standard_normal((1, 2, 300))).astype(np.float32)
+    neg[0, 0, :10] = -0.0
+    neg[0, 0, 10:20] = 0.0
+    _select_case(neg, np.array([300], np.int32), 40, 4)            # signed scores, -0.0 == +0.0
+
+
+# ===================================================================================== score
+
+def _score_case(B, n_h, n_kv, d, s_max, w, seq_lens, wic=True, n_keep=None, pool=7, dtype=torch.bfloat16,
+                generic=False, seed=0, planted=0):
+    _say("score", B, n_h, n_kv, d, s_max, w, list(seq_lens), wic, pool, dtype, "generic" if generic else "mfma")
+    q = _randn((B, n_h, w, d), 100 + seed, dtype)
+    k = _randn((B, n_kv, s_max, d), 200 + seed, dtype)
+    if planted:
+        rng = np.random.default_rng(seed)
+        pos = torch.from_numpy(rng.choice(max(1, s_max - w), planted, replace=False)).to(DEV)
+        u = torch.from_numpy(rng.standard_normal((n_kv, d))).float().to(DEV)
+        u = 4 * np.sqrt(d) * u / u.norm(dim=1, keepdim=True)
+        k[:, :, pos, :] = u[None, :, None, :].to(dtype)
+    n_keep = w if n_keep is None else n_keep
+    raw, pooled = kvc.score_window(q, k, w, seq_lens=seq_lens, window_in_cache=wic, n_keep=n_keep, pool=pool,
+                                   generic=generic)
+    torch.cuda.synchronize()
+    rraw, rpooled = oracle.score_window(host(q), host(k), w, seq_lens=seq_lens, window_in_cache=wic,
+                                        n_keep=n_keep, pool=pool)
+    assert_scores_close(raw, rraw, "raw")
+    assert_scores_close(pooled, rpooled, "pooled")
+    # pooling is exact given the raw scores the GPU produced
+    _, pooled_from_gpu_raw = _pool_np(host(raw), seq_lens, n_keep, pool)
+    assert np.array_equal(host(pooled), pooled_from_gpu_raw)
+    raw2, pooled2 = kvc.score_window(q, k, w, seq_lens=seq_lens, window_in_cache=wic, n_keep=n_keep, pool=pool,
+                                     generic=generic)
+    assert torch.equal(raw, raw2) and torch.equal(pooled, pooled2)
+    return q, k, raw, pooled, rpooled
+
+
+def _pool_np(raw, seq_lens, n_keep, pool):
+    out = np.zeros_like(raw)
+    B, H, s_max = raw.shape
+    h = pool // 2
+    for b in range(B):
+        S = int(seq_lens[b])
+        C = max(0, S - n_keep)
+        for g in range(H):
+            r = raw[b, g]
+            for t in range(S):
+                out[b, g, t] = r[max(0, t - h):min(C - 1, t + h) + 1].max() if t < C else r[t]
+    return raw, out
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_score_gqa_ragged(generic):
+    _score_case(2, 32, 8, 128, 2500, 32, np.array([2500, 1337], np.int32), generic=generic, planted=20)
+
+
+def test_score_mha_and_d64():
+    _score_case(1, 4, 4, 128, 3001, 32, np.array([3001], np.int32), seed=1)           # R = 32
+    _score_case(2, 8, 4, 64, 1500, 32, np.array([1500, 700], np.int32), seed=2)       # d = 64, R = 64
+    _score_case(1, 6, 2, 128, 900, 16, np.array([900], np.int32), seed=3, pool=5)     # R = 48 (padded)
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_score_decode_query_not_in_cache(generic):
+    # one new query per head (w = 1) that sees every cached key; R = 4
+    _score_case(3, 32, 8, 128, 4096, 1, np.array([4096, 2049, 3333], np.int32), wic=False, n_keep=32,
+                generic=generic, seed=4)
+
+
+def test_score_fp32_tiny_config():
+    wl = synth.WORKLOADS[1]
+    _score_case(1, wl.n_h, wl.n_kv, wl.d_h, wl.s_max, wl.w, np.array([wl.s_max], np.int32), pool=wl.pool,
+                dtype=torch.float32, seed=5)
+
+
+def test_score_short_sequences():
+    # S_b < w (rows that see no key), S_b = 0, S_b = 1
+    _score_case(4, 8, 2, 128, 256, 32, np.array([20, 0, 1, 256], np.int32), seed=6)
+    _score_case(4, 8, 2, 128, 256, 32, np.array([20, 0, 1, 256], np.int32), seed=6, generic=True)
+
+
+def test_score_then_select_matches_oracle_rule():
+    sl = np.array([4000], np.int32)
+    q, k, raw, pooled, rpooled = _score_case(1, 32, 8, 128, 4000, 32, sl, planted=40, seed=7)
+    idx, cnt = kvc.select_topk(pooled, 256, 32, seq_lens=sl)
+    ri, rc = oracle.select_topk(rpooled, 256, 32, seq_lens=sl)
+    check_selection(idx, cnt, ri, rc, rpooled, sl, 256, 32)
