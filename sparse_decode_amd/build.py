@@ -23,6 +23,12 @@ ARCH = "gfx950"
 COMMON_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into arch VGPRs: no v_accvgpr_read per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # no kernel produces or propagates NaN (masked logits are -inf, bf16 rounding and
+    # selection keys are integer operations): IEEE mode off drops the NaN
+    # canonicalisation of every min/max operand
+    "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     "-Wno-unused-result",
 ]

@@ -115,31 +115,35 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
     const u32x4 *krow = (const u32x4 *)kc_ + (size_t)unit * cap * VPR + li;
     const u32x4 *vrow = (const u32x4 *)vc_ + (size_t)unit * cap * VPR + li;
+    constexpr int UNR = 4;                  // tokens in flight per lane group
     const int step = kDecWaves * TPW;
-    for (int t = s0 + wv * TPW + ts; t < s1 + 0; t += 2 * step) {
-        // two tokens per lane group in flight
-        const int t2 = t + step;
-        const bool v2 = t2 < s1;
-        u32x4 kv0 = ld_stream(krow + (size_t)t * VPR);
-        u32x4 vv0 = ld_stream(vrow + (size_t)t * VPR);
-        u32x4 kv1 = kv0, vv1 = vv0;
-        if (v2) {
-            kv1 = ld_stream(krow + (size_t)t2 * VPR);
-            vv1 = ld_stream(vrow + (size_t)t2 * VPR);
+    for (int t = s0 + wv * TPW + ts; t < s1; t += UNR * step) {
+        u32x4 kv[UNR], vv[UNR];
+#pragma unroll
+        for (int q = 0; q < UNR; ++q) {
+            const int tq = t + q * step;
+            if (tq < s1) {
+                kv[q] = ld_stream(krow + (size_t)tq * VPR);
+                vv[q] = ld_stream(vrow + (size_t)tq * VPR);
+            }
         }
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            if (pass == 1 && !v2) break;
+        for (int q = 0; q < UNR; ++q) {
+            if (t + q * step >= s1) break;
             float kf[E], vf[E];
-            RV::unpack(pass ? kv1 : kv0, kf);
-            RV::unpack(pass ? vv1 : vv0, vf);
+            RV::unpack(kv[q], kf);
+            RV::unpack(vv[q], vf);
 #pragma unroll
             for (int j = 0; j < RH; ++j) {
                 float s = 0.f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) s = fmaf(qf[j][e], kf[e], s);
+                if (LPT == 16) {
+                    s = row16_sum(s);
+                } else {
 #pragma unroll
-                for (int off = LPT / 2; off > 0; off >>= 1) s += shfl_xor_f(s, off);
+                    for (int off = LPT / 2; off > 0; off >>= 1) s += shfl_xor_f(s, off);
+                }
                 const float mn = fmaxf(m[j], s);
                 const float a = fast_exp2(m[j] - mn);
                 const float p = fast_exp2(s - mn);
@@ -202,31 +206,86 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     }
 }
 
-template <bool BF16, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float *__restrict__ part_o,
-                                                         const float2 *__restrict__ part_ml, int n_h,
-                                                         int n_kv, int r, int n_splits,
-                                                         void *__restrict__ out, float *__restrict__ lse)
+constexpr int kMergeThreads = 256;
+constexpr int kMaxSplits = 1024;
+
+// Deterministic block reductions (fixed shuffle tree, then waves in order).
+__device__ __forceinline__ float block_max(float v, float *red)
 {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, shfl_xor_f(v, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kMergeThreads / kWave; ++i) r = fmaxf(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float *red)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += shfl_xor_f(v, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kMergeThreads / kWave; ++i) r += red[i];
+    __syncthreads();
+    return r;
+}
+
+// One work-group per (b, h): split weights exp2(m_s - M) staged in LDS, then
+// kMergeThreads / D thread groups each fold a strided subset of the splits (8 loads
+// in flight per thread) and the groups are added in group order.
+template <bool BF16, int D>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float *__restrict__ part_o,
+                                                                     const float2 *__restrict__ part_ml, int n_h,
+                                                                     int n_kv, int r, int n_splits,
+                                                                     void *__restrict__ out, float *__restrict__ lse)
+{
+    constexpr int G = kMergeThreads / D;
+    __shared__ float sw[kMaxSplits];
+    __shared__ float red[kMergeThreads / kWave];
+    __shared__ float so[G][D];
     const int bh = blockIdx.x;              // b * n_h + h
     const int b = bh / n_h;
     const int h = bh - b * n_h;
     const int g = h / r;
     const int hl = h - g * r;
     const size_t base = ((size_t)(b * n_kv + g) * r + hl) * n_splits;
-    const int d = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_ml[base + s].x);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < n_splits; ++s) {
-            const float2 ml = part_ml[base + s];
-            const float a = fast_exp2(ml.x - M);
-            L += ml.y * a;
-            O += part_o[(base + s) * D + d] * a;
+    float mloc = -INFINITY;
+    for (int s = threadIdx.x; s < n_splits; s += kMergeThreads) mloc = fmaxf(mloc, part_ml[base + s].x);
+    const float M = block_max(mloc, red);
+    float lloc = 0.f;
+    for (int s = threadIdx.x; s < n_splits; s += kMergeThreads) {
+        const float2 ml = part_ml[base + s];
+        const float wgt = (M == -INFINITY || ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - M);
+        sw[s] = wgt;
+        lloc += wgt * ml.y;
+    }
+    const float L = block_sum(lloc, red);   // also orders the sw[] writes before their reads
+    const int d = threadIdx.x % D;
+    const int grp = threadIdx.x / D;
+    float O = 0.f;
+    for (int s0 = grp; s0 < n_splits; s0 += 8 * G) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int s = s0 + q * G;
+            v[q] = s < n_splits ? part_o[(base + s) * D + d] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int s = s0 + q * G;
+            if (s < n_splits) O = fmaf(sw[s], v[q], O);
         }
     }
-    const float y = (L > 0.f) ? O / L : 0.f;
+    so[grp][d] = O;
+    __syncthreads();
+    if (grp != 0) return;
+    float Ot = so[0][d];
+    for (int g2 = 1; g2 < G; ++g2) Ot += so[g2][d];
+    const float y = (L > 0.f) ? Ot / L : 0.f;
     if (BF16)
         ((uint16_t *)out)[(size_t)bh * D + d] = f32_to_bf16(y);
     else
@@ -267,16 +326,22 @@ DecodePlan plan_decode(int batch, int n_h, int n_kv, int d_h, int cap, int cus)
     if (p.head_chunk < r && r < 8) p.head_chunk *= 2;   // r = 3, 5, 6, 7 -> next power of two
     p.head_chunks = (r + p.head_chunk - 1) / p.head_chunk;
     const long units = (long)batch * n_kv * p.head_chunks;
-    // about two work-groups per CU, splits of at least 32 tokens
+    // about two work-groups per CU, splits of at least 64 tokens (one unrolled
+    // iteration of the work-group), at most kMaxSplits
     long splits = (2L * cus + units - 1) / units;
-    const long max_splits = (cap + 31) / 32;
+    const long max_splits = (cap + 63) / 64;
     if (splits > max_splits) splits = max_splits;
+    if (splits > kMaxSplits) splits = kMaxSplits;
     if (splits < 1) splits = 1;
     long tok = (cap + splits - 1) / splits;
-    tok = ((tok + 15) / 16) * 16;
+    tok = ((tok + 63) / 64) * 64;
     p.split_tokens = (int)tok;
     p.n_splits = (int)((cap + tok - 1) / tok);
     if (p.n_splits < 1) p.n_splits = 1;
+    if (p.n_splits > kMaxSplits) {           // only for caps beyond 64 * kMaxSplits tokens
+        p.split_tokens = (int)(((cap + kMaxSplits - 1) / kMaxSplits + 63) / 64 * 64);
+        p.n_splits = (cap + p.split_tokens - 1) / p.split_tokens;
+    }
     const size_t slots = (size_t)batch * n_kv * r * p.n_splits;
     p.ws_bytes = slots * (size_t)d_h * sizeof(float) + slots * sizeof(float2) + 256;
     return p;
@@ -303,11 +368,11 @@ hipError_t launch_decode(int batch, int n_h, int n_kv, int d_h, bool bf16, const
     if (e != hipSuccess) return e;
     dim3 mgrid(batch * n_h);
     if (bf16) {
-        if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<true, 128>), mgrid, dim3(128), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
-        else hipLaunchKernelGGL((decode_merge_kernel<true, 64>), mgrid, dim3(64), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
+        if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<true, 128>), mgrid, dim3(kMergeThreads), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
+        else hipLaunchKernelGGL((decode_merge_kernel<true, 64>), mgrid, dim3(kMergeThreads), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
     } else {
-        if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<false, 128>), mgrid, dim3(128), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
-        else hipLaunchKernelGGL((decode_merge_kernel<false, 64>), mgrid, dim3(64), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
+        if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<false, 128>), mgrid, dim3(kMergeThreads), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
+        else hipLaunchKernelGGL((decode_merge_kernel<false, 64>), mgrid, dim3(kMergeThreads), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
     }
     return hipGetLastError();
 }

@@ -30,25 +30,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     const int b = unit / heads;
     const int h = unit - b * heads;
     const int list = b * idx_heads + (idx_heads == 1 ? 0 : h);
-    int n = count[list];
-    n = n < 0 ? 0 : (n > cap ? cap : n);
     const int r0 = blockIdx.x * rows_per_block;
     int r1 = r0 + rows_per_block;
     r1 = r1 > cap ? cap : r1;
     const int32_t *lidx = idx + (size_t)list * cap;
-
-    if (pos_out) {
-        for (int j = r0 + threadIdx.x; j < r1; j += kGatherThreads) {
-            int p = -1;
-            if (j < n) {
-                const int t = lidx[j];
-                if (t >= 0 && t < s_max) p = src_pos ? src_pos[(size_t)b * s_max + t] : t;
-            }
-            pos_out[(size_t)unit * cap + j] = p;
-        }
-    }
-    const int rend = r1 < n ? r1 : n;
-    if (rend <= r0) return;
 
     const int tpr = 1 << tpr_log2;
     const int rows_per_iter = kGatherThreads >> tpr_log2;
@@ -57,13 +42,21 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     const size_t src_unit = (size_t)unit * s_max * vpr;
     const size_t dst_unit = (size_t)unit * cap * vpr;
 
-    for (int j0 = r0 + sub; j0 < rend; j0 += rows_per_iter * kGatherUnroll) {
+    // The count and the index list are loaded together (rows past the count are
+    // dropped afterwards), so the row copies wait on one dependent round trip only.
+    int n = count[list];
+    for (int j0 = r0 + sub; j0 < r1; j0 += rows_per_iter * kGatherUnroll) {
         int t[kGatherUnroll];
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
             const int j = j0 + u * rows_per_iter;
-            int tt = j < rend ? lidx[j] : -1;
-            t[u] = (tt >= 0 && tt < s_max) ? tt : -1;
+            t[u] = j < r1 ? lidx[j] : -1;
+        }
+        n = n < 0 ? 0 : (n > cap ? cap : n);
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int j = j0 + u * rows_per_iter;
+            if (j >= n || t[u] < 0 || t[u] >= s_max) t[u] = -1;
         }
         for (int c = col0; c < vpr; c += tpr) {
             u32x4 a[kGatherUnroll], bb[kGatherUnroll];
@@ -82,6 +75,17 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
                     if (src1) dst1[o] = bb[u];
                 }
             }
+        }
+    }
+    if (pos_out) {
+        n = n < 0 ? 0 : (n > cap ? cap : n);
+        for (int j = r0 + threadIdx.x; j < r1; j += kGatherThreads) {
+            int p = -1;
+            if (j < n) {
+                const int tt = lidx[j];
+                if (tt >= 0 && tt < s_max) p = src_pos ? src_pos[(size_t)b * s_max + tt] : tt;
+            }
+            pos_out[(size_t)unit * cap + j] = p;
         }
     }
 }

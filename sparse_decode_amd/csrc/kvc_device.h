@@ -34,6 +34,30 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// Lane exchanges inside a row of 16 lanes, as DPP operand modifiers (plain VALU
+// instructions, no LDS crossbar): the mirrors pair lane i with 15 - i (row) or with
+// 7 - i inside each half row; the quad permutations pair i with i ^ 2 and i ^ 1.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppXor2 = 0x4e;     // quad_perm(2, 3, 0, 1)
+constexpr int kDppXor1 = 0xb1;     // quad_perm(1, 0, 3, 2)
+
+// Sum over the 16 lanes of a row; every lane receives the total.  The pairings
+// (mirror, half mirror, xor 2, xor 1) cover each lane of the row exactly once.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_f<kDppRowMirror>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppXor1>(v);
+    return v;
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t *seq_lens, int b, int s_max)
 {
     int s = seq_lens ? seq_lens[b] : s_max;

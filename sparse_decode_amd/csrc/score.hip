@@ -195,82 +195,198 @@ __global__ __launch_bounds__(256) void pool_kernel(const float *__restrict__ raw
 // bf16 MFMA path
 // ====================================================================================
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfThreads = 256;
 constexpr int kMfWaves = kMfThreads / kWave;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Token (M index) held by accumulator element j of a lane in half `h`.
-__device__ __forceinline__ int acc_token(int j, int h) { return 8 * (j >> 2) + 4 * h + (j & 3); }
-
-template <int D, int RT>
-struct MfmaTile {
-    static constexpr int KS = D / 16;   // MFMA k-steps; a lane covers D/2 contiguous elements
-
-    // A operand: token row t0 + n, elements [h*D/2, h*D/2 + D/2).
-    __device__ static void load_k(const uint16_t *__restrict__ kunit, int t_row, int h, u32x4 *dst)
-    {
-        const u32x4 *p = (const u32x4 *)(kunit + (size_t)t_row * D + h * (D / 2));
-#pragma unroll
-        for (int s = 0; s < KS; ++s) dst[s] = ld_stream(p + s);
-    }
-
-    __device__ static void mma(const u32x4 *ka, const bf16x8_t (*qb)[KS], f32x16_t *acc)
-    {
-#pragma unroll
-        for (int ct = 0; ct < RT; ++ct) {
-            f32x16_t a = {};
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[s]), qb[ct][s], a, 0, 0, 0);
-            acc[ct] = a;
-        }
-    }
-};
-
 struct MfArgs {
     const uint16_t *q_win;
     const uint16_t *k;
     const int32_t *seq_lens;
-    int s_max, n_h, n_kv, w, wic, R, unit0, n_chunks, chunk_tokens, tiles_per_wave;
+    int s_max, n_h, n_kv, w, wic, R, unit0, n_chunks, chunk_tokens;
     float c;                 // scale * log2(e)
-    float2 *part;            // pass 1 out: [group][chunk][RT*32] (m, l)
-    const float2 *fin;       // pass 2 in:  [group][RT*32] (-M*c, 1/L)
+    float2 *part;            // pass 1 out: [group][chunk][RT*16] (m, l)
+    const float2 *fin;       // pass 2 in:  [group][RT*16] (-M*c, 1/L)
     float *raw;              // pass 2 out: [B*n_kv][s_max]
 };
 
-// Loads this lane's B operands (Q^T) for all row blocks: row ct*32 + n, elements
-// [h*D/2, h*D/2 + D/2).  Rows >= R are zero.
+// Work decomposition shared by both passes (a work-group is four waves).  Logits come from
+// v_mfma_f32_16x16x32_bf16 with 16 keys on M and 16 query rows on N: lane
+// l = 16 kg + t supplies token t and elements [32 s + 8 kg, +8) at k-step s for both
+// operands (the dot product runs over the same permutation of d on both sides), and
+// receives row n = l % 16 for tokens 4 kg + j, j < 4.
+//   * The R rows (RT blocks of 16) are split over WPR waves, CPW blocks each; their
+//     B operands (Q^T) are loaded once into registers.  With fewer than four row
+//     blocks the remaining waves form TG token groups.
+//   * K is staged through LDS one stage of ST tokens at a time with coalesced
+//     16-byte loads (every load instruction reads 8 KB contiguous), double
+//     buffered: the next stage's loads are in flight while the current one is
+//     multiplied.  Rows are padded by 16 bytes so the 16 rows a wave reads for one
+//     A operand fall in distinct banks.
 template <int D, int RT>
-__device__ __forceinline__ void load_q(const MfArgs &a, int b, int g, int n, int h,
-                                       bf16x8_t (*qb)[D / 16])
+struct Sc {
+    static constexpr int KS = D / 32;                    // MFMA k-steps
+    static constexpr int WPR = RT < 4 ? RT : 4;          // waves sharing one token tile
+    static constexpr int CPW = RT / WPR;                 // row blocks per wave
+    static constexpr int TG = kMfWaves / WPR;            // token groups
+    static constexpr int ST = 16 * (TG > 2 ? TG : 2);    // tokens per stage (8 KB at d_h = 128)
+    static constexpr int P = RT == 8 ? 3 : 4;            // stages in flight (register ring)
+    static constexpr int TPG = ST / 16 / TG;             // 16-token tiles per group per stage
+    static constexpr int ROWB = 2 * D + 16;              // LDS bytes per row
+    static constexpr int VPR = D / 8;                    // 16-byte vectors per row
+    static constexpr int LOADS = ST * VPR / kMfThreads;  // 16-byte loads per thread per stage
+    static constexpr int STAGE_BYTES = ST * ROWB;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int PAIR = TPG < 2 ? TPG : 2;       // tiles whose logits share one max/rescale
+    static_assert(LOADS >= 1 && ST * VPR % kMfThreads == 0, "stage must split evenly over the threads");
+
+    // Coalesced loads of one stage (rows clamped into [0, S)).
+    __device__ static void load_stage(const uint16_t *__restrict__ kunit, int st0, int S, u32x4 *reg)
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int gid = i * kMfThreads + threadIdx.x;
+            const int row = gid / VPR, col = gid - row * VPR;
+            const int t = min(st0 + row, S - 1);
+            reg[i] = ld_stream((const u32x4 *)(kunit + (size_t)t * D) + col);
+        }
+    }
+
+    __device__ static void store_stage(unsigned char *buf, const u32x4 *reg)
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int gid = i * kMfThreads + threadIdx.x;
+            const int row = gid / VPR, col = gid - row * VPR;
+            *(u32x4 *)(buf + row * ROWB + col * 16) = reg[i];
+        }
+    }
+
+    // This wave's B operands (its CPW row blocks of the group's queries) straight
+    // into registers; rows >= R are zero.
+    __device__ static void load_q(const MfArgs &a, int b, int g, int wr, int n, int kg, u32x4 (*qb)[KS])
+    {
+        const int r = a.n_h / a.n_kv;
+        const uint16_t *q0 = a.q_win + (size_t)(b * a.n_h + g * r) * a.w * D;
+#pragma unroll
+        for (int cb = 0; cb < CPW; ++cb) {
+            const int row = (wr * CPW + cb) * 16 + n;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                qb[cb][s] = row < a.R ? *((const u32x4 *)(q0 + (size_t)row * D + 32 * s + 8 * kg))
+                                      : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    __device__ static void load_a(const unsigned char *buf, int tile, int n, int kg, u32x4 *ka)
+    {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ka[s] = *(const u32x4 *)(buf + (tile * 16 + n) * ROWB + (4 * s + kg) * 16);
+    }
+
+    __device__ static f32x4_t mma(const u32x4 *ka, const u32x4 *qb)
+    {
+        f32x4_t acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[s]), as_bf16x8(qb[s]), acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+// Pass 1: per row, max logit m and sum of exp2((x - m) c) over one chunk's visible
+// tokens, merged across lane groups and token groups in a fixed order.
+// Streams stages [0, n_st) of a chunk through LDS.  Stage j's loads are issued P - 1
+// steps before it is stored to LDS (register ring ring[j % P]), so every work-group
+// keeps up to P stages of K in flight.  BODY(buf, st) runs on the stage in LDS;
+// POST(st) runs after the barrier that ends step st.  The loop is unrolled by P so
+// the ring index is a compile-time constant, and every load and LDS store in it is
+// unconditional (look-ahead past the last stage re-reads the last stage, skipped
+// steps only skip BODY/POST): the compiler can then count outstanding loads exactly
+// instead of draining the ring at every step.
+template <int D, int RT, typename BODY, typename POST>
+__device__ __forceinline__ void stream_stages(const uint16_t *__restrict__ kunit, int ch0, int S, int n_st,
+                                              unsigned char *kbuf, BODY body, POST post)
 {
-    constexpr int KS = D / 16;
-    const int r = a.n_h / a.n_kv;
-    const uint16_t *q0 = a.q_win + (size_t)(b * a.n_h + g * r) * a.w * D;
+    using C = Sc<D, RT>;
+    constexpr int P = C::P;
+    if (n_st <= 0) return;
+    const int last_st = n_st - 1;
+    u32x4 ring[P][C::LOADS];
 #pragma unroll
-    for (int ct = 0; ct < RT; ++ct) {
-        const int row = ct * 32 + n;
-        if (row < a.R) {
-            const u32x4 *p = (const u32x4 *)(q0 + (size_t)row * D + h * (D / 2));
+    for (int q = 0; q < P; ++q) C::load_stage(kunit, ch0 + min(q, last_st) * C::ST, S, ring[q]);
+    C::store_stage(kbuf, ring[0]);
+    __syncthreads();
+    for (int base = 0; base < n_st; base += P) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) qb[ct][s] = as_bf16x8(p[s]);
-        } else {
+        for (int q = 0; q < P; ++q) {
+            const int st = base + q;
+            C::load_stage(kunit, ch0 + min(st + P, last_st) * C::ST, S, ring[q]);
+            if (st < n_st) body(kbuf + (st & 1) * C::STAGE_BYTES, st);
+            C::store_stage(kbuf + ((st + 1) & 1) * C::STAGE_BYTES, ring[(q + 1) % P]);
+            __syncthreads();
+            if (st < n_st) post(st);
+        }
+    }
+}
+
+template <int D, int RT, bool MASK>
+__device__ __forceinline__ void stats_stage(const unsigned char *buf, int st0, int tg, int n, int kg,
+                                            const u32x4 (*qb)[Sc<D, RT>::KS], const int *last, float c,
+                                            float *m, float *l)
+{
+    using C = Sc<D, RT>;
+    constexpr int NV = 4 * C::PAIR;                      // logits per lane per row block per max
 #pragma unroll
-            for (int s = 0; s < KS; ++s) qb[ct][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int p0 = 0; p0 < C::TPG; p0 += C::PAIR) {
+        float x[C::CPW][NV];
+#pragma unroll
+        for (int pp = 0; pp < C::PAIR; ++pp) {
+            const int tile = tg + (p0 + pp) * C::TG;
+            u32x4 ka[C::KS];
+            C::load_a(buf, tile, n, kg, ka);
+#pragma unroll
+            for (int cb = 0; cb < C::CPW; ++cb) {
+                const f32x4_t x4 = C::mma(ka, qb[cb]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[cb][4 * pp + j] = x4[j];
+                    if (MASK && st0 + tile * 16 + 4 * kg + j > last[cb]) x[cb][4 * pp + j] = -INFINITY;
+                }
+            }
+        }
+#pragma unroll
+        for (int cb = 0; cb < C::CPW; ++cb) {
+            float mx = m[cb];
+#pragma unroll
+            for (int j = 0; j < NV; ++j) mx = fmaxf(mx, x[cb][j]);
+            if (!MASK || mx != -INFINITY) {
+                const float nmc = -mx * c;
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int j = 0; j < NV; j += 2) {
+                    s0 += fast_exp2(fmaf(x[cb][j], c, nmc));
+                    s1 += fast_exp2(fmaf(x[cb][j + 1], c, nmc));
+                }
+                l[cb] = fmaf(l[cb], fast_exp2(fmaf(m[cb], c, nmc)), s0 + s1);
+                m[cb] = mx;
+            }
         }
     }
 }
 
 template <int D, int RT>
-__global__ __launch_bounds__(kMfThreads, 1) void mfma_stats_kernel(MfArgs a)
+__global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4))) void mfma_stats_kernel(MfArgs a)
 {
-    using T = MfmaTile<D, RT>;
-    constexpr int KS = T::KS;
-    __shared__ float sm_m[kMfWaves][RT * 32];
-    __shared__ float sm_l[kMfWaves][RT * 32];
+    using C = Sc<D, RT>;
+    constexpr int KS = C::KS;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *kbuf = lds;                           // 2 stages
+    __shared__ float sm_m[C::TG][RT * 16];
+    __shared__ float sm_l[C::TG][RT * 16];
 
     const int chunk = blockIdx.x;
     const int ul = blockIdx.y;
@@ -279,115 +395,171 @@ __global__ __launch_bounds__(kMfThreads, 1) void mfma_stats_kernel(MfArgs a)
     const int g = u - b * a.n_kv;
     const int S = clamp_len(a.seq_lens, b, a.s_max);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int n = lane & 31, h = lane >> 5;
-
-    bf16x8_t qb[RT][KS];
-    load_q<D, RT>(a, b, g, n, h, qb);
-
-    // last visible token of this lane's row in each row block
-    int last[RT];
-#pragma unroll
-    for (int ct = 0; ct < RT; ++ct) {
-        const int row = ct * 32 + n;
-        const int i = row % a.w;
-        last[ct] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
-    }
-    const int all_vis = a.wic ? S - a.w : S - 1;   // every row sees tokens <= all_vis
-
-    float m[RT], l[RT];
-#pragma unroll
-    for (int ct = 0; ct < RT; ++ct) {
-        m[ct] = -INFINITY;
-        l[ct] = 0.f;
-    }
+    const int n = lane & 15, kg = lane >> 4;
+    const int wr = wv % C::WPR, tg = wv / C::WPR;
     const uint16_t *kunit = a.k + (size_t)u * a.s_max * D;
-    const int tile0 = chunk * a.chunk_tokens;
+    const int ch0 = chunk * a.chunk_tokens;
+    int n_st = (min(ch0 + a.chunk_tokens, S) - ch0 + C::ST - 1) / C::ST;
+    n_st = n_st < 0 ? 0 : n_st;
 
-    for (int it = 0; it < a.tiles_per_wave; ++it) {
-        const int t0 = tile0 + (it * kMfWaves + wv) * 32;
-        if (t0 >= S) break;
-        u32x4 ka[KS];
-        T::load_k(kunit, min(t0 + n, S - 1), h, ka);
-        f32x16_t acc[RT];
-        T::mma(ka, qb, acc);
-        const bool full = t0 + 31 <= all_vis;
+    u32x4 qb[C::CPW][KS];
+    C::load_q(a, b, g, wr, n, kg, qb);
+    int last[C::CPW];
 #pragma unroll
-        for (int ct = 0; ct < RT; ++ct) {
-            float x[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) x[j] = acc[ct][j];
-            if (!full) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (t0 + acc_token(j, h) > last[ct]) x[j] = -INFINITY;
-            }
-            float lm = x[0];
-#pragma unroll
-            for (int j = 1; j < 16; ++j) lm = fmaxf(lm, x[j]);
-            const float mn = fmaxf(m[ct], lm);
-            if (mn != -INFINITY) {
-                const float nmc = -mn * a.c;
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) s += fast_exp2(fmaf(x[j], a.c, nmc));
-                l[ct] = fmaf(l[ct], fast_exp2(fmaf(m[ct], a.c, nmc)), s);
-                m[ct] = mn;
-            }
-        }
+    for (int cb = 0; cb < C::CPW; ++cb) {
+        const int i = ((wr * C::CPW + cb) * 16 + n) % a.w;
+        last[cb] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
     }
-    // merge the two lane halves (same rows, different tokens), then the waves
+    const int all_vis = a.wic ? S - a.w : S - 1;          // every row sees tokens <= all_vis
+    float m[C::CPW], l[C::CPW];
 #pragma unroll
-    for (int ct = 0; ct < RT; ++ct) {
-        const float m2 = shfl_xor_f(m[ct], 32);
-        const float l2 = shfl_xor_f(l[ct], 32);
-        const float M = fmaxf(m[ct], m2);
-        if (M != -INFINITY) {
-            l[ct] = l[ct] * fast_exp2((m[ct] - M) * a.c) + l2 * fast_exp2((m2 - M) * a.c);
-            m[ct] = M;
+    for (int cb = 0; cb < C::CPW; ++cb) {
+        m[cb] = -INFINITY;
+        l[cb] = 0.f;
+    }
+    stream_stages<D, RT>(kunit, ch0, S, n_st, kbuf,
+        [&](const unsigned char *cur, int st) {
+            const int st0 = ch0 + st * C::ST;
+            if (st0 + C::ST - 1 <= all_vis)
+                stats_stage<D, RT, false>(cur, st0, tg, n, kg, qb, last, a.c, m, l);
+            else
+                stats_stage<D, RT, true>(cur, st0, tg, n, kg, qb, last, a.c, m, l);
+        },
+        [&](int) {});
+    // merge the four lane groups of a row (lanes n, n+16, n+32, n+48), then the token groups
+#pragma unroll
+    for (int cb = 0; cb < C::CPW; ++cb) {
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+            const float m2 = shfl_xor_f(m[cb], off);
+            const float l2 = shfl_xor_f(l[cb], off);
+            const float Mx = fmaxf(m[cb], m2);
+            if (Mx != -INFINITY) {
+                l[cb] = l[cb] * fast_exp2((m[cb] - Mx) * a.c) + l2 * fast_exp2((m2 - Mx) * a.c);
+                m[cb] = Mx;
+            }
         }
-        if (h == 0) {
-            sm_m[wv][ct * 32 + n] = m[ct];
-            sm_l[wv][ct * 32 + n] = l[ct];
+        if (kg == 0) {
+            sm_m[tg][(wr * C::CPW + cb) * 16 + n] = m[cb];
+            sm_l[tg][(wr * C::CPW + cb) * 16 + n] = l[cb];
         }
     }
     __syncthreads();
-    for (int row = threadIdx.x; row < RT * 32; row += kMfThreads) {
-        float M = -INFINITY;
-        for (int w2 = 0; w2 < kMfWaves; ++w2) M = fmaxf(M, sm_m[w2][row]);
+    for (int row = threadIdx.x; row < RT * 16; row += kMfThreads) {
+        float Mx = -INFINITY;
+        for (int t2 = 0; t2 < C::TG; ++t2) Mx = fmaxf(Mx, sm_m[t2][row]);
         float L = 0.f;
-        if (M != -INFINITY)
-            for (int w2 = 0; w2 < kMfWaves; ++w2) L += sm_l[w2][row] * fast_exp2((sm_m[w2][row] - M) * a.c);
-        a.part[((size_t)ul * a.n_chunks + chunk) * (RT * 32) + row] = make_float2(M, L);
+        if (Mx != -INFINITY)
+            for (int t2 = 0; t2 < C::TG; ++t2) L += sm_l[t2][row] * fast_exp2((sm_m[t2][row] - Mx) * a.c);
+        a.part[((size_t)ul * a.n_chunks + chunk) * (RT * 16) + row] = make_float2(Mx, L);
     }
 }
 
-// Merges the chunk partials of each row in chunk order, in double.
-__global__ __launch_bounds__(128) void mfma_merge_kernel(const float2 *__restrict__ part, int n_chunks, int rpad,
-                                                         int R, float c, float2 *__restrict__ fin)
+// Merges the chunk partials of every row in a fixed order.  blockDim = 1024:
+// thread (slice, row) folds chunks slice, slice + slices, ... online (rescale factors
+// in fp32, sums in double); the slices are then folded in slice order.
+constexpr int kMergeThreads = 1024;
+
+__global__ __launch_bounds__(kMergeThreads) void mfma_merge_kernel(const float2 *__restrict__ part, int n_chunks,
+                                                                    int rpad, int R, float c,
+                                                                    float2 *__restrict__ fin)
 {
-    const int ul = blockIdx.y;
-    const int row = blockIdx.x * 128 + threadIdx.x;
-    if (row >= rpad) return;
+    __shared__ float sm_M[kMergeThreads];
+    __shared__ double sm_L[kMergeThreads];
+    const int ul = blockIdx.x;
+    const int slices = kMergeThreads / rpad;
+    const int row = threadIdx.x % rpad;
+    const int slice = threadIdx.x / rpad;
     const float2 *p = part + (size_t)ul * n_chunks * rpad + row;
-    float M = -INFINITY;
-    for (int ch = 0; ch < n_chunks; ++ch) M = fmaxf(M, p[(size_t)ch * rpad].x);
-    float2 res = make_float2(0.f, 0.f);
-    if (row < R && M != -INFINITY) {
-        double L = 0.0;
-        for (int ch = 0; ch < n_chunks; ++ch) {
-            const float2 v = p[(size_t)ch * rpad];
-            if (v.x != -INFINITY) L += (double)v.y * exp2((double)(v.x - M) * (double)c);
+    float Mx = -INFINITY;
+    double L = 0.0;
+    for (int ch0 = slice; slice < slices && ch0 < n_chunks; ch0 += 8 * slices) {
+        float2 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int ch = ch0 + q * slices;
+            v[q] = ch < n_chunks ? p[(size_t)ch * rpad] : make_float2(-INFINITY, 0.f);
         }
-        if (L > 0.0) res = make_float2(-M * c, (float)(1.0 / L));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (v[q].x == -INFINITY) continue;
+            if (v[q].x > Mx) {
+                L = L * (double)fast_exp2((Mx - v[q].x) * c) + (double)v[q].y;
+                Mx = v[q].x;
+            } else {
+                L += (double)v[q].y * (double)fast_exp2((v[q].x - Mx) * c);
+            }
+        }
+    }
+    sm_M[threadIdx.x] = Mx;
+    sm_L[threadIdx.x] = L;
+    __syncthreads();
+    if (slice != 0) return;
+    float Mt = -INFINITY;
+    for (int s2 = 0; s2 < slices; ++s2) Mt = fmaxf(Mt, sm_M[s2 * rpad + row]);
+    float2 res = make_float2(0.f, 0.f);
+    if (row < R && Mt != -INFINITY) {
+        double Lt = 0.0;
+        for (int s2 = 0; s2 < slices; ++s2) {
+            const float ms = sm_M[s2 * rpad + row];
+            if (ms != -INFINITY) Lt += sm_L[s2 * rpad + row] * (double)fast_exp2((ms - Mt) * c);
+        }
+        if (Lt > 0.0) res = make_float2(-Mt * c, (float)(1.0 / Lt));
     }
     fin[(size_t)ul * rpad + row] = res;
 }
 
-template <int D, int RT>
-__global__ __launch_bounds__(kMfThreads, 1) void mfma_probsum_kernel(MfArgs a)
+// Pass 2: raw[t] = sum over rows of exp2((x - M) c) / L for one chunk.  Each wave
+// sums its rows in-lane, a transposed butterfly over the 16 lanes of a token group
+// (4 -> 2 -> 1 values, then two full-sum steps, all DPP lane exchanges) leaves one
+// token per lane, and the WPR row-slice partials of a token are added in LDS in
+// slice order.
+template <int D, int RT, bool MASK>
+__device__ __forceinline__ void probsum_stage(const unsigned char *buf, int st0, int tg, int wr, int n, int kg,
+                                              const u32x4 (*qb)[Sc<D, RT>::KS], const int *last,
+                                              const float *nmc, const float *il, float c, float *red)
 {
-    using T = MfmaTile<D, RT>;
-    constexpr int KS = T::KS;
+    using C = Sc<D, RT>;
+    const int my_j = 2 * ((n >> 3) & 1) + ((n >> 2) & 1);
+#pragma unroll
+    for (int p = 0; p < C::TPG; ++p) {
+        const int tile = tg + p * C::TG;
+        u32x4 ka[C::KS];
+        C::load_a(buf, tile, n, kg, ka);
+        float cs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < C::CPW; ++cb) {
+            const f32x4_t x = C::mma(ka, qb[cb]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float e = fast_exp2(fmaf(x[j], c, nmc[cb]));
+                if (MASK && st0 + tile * 16 + 4 * kg + j > last[cb]) e = 0.f;
+                cs[j] = fmaf(e, il[cb], cs[j]);
+            }
+        }
+        // halving steps pair lanes with opposite bit 3 (row mirror), then opposite
+        // bit 2 within a half row (half mirror); the partner holds the same token set
+        const bool u8 = (n & 8) != 0;
+        const float v0 = (u8 ? cs[2] : cs[0]) + dpp_f<kDppRowMirror>(u8 ? cs[0] : cs[2]);
+        const float v1 = (u8 ? cs[3] : cs[1]) + dpp_f<kDppRowMirror>(u8 ? cs[1] : cs[3]);
+        const bool u4 = (n & 4) != 0;
+        float v = (u4 ? v1 : v0) + dpp_f<kDppHalfMirror>(u4 ? v0 : v1);
+        v += dpp_f<kDppXor2>(v);
+        v += dpp_f<kDppXor1>(v);
+        if ((n & 3) == 0) red[wr * C::ST + tile * 16 + 4 * kg + my_j] = v;
+    }
+}
+
+template <int D, int RT>
+__global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4))) void mfma_probsum_kernel(MfArgs a)
+{
+    using C = Sc<D, RT>;
+    constexpr int KS = C::KS;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *kbuf = lds;
+    float *rawbuf = (float *)(lds + C::LDS_BYTES);       // the chunk's scores, written once at the end
+    __shared__ float red[2][C::WPR * C::ST];
+
     const int chunk = blockIdx.x;
     const int ul = blockIdx.y;
     const int u = a.unit0 + ul;
@@ -395,81 +567,65 @@ __global__ __launch_bounds__(kMfThreads, 1) void mfma_probsum_kernel(MfArgs a)
     const int g = u - b * a.n_kv;
     const int S = clamp_len(a.seq_lens, b, a.s_max);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int n = lane & 31, h = lane >> 5;
-
-    bf16x8_t qb[RT][KS];
-    load_q<D, RT>(a, b, g, n, h, qb);
-    float nmc[RT], il[RT];
-    int last[RT];
-#pragma unroll
-    for (int ct = 0; ct < RT; ++ct) {
-        const int row = ct * 32 + n;
-        const float2 f = a.fin[(size_t)ul * (RT * 32) + row];
-        nmc[ct] = f.x;
-        il[ct] = f.y;
-        const int i = row % a.w;
-        last[ct] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
-    }
-    const int all_vis = a.wic ? S - a.w : S - 1;
+    const int n = lane & 15, kg = lane >> 4;
+    const int wr = wv % C::WPR, tg = wv / C::WPR;
     const uint16_t *kunit = a.k + (size_t)u * a.s_max * D;
     float *rawu = a.raw + (size_t)u * a.s_max;
-    const int tile0 = chunk * a.chunk_tokens;
-    // this lane's token after the transposed reduction, and whether it writes
-    const int v = 8 * ((n >> 4) & 1) + 4 * ((n >> 3) & 1) + 2 * ((n >> 2) & 1) + ((n >> 1) & 1);
-    const int my_tok = acc_token(v, h);
-    const bool writer = (n & 1) == 0;
+    const int ch0 = chunk * a.chunk_tokens;
+    const int ch1 = min(ch0 + a.chunk_tokens, a.s_max);
+    int n_st = (min(ch1, S) - ch0 + C::ST - 1) / C::ST;   // stages holding cached tokens
+    n_st = n_st < 0 ? 0 : n_st;
 
-    for (int it = 0; it < a.tiles_per_wave; ++it) {
-        const int t0 = tile0 + (it * kMfWaves + wv) * 32;
-        if (t0 >= a.s_max) break;
-        if (t0 >= S) {
-            if (writer && t0 + my_tok < a.s_max) rawu[t0 + my_tok] = 0.f;
-            continue;
-        }
-        u32x4 ka[KS];
-        T::load_k(kunit, min(t0 + n, S - 1), h, ka);
-        f32x16_t acc[RT];
-        T::mma(ka, qb, acc);
-        const bool full = t0 + 31 <= all_vis;
-        float cs[16];
+    u32x4 qb[C::CPW][KS];
+    C::load_q(a, b, g, wr, n, kg, qb);
+    float nmc[C::CPW], il[C::CPW];
+    int last[C::CPW];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) cs[j] = 0.f;
-#pragma unroll
-        for (int ct = 0; ct < RT; ++ct) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float e = fast_exp2(fmaf(acc[ct][j], a.c, nmc[ct]));
-                if (!full && t0 + acc_token(j, h) > last[ct]) e = 0.f;
-                cs[j] = fmaf(e, il[ct], cs[j]);
+    for (int cb = 0; cb < C::CPW; ++cb) {
+        const int row = (wr * C::CPW + cb) * 16 + n;
+        const float2 f = a.fin[(size_t)ul * (RT * 16) + row];
+        nmc[cb] = f.x;
+        il[cb] = f.y;
+        const int i = row % a.w;
+        last[cb] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
+    }
+    const int all_vis = a.wic ? S - a.w : S - 1;
+    stream_stages<D, RT>(kunit, ch0, S, n_st, kbuf,
+        [&](const unsigned char *cur, int st) {
+            const int st0 = ch0 + st * C::ST;
+            float *rd = red[st & 1];
+            if (st0 + C::ST - 1 <= all_vis)
+                probsum_stage<D, RT, false>(cur, st0, tg, wr, n, kg, qb, last, nmc, il, a.c, rd);
+            else
+                probsum_stage<D, RT, true>(cur, st0, tg, wr, n, kg, qb, last, nmc, il, a.c, rd);
+        },
+        [&](int st) {
+            // add the row slices of this stage in order; red[st & 1] is rewritten two steps later
+            const float *rd = red[st & 1];
+            for (int t = threadIdx.x; t < C::ST; t += kMfThreads) {
+                float v = 0.f;
+                for (int r2 = 0; r2 < C::WPR; ++r2) v += rd[r2 * C::ST + t];
+                rawbuf[st * C::ST + t] = v;
             }
-        }
-        // transposed butterfly over the 32 lanes of each half: 16 -> 8 -> 4 -> 2 -> 1
-#pragma unroll
-        for (int step = 0; step < 4; ++step) {
-            const int mask = 16 >> step;
-            const int half_n = 8 >> step;
-            const bool upper = (n & mask) != 0;
-#pragma unroll
-            for (int i = 0; i < half_n; ++i) {
-                const float send = upper ? cs[i] : cs[i + half_n];
-                const float keep = upper ? cs[i + half_n] : cs[i];
-                cs[i] = keep + shfl_xor_f(send, mask);
-            }
-        }
-        cs[0] += shfl_xor_f(cs[0], 1);
-        const int t = t0 + my_tok;
-        if (writer && t < a.s_max) rawu[t] = t < S ? cs[0] : 0.f;
+        });
+    __syncthreads();
+    // the chunk's scores, 0 past the cached length
+    for (int t = threadIdx.x; ch0 + t < ch1; t += kMfThreads) {
+        const int tok = ch0 + t;
+        rawu[tok] = (tok < S && t < n_st * C::ST) ? rawbuf[t] : 0.f;
     }
 }
 
 template <int D, int RT>
 void launch_mfma_group(const MfArgs &a, int group_units, hipStream_t stream)
 {
+    using C = Sc<D, RT>;
     dim3 grid(a.n_chunks, group_units);
-    hipLaunchKernelGGL((mfma_stats_kernel<D, RT>), grid, dim3(kMfThreads), 0, stream, a);
-    hipLaunchKernelGGL(mfma_merge_kernel, dim3((RT * 32 + 127) / 128, group_units), dim3(128), 0, stream,
-                       (const float2 *)a.part, a.n_chunks, RT * 32, a.R, a.c, (float2 *)a.fin);
-    hipLaunchKernelGGL((mfma_probsum_kernel<D, RT>), grid, dim3(kMfThreads), 0, stream, a);
+    hipLaunchKernelGGL((mfma_stats_kernel<D, RT>), grid, dim3(kMfThreads), C::LDS_BYTES, stream, a);
+    hipLaunchKernelGGL(mfma_merge_kernel, dim3(group_units), dim3(kMergeThreads), 0, stream,
+                       (const float2 *)a.part, a.n_chunks, RT * 16, a.R, a.c, (float2 *)a.fin);
+    hipLaunchKernelGGL((mfma_probsum_kernel<D, RT>), grid, dim3(kMfThreads),
+                       C::LDS_BYTES + (size_t)a.chunk_tokens * sizeof(float), stream, a);
 }
 
 template <int D>
@@ -478,8 +634,8 @@ void launch_mfma_group_rt(int rt, const MfArgs &a, int group_units, hipStream_t 
     switch (rt) {
     case 1: launch_mfma_group<D, 1>(a, group_units, stream); break;
     case 2: launch_mfma_group<D, 2>(a, group_units, stream); break;
-    case 3: launch_mfma_group<D, 3>(a, group_units, stream); break;
-    default: launch_mfma_group<D, 4>(a, group_units, stream); break;
+    case 4: launch_mfma_group<D, 4>(a, group_units, stream); break;
+    default: launch_mfma_group<D, 8>(a, group_units, stream); break;
     }
 }
 
@@ -494,23 +650,25 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
     const int units = batch * n_kv;
     p.mfma = !generic && bf16 && (d_h == 64 || d_h == 128) && p.R <= 128;
     if (p.mfma) {
-        const int rpad = (p.R + 31) / 32 * 32;
+        const int rt = p.R <= 16 ? 1 : (p.R <= 32 ? 2 : (p.R <= 64 ? 4 : 8));
+        const int rpad = rt * 16;
         // group of units whose K (bf16) fits comfortably in the MALL between passes
         const size_t unit_k = (size_t)s_max * d_h * 2;
         size_t gu = (size_t)(128u << 20) / (unit_k ? unit_k : 1);
         if (gu < 1) gu = 1;
         if (gu > (size_t)units) gu = units;
         p.group_units = (int)gu;
-        // tiles per wave: largest in {8,4,2,1} that still gives >= 2 work-groups per CU
-        int tpw = 8;
-        while (tpw > 1) {
-            const long chunks = (s_max + 128L * tpw - 1) / (128L * tpw);
-            if (chunks * p.group_units >= 2L * cus) break;
-            tpw >>= 1;
+        // tokens per work-group: the largest of 2048, 1024, 512, 256 that still gives
+        // at least four work-groups per CU (a multiple of every stage size)
+        int ct_tok = 2048;
+        while (ct_tok > 256) {
+            const long chunks = (s_max + ct_tok - 1) / ct_tok;
+            if (chunks * p.group_units >= 4L * cus) break;
+            ct_tok >>= 1;
         }
-        p.tiles_per_wave = tpw;
-        p.chunk_tokens = 128 * tpw;
-        p.n_chunks = (s_max + p.chunk_tokens - 1) / p.chunk_tokens;
+        p.tiles_per_wave = 0;
+        p.chunk_tokens = ct_tok;
+        p.n_chunks = (s_max + ct_tok - 1) / ct_tok;
         p.ws_bytes = align256((size_t)p.group_units * p.n_chunks * rpad * sizeof(float2)) +
                      align256((size_t)p.group_units * rpad * sizeof(float2)) + 256;
     } else {
@@ -528,8 +686,8 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
 {
     const int units = batch * n_kv;
     if (plan.mfma) {
-        const int rpad = (plan.R + 31) / 32 * 32;
-        const int rt = rpad / 32;
+        const int rt = plan.R <= 16 ? 1 : (plan.R <= 32 ? 2 : (plan.R <= 64 ? 4 : 8));
+        const int rpad = rt * 16;
         MfArgs a;
         a.q_win = (const uint16_t *)q_win;
         a.k = (const uint16_t *)k;
@@ -542,7 +700,6 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         a.R = plan.R;
         a.n_chunks = plan.n_chunks;
         a.chunk_tokens = plan.chunk_tokens;
-        a.tiles_per_wave = plan.tiles_per_wave;
         a.c = scale * kLog2e;
         a.part = (float2 *)ws;
         a.fin = (const float2 *)((char *)ws + align256((size_t)plan.group_units * plan.n_chunks * rpad * sizeof(float2)));

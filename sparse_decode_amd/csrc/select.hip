@@ -4,9 +4,11 @@
 // section "Quand la reutilisation est-elle exacte ?": keep original positions).
 //
 // One 1024-thread work-group per unit.  Scores become order-preserving uint32 keys
-// (-0.0 folded onto +0.0).  Three radix passes (11 + 11 + 10 bits) over a 2048-bin
-// LDS histogram find the exact k-th largest key T and how many keys equal to T are
-// still needed.  An ordered compaction then writes every key > T and the first
+// (-0.0 folded onto +0.0).  Four radix passes of 8 bits over 256-bin LDS histograms
+// find the exact k-th largest key T and how many keys equal to T are still needed.
+// Window scores cluster in a few exponents, so the lanes of one atomic instruction
+// would collide on a handful of bins; each lane adds into one of 16 histogram copies
+// (lane & 15), which caps a collision at 4 lanes.  An ordered compaction then writes every key > T and the first
 // "needed" keys == T in index order: each wave owns a contiguous slice of the
 // candidates, ballots give in-wave prefix counts, and per-wave totals give the
 // offsets -- so the indices come out ascending with no sort, and ties resolve to
@@ -20,7 +22,8 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kBins = 2048;
+constexpr int kBins = 256;          // 8-bit digits, four passes
+constexpr int kBatch = 8;           // loads in flight per thread
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -29,14 +32,15 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kCopies = 16;         // histogram copies, picked by lane & 15
+
 struct SelShared {
-    int hist[kBins];
+    int hist[kCopies][kBins];       // lanes of one instruction spread over 16 copies
     int scan[32];
     int wave_gt[kSelWaves];
     int wave_eq[kSelWaves];
     int wave_eq_base[kSelWaves];
     int wave_sel_base[kSelWaves];
-    int wave_sel_eq[kSelWaves];
     int digit;
     int above;
 };
@@ -72,37 +76,56 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         for (int t = tid; t < C; t += kSelThreads) out[t] = t;
     } else if (k_eff > 0) {
         if (RESIDENT) {
-            for (int t = tid; t < C; t += kSelThreads) keys[t] = order_key(sc[t]);
-            __syncthreads();
+            for (int t0 = tid; t0 < C; t0 += kBatch * kSelThreads) {
+                float v[kBatch];
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) {
+                    const int t = t0 + q * kSelThreads;
+                    v[q] = t < C ? sc[t] : 0.f;
+                }
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) {
+                    const int t = t0 + q * kSelThreads;
+                    if (t < C) keys[t] = order_key(v[q]);
+                }
+            }
         }
         uint32_t prefix = 0, pmask = 0;
         int k_rem = k_eff;
 #pragma unroll 1
-        for (int pass = 0; pass < 3; ++pass) {
-            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-            const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
-            for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            for (int i = tid; i < kCopies * kBins; i += kSelThreads) (&sh.hist[0][0])[i] = 0;
+            int *hw = sh.hist[lane & (kCopies - 1)];
             __syncthreads();
-            for (int t = tid; t < C; t += kSelThreads) {
-                const uint32_t kk = load_key<RESIDENT>(sc, keys, t);
-                if ((kk & pmask) == prefix) atomicAdd(&sh.hist[(kk >> shift) & dmask], 1);
+            for (int t0 = tid; t0 < C; t0 += kBatch * kSelThreads) {
+                uint32_t kk[kBatch];
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) {
+                    const int t = t0 + q * kSelThreads;
+                    kk[q] = t < C ? load_key<RESIDENT>(sc, keys, t) : 0u;
+                }
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) {
+                    const int t = t0 + q * kSelThreads;
+                    if (t < C && (kk[q] & pmask) == prefix) atomicAdd(&hw[(kk[q] >> shift) & 0xffu], 1);
+                }
             }
             __syncthreads();
-            // thread i owns digits 2047-2i (higher) and 2046-2i; prefix counts run from the top
-            const int d_hi = kBins - 1 - 2 * tid, d_lo = d_hi - 1;
-            const int c_hi = sh.hist[d_hi], c_lo = sh.hist[d_lo];
+            // thread i < 256 owns digit 255 - i; prefix counts run from the top digit down
+            int cnt = 0;
+            const int d = kBins - 1 - tid;
+            if (tid < kBins)
+                for (int c2 = 0; c2 < kCopies; ++c2) cnt += sh.hist[c2][d];
             int tot;
-            const int above = block_exclusive_scan(c_hi + c_lo, sh.scan, &tot);
-            if (above < k_rem && above + c_hi >= k_rem) {
-                sh.digit = d_hi;
+            const int above = block_exclusive_scan(cnt, sh.scan, &tot);
+            if (tid < kBins && above < k_rem && above + cnt >= k_rem) {
+                sh.digit = d;
                 sh.above = above;
-            } else if (above + c_hi < k_rem && above + c_hi + c_lo >= k_rem) {
-                sh.digit = d_lo;
-                sh.above = above + c_hi;
             }
             __syncthreads();
             prefix |= (uint32_t)sh.digit << shift;
-            pmask |= dmask << shift;
+            pmask |= 0xffu << shift;
             k_rem -= sh.above;
             __syncthreads();
         }
@@ -114,10 +137,19 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         const int w0 = wid * seg;
         const int w1 = min(C, w0 + seg);
         int gt = 0, eq = 0;
-        for (int t = w0 + lane; t < w1; t += kWave) {
-            const uint32_t kk = load_key<RESIDENT>(sc, keys, t);
-            gt += kk > T;
-            eq += kk == T;
+        for (int t0 = w0 + lane; t0 < w1; t0 += kBatch * kWave) {
+            uint32_t kk[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int t = t0 + q * kWave;
+                kk[q] = t < w1 ? load_key<RESIDENT>(sc, keys, t) : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int t = t0 + q * kWave;
+                gt += (t < w1) && kk[q] > T;
+                eq += (t < w1) && kk[q] == T;
+            }
         }
 #pragma unroll
         for (int o = kWave / 2; o > 0; o >>= 1) {
@@ -136,7 +168,6 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
                 take = take < 0 ? 0 : (take > sh.wave_eq[w2] ? sh.wave_eq[w2] : take);
                 sh.wave_eq_base[w2] = eq_run;
                 sh.wave_sel_base[w2] = sel_run;
-                sh.wave_sel_eq[w2] = take;
                 eq_run += sh.wave_eq[w2];
                 sel_run += sh.wave_gt[w2] + take;
             }
@@ -145,20 +176,27 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         int pos = sh.wave_sel_base[wid];
         int eq_seen = sh.wave_eq_base[wid];
         const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        for (int t0 = w0; t0 < w1; t0 += kWave) {
-            const int t = t0 + lane;
-            uint32_t kk = 0;
-            if (t < w1) kk = load_key<RESIDENT>(sc, keys, t);
-            const bool is_gt = (t < w1) && kk > T;
-            const bool is_eq = (t < w1) && kk == T;
-            const unsigned long long m_eq = __ballot(is_eq);
-            const int rank = eq_seen + __popcll(m_eq & below);
-            const bool sel = is_gt || (is_eq && rank < ties);
-            const unsigned long long m_sel = __ballot(sel);
-            const int p = pos + __popcll(m_sel & below);
-            if (sel && p < k_eff) out[p] = t;            // never past the budget
-            pos += __popcll(m_sel);
-            eq_seen += __popcll(m_eq);
+        for (int tb = w0; tb < w1; tb += kBatch * kWave) {
+            uint32_t kk[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int t = tb + q * kWave + lane;
+                kk[q] = t < w1 ? load_key<RESIDENT>(sc, keys, t) : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int t = tb + q * kWave + lane;
+                const bool is_gt = (t < w1) && kk[q] > T;
+                const bool is_eq = (t < w1) && kk[q] == T;
+                const unsigned long long m_eq = __ballot(is_eq);
+                const int rank = eq_seen + __popcll(m_eq & below);
+                const bool sel = is_gt || (is_eq && rank < ties);
+                const unsigned long long m_sel = __ballot(sel);
+                const int p = pos + __popcll(m_sel & below);
+                if (sel && p < k_eff) out[p] = t;            // never past the budget
+                pos += __popcll(m_sel);
+                eq_seen += __popcll(m_eq);
+            }
         }
     }
     // the always-kept trailing tokens, the -1 padding and the count
