@@ -33,8 +33,14 @@
  * Conventions for every call:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
  *     allocates no memory; scratch space is the caller's `ws` buffer, sized by the
- *     matching *_workspace() query.  Workspaces need no initialisation and may be
- *     reused freely between calls that are ordered on one stream.
+ *     matching *_workspace() query.  Where a call says so, its workspace must be
+ *     zero-filled once before first use (hipMemset, torch.zeros): every call that
+ *     completes leaves the parts it uses as counters and accumulators zero again,
+ *     so the workspace may be reused between calls of the same kind that are
+ *     ordered on one stream, under the shape rule stated with the call.  Such a
+ *     workspace written by anything else, used under another shape, or whose last
+ *     call did not complete, must be zero-filled again.  Other workspaces are
+ *     scratch: any contents will do.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Nothing blocks the host.  Calls sharing a workspace must
  *     be ordered on one stream.
@@ -126,6 +132,8 @@ const char *kvc_status_str(kvc_status status);
  * raw        [B][n_kv][s_max] float, written (required)
  * pooled     [B][n_kv][s_max] float, written (required)
  * flags      0 or KVC_SCORE_GENERIC
+ * ws         at least kvc_score_window_workspace(dims, w, flags) bytes, 16-byte
+ *            aligned: per-chunk row statistics (scratch only; any contents)
  * Arithmetic: fp32 logits (bf16 products are exact), fp32 exp2-based softmax with
  * the row sums accumulated per lane and merged in double; raw agrees with a
  * double-precision evaluation to about 1e-6 relative.  Probabilities below the
@@ -153,6 +161,13 @@ kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void 
  * k, n_keep  >= 0, cap = k + n_keep >= 1
  * idx    [B][H][k + n_keep] int32, H = n_kv, or 1 with KVC_SELECT_SHARED_HEADS
  * count  [B][H] int32
+ * ws     at least kvc_select_topk_workspace(dims, k, n_keep, flags) bytes, 16-byte
+ *        aligned, zero-filled before first use: per-unit radix histograms and a
+ *        completion counter (returned to zero by each call), per-chunk counts (and
+ *        the head sum when shared); the size depends on batch, n_kv, s_max, n_keep
+ *        and flags.  Calls with the same batch, n_kv and flags may share one
+ *        workspace without zero-filling it again (s_max, n_keep, k and seq_lens may
+ *        differ if it is large enough for each)
  * The result is unique (ties are ordered by index) and bit-reproducible.
  */
 size_t kvc_select_topk_workspace(const kvc_dims *dims, int32_t k, int32_t n_keep, int32_t flags);
@@ -201,6 +216,9 @@ kvc_status kvc_gather_compact(int32_t batch, int32_t heads, int32_t s_max, int32
  * count      [B][n_kv] int32
  * out        [B][n_h][d_h] dtype (bf16: round to nearest even)
  * lse        [B][n_h] float or NULL
+ * q, kc, vc and out 16-byte aligned
+ * ws         at least kvc_decode_attn_workspace(dims, cap) bytes, 16-byte aligned:
+ *            the split partials (scratch only; any contents, no zero-filling needed)
  * Splits over t are merged in a fixed order: results are bit-reproducible.
  */
 size_t kvc_decode_attn_workspace(const kvc_dims *dims, int32_t cap);

@@ -3,14 +3,16 @@
 // "Variantes de l'attention et compression du cache KV", section "MHA et GQA":
 // query head h reads KV head h / (n_h / n_kv)).
 //
-// Split-K over tokens.  One work-group per (KV head, token split, head chunk) loads
-// each K/V row once from HBM and uses it for every query head of the GQA group it
-// holds (up to 8), so the kernel streams the compacted cache exactly once.  A lane
-// owns 16 bytes of a row (8 bf16 or 4 fp32); a row is split over d_h/8 lanes and a
-// wave works on 64/(d_h/8) tokens at a time.  Each lane group keeps an online
-// softmax state (running max m, sum l, output o), merged across lane groups, then
-// waves, then splits -- always in the same order, so results are reproducible.
-// Logits are kept in log2 units: q is pre-multiplied by scale * log2(e).
+// Split-K over tokens.  A work-group per (token split, KV head, head chunk) loads
+// each K/V row of its split once and uses it for every query head of the chunk (up
+// to 8), so the compacted cache is streamed exactly once.  A lane owns 16 bytes of a
+// row (8 bf16 or 4 fp32); a row is spread over d_h/8 (d_h/4) lanes, a lane group.
+// Each lane group keeps an online softmax state (max m, sum l, output o); the groups
+// are folded in group order into the split's partial state, and a second kernel
+// folds the splits in split order (a kernel boundary, rather than a device-wide
+// fence per work-group, makes the partials visible across XCDs).  The result does
+// not depend on scheduling.  Logits are kept in log2 units: q is pre-multiplied by
+// scale * log2(e).
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -54,56 +56,85 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float *o, float 
     m = M;
 }
 
+struct DecArgs {
+    const void *q, *kc, *vc;
+    const int32_t *count;
+    int cap, n_h, n_kv, r, n_splits, split_tokens;
+    float c;                  // scale * log2(e)
+    float *part_o;            // [units][r][n_splits][D]
+    float2 *part_ml;          // [units][r][n_splits] (max, sum) in log2 units
+};
+
+constexpr int kMaxSplits = 1024;   // longer caches take longer splits
+constexpr int kUnroll = 4;          // token rows in flight per lane group
+
+// One work-group per (token split, KV head, head chunk) streams the split's K and V
+// rows once (the first rows are requested before the queries) and keeps an online
+// softmax state per lane group, updated once per kUnroll rows; the lane groups are
+// folded through LDS in group order and the split's partial state is stored.
 template <bool BF16, int D, int RH>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
-    const void *__restrict__ q_, const void *__restrict__ kc_, const void *__restrict__ vc_,
-    const int32_t *__restrict__ count, int cap, int n_h, int n_kv, int r, int n_splits,
-    int split_tokens, float c, float *__restrict__ part_o, float2 *__restrict__ part_ml)
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
 {
     using RV = RowVec<BF16>;
     constexpr int E = RV::kElems;           // elements per lane
     constexpr int LPT = D / E;              // lanes per token row
     constexpr int TPW = kWave / LPT;        // token rows per wave step
     constexpr int VPR = D / E;              // 16-byte vectors per row (== LPT)
+    constexpr int G = kDecWaves * TPW;      // lane groups per work-group
     static_assert(LPT <= kWave && (kWave % LPT) == 0, "row must fit a wave");
 
-    __shared__ float sm_o[kDecWaves][RH][D];
-    __shared__ float sm_m[kDecWaves][RH];
-    __shared__ float sm_l[kDecWaves][RH];
+    __shared__ float sm_o[G][RH][D];
+    __shared__ float sm_m[G][RH];
+    __shared__ float sm_l[G][RH];
+    __shared__ float sm_w[G][RH];
+    __shared__ float sm_M[RH];
 
     const int split = blockIdx.x;
     const int unit = blockIdx.y;            // b * n_kv + g
     const int hc = blockIdx.z;
-    const int b = unit / n_kv;
-    const int g = unit - b * n_kv;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x >> 6;
+    const int b = unit / a.n_kv;
+    const int g = unit - b * a.n_kv;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid >> 6;
     const int li = lane % LPT;
     const int ts = lane / LPT;
+    const int grp = wv * TPW + ts;
+    const int r = a.r;
+    const int heads = min(RH, r - hc * RH);  // query heads of this chunk
 
-    int n = count[unit];
-    n = n < 0 ? 0 : (n > cap ? cap : n);
-    const int s0 = split * split_tokens;
-    int s1 = s0 + split_tokens;
-    s1 = s1 > n ? n : s1;
+    int n = a.count[unit];
+    n = n < 0 ? 0 : (n > a.cap ? a.cap : n);
+    const int s0 = split * a.split_tokens;
+    const int s1 = min(s0 + a.split_tokens, n);
 
+    // ---- phase 1: this split
+    constexpr int step = G;                 // token rows per work-group step
+    const u32x4 *krow = (const u32x4 *)a.kc + (size_t)unit * a.cap * VPR + li;
+    const u32x4 *vrow = (const u32x4 *)a.vc + (size_t)unit * a.cap * VPR + li;
+    u32x4 kv[kUnroll], vv[kUnroll];
+    int t = s0 + grp;
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) {
+        const int tq = t + q * step;
+        kv[q] = tq < s1 ? ld_stream(krow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
+        vv[q] = tq < s1 ? ld_stream(vrow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
+    }
     // queries of this chunk of the group, pre-scaled into log2 units
     float qf[RH][E];
     const int h_first = g * r + hc * RH;
 #pragma unroll
     for (int j = 0; j < RH; ++j) {
-        const int hl = hc * RH + j;
-        if (hl < r) {
-            const u32x4 v = *((const u32x4 *)q_ + ((size_t)(b * n_h + h_first + j)) * VPR + li);
+        if (j < heads) {
+            const u32x4 v = *((const u32x4 *)a.q + ((size_t)(b * a.n_h + h_first + j)) * VPR + li);
             RV::unpack(v, qf[j]);
 #pragma unroll
-            for (int e = 0; e < E; ++e) qf[j][e] *= c;
+            for (int e = 0; e < E; ++e) qf[j][e] *= a.c;
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) qf[j][e] = 0.f;
         }
     }
-
     float m[RH], l[RH], o[RH][E];
 #pragma unroll
     for (int j = 0; j < RH; ++j) {
@@ -112,102 +143,106 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) o[j][e] = 0.f;
     }
-
-    const u32x4 *krow = (const u32x4 *)kc_ + (size_t)unit * cap * VPR + li;
-    const u32x4 *vrow = (const u32x4 *)vc_ + (size_t)unit * cap * VPR + li;
-    constexpr int UNR = 4;                  // tokens in flight per lane group
-    const int step = kDecWaves * TPW;
-    for (int t = s0 + wv * TPW + ts; t < s1; t += UNR * step) {
-        u32x4 kv[UNR], vv[UNR];
+    // A lane group is entirely in or out of range (t depends on the group only), so
+    // the row sums inside the loop always see a whole group.
+    for (; t < s1; t += kUnroll * step) {
+        u32x4 kn[kUnroll], vn[kUnroll];
+        const int tn = t + kUnroll * step;
+        if (tn < s1) {                       // next rows, requested before this batch is used
 #pragma unroll
-        for (int q = 0; q < UNR; ++q) {
-            const int tq = t + q * step;
-            if (tq < s1) {
-                kv[q] = ld_stream(krow + (size_t)tq * VPR);
-                vv[q] = ld_stream(vrow + (size_t)tq * VPR);
+            for (int q = 0; q < kUnroll; ++q) {
+                const int tq = tn + q * step;
+                kn[q] = tq < s1 ? ld_stream(krow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
+                vn[q] = tq < s1 ? ld_stream(vrow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
             }
         }
+        float x[kUnroll][RH];
 #pragma unroll
-        for (int q = 0; q < UNR; ++q) {
-            if (t + q * step >= s1) break;
-            float kf[E], vf[E];
+        for (int q = 0; q < kUnroll; ++q) {
+            float kf[E];
             RV::unpack(kv[q], kf);
-            RV::unpack(vv[q], vf);
 #pragma unroll
             for (int j = 0; j < RH; ++j) {
-                float s = 0.f;
+                float sdot = 0.f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) s = fmaf(qf[j][e], kf[e], s);
+                for (int e = 0; e < E; ++e) sdot = fmaf(qf[j][e], kf[e], sdot);
                 if (LPT == 16) {
-                    s = row16_sum(s);
+                    sdot = row16_sum(sdot);
                 } else {
 #pragma unroll
-                    for (int off = LPT / 2; off > 0; off >>= 1) s += shfl_xor_f(s, off);
+                    for (int off = LPT / 2; off > 0; off >>= 1) sdot += shfl_xor_f(sdot, off);
                 }
-                const float mn = fmaxf(m[j], s);
-                const float a = fast_exp2(m[j] - mn);
-                const float p = fast_exp2(s - mn);
-                l[j] = l[j] * a + p;
+                x[q][j] = t + q * step < s1 ? sdot : -INFINITY;
+            }
+        }
 #pragma unroll
-                for (int e = 0; e < E; ++e) o[j][e] = fmaf(o[j][e], a, p * vf[e]);
-                m[j] = mn;
+        for (int j = 0; j < RH; ++j) {
+            float mx = m[j];
+#pragma unroll
+            for (int q = 0; q < kUnroll; ++q) mx = fmaxf(mx, x[q][j]);
+            const float al = fast_exp2(m[j] - mx);           // m = -inf: 0 (l, o are 0 too)
+            float p[kUnroll], ps = 0.f;
+#pragma unroll
+            for (int q = 0; q < kUnroll; ++q) {
+                p[q] = fast_exp2(x[q][j] - mx);                // invalid rows: exp2(-inf) = 0
+                ps += p[q];
+            }
+            l[j] = fmaf(l[j], al, ps);
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[j][e] *= al;
+#pragma unroll
+            for (int q = 0; q < kUnroll; ++q) {
+                float vf[E];
+                RV::unpack(vv[q], vf);
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[j][e] = fmaf(p[q], vf[e], o[j][e]);
+            }
+            m[j] = mx;
+        }
+        if (tn < s1) {
+#pragma unroll
+            for (int q = 0; q < kUnroll; ++q) {
+                kv[q] = kn[q];
+                vv[q] = vn[q];
             }
         }
     }
-    // Lanes whose group saw no token jump here with m = -inf.  The loop above only
-    // runs for valid tokens, but the shuffles inside it need every lane of a token
-    // group: a group is either entirely in range or entirely out, since t depends
-    // on ts and the wave only.
-
-    // merge the token groups of the wave (lanes li, li + LPT, li + 2 LPT, ...)
+    // lane-group states -> LDS; the groups are folded in group order
 #pragma unroll
-    for (int off = LPT; off < kWave; off <<= 1) {
+    for (int j = 0; j < RH; ++j) {
 #pragma unroll
-        for (int j = 0; j < RH; ++j) {
-            const float m2 = shfl_xor_f(m[j], off);
-            const float l2 = shfl_xor_f(l[j], off);
-            float o2[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) o2[e] = shfl_xor_f(o[j][e], off);
-            merge_state<E>(m[j], l[j], o[j], m2, l2, o2);
-        }
-    }
-    if (ts == 0) {
-#pragma unroll
-        for (int j = 0; j < RH; ++j) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) sm_o[wv][j][li * E + e] = o[j][e];
-            if (li == 0) {
-                sm_m[wv][j] = m[j];
-                sm_l[wv][j] = l[j];
-            }
+        for (int e = 0; e < E; ++e) sm_o[grp][j][li * E + e] = o[j][e];
+        if (li == 0) {
+            sm_m[grp][j] = m[j];
+            sm_l[grp][j] = l[j];
         }
     }
     __syncthreads();
-    // merge the waves in order and write this split's partial state
-    for (int x = threadIdx.x; x < RH * D; x += kDecThreads) {
-        const int j = x / D;
-        const int d = x - j * D;
-        const int hl = hc * RH + j;
-        if (hl >= r) continue;
+    if (tid < G * RH) {
+        const int g2 = tid / RH, j = tid - (tid / RH) * RH;
         float M = -INFINITY;
-        for (int w2 = 0; w2 < kDecWaves; ++w2) M = fmaxf(M, sm_m[w2][j]);
-        float L = 0.f, O = 0.f;
-        if (M != -INFINITY) {
-            for (int w2 = 0; w2 < kDecWaves; ++w2) {
-                const float a = fast_exp2(sm_m[w2][j] - M);
-                L += sm_l[w2][j] * a;
-                O += sm_o[w2][j][d] * a;
-            }
-        }
-        const size_t slot = ((size_t)unit * r + hl) * n_splits + split;
-        part_o[slot * D + d] = O;
-        if (d == 0) part_ml[slot] = make_float2(M, L);
+        for (int x2 = 0; x2 < G; ++x2) M = fmaxf(M, sm_m[x2][j]);
+        const float mg = sm_m[g2][j];
+        sm_w[g2][j] = mg == -INFINITY ? 0.f : fast_exp2(mg - M);
+        if (g2 == 0) sm_M[j] = M;
     }
+    __syncthreads();
+    for (int x2 = tid; x2 < heads * D; x2 += kDecThreads) {
+        const int j = x2 / D;
+        const int d = x2 - j * D;
+        float L = 0.f, O = 0.f;
+        for (int g2 = 0; g2 < G; ++g2) {
+            L = fmaf(sm_w[g2][j], sm_l[g2][j], L);
+            O = fmaf(sm_w[g2][j], sm_o[g2][j][d], O);
+        }
+        const size_t slot = ((size_t)unit * r + hc * RH + j) * a.n_splits + split;
+        a.part_o[slot * D + d] = O;
+        if (d == 0) a.part_ml[slot] = make_float2(sm_M[j], L);
+    }
+
 }
 
 constexpr int kMergeThreads = 256;
-constexpr int kMaxSplits = 1024;
 
 // Deterministic block reductions (fixed shuffle tree, then waves in order).
 __device__ __forceinline__ float block_max(float v, float *red)
@@ -293,33 +328,22 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     if (lse && d == 0) lse[bh] = (L > 0.f) ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <bool BF16, int D, int RH>
-void launch_split(dim3 grid, hipStream_t stream, const void *q, const void *kc, const void *vc,
-                  const int32_t *count, int cap, int n_h, int n_kv, int r, int n_splits, int split_tokens,
-                  float c, float *part_o, float2 *part_ml)
-{
-    hipLaunchKernelGGL((decode_split_kernel<BF16, D, RH>), grid, dim3(kDecThreads), 0, stream, q, kc, vc,
-                       count, cap, n_h, n_kv, r, n_splits, split_tokens, c, part_o, part_ml);
-}
-
 template <bool BF16, int D>
-void launch_split_rh(int rh, dim3 grid, hipStream_t stream, const void *q, const void *kc, const void *vc,
-                     const int32_t *count, int cap, int n_h, int n_kv, int r, int n_splits,
-                     int split_tokens, float c, float *part_o, float2 *part_ml)
+hipError_t launch_rh(int rh, dim3 grid, hipStream_t stream, const DecArgs &a)
 {
     switch (rh) {
-    case 1: launch_split<BF16, D, 1>(grid, stream, q, kc, vc, count, cap, n_h, n_kv, r, n_splits, split_tokens, c, part_o, part_ml); break;
-    case 2: launch_split<BF16, D, 2>(grid, stream, q, kc, vc, count, cap, n_h, n_kv, r, n_splits, split_tokens, c, part_o, part_ml); break;
-    case 4: launch_split<BF16, D, 4>(grid, stream, q, kc, vc, count, cap, n_h, n_kv, r, n_splits, split_tokens, c, part_o, part_ml); break;
-    default: launch_split<BF16, D, 8>(grid, stream, q, kc, vc, count, cap, n_h, n_kv, r, n_splits, split_tokens, c, part_o, part_ml); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<BF16, D, 1>), grid, dim3(kDecThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<BF16, D, 2>), grid, dim3(kDecThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<BF16, D, 4>), grid, dim3(kDecThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<BF16, D, 8>), grid, dim3(kDecThreads), 0, stream, a); break;
     }
+    return hipGetLastError();
 }
 
 }  // namespace
 
 DecodePlan plan_decode(int batch, int n_h, int n_kv, int d_h, int cap, int cus)
 {
-    (void)d_h;
     DecodePlan p;
     const int r = n_h / n_kv;
     p.head_chunk = r >= 8 ? 8 : (r >= 4 ? 4 : (r >= 2 ? 2 : 1));
@@ -338,12 +362,9 @@ DecodePlan plan_decode(int batch, int n_h, int n_kv, int d_h, int cap, int cus)
     p.split_tokens = (int)tok;
     p.n_splits = (int)((cap + tok - 1) / tok);
     if (p.n_splits < 1) p.n_splits = 1;
-    if (p.n_splits > kMaxSplits) {           // only for caps beyond 64 * kMaxSplits tokens
-        p.split_tokens = (int)(((cap + kMaxSplits - 1) / kMaxSplits + 63) / 64 * 64);
-        p.n_splits = (cap + p.split_tokens - 1) / p.split_tokens;
-    }
     const size_t slots = (size_t)batch * n_kv * r * p.n_splits;
-    p.ws_bytes = slots * (size_t)d_h * sizeof(float) + slots * sizeof(float2) + 256;
+    p.o_bytes = (slots * (size_t)d_h * sizeof(float) + 255) / 256 * 256;
+    p.ws_bytes = p.o_bytes + slots * sizeof(float2);
     return p;
 }
 
@@ -351,28 +372,33 @@ hipError_t launch_decode(int batch, int n_h, int n_kv, int d_h, bool bf16, const
                          const void *vc, const int32_t *count, int cap, float scale, void *out, float *lse,
                          void *ws, const DecodePlan &plan, hipStream_t stream)
 {
-    const int r = n_h / n_kv;
-    const size_t slots = (size_t)batch * n_kv * r * plan.n_splits;
-    float *part_o = (float *)ws;
-    float2 *part_ml = (float2 *)((char *)ws + ((slots * d_h * sizeof(float) + 255) / 256) * 256);
-    const float c = scale * 1.4426950408889634f;
-    dim3 grid(plan.n_splits, batch * n_kv, plan.head_chunks);
-    if (bf16) {
-        if (d_h == 128) launch_split_rh<true, 128>(plan.head_chunk, grid, stream, q, kc, vc, count, cap, n_h, n_kv, r, plan.n_splits, plan.split_tokens, c, part_o, part_ml);
-        else launch_split_rh<true, 64>(plan.head_chunk, grid, stream, q, kc, vc, count, cap, n_h, n_kv, r, plan.n_splits, plan.split_tokens, c, part_o, part_ml);
-    } else {
-        if (d_h == 128) launch_split_rh<false, 128>(plan.head_chunk, grid, stream, q, kc, vc, count, cap, n_h, n_kv, r, plan.n_splits, plan.split_tokens, c, part_o, part_ml);
-        else launch_split_rh<false, 64>(plan.head_chunk, grid, stream, q, kc, vc, count, cap, n_h, n_kv, r, plan.n_splits, plan.split_tokens, c, part_o, part_ml);
-    }
-    hipError_t e = hipGetLastError();
+    DecArgs a;
+    a.q = q;
+    a.kc = kc;
+    a.vc = vc;
+    a.count = count;
+    a.cap = cap;
+    a.n_h = n_h;
+    a.n_kv = n_kv;
+    a.r = n_h / n_kv;
+    a.n_splits = plan.n_splits;
+    a.split_tokens = plan.split_tokens;
+    a.c = scale * 1.4426950408889634f;
+    a.part_o = (float *)ws;
+    a.part_ml = (float2 *)((char *)ws + plan.o_bytes);
+    const dim3 grid(plan.n_splits, batch * n_kv, plan.head_chunks);
+    hipError_t e = bf16 ? (d_h == 128 ? launch_rh<true, 128>(plan.head_chunk, grid, stream, a)
+                                      : launch_rh<true, 64>(plan.head_chunk, grid, stream, a))
+                        : (d_h == 128 ? launch_rh<false, 128>(plan.head_chunk, grid, stream, a)
+                                      : launch_rh<false, 64>(plan.head_chunk, grid, stream, a));
     if (e != hipSuccess) return e;
-    dim3 mgrid(batch * n_h);
+    const dim3 mgrid(batch * n_h);
     if (bf16) {
-        if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<true, 128>), mgrid, dim3(kMergeThreads), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
-        else hipLaunchKernelGGL((decode_merge_kernel<true, 64>), mgrid, dim3(kMergeThreads), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
+        if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<true, 128>), mgrid, dim3(kMergeThreads), 0, stream, a.part_o, a.part_ml, n_h, n_kv, a.r, a.n_splits, out, lse);
+        else hipLaunchKernelGGL((decode_merge_kernel<true, 64>), mgrid, dim3(kMergeThreads), 0, stream, a.part_o, a.part_ml, n_h, n_kv, a.r, a.n_splits, out, lse);
     } else {
-        if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<false, 128>), mgrid, dim3(kMergeThreads), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
-        else hipLaunchKernelGGL((decode_merge_kernel<false, 64>), mgrid, dim3(kMergeThreads), 0, stream, part_o, part_ml, n_h, n_kv, r, plan.n_splits, out, lse);
+        if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<false, 128>), mgrid, dim3(kMergeThreads), 0, stream, a.part_o, a.part_ml, n_h, n_kv, a.r, a.n_splits, out, lse);
+        else hipLaunchKernelGGL((decode_merge_kernel<false, 64>), mgrid, dim3(kMergeThreads), 0, stream, a.part_o, a.part_ml, n_h, n_kv, a.r, a.n_splits, out, lse);
     }
     return hipGetLastError();
 }

@@ -143,7 +143,7 @@ static kvc_status select_args(const kvc_dims *d, int32_t k, int32_t n_keep, int3
 KVC_EXPORT size_t kvc_select_topk_workspace(const kvc_dims *dims, int32_t k, int32_t n_keep, int32_t flags)
 {
     if (select_args(dims, k, n_keep, flags) != KVC_OK) return 0;
-    return kvc::select_ws_bytes(dims->batch, dims->n_kv, dims->s_max, (flags & KVC_SELECT_SHARED_HEADS) != 0);
+    return kvc::select_ws_bytes(dims->batch, dims->n_kv, dims->s_max, n_keep, (flags & KVC_SELECT_SHARED_HEADS) != 0);
 }
 
 KVC_EXPORT kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores, int32_t k, int32_t n_keep,
@@ -154,7 +154,7 @@ KVC_EXPORT kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores,
     if (st != KVC_OK) return st;
     if (!scores || !idx || !count) return KVC_ERR_INVALID_ARG;
     const bool shared = (flags & KVC_SELECT_SHARED_HEADS) != 0;
-    const size_t need = kvc::select_ws_bytes(dims->batch, dims->n_kv, dims->s_max, shared);
+    const size_t need = kvc::select_ws_bytes(dims->batch, dims->n_kv, dims->s_max, n_keep, shared);
     if (need && (!ws || ws_bytes < need || !aligned16(ws))) return KVC_ERR_WORKSPACE;
     kvc::DeviceInfo dev;
     if (kvc::device_info(&dev) != hipSuccess) return KVC_ERR_HIP;
@@ -205,7 +205,7 @@ KVC_EXPORT kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const
     if (cap < 1 || cap > (1 << 30)) return KVC_ERR_INVALID_ARG;
     if (!q || !kc || !vc || !count || !out) return KVC_ERR_INVALID_ARG;
     if (!(scale >= 0.f) || scale > 1e30f) return KVC_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(kc) || !aligned16(vc)) return KVC_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(out)) return KVC_ERR_INVALID_ARG;
     kvc::DecodePlan plan = kvc::plan_decode(dims->batch, dims->n_h, dims->n_kv, dims->d_h, cap, kPlanCus);
     if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)) return KVC_ERR_WORKSPACE;
     const float sc = scale == 0.f ? 1.0f / sqrtf((float)dims->d_h) : scale;

@@ -77,30 +77,28 @@ __device__ __forceinline__ int wave_inclusive_scan(int v)
 }
 
 // Exclusive prefix sum across the work-group (blockDim.x a multiple of 64, at most
-// 1024).  `scratch` holds at least 17 ints of LDS.  Returns the exclusive prefix and
-// writes the group total to *total.  Contains barriers: call from every thread.
+// 1024).  `scratch` holds at least 16 ints of LDS.  Returns the exclusive prefix and
+// writes the group total to *total.  Every wave adds the wave totals it needs itself
+// (broadcast LDS reads), so there is no serial pass.  Contains barriers: call from
+// every thread.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *total)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
-    int inc = wave_inclusive_scan(v);
+    const int inc = wave_inclusive_scan(v);
     if (lane == kWave - 1) scratch[wid] = inc;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int i = 0; i < nw; ++i) {
-            int t = scratch[i];
-            scratch[i] = run;
-            run += t;
-        }
-        scratch[16] = run;
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int t = i < nw ? scratch[i] : 0;
+        pre += i < wid ? t : 0;
+        tot += t;
     }
+    *total = tot;
     __syncthreads();
-    int res = scratch[wid] + inc - v;
-    *total = scratch[16];
-    __syncthreads();
-    return res;
+    return pre + inc - v;
 }
 
 }  // namespace kvc

@@ -28,6 +28,7 @@ struct DecodePlan {
     int split_tokens = 0;
     int head_chunk = 1;        // query heads handled per work-group
     int head_chunks = 1;
+    size_t o_bytes = 0;        // split partial outputs
     size_t ws_bytes = 0;
 };
 DecodePlan plan_decode(int batch, int n_h, int n_kv, int d_h, int cap, int cus);
@@ -36,7 +37,7 @@ hipError_t launch_decode(int batch, int n_h, int n_kv, int d_h, bool bf16, const
                          void *out, float *lse, void *ws, const DecodePlan &plan, hipStream_t stream);
 
 // ---- select -------------------------------------------------------------------------
-size_t select_ws_bytes(int batch, int n_kv, int s_max, bool shared);
+size_t select_ws_bytes(int batch, int n_kv, int s_max, int n_keep, bool shared);
 hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
                          int k, int n_keep, bool shared, int32_t *idx, int32_t *count, void *ws,
                          const DeviceInfo &dev, hipStream_t stream);

@@ -3,27 +3,47 @@
 // original order (Tutorial "Variantes de l'attention et compression du cache KV",
 // section "Quand la reutilisation est-elle exacte ?": keep original positions).
 //
-// One 1024-thread work-group per unit.  Scores become order-preserving uint32 keys
-// (-0.0 folded onto +0.0).  Four radix passes of 8 bits over 256-bin LDS histograms
-// find the exact k-th largest key T and how many keys equal to T are still needed.
-// Window scores cluster in a few exponents, so the lanes of one atomic instruction
-// would collide on a handful of bins; each lane adds into one of 16 histogram copies
-// (lane & 15), which caps a collision at 4 lanes.  An ordered compaction then writes every key > T and the first
-// "needed" keys == T in index order: each wave owns a contiguous slice of the
-// candidates, ballots give in-wave prefix counts, and per-wave totals give the
-// offsets -- so the indices come out ascending with no sort, and ties resolve to
-// the lower index exactly.  When the unit's keys fit in LDS they are read from HBM
-// once; otherwise each pass streams them again (from L2/MALL).
+// Scores become order-preserving uint32 keys (-0.0 folded onto +0.0).  The exact
+// k-th largest key T of a unit, and how many keys equal to T are still needed, come
+// from a three-level radix select over the key bits [21, 32), [10, 21) and [0, 10);
+// the selected set is every key > T plus the lowest-indexed keys == T, written in
+// index order.  One work-group alone streams a unit's keys far below the chip's
+// bandwidth (a CU keeps only so many cache lines in flight), so every pass is spread
+// over the unit's chunks of 2048 keys (one work-group each, every key loaded once
+// into registers) and the levels meet through per-unit histograms in global memory:
+//
+//   level1  grid (chunks, units): histogram of the top 11 bits of the chunk's keys,
+//           added into the unit histogram H1
+//   level2  finds the H1 bin d1 that holds T, histograms the next 11 bits of the
+//           chunk's keys in bin d1, adds into H2
+//   level3  finds d1 and d2, histograms the low 10 bits of the chunk's keys with
+//           prefix (d1, d2) into H3; stores the chunk's count of keys above that
+//           prefix and the suffix sums of its own level-3 histogram
+//   write   finds T and the ties to take; every chunk's count above T and at T
+//           follows from the stored per-chunk figures, so each work-group derives
+//           its output offset from the chunks before it and compacts its chunk in
+//           order (ballots give in-wave prefix counts); chunk 0 also writes the
+//           window, the padding and the count
+//
+// The unit histograms and a per-unit counter live in the workspace, which must be
+// zero when a call starts: the last write work-group of each unit clears them again.
+// Every figure is an integer count, so the result does not depend on scheduling.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
 namespace kvc {
 namespace {
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kBins = 256;          // 8-bit digits, four passes
-constexpr int kBatch = 8;           // loads in flight per thread
+constexpr int kB1 = 2048;           // key bits [21, 32)
+constexpr int kB2 = 2048;           // key bits [10, 21)
+constexpr int kB3 = 1024;           // key bits [0, 10)
+constexpr int kHistInts = kB1 + kB2 + kB3;
+constexpr int kSfx = kB3 + 4;       // suffix sums [0, kB3] of one chunk, padded
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kChunk = 2048;        // candidates per work-group
+constexpr int kKeysPerThread = kChunk / kThreads;
+constexpr int kCopies = 4;          // LDS histogram copies, picked by lane & 3
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -32,178 +52,392 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kCopies = 16;         // histogram copies, picked by lane & 15
-
-struct SelShared {
-    int hist[kCopies][kBins];       // lanes of one instruction spread over 16 copies
-    int scan[32];
-    int wave_gt[kSelWaves];
-    int wave_eq[kSelWaves];
-    int wave_eq_base[kSelWaves];
-    int wave_sel_base[kSelWaves];
-    int digit;
-    int above;
+struct UnitShape {
+    int S, C, k_eff;
 };
 
-template <bool RESIDENT>
-__device__ __forceinline__ uint32_t load_key(const float *__restrict__ sc, const uint32_t *keys, int t)
+__device__ __forceinline__ UnitShape unit_shape(const int32_t *seq_lens, int b, int s_max, int k, int n_keep)
 {
-    if (RESIDENT) return keys[t];
-    return order_key(sc[t]);
+    UnitShape s;
+    s.S = clamp_len(seq_lens, b, s_max);
+    s.C = s.S - n_keep > 0 ? s.S - n_keep : 0;
+    s.k_eff = k < s.C ? k : s.C;
+    return s;
 }
 
-template <bool RESIDENT>
-__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
-    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens, int s_max, int H, int k,
-    int n_keep, int cap, int32_t *__restrict__ idx, int32_t *__restrict__ count)
-{
-    extern __shared__ uint32_t dyn[];
-    __shared__ SelShared sh;
-    uint32_t *keys = dyn;
+struct SelArgs {
+    const float *scores;      // [units][s_max]
+    const int32_t *seq_lens;
+    int s_max, H, k, n_keep, cap;
+    int n_chunks;
+    int32_t *hist;            // [units][kHistInts]: H1, H2, H3 (zero between calls)
+    int32_t *done;            // [units]: write work-groups past their histogram reads (zero between calls)
+    int32_t *above12;         // [units][n_chunks]: chunk keys above prefix (d1, d2)
+    int32_t *sfx3;            // [units][n_chunks][kSfx]: suffix sums of the chunk's H3 part
+    int32_t *idx;             // [units][cap]
+    int32_t *count;           // [units]
+};
 
-    const int u = blockIdx.x;
-    const int b = u / H;
+// Histogram increment with leader aggregation: the lanes whose bin equals the first
+// active lane's bin add their count with one atomic (neighbouring tokens often share
+// a bin); the others add into their own histogram copy.
+__device__ __forceinline__ void hist_add(int *h_copy, int *h_lead, int bin)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lead = __builtin_amdgcn_readfirstlane(bin);
+    const unsigned long long act = __ballot(1);
+    const unsigned long long m = __ballot(bin == lead);
+    if (bin == lead) {
+        if (lane == __ffsll((long long)act) - 1) atomicAdd(&h_lead[lead], __popcll(m));
+    } else {
+        atomicAdd(&h_copy[bin], 1);
+    }
+}
+
+__device__ __forceinline__ void lds_clear(int (*h)[kB1])
+{
+    for (int i = threadIdx.x; i < kCopies * kB1 / 4; i += kThreads)
+        reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
+}
+
+// Adds the non-zero bins of the LDS histogram copies into the global histogram g.
+template <int NB>
+__device__ __forceinline__ void flush_hist(int (*h)[kB1], int32_t *g)
+{
+    for (int b = threadIdx.x; b < NB; b += kThreads) {
+        int s = 0;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) s += h[c][b];
+        if (s) atomicAdd(&g[b], s);
+    }
+}
+
+struct Digit {
+    int digit, above;
+};
+
+// Thread i owns bins NB-1-i*per down to NB-per-i*per of a histogram; c[p] receives
+// the count of bin (NB-1-i*per) - p.  Two 16-byte loads per 8 bins.
+template <int NB>
+__device__ __forceinline__ void load_bins(const int32_t *__restrict__ g, int (&c)[NB / kThreads])
+{
+    constexpr int per = NB / kThreads;
+    const int top = NB - 1 - (int)threadIdx.x * per;
+    const int4 *g4 = reinterpret_cast<const int4 *>(g + top - per + 1);
+#pragma unroll
+    for (int v = 0; v < per / 4; ++v) {
+        const int4 x = g4[v];                            // bins top-per+1+4v .. top-per+4+4v
+        c[per - 1 - 4 * v] = x.x;
+        c[per - 2 - 4 * v] = x.y;
+        c[per - 3 - 4 * v] = x.z;
+        c[per - 4 - 4 * v] = x.w;
+    }
+}
+
+// The bin that holds the k_rem-th largest key (counting from the top bin) and the
+// number of keys in the bins above it, from the counts load_bins gave every thread.
+template <int NB>
+__device__ __forceinline__ Digit find_digit(const int (&c)[NB / kThreads], int k_rem, int *scan, Digit *out)
+{
+    constexpr int per = NB / kThreads;
+    const int top = NB - 1 - (int)threadIdx.x * per;
+    int cnt = 0;
+#pragma unroll
+    for (int p = 0; p < per; ++p) cnt += c[p];
+    int tot;
+    int above = block_exclusive_scan(cnt, scan, &tot);
+#pragma unroll
+    for (int p = 0; p < per; ++p) {
+        if (above < k_rem && above + c[p] >= k_rem) *out = Digit{top - p, above};
+        above += c[p];
+    }
+    __syncthreads();
+    const Digit d = *out;
+    __syncthreads();
+    return d;
+}
+
+// A chunk is kChunk consecutive candidates; thread i holds keys t0 + i + q * kThreads
+// (q < kKeysPerThread), loaded once.  Slots past the chunk's end hold key 0 and are
+// masked by `valid`.
+struct ChunkKeys {
+    uint32_t key[kKeysPerThread];
+    int t0, t1;
+};
+
+__device__ __forceinline__ void load_chunk(const float *__restrict__ sc, int t0, int t1, ChunkKeys &ck)
+{
+    ck.t0 = t0;
+    ck.t1 = t1;
+    float v[kKeysPerThread];
+#pragma unroll
+    for (int q = 0; q < kKeysPerThread; ++q) {
+        const int t = t0 + (int)threadIdx.x + q * kThreads;
+        v[q] = t < t1 ? sc[t] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < kKeysPerThread; ++q) ck.key[q] = order_key(v[q]);
+}
+
+__device__ __forceinline__ bool chunk_valid(const ChunkKeys &ck, int q)
+{
+    return ck.t0 + (int)threadIdx.x + q * kThreads < ck.t1;
+}
+
+// ------------------------------------------------------------------------------ kernels
+// The work-group's unit and chunk; false when the chunk has nothing to histogram.
+__device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t0, int &t1)
+{
+    us = unit_shape(a.seq_lens, (int)blockIdx.y / a.H, a.s_max, a.k, a.n_keep);
+    t0 = (int)blockIdx.x * kChunk;
+    t1 = min(us.C, t0 + kChunk);
+    return us.k_eff > 0 && us.k_eff < us.C && t0 < us.C;
+}
+
+__global__ __launch_bounds__(kThreads) void sel_level1_kernel(SelArgs a)
+{
+    __shared__ int h[kCopies][kB1];
+    const int u = blockIdx.y;
+    UnitShape us;
+    int t0, t1;
+    if (!chunk_of(a, us, t0, t1)) return;
+    ChunkKeys ck;
+    load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
+    lds_clear(h);
+    __syncthreads();
+    int *hc = h[threadIdx.x & (kCopies - 1)];
+#pragma unroll
+    for (int q = 0; q < kKeysPerThread; ++q)
+        if (chunk_valid(ck, q)) hist_add(hc, h[0], (int)(ck.key[q] >> 21));
+    __syncthreads();
+    flush_hist<kB1>(h, a.hist + (size_t)u * kHistInts);
+}
+
+__global__ __launch_bounds__(kThreads) void sel_level2_kernel(SelArgs a)
+{
+    __shared__ int h[kCopies][kB1];
+    __shared__ int scan[16];
+    __shared__ Digit dg;
+    const int u = blockIdx.y;
+    UnitShape us;
+    int t0, t1;
+    if (!chunk_of(a, us, t0, t1)) return;
+    const int32_t *H = a.hist + (size_t)u * kHistInts;
+    int c1[kB1 / kThreads];
+    load_bins<kB1>(H, c1);
+    ChunkKeys ck;
+    load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
+    lds_clear(h);
+    const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
+    int *hc = h[threadIdx.x & (kCopies - 1)];
+#pragma unroll
+    for (int q = 0; q < kKeysPerThread; ++q)
+        if (chunk_valid(ck, q) && (int)(ck.key[q] >> 21) == d1.digit)
+            hist_add(hc, h[0], (int)((ck.key[q] >> 10) & (kB2 - 1)));
+    __syncthreads();
+    flush_hist<kB2>(h, a.hist + (size_t)u * kHistInts + kB1);
+}
+
+__global__ __launch_bounds__(kThreads) void sel_level3_kernel(SelArgs a)
+{
+    __shared__ int h[kCopies][kB1];
+    __shared__ int scan[16];
+    __shared__ int wave_above[kWaves];
+    __shared__ Digit dg;
+    const int u = blockIdx.y;
+    const int j = blockIdx.x;
+    UnitShape us;
+    int t0, t1;
+    if (!chunk_of(a, us, t0, t1)) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int32_t *H = a.hist + (size_t)u * kHistInts;
+    int c1[kB1 / kThreads], c2[kB2 / kThreads];
+    load_bins<kB1>(H, c1);
+    load_bins<kB2>(H + kB1, c2);
+    ChunkKeys ck;
+    load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
+    lds_clear(h);
+    const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
+    const Digit d2 = find_digit<kB2>(c2, us.k_eff - d1.above, scan, &dg);
+    const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
+    int *hc = h[tid & (kCopies - 1)];
+    int above = 0;                                       // keys whose top 22 bits exceed pre2
+#pragma unroll
+    for (int q = 0; q < kKeysPerThread; ++q) {
+        if (!chunk_valid(ck, q)) continue;
+        const uint32_t k22 = ck.key[q] >> 10;
+        above += k22 > pre2;
+        if (k22 == pre2) hist_add(hc, h[0], (int)(ck.key[q] & (kB3 - 1)));
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) above += shfl_xor_i(above, o);
+    if (lane == 0) wave_above[tid >> 6] = above;
+    __syncthreads();
+    flush_hist<kB3>(h, a.hist + (size_t)u * kHistInts + kB1 + kB2);
+    // suffix sums of the chunk's own level-3 histogram: sfx[b] = keys with low bits >= b
+    constexpr int per = kB3 / kThreads;
+    const int top = kB3 - 1 - tid * per;
+    int c[per], cnt = 0;
+#pragma unroll
+    for (int p = 0; p < per; ++p) {
+        int s2 = 0;
+#pragma unroll
+        for (int cc = 0; cc < kCopies; ++cc) s2 += h[cc][top - p];
+        c[p] = s2;
+        cnt += s2;
+    }
+    int tot;
+    int run = block_exclusive_scan(cnt, scan, &tot);
+    int32_t *sfx = a.sfx3 + ((size_t)u * a.n_chunks + j) * kSfx;
+#pragma unroll
+    for (int p = 0; p < per; ++p) {
+        run += c[p];
+        sfx[top - p] = run;
+    }
+    if (tid == 0) {
+        sfx[kB3] = 0;
+        int s2 = 0;
+        for (int w = 0; w < kWaves; ++w) s2 += wave_above[w];
+        a.above12[(size_t)u * a.n_chunks + j] = s2;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
+{
+    __shared__ int scan[16];
+    __shared__ Digit dg;
+    __shared__ int wave_gt[kWaves], wave_eq[kWaves];
+    __shared__ int chunk_take, is_last;
+    const int u = blockIdx.y;
+    const int j = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
-    const int S = clamp_len(seq_lens, b, s_max);
-    const int C = S - n_keep > 0 ? S - n_keep : 0;
-    const int k_eff = k < C ? k : C;
-    const float *sc = scores + (size_t)u * s_max;
-    int32_t *out = idx + (size_t)u * cap;
-
-    if (k_eff == C) {
-        for (int t = tid; t < C; t += kSelThreads) out[t] = t;
-    } else if (k_eff > 0) {
-        if (RESIDENT) {
-            for (int t0 = tid; t0 < C; t0 += kBatch * kSelThreads) {
-                float v[kBatch];
-#pragma unroll
-                for (int q = 0; q < kBatch; ++q) {
-                    const int t = t0 + q * kSelThreads;
-                    v[q] = t < C ? sc[t] : 0.f;
-                }
-#pragma unroll
-                for (int q = 0; q < kBatch; ++q) {
-                    const int t = t0 + q * kSelThreads;
-                    if (t < C) keys[t] = order_key(v[q]);
-                }
-            }
-        }
-        uint32_t prefix = 0, pmask = 0;
-        int k_rem = k_eff;
-#pragma unroll 1
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            for (int i = tid; i < kCopies * kBins; i += kSelThreads) (&sh.hist[0][0])[i] = 0;
-            int *hw = sh.hist[lane & (kCopies - 1)];
-            __syncthreads();
-            for (int t0 = tid; t0 < C; t0 += kBatch * kSelThreads) {
-                uint32_t kk[kBatch];
-#pragma unroll
-                for (int q = 0; q < kBatch; ++q) {
-                    const int t = t0 + q * kSelThreads;
-                    kk[q] = t < C ? load_key<RESIDENT>(sc, keys, t) : 0u;
-                }
-#pragma unroll
-                for (int q = 0; q < kBatch; ++q) {
-                    const int t = t0 + q * kSelThreads;
-                    if (t < C && (kk[q] & pmask) == prefix) atomicAdd(&hw[(kk[q] >> shift) & 0xffu], 1);
-                }
-            }
-            __syncthreads();
-            // thread i < 256 owns digit 255 - i; prefix counts run from the top digit down
-            int cnt = 0;
-            const int d = kBins - 1 - tid;
-            if (tid < kBins)
-                for (int c2 = 0; c2 < kCopies; ++c2) cnt += sh.hist[c2][d];
-            int tot;
-            const int above = block_exclusive_scan(cnt, sh.scan, &tot);
-            if (tid < kBins && above < k_rem && above + cnt >= k_rem) {
-                sh.digit = d;
-                sh.above = above;
-            }
-            __syncthreads();
-            prefix |= (uint32_t)sh.digit << shift;
-            pmask |= 0xffu << shift;
-            k_rem -= sh.above;
-            __syncthreads();
-        }
-        const uint32_t T = prefix;
-        const int ties = k_rem;                       // keys == T to take, lowest index first
-
-        // ordered compaction: wave w owns candidates [w*seg, (w+1)*seg)
-        const int seg = (((C + kSelWaves - 1) / kSelWaves) + kWave - 1) / kWave * kWave;
-        const int w0 = wid * seg;
-        const int w1 = min(C, w0 + seg);
-        int gt = 0, eq = 0;
-        for (int t0 = w0 + lane; t0 < w1; t0 += kBatch * kWave) {
-            uint32_t kk[kBatch];
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int t = t0 + q * kWave;
-                kk[q] = t < w1 ? load_key<RESIDENT>(sc, keys, t) : 0u;
-            }
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int t = t0 + q * kWave;
-                gt += (t < w1) && kk[q] > T;
-                eq += (t < w1) && kk[q] == T;
-            }
-        }
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            gt += shfl_xor_i(gt, o);
-            eq += shfl_xor_i(eq, o);
-        }
-        if (lane == 0) {
-            sh.wave_gt[wid] = gt;
-            sh.wave_eq[wid] = eq;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int eq_run = 0, sel_run = 0;
-            for (int w2 = 0; w2 < kSelWaves; ++w2) {
-                int take = ties - eq_run;
-                take = take < 0 ? 0 : (take > sh.wave_eq[w2] ? sh.wave_eq[w2] : take);
-                sh.wave_eq_base[w2] = eq_run;
-                sh.wave_sel_base[w2] = sel_run;
-                eq_run += sh.wave_eq[w2];
-                sel_run += sh.wave_gt[w2] + take;
-            }
-        }
-        __syncthreads();
-        int pos = sh.wave_sel_base[wid];
-        int eq_seen = sh.wave_eq_base[wid];
-        const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        for (int tb = w0; tb < w1; tb += kBatch * kWave) {
-            uint32_t kk[kBatch];
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int t = tb + q * kWave + lane;
-                kk[q] = t < w1 ? load_key<RESIDENT>(sc, keys, t) : 0u;
-            }
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int t = tb + q * kWave + lane;
-                const bool is_gt = (t < w1) && kk[q] > T;
-                const bool is_eq = (t < w1) && kk[q] == T;
-                const unsigned long long m_eq = __ballot(is_eq);
-                const int rank = eq_seen + __popcll(m_eq & below);
-                const bool sel = is_gt || (is_eq && rank < ties);
-                const unsigned long long m_sel = __ballot(sel);
-                const int p = pos + __popcll(m_sel & below);
-                if (sel && p < k_eff) out[p] = t;            // never past the budget
-                pos += __popcll(m_sel);
-                eq_seen += __popcll(m_eq);
-            }
-        }
+    const UnitShape us = unit_shape(a.seq_lens, u / a.H, a.s_max, a.k, a.n_keep);
+    int32_t *out = a.idx + (size_t)u * a.cap;
+    if (j == 0) {
+        // the always-kept trailing tokens, the -1 padding and the count
+        const int nw = us.S - us.C;
+        for (int i = tid; i < nw; i += kThreads) out[us.k_eff + i] = us.C + i;
+        for (int i = us.k_eff + nw + tid; i < a.cap; i += kThreads) out[i] = -1;
+        if (tid == 0) a.count[u] = us.k_eff + nw;
     }
-    // the always-kept trailing tokens, the -1 padding and the count
-    const int nw = S - C;
-    for (int j = tid; j < nw; j += kSelThreads) out[k_eff + j] = C + j;
-    for (int j = k_eff + nw + tid; j < cap; j += kSelThreads) out[j] = -1;
-    if (tid == 0) count[u] = k_eff + nw;
+    const int t0 = j * kChunk;
+    if (us.k_eff == 0 || t0 >= us.C) return;
+    const int t1 = min(us.C, t0 + kChunk);
+    if (us.k_eff == us.C) {
+        for (int t = t0 + tid; t < t1; t += kThreads) out[t] = t;
+        return;
+    }
+    // wave w owns the contiguous quarter [w0, w0 + kChunk/4) of the chunk; lane l holds
+    // keys w0 + l + 64 q
+    const int w0 = t0 + wid * (kChunk / kWaves);
+    const float *sc = a.scores + (size_t)u * a.s_max;
+    const int32_t *H = a.hist + (size_t)u * kHistInts;
+    int c1[kB1 / kThreads], c2[kB2 / kThreads], c3[kB3 / kThreads];
+    load_bins<kB1>(H, c1);
+    load_bins<kB2>(H + kB1, c2);
+    load_bins<kB3>(H + kB1 + kB2, c3);
+    uint32_t key[kKeysPerThread];
+    {
+        float v[kKeysPerThread];
+#pragma unroll
+        for (int q = 0; q < kKeysPerThread; ++q) {
+            const int t = w0 + lane + q * kWave;
+            v[q] = t < t1 ? sc[t] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < kKeysPerThread; ++q) key[q] = order_key(v[q]);
+    }
+    const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
+    const Digit d2 = find_digit<kB2>(c2, us.k_eff - d1.above, scan, &dg);
+    const Digit d3 = find_digit<kB3>(c3, us.k_eff - d1.above - d2.above, scan, &dg);
+    const uint32_t T = ((uint32_t)d1.digit << 21) | ((uint32_t)d2.digit << 10) | (uint32_t)d3.digit;
+    const int ties = us.k_eff - d1.above - d2.above - d3.above;     // keys == T to take, lowest index first
+    // the last of the unit's work-groups to get here (all others have read H) returns
+    // the histograms and the counter to zero for the next call
+    if (tid == 0) {
+        const int n_wg = (us.C + kChunk - 1) / kChunk;
+        is_last = atomicAdd(&a.done[u], 1) == n_wg - 1;
+    }
+    __syncthreads();
+    if (is_last) {
+        int4 *h4 = reinterpret_cast<int4 *>(a.hist + (size_t)u * kHistInts);
+        for (int i = tid; i < kHistInts / 4; i += kThreads) h4[i] = make_int4(0, 0, 0, 0);
+        if (tid == 0) a.done[u] = 0;
+    }
+    __syncthreads();
+
+    // output offset of this chunk: the chunks before it contribute their keys above T
+    // and, lowest chunk first, their keys equal to T until `ties` are taken.  Thread i
+    // of each block of kThreads chunks holds one chunk.
+    int base = 0, eq_run = 0;
+    for (int jb = 0; jb <= j; jb += kThreads) {
+        const int jj = jb + tid;
+        int gt = 0, eq = 0;
+        if (jj <= j) {
+            const int32_t *sfx = a.sfx3 + ((size_t)u * a.n_chunks + jj) * kSfx;
+            const int s_hi = sfx[d3.digit + 1], s_at = sfx[d3.digit];
+            gt = a.above12[(size_t)u * a.n_chunks + jj] + s_hi;
+            eq = s_at - s_hi;
+        }
+        int eq_tot;
+        const int eq_before = eq_run + block_exclusive_scan(eq, scan, &eq_tot);
+        int take = ties - eq_before;
+        take = take < 0 ? 0 : (take > eq ? eq : take);
+        if (jj == j) {
+            chunk_take = take;
+        }
+        int sel_tot;
+        block_exclusive_scan(jj < j ? gt + take : 0, scan, &sel_tot);
+        base += sel_tot;
+        eq_run += eq_tot;
+    }
+    __syncthreads();
+    const int take_j = chunk_take;
+
+    // ordered compaction: per-wave counts, then ballots give in-wave prefix counts
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int q = 0; q < kKeysPerThread; ++q) {
+        const bool ok = w0 + lane + q * kWave < t1;
+        gt += ok && key[q] > T;
+        eq += ok && key[q] == T;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        gt += shfl_xor_i(gt, o);
+        eq += shfl_xor_i(eq, o);
+    }
+    if (lane == 0) {
+        wave_gt[wid] = gt;
+        wave_eq[wid] = eq;
+    }
+    __syncthreads();
+    int pos = base, eq_seen = 0;
+    for (int w = 0; w < wid; ++w) {
+        int take = take_j - eq_seen;
+        take = take < 0 ? 0 : (take > wave_eq[w] ? wave_eq[w] : take);
+        pos += wave_gt[w] + take;
+        eq_seen += wave_eq[w];
+    }
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int q = 0; q < kKeysPerThread; ++q) {
+        const int t = w0 + lane + q * kWave;
+        const bool ok = t < t1;
+        const bool is_gt = ok && key[q] > T;
+        const bool is_eq = ok && key[q] == T;
+        const unsigned long long m_eq = __ballot(is_eq);
+        const int rank = eq_seen + __popcll(m_eq & below);
+        const bool sel = is_gt || (is_eq && rank < take_j);
+        const unsigned long long m_sel = __ballot(sel);
+        const int p = pos + __popcll(m_sel & below);
+        if (sel && p < us.k_eff) out[p] = t;                     // never past the budget
+        pos += __popcll(m_sel);
+        eq_seen += __popcll(m_eq);
+    }
 }
 
 // TSP score: float sum over KV heads in head order (one selection per sequence).
@@ -219,41 +453,86 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const float *__restrict__
     out[(size_t)b * s_max + t] = s;
 }
 
+struct SelLayout {
+    int n_chunks;
+    size_t sum_off, hist_off, done_off, above_off, sfx_off, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The parts that must be zero when a call starts (counters, histograms) come first and
+// depend only on the number of units, so calls with the same batch, n_kv and flags
+// can share a workspace whatever their s_max, n_keep, k and lengths; the per-call
+// scratch follows.
+SelLayout sel_layout(int batch, int n_kv, int s_max, int n_keep, bool shared)
+{
+    SelLayout L;
+    const long units = shared ? batch : (long)batch * n_kv;
+    const long c_max = s_max - n_keep > 1 ? (long)s_max - n_keep : 1;
+    L.n_chunks = (int)((c_max + kChunk - 1) / kChunk);
+    size_t off = 0;
+    L.done_off = off;
+    off += align256((size_t)units * sizeof(int32_t));
+    L.hist_off = off;
+    off += align256((size_t)units * kHistInts * sizeof(int32_t));
+    L.sum_off = off;
+    if (shared) off += align256((size_t)batch * s_max * sizeof(float));
+    L.above_off = off;
+    off += align256((size_t)units * L.n_chunks * sizeof(int32_t));
+    L.sfx_off = off;
+    off += align256((size_t)units * L.n_chunks * kSfx * sizeof(int32_t));
+    L.bytes = off;
+    return L;
+}
+
+static_assert(kChunk == kKeysPerThread * kThreads && kChunk % (kWaves * kWave) == 0, "chunk shape");
+static_assert(kHistInts % 4 == 0 && kSfx % 4 == 0 && kB1 % 4 == 0, "16-byte aligned histogram parts");
+
 }  // namespace
 
-size_t select_ws_bytes(int batch, int n_kv, int s_max, bool shared)
+size_t select_ws_bytes(int batch, int n_kv, int s_max, int n_keep, bool shared)
 {
-    (void)n_kv;
-    return shared ? (size_t)batch * s_max * sizeof(float) + 256 : 0;
+    return sel_layout(batch, n_kv, s_max, n_keep, shared).bytes;
 }
 
 hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
                          int k, int n_keep, bool shared, int32_t *idx, int32_t *count, void *ws,
                          const DeviceInfo &dev, hipStream_t stream)
 {
-    const float *src = scores;
-    int H = n_kv;
+    (void)dev;
+    const SelLayout L = sel_layout(batch, n_kv, s_max, n_keep, shared);
+    char *w = (char *)ws;
+    SelArgs a;
+    a.scores = scores;
+    a.H = n_kv;
     if (shared) {
-        float *sum = (float *)ws;
+        float *sum = (float *)(w + L.sum_off);
         hipLaunchKernelGGL(head_sum_kernel, dim3((s_max + 255) / 256, batch), dim3(256), 0, stream, scores,
                            n_kv, s_max, sum);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        src = sum;
-        H = 1;
+        a.scores = sum;
+        a.H = 1;
     }
-    const int cap = k + n_keep;
-    const size_t static_lds = sizeof(SelShared);
-    const size_t need = (size_t)s_max * sizeof(uint32_t);
-    const bool resident = static_lds + need + 1024 <= (size_t)dev.max_lds_per_block;
-    dim3 grid(batch * H);
-    if (resident) {
-        hipLaunchKernelGGL(select_topk_kernel<true>, grid, dim3(kSelThreads), need, stream, src, seq_lens,
-                           s_max, H, k, n_keep, cap, idx, count);
-    } else {
-        hipLaunchKernelGGL(select_topk_kernel<false>, grid, dim3(kSelThreads), 0, stream, src, seq_lens, s_max,
-                           H, k, n_keep, cap, idx, count);
-    }
+    const int units = batch * a.H;
+    a.seq_lens = seq_lens;
+    a.s_max = s_max;
+    a.k = k;
+    a.n_keep = n_keep;
+    a.cap = k + n_keep;
+    a.n_chunks = L.n_chunks;
+    a.hist = (int32_t *)(w + L.hist_off);
+    a.done = (int32_t *)(w + L.done_off);
+    a.above12 = (int32_t *)(w + L.above_off);
+    a.sfx3 = (int32_t *)(w + L.sfx_off);
+    a.idx = idx;
+    a.count = count;
+
+    const dim3 grid(L.n_chunks, units);
+    hipLaunchKernelGGL(sel_level1_kernel, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(sel_level2_kernel, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(sel_level3_kernel, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(sel_write_kernel, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -150,7 +150,7 @@ def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=Non
         pooled = torch.empty((B, n_kv, s_max), dtype=torch.float32, device=k.device)
     need = score_window_workspace(dims, w, flags)
     if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=k.device)
     st = lib().kvc_score_window(ctypes.byref(dims), _ptr(q_win), _ptr(k), int(w), int(bool(window_in_cache)),
                                 int(n_keep), int(pool), float(scale), _ptr(raw), _ptr(pooled), flags,
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
@@ -182,7 +182,7 @@ def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=Non
         count = torch.empty((B, H), dtype=torch.int32, device=scores.device)
     need = select_topk_workspace(dims, k, n_keep, flags)
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=scores.device)
     st = lib().kvc_select_topk(ctypes.byref(dims), _ptr(scores), int(k), int(n_keep), flags, _ptr(idx),
                                _ptr(count), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                _stream(stream))
@@ -236,7 +236,7 @@ def decode_attn(q, kc, vc, count, *, scale=0.0, out=None, lse=None, want_lse=Tru
         lse = torch.empty((B, n_h), dtype=torch.float32, device=q.device)
     need = decode_attn_workspace(dims, cap)
     if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     st = lib().kvc_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(kc), _ptr(vc), _ptr(count), int(cap),
                                float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream))

@@ -39,9 +39,12 @@ class LayerPath:
         self.lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
         code = kvc.KVC_BF16 if wl.dtype == "bf16" else kvc.KVC_F32
         dims = kvc.make_dims(B, S, nh, nkv, d, code)
-        self.ws_score = torch.empty(max(256, kvc.score_window_workspace(dims, wl.w)), dtype=torch.uint8, device=dev)
-        self.ws_decode = torch.empty(max(256, kvc.decode_attn_workspace(dims, self.cap)), dtype=torch.uint8,
+        self.ws_score = torch.zeros(max(256, kvc.score_window_workspace(dims, wl.w)), dtype=torch.uint8, device=dev)
+        self.ws_decode = torch.zeros(max(256, kvc.decode_attn_workspace(dims, self.cap)), dtype=torch.uint8,
                                      device=dev)
+        sdims = kvc.make_dims(B, S, nkv, nkv, 128, kvc.KVC_F32)
+        self.ws_select = torch.zeros(max(256, kvc.select_topk_workspace(sdims, self.k, wl.n_keep)),
+                                     dtype=torch.uint8, device=dev)
 
     def score(self, q_win, k, seq_lens=None):
         wl = self.wl
@@ -51,7 +54,7 @@ class LayerPath:
 
     def select(self, seq_lens=None):
         return kvc.select_topk(self.pooled, self.k, self.wl.n_keep, seq_lens=seq_lens, idx=self.idx,
-                               count=self.count)
+                               count=self.count, ws=self.ws_select)
 
     def gather(self, k, v, src_pos=None):
         return kvc.gather_compact(k, self.idx, self.count, src1=v, src_pos=src_pos, dst0=self.kc, dst1=self.vc,
@@ -87,7 +90,7 @@ class TspStep:
         self.pos = torch.empty((B, 1, self.cap), dtype=torch.int32, device=dev)
         dims = kvc.make_dims(B, self.S, wl.n_kv, wl.n_kv, wl.d_h, kvc.KVC_F32)
         need = kvc.select_topk_workspace(dims, self.k, wl.n_keep, kvc.KVC_SELECT_SHARED_HEADS)
-        self.ws = torch.empty(max(256, need), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(256, need), dtype=torch.uint8, device=dev)
 
     def run(self, pooled, hidden, seq_lens=None):
         kvc.select_topk(pooled, self.k, self.wl.n_keep, seq_lens=seq_lens, shared_heads=True, idx=self.idx,

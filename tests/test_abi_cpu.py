@@ -88,8 +88,11 @@ def test_workspace_queries():
     assert 0 < small <= big
     gen = kvc.score_window_workspace(_dims(s_max=4096), 32, kvc.KVC_SCORE_GENERIC)
     assert gen >= 32 * 4 * 4096 * 4 * 8     # stored logits
-    assert kvc.select_topk_workspace(d, 64, 16) == 0
-    assert kvc.select_topk_workspace(d, 64, 16, kvc.KVC_SELECT_SHARED_HEADS) >= 1024 * 4
+    plain = kvc.select_topk_workspace(d, 64, 16)
+    assert plain >= 8 * 5120 * 4                  # three radix histograms (2048 + 2048 + 1024) per unit
+    shared = kvc.select_topk_workspace(d, 64, 16, kvc.KVC_SELECT_SHARED_HEADS)
+    assert shared >= 1024 * 4 + 5120 * 4          # head sum + one unit's histograms
+    assert kvc.select_topk_workspace(_dims(s_max=131072), 1311, 32) > plain
     assert kvc.select_topk_workspace(d, -1, 16) == 0
     assert kvc.decode_attn_workspace(d, 2080) > 0
     assert kvc.decode_attn_workspace(d, 2080) <= kvc.decode_attn_workspace(d, 8192)
@@ -111,7 +114,10 @@ def test_select_rejects_invalid_arguments():
     assert _select(_dims(), scores=None) == E
     assert _select(_dims(), idx=None) == E
     assert _select(_dims(), count=None) == E
+    assert _select(_dims()) == W                 # every selection needs its workspace
     assert _select(_dims(), flags=kvc.KVC_SELECT_SHARED_HEADS) == W
+    need = kvc.select_topk_workspace(_dims(), 64, 16)
+    assert _select(_dims(), ws=BAD, ws_bytes=need - 1) == W
 
 
 def _gather(**kw):
@@ -162,6 +168,6 @@ def test_decode_rejects_invalid_arguments():
 def test_valid_call_without_gpu_reports_hip_error():
     # every argument passes validation, so the call reaches the HIP runtime, which has no device
     assert _gather() == kvc.KVC_ERR_HIP
-    assert _select(_dims()) == kvc.KVC_ERR_HIP
+    assert _select(_dims(), ws=BAD, ws_bytes=kvc.select_topk_workspace(_dims(), 64, 16)) == kvc.KVC_ERR_HIP
     assert _decode(_dims()) == kvc.KVC_ERR_HIP
     assert _score(_dims()) == kvc.KVC_ERR_HIP

@@ -114,6 +114,26 @@ def test_decode_vs_oracle(dtype, d, n_h, n_kv, cap):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+def test_decode_workspace_reuse():
+    # one zero-filled workspace, sized for the largest cap, serves calls with the same
+    # batch and heads but other caps and counts (the finish counters reset each call)
+    _say("decode ws reuse")
+    B, n_h, n_kv, d = 2, 32, 8, 128
+    dims = kvc.make_dims(B, 1, n_h, n_kv, d, kvc.KVC_BF16)
+    ws = torch.zeros(kvc.decode_attn_workspace(dims, 5000), dtype=torch.uint8, device=DEV)
+    q = _randn((B, n_h, d), 21)
+    for cap, seed in [(5000, 1), (2080, 2), (64, 3), (5000, 4), (1, 5)]:
+        kc = _randn((B, n_kv, cap, d), 30 + seed)
+        vc = _randn((B, n_kv, cap, d), 40 + seed)
+        cnt = np.full((B, n_kv), cap, np.int32)
+        cnt[0, 1] = 0
+        cnt[1, 2] = max(0, cap // 3)
+        out, lse = kvc.decode_attn(q, kc, vc, torch.from_numpy(cnt).to(DEV), ws=ws)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.decode(host(q), host(kc), host(vc), cnt)
+        assert_decode_close(out, ref, True)
+
+
 def test_decode_closed_forms():
     _say("decode closed forms")
     n_h, n_kv, cap, d = 8, 2, 64, 128
@@ -134,9 +154,9 @@ def test_decode_closed_forms():
 
 # ===================================================================================== select
 
-def _select_case(scores_np, seq_lens, k, n_keep, shared=False):
+def _select_case(scores_np, seq_lens, k, n_keep, shared=False, ws=None):
     sc = torch.from_numpy(scores_np).to(DEV)
-    idx, cnt = kvc.select_topk(sc, k, n_keep, seq_lens=seq_lens, shared_heads=shared)
+    idx, cnt = kvc.select_topk(sc, k, n_keep, seq_lens=seq_lens, shared_heads=shared, ws=ws)
     torch.cuda.synchronize()
     ri, rc = oracle.select_topk(scores_np, k, n_keep, seq_lens=seq_lens, shared_heads=shared)
     assert np.array_equal(host(cnt), rc)
@@ -165,6 +185,11 @@ def test_select_bitexact_continuous(s_max):
     sc[0, 0, 1000:1100] = 0.5                     # a tie wall
     sc[0, 1] = 0.25                               # all equal
     sc[0, 2, ::7] = 0.0
+    # window-score-like: one narrow mode (most keys share the top 11 key bits) plus a
+    # few large outliers
+    sc[0, 3] = (0.004 * (1.0 + 0.12 * rng.standard_normal(s_max))).astype(np.float32)
+    sc[0, 3, rng.choice(s_max, s_max // 100, replace=False)] = 0.5
+    sc[0, 4] = np.float32(0.004) + np.float32(2 ** -31) * rng.integers(0, 64, s_max).astype(np.float32)
     sl = np.array([s_max], np.int32)
     for k in (1311, 2048, 7):
         _select_case(sc, sl, k, 32)
@@ -183,6 +208,26 @@ def test_select_shared_heads_and_degenerate():
     neg[0, 0, :10] = -0.0
     neg[0, 0, 10:20] = 0.0
     _select_case(neg, np.array([300], np.int32), 40, 4)            # signed scores, -0.0 == +0.0
+
+
+def test_select_workspace_reuse_across_shapes():
+    # one zero-filled workspace serves a run of calls with the same batch, n_kv and
+    # flags but other budgets, windows and lengths: each call must leave it ready
+    _say("select ws reuse")
+    rng = np.random.default_rng(11)
+    s_max = 20000
+    sc = (0.004 * (1.0 + 0.12 * rng.standard_normal((4, 8, s_max)))).astype(np.float32)
+    sc[:, :, ::97] = 0.5
+    for shared in (False, True):
+        dims = kvc.make_dims(4, s_max, 8, 8, 128, kvc.KVC_F32)
+        flags = kvc.KVC_SELECT_SHARED_HEADS if shared else 0
+        ws = torch.zeros(kvc.select_topk_workspace(dims, 1, 0, flags), dtype=torch.uint8, device=DEV)
+        for k, n_keep, lens in [(1500, 32, [20000, 7000, 20000, 1]),
+                                (10, 0, [20000, 20000, 20000, 20000]),
+                                (19990, 16, [20000, 19000, 5, 12000]),     # k >= C for some units
+                                (700, 8, [15000, 20000, 3000, 9000]),
+                                (1500, 32, [20000, 7000, 20000, 1])]:
+            _select_case(sc, np.array(lens, np.int32), k, n_keep, shared=shared, ws=ws)
 
 
 # ===================================================================================== score
