@@ -7,9 +7,14 @@ GQA decode attention over the compacted cache.  The default workload is the
 Llama-3-8B-shaped cache (32 layers, S = 32768, 32 query / 8 KV heads, d_h = 128,
 bf16, w = 32, pool 7, k = 2048 + 32 kept) with every layer's K/V resident in HBM.
 
+The timed step compresses the existing cache of all layers with one call each of
+score, select and gather (the layers are independent units of the batch), then
+runs one decode call per layer, as a model's decode step does.  The same step with
+one call per layer for every part is timed as well ("layerwise").
+
 Prints one JSON line.  `value` is whole-step algorithmic HBM traffic per second
-(GB/s); the per-step breakdown, the decode-attention GB/s over the compacted cache,
-the roofline of the dominant call and the CPU-oracle baseline ride along.
+(GB/s); the per-layer breakdown, the layerwise figures, the roofline of the
+dominant call and the CPU-oracle baseline ride along.
 """
 from __future__ import annotations
 
@@ -73,46 +78,69 @@ def main():
     kvc.lib()
     wl = synth.by_name(args.workload)
     L = args.layers or wl.layers
+    B = wl.batch
     dev = torch.device("cuda")
     print("[bench] generating %s: %d layers" % (wl.name, L), file=sys.stderr, flush=True)
-    layers = []
+    # Every layer's cache lives in one tensor with the layers folded into the batch
+    # ([L*B][n_kv][S][d_h]); a per-layer view is a contiguous slice of it.
+    S, d, nh, nkv = wl.s_max, wl.d_h, wl.n_h, wl.n_kv
+    K = torch.empty((L * B, nkv, S, d), dtype=wl.torch_dtype, device=dev)
+    V = torch.empty_like(K)
+    QW = torch.empty((L * B, nh, wl.w, d), dtype=wl.torch_dtype, device=dev)
+    QD = torch.empty((L, B, nh, d), dtype=wl.torch_dtype, device=dev)
+    seq_np = None
     for l in range(L):
         inp = synth.layer_inputs(wl, l, device=dev)
-        inp["seq_lens_dev"] = torch.from_numpy(inp["seq_lens"]).to(dev)
-        layers.append(inp)
+        K[l * B:(l + 1) * B].copy_(inp["k"])
+        V[l * B:(l + 1) * B].copy_(inp["v"])
+        QW[l * B:(l + 1) * B].copy_(inp["q_win"])
+        QD[l].copy_(inp["q_dec"])
+        seq_np = inp["seq_lens"]
+        del inp
     torch.cuda.synchronize()
-    path = LayerPath(wl, device=dev)        # one set of output buffers, reused by every layer
-    S, cap = wl.s_max, path.cap
-    mean_S = float(np.mean(layers[0]["seq_lens"]))
+    sl_layer = torch.from_numpy(seq_np).to(dev)
+    sl_all = torch.from_numpy(np.tile(seq_np, L)).to(dev)
+    layers = [dict(q_win=QW[l * B:(l + 1) * B], k=K[l * B:(l + 1) * B], v=V[l * B:(l + 1) * B], q_dec=QD[l],
+                   seq_lens=seq_np, seq_lens_dev=sl_layer) for l in range(L)]
+
+    path = LayerPath(wl, device=dev)                    # one layer per call, buffers reused by every layer
+    fold = LayerPath(wl, device=dev, batch=L * B)       # every layer in one call (layers folded into the batch)
+    cap = path.cap
+    mean_S = float(np.mean(seq_np))
     by = layer_bytes(wl, mean_S, cap)
     step_bytes = L * (by["score"] + by["select"] + by["gather"] + by["decode"])
+    outs = torch.empty((L, B, nh, d), dtype=wl.torch_dtype, device=dev)
+    lses = torch.empty((L, B, nh), dtype=torch.float32, device=dev)
 
-    def one_step():
+    def decode_layer(l):
+        sl = slice(l * B, (l + 1) * B)
+        kvc.decode_attn(QD[l], fold.kc[sl], fold.vc[sl], fold.count[sl], out=outs[l], lse=lses[l],
+                        ws=fold.ws_decode)
+
+    def step_folded():
+        fold.score(QW, K, sl_all)
+        fold.select(sl_all)
+        fold.gather(K, V)
+        for l in range(L):
+            decode_layer(l)
+
+    def step_per_layer():
         for inp in layers:
             path.run(inp["q_win"], inp["k"], inp["v"], inp["q_dec"], inp["seq_lens_dev"])
 
-    calls = {
+    folded_calls = {
+        "score": lambda: fold.score(QW, K, sl_all),
+        "select": lambda: fold.select(sl_all),
+        "gather": lambda: fold.gather(K, V),
+        "decode": lambda: [decode_layer(l) for l in range(L)],
+    }
+    layer_calls = {
         "score": lambda inp: path.score(inp["q_win"], inp["k"], inp["seq_lens_dev"]),
         "select": lambda inp: path.select(inp["seq_lens_dev"]),
         "gather": lambda inp: path.gather(inp["k"], inp["v"]),
         "decode": lambda inp: path.decode(inp["q_dec"]),
     }
-    names = tuple(calls)
-
-    # A decode step of the model reads every layer's compacted cache in turn; give each
-    # layer its own compacted buffers so the working set is the model's (272 MB, more
-    # than the MALL), not one layer's.
-    kcs = []
-    for inp in layers:
-        path.score(inp["q_win"], inp["k"], inp["seq_lens_dev"])
-        path.select(inp["seq_lens_dev"])
-        path.gather(inp["k"], inp["v"])
-        kcs.append((path.kc.clone(), path.vc.clone(), path.count.clone(), inp["q_dec"]))
-    torch.cuda.synchronize()
-
-    def decode_all():
-        for kc, vc, cnt, q in kcs:
-            kvc.decode_attn(q, kc, vc, cnt, out=path.out, lse=path.lse, ws=path.ws_decode)
+    names = tuple(layer_calls)
 
     # Capture every timed sequence as a HIP graph: a serving loop replays the step
     # rather than paying a Python launch per kernel.
@@ -129,9 +157,12 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    g_step = capture(one_step)
-    g_call = {n: capture(lambda n=n: [calls[n](inp) for inp in layers]) for n in names}
-    g_dec_all = capture(decode_all)
+    step_folded()                       # fills fold.kc/vc/count before the decode graph is captured
+    torch.cuda.synchronize()
+    g_step = capture(step_folded)
+    g_layer_step = capture(step_per_layer)
+    g_fold = {n: capture(folded_calls[n]) for n in names}
+    g_call = {n: capture(lambda n=n: [layer_calls[n](inp) for inp in layers]) for n in names}
 
     def timed(fn, reps):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -144,7 +175,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps       # ms
 
-    # ---------------------------------------------------------------- timed region 1: whole steps
+    # ---------------------------------------------------------------- timed region: whole steps
     for _ in range(args.warmup):
         g_step.replay()
     torch.cuda.synchronize()
@@ -153,15 +184,17 @@ def main():
     wall = time.perf_counter() - t0
     print("[bench] %d steps: %.3f ms/step (wall %.3f s)" % (args.steps, ms_per_step, wall), file=sys.stderr, flush=True)
 
-    # ---------------------------------------------------------------- timed region 2: each call over all layers
-    us = {}
+    # ---------------------------------------------------------------- breakdowns (graphs, HIP events)
+    g_layer_step.replay()
+    ms_per_step_layerwise = timed(g_layer_step.replay, args.steps)
+    us = {}              # folded: one call over all layers, per layer
+    us_layer = {}        # one call per layer
     for n in names:
+        g_fold[n].replay()
+        us[n] = 1000.0 * timed(g_fold[n].replay, args.steps) / L
         g_call[n].replay()
-        us[n] = 1000.0 * timed(g_call[n].replay, args.steps) / L
-    g_dec_all.replay()
-    decode_only_us = 1000.0 * timed(g_dec_all.replay, args.steps) / L
-    eager_ms = timed(one_step, max(1, args.steps // 4))
-    del kcs, g_dec_all
+        us_layer[n] = 1000.0 * timed(g_call[n].replay, args.steps) / L
+    eager_ms = timed(step_folded, max(1, args.steps // 4))
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -199,14 +232,17 @@ def main():
                "ms_per_layer": round(1000.0 * t_cpu / done, 2)}
 
     gbps = {n: by[n] / (us[n] * 1e-6) / 1e9 for n in names}
+    gbps_layer = {n: by[n] / (us_layer[n] * 1e-6) / 1e9 for n in names}
     dominant = max(names, key=lambda n: us[n])
+    kern = {"score": "kvc_score_window", "select": "kvc_select_topk", "gather": "kvc_gather_compact",
+            "decode": "kvc_decode_attn"}
     roof = {"bound": "hbm", "achieved": round(gbps[dominant], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "kvc_%s (one call)" % (
-                {"score": "score_window", "select": "select_topk", "gather": "gather_compact",
-                 "decode": "decode_attn"}[dominant]),
-            "bytes_per_launch": int(by[dominant]), "us_per_launch": round(us[dominant], 3)}
+            "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4), "traffic": None,
+            "kernel": "%s (one call over all %d layers)" % (kern[dominant], L) if dominant != "decode" else
+                      "kvc_decode_attn (one call per layer)",
+            "bytes_per_launch": int(by[dominant] * (L if dominant != "decode" else 1)),
+            "us_per_launch": round(us[dominant] * (L if dominant != "decode" else 1), 3)}
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    decode_only_gbps = by["decode"] / (decode_only_us * 1e-6) / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -221,16 +257,19 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V with planted heavy hitters; no model weights)",
         "config": {"workload": wl.name, "layers": L, "batch": wl.batch, "seq_len": S, "n_h": wl.n_h,
-                   "n_kv": wl.n_kv, "d_h": wl.d_h, "w": wl.w, "pool": wl.pool, "k": wl.k, "n_keep": wl.n_keep},
+                   "n_kv": wl.n_kv, "d_h": wl.d_h, "w": wl.w, "pool": wl.pool, "k": wl.k, "n_keep": wl.n_keep,
+                   "schedule": "score/select/gather: one call over all layers; decode: one call per layer"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_layer_us": {n: round(us[n], 3) for n in names},
         "per_layer_GBps": {n: round(gbps[n], 1) for n in names},
         "per_layer_hbm_frac": {n: round(gbps[n] / HBM_PEAK_GBPS, 4) for n in names},
-        "decode_attn_GBps_all_layers": round(decode_only_gbps, 1),
+        "layerwise": {"ms_per_step": round(ms_per_step_layerwise, 4),
+                      "value": round(step_bytes / (ms_per_step_layerwise * 1e-3) / 1e9, 2),
+                      "per_call_us": {n: round(us_layer[n], 3) for n in names},
+                      "per_call_GBps": {n: round(gbps_layer[n], 1) for n in names}},
         "eager_ms_per_step": round(eager_ms, 4),
         "timing": "HIP graph replays between HIP events on the launch stream",
-        "decode_attn_us_all_layers": round(decode_only_us, 3),
         "score_mfma_frac_algorithmic": round(by["flops_score"] / (us["score"] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
         "wall_s_timed_region": round(wall, 3),
     }

@@ -5,8 +5,7 @@
 //
 // Pure data movement, bound by HBM bandwidth: every kept row is read once and
 // written once with 16-byte vector accesses.  A row of d_h = 128 bf16 is 256 B =
-// 16 lanes; a 4096-wide hidden-state row is 8 KiB = 512 lanes.  Each thread keeps
-// several independent 16-byte loads in flight before it stores.
+// 16 lanes; a 4096-wide hidden-state row is 8 KiB = 512 lanes.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -14,11 +13,14 @@ namespace kvc {
 namespace {
 
 constexpr int kGatherThreads = 256;
-constexpr int kGatherUnroll = 4;
+constexpr int kGatherUnroll = 8;
+constexpr int kMaxBlockRows = 4096;     // rows per work-group (their indices sit in LDS)
 
 // Work-group (blockIdx.x, blockIdx.y) copies rows [blockIdx.x * rows_per_block, ...)
-// of unit blockIdx.y = b * heads + h.  tpr threads share one row (a power of two
-// <= 256); a row wider than 256 vectors is walked in strides of 256.
+// of unit blockIdx.y = b * heads + h.  The block's source rows are resolved once
+// into LDS (one dependent round trip), then every thread keeps kGatherUnroll rows
+// of 16-byte loads (times two with src1) in flight.  tpr threads share one row (a
+// power of two <= 256); a row wider than 256 vectors is walked in strides of 256.
 __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     const u32x4 *__restrict__ src0, const u32x4 *__restrict__ src1,
     const int32_t *__restrict__ src_pos, const int32_t *__restrict__ idx,
@@ -26,37 +28,39 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     int cap, int rows_per_block, u32x4 *__restrict__ dst0, u32x4 *__restrict__ dst1,
     int32_t *__restrict__ pos_out)
 {
+    __shared__ int rows[kMaxBlockRows];
     const int unit = blockIdx.y;
     const int b = unit / heads;
     const int h = unit - b * heads;
     const int list = b * idx_heads + (idx_heads == 1 ? 0 : h);
     const int r0 = blockIdx.x * rows_per_block;
-    int r1 = r0 + rows_per_block;
-    r1 = r1 > cap ? cap : r1;
+    const int r1 = min(r0 + rows_per_block, cap);
     const int32_t *lidx = idx + (size_t)list * cap;
+    int n = count[list];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+
+    // source row of every output row of the block, -1 where nothing is copied
+    for (int j = r0 + (int)threadIdx.x; j < r1; j += kGatherThreads) {
+        const int t = lidx[j];
+        const bool ok = j < n && t >= 0 && t < s_max;
+        rows[j - r0] = ok ? t : -1;
+        if (pos_out) pos_out[(size_t)unit * cap + j] = ok ? (src_pos ? src_pos[(size_t)b * s_max + t] : t) : -1;
+    }
+    __syncthreads();
 
     const int tpr = 1 << tpr_log2;
     const int rows_per_iter = kGatherThreads >> tpr_log2;
-    const int sub = threadIdx.x >> tpr_log2;          // row offset within one iteration
+    const int sub = threadIdx.x >> tpr_log2;
     const int col0 = threadIdx.x & (tpr - 1);
     const size_t src_unit = (size_t)unit * s_max * vpr;
     const size_t dst_unit = (size_t)unit * cap * vpr;
-
-    // The count and the index list are loaded together (rows past the count are
-    // dropped afterwards), so the row copies wait on one dependent round trip only.
-    int n = count[list];
-    for (int j0 = r0 + sub; j0 < r1; j0 += rows_per_iter * kGatherUnroll) {
+    const int m = min(r1, n) - r0;                       // rows of this block that are copied
+    for (int j0 = sub; j0 < m; j0 += rows_per_iter * kGatherUnroll) {
         int t[kGatherUnroll];
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
             const int j = j0 + u * rows_per_iter;
-            t[u] = j < r1 ? lidx[j] : -1;
-        }
-        n = n < 0 ? 0 : (n > cap ? cap : n);
-#pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
-            const int j = j0 + u * rows_per_iter;
-            if (j >= n || t[u] < 0 || t[u] >= s_max) t[u] = -1;
+            t[u] = j < m ? rows[j] : -1;
         }
         for (int c = col0; c < vpr; c += tpr) {
             u32x4 a[kGatherUnroll], bb[kGatherUnroll];
@@ -70,22 +74,11 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
 #pragma unroll
             for (int u = 0; u < kGatherUnroll; ++u) {
                 if (t[u] >= 0) {
-                    const size_t o = dst_unit + (size_t)(j0 + u * rows_per_iter) * vpr + c;
+                    const size_t o = dst_unit + (size_t)(r0 + j0 + u * rows_per_iter) * vpr + c;
                     dst0[o] = a[u];
                     if (src1) dst1[o] = bb[u];
                 }
             }
-        }
-    }
-    if (pos_out) {
-        n = n < 0 ? 0 : (n > cap ? cap : n);
-        for (int j = r0 + threadIdx.x; j < r1; j += kGatherThreads) {
-            int p = -1;
-            if (j < n) {
-                const int tt = lidx[j];
-                if (tt >= 0 && tt < s_max) p = src_pos ? src_pos[(size_t)b * s_max + tt] : tt;
-            }
-            pos_out[(size_t)unit * cap + j] = p;
         }
     }
 }
@@ -102,13 +95,14 @@ hipError_t launch_gather(int batch, int heads, int s_max, int row_bytes, const v
     while ((1 << (tpr_log2 + 1)) <= vpr && (1 << (tpr_log2 + 1)) <= kGatherThreads) ++tpr_log2;
     const int rows_per_iter = kGatherThreads >> tpr_log2;
     const long units = (long)batch * heads;
-    // Enough work-groups to cover every CU several times; at least one full
-    // unrolled iteration of rows per group.
+    // Enough work-groups to cover every CU several times (a small cache is spread
+    // thin: the copy is latency-bound there), at most kMaxBlockRows rows each.
     const long want_blocks = 4L * dev.cus;
     long rpb = (long)cap * units / (want_blocks > 0 ? want_blocks : 1);
-    const long min_rows = (long)rows_per_iter * kGatherUnroll;
+    const long min_rows = (long)rows_per_iter * 2;
     if (rpb < min_rows) rpb = min_rows;
     rpb = ((rpb + min_rows - 1) / min_rows) * min_rows;
+    if (rpb > kMaxBlockRows) rpb = kMaxBlockRows;
     if (rpb > cap) rpb = cap;
     if (rpb < 1) rpb = 1;
     dim3 grid((unsigned)((cap + rpb - 1) / rpb), (unsigned)units);

@@ -14,17 +14,18 @@
 //   merge   chunk partials -> (M_r, 1/L_r) per row, in chunk order, in double
 //   pass 2  logits again -> sum_r exp(x - M_r) / L_r per token
 //   pool    centred max over the candidate region
-// Units are processed in groups whose K fits the 256 MB MALL, so pass 2 re-reads K
-// from the MALL rather than from HBM.
+// All units go into one launch of each kernel.  Both passes stream K from HBM; on
+// this chip the second read is not served faster by the MALL, so nothing is gained
+// by grouping units to fit it.
 //
-// The bf16 path computes logits with v_mfma_f32_32x32x16_bf16: a wave multiplies a
-// 32-token K tile (A operand, loaded straight from HBM into registers, 128
-// contiguous bytes per lane) by the group's Q^T (B operand, resident in registers
-// for the whole chunk), giving a 32-token x 32-row fp32 tile per row block.  With
-// tokens on the M side each lane owns one row, so the row statistics of pass 1 stay
-// in-lane; pass 2 sums over rows across lanes with a transposed butterfly.  Both
-// passes evaluate exactly the same MFMA sequence, so their logits are identical.
-// Exponentials use exp2 with scale * log2(e) folded into one FMA.
+// The bf16 path computes logits with v_mfma_f32_16x16x32_bf16 (16 tokens x 16 rows
+// per tile).  K is staged through LDS with coalesced 16-byte loads, a register ring
+// keeping several stages in flight; each wave holds its rows' Q^T operands in
+// registers for the whole chunk.  Pass 1 keeps the row statistics in-lane (tokens
+// on the M side give each lane one row); pass 2 sums over rows across lanes with a
+// transposed butterfly of DPP lane exchanges.  Both passes evaluate exactly the
+// same MFMA sequence, so their logits are identical.  Exponentials use exp2 with
+// scale * log2(e) folded into one FMA.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -169,26 +170,45 @@ __global__ __launch_bounds__(kGenThreads) void gen_probsum_kernel(const float *_
 // ====================================================================================
 // Pooling: centred max of raw over the candidate region (shared by both paths)
 // ====================================================================================
-__global__ __launch_bounds__(256) void pool_kernel(const float *__restrict__ raw, const int32_t *__restrict__ seq_lens,
-                                                   int s_max, int n_kv, int n_keep, int half,
-                                                   float *__restrict__ pooled)
+constexpr int kPoolThreads = 256;
+constexpr int kPoolTile = 1024;     // tokens per work-group
+constexpr int kMaxHalf = 31;        // pool kernels up to 63
+
+// One work-group per kPoolTile tokens of a unit: the tile and its halo are staged in
+// LDS once (coalesced), then each output is the max over its window.
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restrict__ raw,
+                                                            const int32_t *__restrict__ seq_lens, int s_max,
+                                                            int n_kv, int n_keep, int half,
+                                                            float *__restrict__ pooled)
 {
+    __shared__ float tile[kPoolTile + 2 * kMaxHalf];
     const int u = blockIdx.y;
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
     const int C = S - n_keep > 0 ? S - n_keep : 0;
-    const int t = blockIdx.x * 256 + threadIdx.x;
-    if (t >= s_max) return;
+    const int t0 = blockIdx.x * kPoolTile;
     const float *rw = raw + (size_t)u * s_max;
-    float v;
-    if (t < C) {
-        const int lo = t - half < 0 ? 0 : t - half;
-        const int hi = t + half > C - 1 ? C - 1 : t + half;
-        v = rw[lo];
-        for (int x = lo + 1; x <= hi; ++x) v = fmaxf(v, rw[x]);
-    } else {
-        v = t < S ? rw[t] : 0.f;
+    const int base = t0 - half;                          // tile[i] holds raw[base + i]
+    for (int i = threadIdx.x; i < kPoolTile + 2 * half; i += kPoolThreads) {
+        const int t = base + i;
+        tile[i] = (t >= 0 && t < s_max) ? rw[t] : 0.f;
     }
-    pooled[(size_t)u * s_max + t] = v;
+    __syncthreads();
+    float *out = pooled + (size_t)u * s_max;
+#pragma unroll
+    for (int q = 0; q < kPoolTile / kPoolThreads; ++q) {
+        const int t = t0 + q * kPoolThreads + (int)threadIdx.x;
+        if (t >= s_max) break;
+        float v;
+        if (t < C) {
+            const int lo = t - half < 0 ? 0 : t - half;
+            const int hi = t + half > C - 1 ? C - 1 : t + half;
+            v = tile[lo - base];
+            for (int x = lo + 1; x <= hi; ++x) v = fmaxf(v, tile[x - base]);
+        } else {
+            v = t < S ? tile[t - base] : 0.f;
+        }
+        out[t] = v;
+    }
 }
 
 // ====================================================================================
@@ -243,7 +263,10 @@ struct Sc {
     static constexpr int PAIR = TPG < 2 ? TPG : 2;       // tiles whose logits share one max/rescale
     static_assert(LOADS >= 1 && ST * VPR % kMfThreads == 0, "stage must split evenly over the threads");
 
-    // Coalesced loads of one stage (rows clamped into [0, S)).
+    // Coalesced loads of one stage (rows clamped into [0, S)).  KEEP: ordinary loads,
+    // which leave K in the caches (the MALL) for the second pass; else loads hinted
+    // as streamed (the second pass is K's last use).
+    template <bool KEEP>
     __device__ static void load_stage(const uint16_t *__restrict__ kunit, int st0, int S, u32x4 *reg)
     {
 #pragma unroll
@@ -251,7 +274,8 @@ struct Sc {
             const int gid = i * kMfThreads + threadIdx.x;
             const int row = gid / VPR, col = gid - row * VPR;
             const int t = min(st0 + row, S - 1);
-            reg[i] = ld_stream((const u32x4 *)(kunit + (size_t)t * D) + col);
+            const u32x4 *src = (const u32x4 *)(kunit + (size_t)t * D) + col;
+            reg[i] = KEEP ? *src : ld_stream(src);
         }
     }
 
@@ -307,7 +331,7 @@ struct Sc {
 // unconditional (look-ahead past the last stage re-reads the last stage, skipped
 // steps only skip BODY/POST): the compiler can then count outstanding loads exactly
 // instead of draining the ring at every step.
-template <int D, int RT, typename BODY, typename POST>
+template <int D, int RT, bool KEEP, typename BODY, typename POST>
 __device__ __forceinline__ void stream_stages(const uint16_t *__restrict__ kunit, int ch0, int S, int n_st,
                                               unsigned char *kbuf, BODY body, POST post)
 {
@@ -317,14 +341,14 @@ __device__ __forceinline__ void stream_stages(const uint16_t *__restrict__ kunit
     const int last_st = n_st - 1;
     u32x4 ring[P][C::LOADS];
 #pragma unroll
-    for (int q = 0; q < P; ++q) C::load_stage(kunit, ch0 + min(q, last_st) * C::ST, S, ring[q]);
+    for (int q = 0; q < P; ++q) C::template load_stage<KEEP>(kunit, ch0 + min(q, last_st) * C::ST, S, ring[q]);
     C::store_stage(kbuf, ring[0]);
     __syncthreads();
     for (int base = 0; base < n_st; base += P) {
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const int st = base + q;
-            C::load_stage(kunit, ch0 + min(st + P, last_st) * C::ST, S, ring[q]);
+            C::template load_stage<KEEP>(kunit, ch0 + min(st + P, last_st) * C::ST, S, ring[q]);
             if (st < n_st) body(kbuf + (st & 1) * C::STAGE_BYTES, st);
             C::store_stage(kbuf + ((st + 1) & 1) * C::STAGE_BYTES, ring[(q + 1) % P]);
             __syncthreads();
@@ -417,7 +441,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         m[cb] = -INFINITY;
         l[cb] = 0.f;
     }
-    stream_stages<D, RT>(kunit, ch0, S, n_st, kbuf,
+    stream_stages<D, RT, true>(kunit, ch0, S, n_st, kbuf,
         [&](const unsigned char *cur, int st) {
             const int st0 = ch0 + st * C::ST;
             if (st0 + C::ST - 1 <= all_vis)
@@ -590,7 +614,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         last[cb] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
     }
     const int all_vis = a.wic ? S - a.w : S - 1;
-    stream_stages<D, RT>(kunit, ch0, S, n_st, kbuf,
+    stream_stages<D, RT, false>(kunit, ch0, S, n_st, kbuf,
         [&](const unsigned char *cur, int st) {
             const int st0 = ch0 + st * C::ST;
             float *rd = red[st & 1];
@@ -652,12 +676,10 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
     if (p.mfma) {
         const int rt = p.R <= 16 ? 1 : (p.R <= 32 ? 2 : (p.R <= 64 ? 4 : 8));
         const int rpad = rt * 16;
-        // group of units whose K (bf16) fits comfortably in the MALL between passes
-        const size_t unit_k = (size_t)s_max * d_h * 2;
-        size_t gu = (size_t)(128u << 20) / (unit_k ? unit_k : 1);
-        if (gu < 1) gu = 1;
-        if (gu > (size_t)units) gu = units;
-        p.group_units = (int)gu;
+        // every unit in one launch: the second pass streams K from HBM again either
+        // way (measured: keeping a group's K within the MALL size does not make the
+        // re-read faster), and one launch amortises the kernel boundaries
+        p.group_units = units;
         // tokens per work-group: the largest of 2048, 1024, 512, 256 that still gives
         // at least four work-groups per CU (a multiple of every stage size)
         int ct_tok = 2048;
@@ -730,8 +752,8 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(pool_kernel, dim3((s_max + 255) / 256, units), dim3(256), 0, stream, raw, seq_lens, s_max,
-                       n_kv, n_keep, pool / 2, pooled);
+    hipLaunchKernelGGL(pool_kernel, dim3((s_max + kPoolTile - 1) / kPoolTile, units), dim3(kPoolThreads), 0, stream,
+                       raw, seq_lens, s_max, n_kv, n_keep, pool / 2, pooled);
     return hipGetLastError();
 }
 

@@ -98,6 +98,36 @@ def test_cfg2_llama3_8b_32k():
     _layer_parity(wl, 31, check_planted=False)
 
 
+def test_cfg2_layers_folded_into_batch():
+    # compressing an existing cache of several layers in one call: the layers are
+    # independent units of the batch; every layer must match the oracle on its own
+    wl = synth.WORKLOADS[2]
+    layers = (0, 7, 31)
+    _say(wl.name, "layers", layers, "in one call")
+    inps = [synth.layer_inputs(wl, l, device="cuda") for l in layers]
+    q = torch.cat([x["q_win"] for x in inps]).contiguous()
+    k = torch.cat([x["k"] for x in inps]).contiguous()
+    v = torch.cat([x["v"] for x in inps]).contiguous()
+    sl = np.concatenate([x["seq_lens"] for x in inps])
+    sl_dev = torch.from_numpy(sl).cuda()
+    path = LayerPath(wl, batch=len(layers))
+    path.score(q, k, sl_dev)
+    path.select(sl_dev)
+    path.gather(k, v)
+    torch.cuda.synchronize()
+    for i, x in enumerate(inps):
+        _say("  layer", layers[i])
+        rraw, rpooled = oracle.score_window(host(x["q_win"]), host(x["k"]), wl.w, seq_lens=x["seq_lens"],
+                                            window_in_cache=wl.window_in_cache, n_keep=wl.n_keep, pool=wl.pool)
+        assert_scores_close(path.raw[i:i + 1], rraw, "raw")
+        assert_scores_close(path.pooled[i:i + 1], rpooled, "pooled")
+        ri, rc = oracle.select_topk(rpooled, wl.k, wl.n_keep, seq_lens=x["seq_lens"])
+        check_selection(path.idx[i:i + 1], path.count[i:i + 1], ri, rc, rpooled, x["seq_lens"], wl.k, wl.n_keep)
+        gi, gc = host(path.idx[i:i + 1]), host(path.count[i:i + 1])
+        ref, _ = oracle.gather(_bits(x["k"]), gi, gc, dst=_bits(path.kc[i:i + 1]))
+        assert np.array_equal(_bits(path.kc[i:i + 1]), ref)
+
+
 def test_cfg3_ctx_128k():
     wl = synth.WORKLOADS[3]
     assert wl.k == synth.budget_from_rate(0.01, wl.s_max) == 1311
