@@ -19,6 +19,7 @@ dominant call and the CPU-oracle baseline ride along.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,6 +44,32 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling PMC byte counters)")
     return ap.parse_args()
+
+
+def measured_traffic(workload, layers, full_layers):
+    """HBM bytes of one folded kvc_score_window call, from the committed PMC summary
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated on a 1 GiB copy), or None when the
+    score sources changed since those counters were taken or the shape differs."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_%s.md" % workload)
+    if layers != full_layers or not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    try:
+        want = fields["score_sources_sha256"]
+        srcs = fields["score_sources"].split()
+        nbytes = int(fields["score_call_traffic_bytes"])
+    except (KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for src in srcs:
+        with open(os.path.join(root, src), "rb") as fh:
+            h.update(fh.read())
+    return nbytes if h.hexdigest() == want else None
 
 
 def layer_bytes(wl, S, cap):
@@ -236,8 +263,9 @@ def main():
     dominant = max(names, key=lambda n: us[n])
     kern = {"score": "kvc_score_window", "select": "kvc_select_topk", "gather": "kvc_gather_compact",
             "decode": "kvc_decode_attn"}
+    traffic = measured_traffic(wl.name, L, wl.layers) if dominant == "score" else None
     roof = {"bound": "hbm", "achieved": round(gbps[dominant], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4), "traffic": traffic,
             "kernel": "%s (one call over all %d layers)" % (kern[dominant], L) if dominant != "decode" else
                       "kvc_decode_attn (one call per layer)",
             "bytes_per_launch": int(by[dominant] * (L if dominant != "decode" else 1)),
