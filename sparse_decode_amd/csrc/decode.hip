@@ -269,9 +269,13 @@ __device__ __forceinline__ float block_sum(float v, float *red)
     return r;
 }
 
-// One work-group per (b, h): split weights exp2(m_s - M) staged in LDS, then
-// kMergeThreads / D thread groups each fold a strided subset of the splits (8 loads
-// in flight per thread) and the groups are added in group order.
+// One work-group per (b, h).  Every split's (m, l) and the first kMergeBatch split
+// outputs of each thread are requested together up front (one dependent round trip
+// for up to G * kMergeBatch splits); the split weights exp2(m_s - M) go to LDS, the
+// kMergeThreads / D thread groups fold their strided subsets of the splits and the
+// groups are added in group order.
+constexpr int kMergeBatch = 16;
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float *__restrict__ part_o,
                                                                      const float2 *__restrict__ part_ml, int n_h,
@@ -279,6 +283,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
                                                                      void *__restrict__ out, float *__restrict__ lse)
 {
     constexpr int G = kMergeThreads / D;
+    constexpr int MLPT = kMaxSplits / kMergeThreads;       // (m, l) pairs per thread
     __shared__ float sw[kMaxSplits];
     __shared__ float red[kMergeThreads / kWave];
     __shared__ float so[G][D];
@@ -288,29 +293,47 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     const int g = h / r;
     const int hl = h - g * r;
     const size_t base = ((size_t)(b * n_kv + g) * r + hl) * n_splits;
-    float mloc = -INFINITY;
-    for (int s = threadIdx.x; s < n_splits; s += kMergeThreads) mloc = fmaxf(mloc, part_ml[base + s].x);
-    const float M = block_max(mloc, red);
-    float lloc = 0.f;
-    for (int s = threadIdx.x; s < n_splits; s += kMergeThreads) {
-        const float2 ml = part_ml[base + s];
-        const float wgt = (M == -INFINITY || ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - M);
-        sw[s] = wgt;
-        lloc += wgt * ml.y;
-    }
-    const float L = block_sum(lloc, red);   // also orders the sw[] writes before their reads
     const int d = threadIdx.x % D;
     const int grp = threadIdx.x / D;
-    float O = 0.f;
-    for (int s0 = grp; s0 < n_splits; s0 += 8 * G) {
-        float v[8];
+    float v[kMergeBatch];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kMergeBatch; ++q) {
+        const int s = grp + q * G;
+        v[q] = s < n_splits ? part_o[(base + s) * D + d] : 0.f;
+    }
+    float2 ml[MLPT];
+#pragma unroll
+    for (int i = 0; i < MLPT; ++i) {
+        const int s = (int)threadIdx.x + i * kMergeThreads;
+        ml[i] = s < n_splits ? part_ml[base + s] : make_float2(-INFINITY, 0.f);
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < MLPT; ++i) mloc = fmaxf(mloc, ml[i].x);
+    const float M = block_max(mloc, red);
+    float lloc = 0.f;
+#pragma unroll
+    for (int i = 0; i < MLPT; ++i) {
+        const int s = (int)threadIdx.x + i * kMergeThreads;
+        const float wgt = (M == -INFINITY || ml[i].x == -INFINITY) ? 0.f : fast_exp2(ml[i].x - M);
+        if (s < n_splits) sw[s] = wgt;
+        lloc += wgt * ml[i].y;
+    }
+    const float L = block_sum(lloc, red);   // also orders the sw[] writes before their reads
+    float O = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) {
+        const int s = grp + q * G;
+        if (s < n_splits) O = fmaf(sw[s], v[q], O);
+    }
+    for (int s0 = grp + kMergeBatch * G; s0 < n_splits; s0 += kMergeBatch * G) {
+#pragma unroll
+        for (int q = 0; q < kMergeBatch; ++q) {
             const int s = s0 + q * G;
             v[q] = s < n_splits ? part_o[(base + s) * D + d] : 0.f;
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < kMergeBatch; ++q) {
             const int s = s0 + q * G;
             if (s < n_splits) O = fmaf(sw[s], v[q], O);
         }

@@ -5,7 +5,7 @@
 
 #include <mutex>
 
-#include "../../include/kvc.h"
+#include "kvc.h"
 #include "kvc_launch.h"
 
 #define KVC_EXPORT extern "C" __attribute__((visibility("default")))

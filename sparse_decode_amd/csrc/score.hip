@@ -129,9 +129,8 @@ __global__ __launch_bounds__(kGenThreads) void gen_rowstats_kernel(const float *
         return;
     }
     const float nmc = -m * kLog2e;
-    float s = 0.f;
-    for (int t = threadIdx.x; t < s_max; t += kGenThreads) s += fast_exp2(fmaf(lg[t], kLog2e, nmc));
-    double sd = s;
+    double sd = 0.0;
+    for (int t = threadIdx.x; t < s_max; t += kGenThreads) sd += (double)fast_exp2(fmaf(lg[t], kLog2e, nmc));
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) sd += __shfl_xor(sd, o, kWave);
     if ((threadIdx.x & 63) == 0) red_l[threadIdx.x >> 6] = sd;
@@ -360,7 +359,7 @@ __device__ __forceinline__ void stream_stages(const uint16_t *__restrict__ kunit
 template <int D, int RT, bool MASK>
 __device__ __forceinline__ void stats_stage(const unsigned char *buf, int st0, int tg, int n, int kg,
                                             const u32x4 (*qb)[Sc<D, RT>::KS], const int *last, float c,
-                                            float *m, float *l)
+                                            float *m, double *l)
 {
     using C = Sc<D, RT>;
     constexpr int NV = 4 * C::PAIR;                      // logits per lane per row block per max
@@ -395,7 +394,11 @@ __device__ __forceinline__ void stats_stage(const unsigned char *buf, int st0, i
                     s0 += fast_exp2(fmaf(x[cb][j], c, nmc));
                     s1 += fast_exp2(fmaf(x[cb][j + 1], c, nmc));
                 }
-                l[cb] = fmaf(l[cb], fast_exp2(fmaf(m[cb], c, nmc)), s0 + s1);
+                // rescale by exp2((m_old - mx) c): exactly 1 while the max stands (an
+                // fma against the rounded -mx c would be 1 +- 1e-6 and, applied at every
+                // update of a long chunk, drift the sum past 1e-5); the running sum is
+                // kept in double for the same reason
+                l[cb] = fma(l[cb], (double)fast_exp2((m[cb] - mx) * c), (double)(s0 + s1));
                 m[cb] = mx;
             }
         }
@@ -435,11 +438,12 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         last[cb] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
     }
     const int all_vis = a.wic ? S - a.w : S - 1;          // every row sees tokens <= all_vis
-    float m[C::CPW], l[C::CPW];
+    float m[C::CPW];
+    double l[C::CPW];
 #pragma unroll
     for (int cb = 0; cb < C::CPW; ++cb) {
         m[cb] = -INFINITY;
-        l[cb] = 0.f;
+        l[cb] = 0.0;
     }
     stream_stages<D, RT, true>(kunit, ch0, S, n_st, kbuf,
         [&](const unsigned char *cur, int st) {
@@ -456,16 +460,16 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
         for (int off = 16; off < 64; off <<= 1) {
             const float m2 = shfl_xor_f(m[cb], off);
-            const float l2 = shfl_xor_f(l[cb], off);
+            const double l2 = __shfl_xor(l[cb], off, kWave);
             const float Mx = fmaxf(m[cb], m2);
             if (Mx != -INFINITY) {
-                l[cb] = l[cb] * fast_exp2((m[cb] - Mx) * a.c) + l2 * fast_exp2((m2 - Mx) * a.c);
+                l[cb] = l[cb] * (double)fast_exp2((m[cb] - Mx) * a.c) + l2 * (double)fast_exp2((m2 - Mx) * a.c);
                 m[cb] = Mx;
             }
         }
         if (kg == 0) {
             sm_m[tg][(wr * C::CPW + cb) * 16 + n] = m[cb];
-            sm_l[tg][(wr * C::CPW + cb) * 16 + n] = l[cb];
+            sm_l[tg][(wr * C::CPW + cb) * 16 + n] = (float)l[cb];
         }
     }
     __syncthreads();
