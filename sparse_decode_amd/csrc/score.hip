@@ -221,6 +221,21 @@ constexpr int kMfWaves = kMfThreads / kWave;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Raw buffer resource (gfx9 descriptor word 3) over `bytes` bytes from p, and the
+// cache-policy bit of a streamed (non-temporal) buffer load.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kAuxNt = 2;
+// Every argument is wave-uniform; readfirstlane lets the compiler keep the
+// descriptor in scalar registers (a vector one would need a waterfall loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int bytes)
+{
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *q = (void *)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufferWord3);
+}
+
 struct MfArgs {
     const uint16_t *q_win;
     const uint16_t *k;
@@ -262,19 +277,20 @@ struct Sc {
     static constexpr int PAIR = TPG < 2 ? TPG : 2;       // tiles whose logits share one max/rescale
     static_assert(LOADS >= 1 && ST * VPR % kMfThreads == 0, "stage must split evenly over the threads");
 
-    // Coalesced loads of one stage (rows clamped into [0, S)).  KEEP: ordinary loads,
-    // which leave K in the caches (the MALL) for the second pass; else loads hinted
-    // as streamed (the second pass is K's last use).
+    // Coalesced loads of one stage through a buffer resource over the unit's S cached
+    // rows: the stage's first row is a scalar offset, each thread's part a constant
+    // vector offset (no per-load address arithmetic), and rows at or past S read as
+    // zero (the hardware range check).  KEEP: ordinary loads, which leave K in the
+    // caches for the second pass; else loads hinted as streamed (K's last use).
     template <bool KEEP>
-    __device__ static void load_stage(const uint16_t *__restrict__ kunit, int st0, int S, u32x4 *reg)
+    __device__ static void load_stage(__amdgpu_buffer_rsrc_t rsrc, int st0, u32x4 *reg)
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int gid = i * kMfThreads + threadIdx.x;
             const int row = gid / VPR, col = gid - row * VPR;
-            const int t = min(st0 + row, S - 1);
-            const u32x4 *src = (const u32x4 *)(kunit + (size_t)t * D) + col;
-            reg[i] = KEEP ? *src : ld_stream(src);
+            reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                rsrc, row * (2 * D) + col * 16, __builtin_amdgcn_readfirstlane(st0 * (2 * D)), KEEP ? 0 : kAuxNt));
         }
     }
 
@@ -331,7 +347,7 @@ struct Sc {
 // steps only skip BODY/POST): the compiler can then count outstanding loads exactly
 // instead of draining the ring at every step.
 template <int D, int RT, bool KEEP, typename BODY, typename POST>
-__device__ __forceinline__ void stream_stages(const uint16_t *__restrict__ kunit, int ch0, int S, int n_st,
+__device__ __forceinline__ void stream_stages(__amdgpu_buffer_rsrc_t kunit, int ch0, int n_st,
                                               unsigned char *kbuf, BODY body, POST post)
 {
     using C = Sc<D, RT>;
@@ -340,14 +356,14 @@ __device__ __forceinline__ void stream_stages(const uint16_t *__restrict__ kunit
     const int last_st = n_st - 1;
     u32x4 ring[P][C::LOADS];
 #pragma unroll
-    for (int q = 0; q < P; ++q) C::template load_stage<KEEP>(kunit, ch0 + min(q, last_st) * C::ST, S, ring[q]);
+    for (int q = 0; q < P; ++q) C::template load_stage<KEEP>(kunit, ch0 + min(q, last_st) * C::ST, ring[q]);
     C::store_stage(kbuf, ring[0]);
     __syncthreads();
     for (int base = 0; base < n_st; base += P) {
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const int st = base + q;
-            C::template load_stage<KEEP>(kunit, ch0 + min(st + P, last_st) * C::ST, S, ring[q]);
+            C::template load_stage<KEEP>(kunit, ch0 + min(st + P, last_st) * C::ST, ring[q]);
             if (st < n_st) body(kbuf + (st & 1) * C::STAGE_BYTES, st);
             C::store_stage(kbuf + ((st + 1) & 1) * C::STAGE_BYTES, ring[(q + 1) % P]);
             __syncthreads();
@@ -420,11 +436,11 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int u = a.unit0 + ul;
     const int b = u / a.n_kv;
     const int g = u - b * a.n_kv;
-    const int S = clamp_len(a.seq_lens, b, a.s_max);
+    const int S = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, b, a.s_max));   // uniform: scalar offsets below
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n = lane & 15, kg = lane >> 4;
     const int wr = wv % C::WPR, tg = wv / C::WPR;
-    const uint16_t *kunit = a.k + (size_t)u * a.s_max * D;
+    const __amdgpu_buffer_rsrc_t kunit = buffer_rsrc(a.k + (size_t)u * a.s_max * D, S * (2 * D));
     const int ch0 = chunk * a.chunk_tokens;
     int n_st = (min(ch0 + a.chunk_tokens, S) - ch0 + C::ST - 1) / C::ST;
     n_st = n_st < 0 ? 0 : n_st;
@@ -445,7 +461,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         m[cb] = -INFINITY;
         l[cb] = 0.0;
     }
-    stream_stages<D, RT, true>(kunit, ch0, S, n_st, kbuf,
+    stream_stages<D, RT, true>(kunit, ch0, n_st, kbuf,
         [&](const unsigned char *cur, int st) {
             const int st0 = ch0 + st * C::ST;
             if (st0 + C::ST - 1 <= all_vis)
@@ -593,11 +609,11 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int u = a.unit0 + ul;
     const int b = u / a.n_kv;
     const int g = u - b * a.n_kv;
-    const int S = clamp_len(a.seq_lens, b, a.s_max);
+    const int S = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, b, a.s_max));   // uniform: scalar offsets below
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n = lane & 15, kg = lane >> 4;
     const int wr = wv % C::WPR, tg = wv / C::WPR;
-    const uint16_t *kunit = a.k + (size_t)u * a.s_max * D;
+    const __amdgpu_buffer_rsrc_t kunit = buffer_rsrc(a.k + (size_t)u * a.s_max * D, S * (2 * D));
     float *rawu = a.raw + (size_t)u * a.s_max;
     const int ch0 = chunk * a.chunk_tokens;
     const int ch1 = min(ch0 + a.chunk_tokens, a.s_max);
@@ -618,7 +634,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         last[cb] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
     }
     const int all_vis = a.wic ? S - a.w : S - 1;
-    stream_stages<D, RT, false>(kunit, ch0, S, n_st, kbuf,
+    stream_stages<D, RT, false>(kunit, ch0, n_st, kbuf,
         [&](const unsigned char *cur, int st) {
             const int st0 = ch0 + st * C::ST;
             float *rd = red[st & 1];
