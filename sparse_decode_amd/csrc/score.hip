@@ -334,6 +334,17 @@ struct Sc {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[s]), as_bf16x8(qb[s]), acc, 0, 0, 0);
         return acc;
     }
+
+    // The same tile with the operands swapped (query rows on M, tokens on N): lane
+    // l = 16 kg + n receives token n for rows 4 kg + j, j < 4.
+    __device__ static f32x4_t mma_rows(const u32x4 *qb, const u32x4 *ka)
+    {
+        f32x4_t acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qb[s]), as_bf16x8(ka[s]), acc, 0, 0, 0);
+        return acc;
+    }
 };
 
 // Pass 1: per row, max logit m and sum of exp2((x - m) c) over one chunk's visible
@@ -553,44 +564,42 @@ __global__ __launch_bounds__(kMergeThreads) void mfma_merge_kernel(const float2 
     fin[(size_t)ul * rpad + row] = res;
 }
 
-// Pass 2: raw[t] = sum over rows of exp2((x - M) c) / L for one chunk.  Each wave
-// sums its rows in-lane, a transposed butterfly over the 16 lanes of a token group
-// (4 -> 2 -> 1 values, then two full-sum steps, all DPP lane exchanges) leaves one
-// token per lane, and the WPR row-slice partials of a token are added in LDS in
-// slice order.
+// Pass 2: raw[t] = sum over rows of exp2((x - M) c) / L for one chunk.  The tiles
+// are multiplied with the query rows on M and the tokens on N, so each lane holds one
+// token of a tile for four rows of every row block and sums them in-lane; the four
+// lane groups of a token (lanes n, n + 16, n + 32, n + 48) are added with two lane
+// swaps (rows of 32, then of 16 lanes), and the WPR row slices in LDS, in a fixed
+// order, once per stage.
 template <int D, int RT, bool MASK>
 __device__ __forceinline__ void probsum_stage(const unsigned char *buf, int st0, int tg, int wr, int n, int kg,
-                                              const u32x4 (*qb)[Sc<D, RT>::KS], const int *last,
-                                              const float *nmc, const float *il, float c, float *red)
+                                              const u32x4 (*qb)[Sc<D, RT>::KS], const int (*last)[4],
+                                              const float (*nmc)[4], const float (*il)[4], float c, float *red)
 {
     using C = Sc<D, RT>;
-    const int my_j = 2 * ((n >> 3) & 1) + ((n >> 2) & 1);
 #pragma unroll
     for (int p = 0; p < C::TPG; ++p) {
         const int tile = tg + p * C::TG;
         u32x4 ka[C::KS];
         C::load_a(buf, tile, n, kg, ka);
-        float cs[4] = {0.f, 0.f, 0.f, 0.f};
+        const int tok = st0 + tile * 16 + n;
+        float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
         for (int cb = 0; cb < C::CPW; ++cb) {
-            const f32x4_t x = C::mma(ka, qb[cb]);
+            const f32x4_t x = C::mma_rows(qb[cb], ka);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float e = fast_exp2(fmaf(x[j], c, nmc[cb]));
-                if (MASK && st0 + tile * 16 + 4 * kg + j > last[cb]) e = 0.f;
-                cs[j] = fmaf(e, il[cb], cs[j]);
+                float e = fast_exp2(fmaf(x[j], c, nmc[cb][j]));
+                if (MASK && tok > last[cb][j]) e = 0.f;
+                if (j & 1) acc1 = fmaf(e, il[cb][j], acc1);
+                else acc0 = fmaf(e, il[cb][j], acc0);
             }
         }
-        // halving steps pair lanes with opposite bit 3 (row mirror), then opposite
-        // bit 2 within a half row (half mirror); the partner holds the same token set
-        const bool u8 = (n & 8) != 0;
-        const float v0 = (u8 ? cs[2] : cs[0]) + dpp_f<kDppRowMirror>(u8 ? cs[0] : cs[2]);
-        const float v1 = (u8 ? cs[3] : cs[1]) + dpp_f<kDppRowMirror>(u8 ? cs[1] : cs[3]);
-        const bool u4 = (n & 4) != 0;
-        float v = (u4 ? v1 : v0) + dpp_f<kDppHalfMirror>(u4 ? v0 : v1);
-        v += dpp_f<kDppXor2>(v);
-        v += dpp_f<kDppXor1>(v);
-        if ((n & 3) == 0) red[wr * C::ST + tile * 16 + 4 * kg + my_j] = v;
+        const float v = acc0 + acc1;
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const float v2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);   // + lane l ^ 32
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2), false, false);
+        const float v4 = __uint_as_float(q[0]) + __uint_as_float(q[1]);   // + lane l ^ 16
+        if (kg == 0) red[wr * C::ST + tile * 16 + n] = v4;                // [row slice][token]
     }
 }
 
@@ -622,16 +631,20 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
 
     u32x4 qb[C::CPW][KS];
     C::load_q(a, b, g, wr, n, kg, qb);
-    float nmc[C::CPW], il[C::CPW];
-    int last[C::CPW];
+    // row constants of this lane's rows (4 kg + j of each row block)
+    float nmc[C::CPW][4], il[C::CPW][4];
+    int last[C::CPW][4];
 #pragma unroll
     for (int cb = 0; cb < C::CPW; ++cb) {
-        const int row = (wr * C::CPW + cb) * 16 + n;
-        const float2 f = a.fin[(size_t)ul * (RT * 16) + row];
-        nmc[cb] = f.x;
-        il[cb] = f.y;
-        const int i = row % a.w;
-        last[cb] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (wr * C::CPW + cb) * 16 + 4 * kg + j;
+            const float2 f = a.fin[(size_t)ul * (RT * 16) + row];
+            nmc[cb][j] = f.x;
+            il[cb][j] = f.y;
+            const int i = row % a.w;
+            last[cb][j] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
+        }
     }
     const int all_vis = a.wic ? S - a.w : S - 1;
     stream_stages<D, RT, false>(kunit, ch0, n_st, kbuf,
@@ -644,7 +657,8 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
                 probsum_stage<D, RT, true>(cur, st0, tg, wr, n, kg, qb, last, nmc, il, a.c, rd);
         },
         [&](int st) {
-            // add the row slices of this stage in order; red[st & 1] is rewritten two steps later
+            // add the row slices of this stage in order; red[st & 1] is rewritten two
+            // steps later
             const float *rd = red[st & 1];
             for (int t = threadIdx.x; t < C::ST; t += kMfThreads) {
                 float v = 0.f;
