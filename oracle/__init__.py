@@ -9,7 +9,9 @@ from .ref import (  # noqa: F401
     cache_bytes,
     decode,
     gather,
+    query_similarity,
     score_window,
     select_topk,
     set_threads,
+    speculative_step,
 )

@@ -303,3 +303,39 @@ KVO_API void kvo_decode(int B, int n_h, int n_kv, int d_h, const float *q, const
         }
     }
 }
+
+/*
+ * Query similarity of two adjacent decode steps and the heads it sends to
+ * correction (FreeKV technical summary 2.A: queries of adjacent steps are very
+ * similar, so step i attends over the subset selected with the query of step
+ * i - 1; when the cosine similarity of the two queries of a head falls below a
+ * threshold tau, selection and retrieval run again for that head before attention).
+ *
+ * q_cur, q_prev [B][n_h][d_h]
+ * cos_out [B][n_h] = <q_cur, q_prev> / (|q_cur| |q_prev|), 0 when either norm is 0
+ * refresh [B][n_kv] = 1 iff some query head h of KV head g (h / (n_h/n_kv) == g)
+ *                     has cos_out < tau, else 0 (selection is per KV head, so a KV
+ *                     head is corrected as soon as one of its query heads drifted)
+ * Sums in double; the comparison with tau is on the double cosine.
+ */
+KVO_API void kvo_query_similarity(int B, int n_h, int n_kv, int d_h, const float *q_cur,
+                                  const float *q_prev, double tau, double *cos_out, int32_t *refresh)
+{
+    const int r = n_h / n_kv;
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < n_kv; ++g) refresh[(size_t)b * n_kv + g] = 0;
+        for (int h = 0; h < n_h; ++h) {
+            const float *x = q_cur + ((size_t)b * n_h + h) * d_h;
+            const float *y = q_prev + ((size_t)b * n_h + h) * d_h;
+            double xy = 0.0, xx = 0.0, yy = 0.0;
+            for (int d = 0; d < d_h; ++d) {
+                xy += (double)x[d] * (double)y[d];
+                xx += (double)x[d] * (double)x[d];
+                yy += (double)y[d] * (double)y[d];
+            }
+            const double c = (xx > 0.0 && yy > 0.0) ? xy / (sqrt(xx) * sqrt(yy)) : 0.0;
+            cos_out[(size_t)b * n_h + h] = c;
+            if (c < tau) refresh[(size_t)b * n_kv + h / r] = 1;
+        }
+    }
+}

@@ -55,6 +55,8 @@ def _load():
             lib.kvo_gather.argtypes = [I, I, I, I, P, P, P, P, I, P, P]
             lib.kvo_decode.restype = None
             lib.kvo_decode.argtypes = [I, I, I, I, P, P, P, P, I, ctypes.c_double, P, P]
+            lib.kvo_query_similarity.restype = None
+            lib.kvo_query_similarity.argtypes = [I, I, I, I, P, P, ctypes.c_double, P, P]
             _lib = lib
     return _lib
 
@@ -173,3 +175,64 @@ def decode(q, kc, vc, count, *, scale=None):
     _load().kvo_decode(B, n_h, n_kv, d_h, _ptr(q), _ptr(kc), _ptr(vc), _ptr(count), int(cap),
                        float(scale), _ptr(out), _ptr(lse))
     return out, lse
+
+
+def query_similarity(q_cur, q_prev, n_kv, tau):
+    """FreeKV technical summary 2.A: per query head cosine of the queries of two
+    adjacent decode steps, and the KV heads to correct (some query head below tau).
+
+    q_cur, q_prev [B][n_h][d_h] float32.  Returns (cos float64 [B][n_h],
+    refresh int32 [B][n_kv]).
+    """
+    q_cur = _f32(q_cur)
+    q_prev = _f32(q_prev)
+    B, n_h, d_h = q_cur.shape
+    assert q_prev.shape == q_cur.shape and n_h % n_kv == 0
+    cos = np.zeros((B, n_h), np.float64)
+    refresh = np.zeros((B, n_kv), np.int32)
+    _load().kvo_query_similarity(B, n_h, n_kv, d_h, _ptr(q_cur), _ptr(q_prev), float(tau), _ptr(cos),
+                                 _ptr(refresh))
+    return cos, refresh
+
+
+def speculative_step(q_cur, q_prev, k, v, prev_sel, *, seq_lens, k_budget, n_keep, pool, tau,
+                     refresh=None, scale=None):
+    """One decode step of speculative retrieval with fine-grained correction
+    (FreeKV technical summary 2.A), composed from the steps above.
+
+    q_cur, q_prev [B][n_h][d_h] (q_prev None at the first step), k, v
+    [B][n_kv][s_max][d_h] float32; prev_sel = (idx, count) selected with q_prev
+    (None at the first step).  The query of a step is not in the cache: it scores
+    every cached key (w = 1, window_in_cache False) and the n_keep trailing tokens
+    are always kept.
+
+    Heads are corrected where the similarity says so (every head at the first
+    step, or ``refresh`` when the caller fixes the decision); a corrected head
+    attends over the selection made with q_cur, every other head over prev_sel.
+    Returns a dict: out, lse (float64), refresh, cos (None at the first step),
+    idx/count used by attention, and next_sel = the selection made with q_cur for
+    every head (what the next step reuses).
+    """
+    B, n_h, d_h = q_cur.shape
+    n_kv = k.shape[1]
+    q1 = np.ascontiguousarray(q_cur[:, :, None, :])
+    _, pooled = score_window(q1, k, 1, seq_lens=seq_lens, window_in_cache=False, n_keep=n_keep,
+                             pool=pool, scale=scale)
+    sel_idx, sel_cnt = select_topk(pooled, k_budget, n_keep, seq_lens=seq_lens)
+    cos = None
+    if prev_sel is None:
+        ref = np.ones((B, n_kv), np.int32)
+    elif refresh is not None:
+        ref = np.asarray(refresh, np.int32)
+    else:
+        cos, ref = query_similarity(q_cur, q_prev, n_kv, tau)
+    if prev_sel is None:
+        use_idx, use_cnt = sel_idx, sel_cnt
+    else:
+        use_idx = np.where(ref[:, :, None] != 0, sel_idx, prev_sel[0]).astype(np.int32)
+        use_cnt = np.where(ref != 0, sel_cnt, prev_sel[1]).astype(np.int32)
+    kc, _ = gather(k, use_idx, use_cnt)
+    vc, _ = gather(v, use_idx, use_cnt)
+    out, lse = decode(q_cur, kc, vc, use_cnt, scale=scale)
+    return dict(out=out, lse=lse, refresh=ref, cos=cos, idx=use_idx, count=use_cnt,
+                next_sel=(sel_idx, sel_cnt), pooled=pooled)

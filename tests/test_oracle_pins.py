@@ -411,3 +411,114 @@ def test_decode_closed_forms():
         y = kc[0, 0].astype(np.float64) @ q[0, h].astype(np.float64) / math.sqrt(d)
         p = np.exp(y - y.max())
         assert np.allclose(out[0, h], (p / p.sum()) @ vc[0, 0].astype(np.float64), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------
+# Speculative retrieval with fine-grained correction (FreeKV technical summary 2.A)
+# ----------------------------------------------------------------------------------
+def test_query_similarity_closed_forms():
+    d = 64
+    base = np.zeros((1, 8, d), np.float32)
+    prev = np.zeros((1, 8, d), np.float32)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(d).astype(np.float32)
+    base[0, 0], prev[0, 0] = x, x                        # identical -> 1
+    base[0, 1], prev[0, 1] = x, -x                       # opposite -> -1
+    base[0, 2, 0], prev[0, 2, 1] = 1.0, 1.0              # orthogonal -> 0
+    base[0, 3, :2], prev[0, 3, :2] = (3.0, 4.0), (4.0, 3.0)   # 24 / 25
+    base[0, 4], prev[0, 4] = x, np.float32(4.0) * x      # scale invariant -> 1
+    prev[0, 5] = x                                       # zero query -> 0 by convention
+    base[0, 6, :3], prev[0, 6, :3] = (1.0, 0.0, 0.0), (1.0, 1.0, 0.0)   # 45 degrees
+    base[0, 7, :2], prev[0, 7, :2] = (1.0, 2.0), (-2.0, 1.0)            # orthogonal, not axis-aligned
+    cos, _ = oracle.query_similarity(base, prev, 2, 0.5)
+    want = [1.0, -1.0, 0.0, 24.0 / 25.0, 1.0, 0.0, 1.0 / math.sqrt(2.0), 0.0]
+    assert np.allclose(cos[0], want, rtol=0, atol=1e-12)
+
+
+def test_query_similarity_matches_distance_identity():
+    # |a - b|^2 = |a|^2 + |b|^2 - 2 |a| |b| cos: an independent route to the cosine,
+    # and invariance under a common rotation of both queries
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal((3, 16, 128)).astype(np.float32)
+    b = (0.9 * a + 0.5 * rng.standard_normal((3, 16, 128))).astype(np.float32)
+    cos, _ = oracle.query_similarity(a, b, 4, 0.0)
+    A, B = a.astype(np.float64), b.astype(np.float64)
+    na, nb = np.linalg.norm(A, axis=2), np.linalg.norm(B, axis=2)
+    dist2 = np.sum((A - B) ** 2, axis=2)
+    assert np.allclose(dist2, na ** 2 + nb ** 2 - 2 * na * nb * cos, rtol=1e-10, atol=1e-9)
+    Q, _ = np.linalg.qr(rng.standard_normal((128, 128)))
+    cos_rot, _ = oracle.query_similarity((A @ Q).astype(np.float32), (B @ Q).astype(np.float32), 4, 0.0)
+    assert np.allclose(cos_rot, cos, atol=2e-6)
+
+
+def test_query_similarity_correction_flags():
+    # one drifted query head marks exactly its own KV head (h // r), below tau only
+    rng = np.random.default_rng(13)
+    B, n_h, n_kv, d = 2, 8, 2, 32
+    q = rng.standard_normal((B, n_h, d)).astype(np.float32)
+    prev = q.copy()
+    prev[1, 5] = rng.standard_normal(d).astype(np.float32)   # sequence 1, head 5 -> KV head 1
+    cos, ref = oracle.query_similarity(q, prev, n_kv, 0.9)
+    assert cos[1, 5] < 0.9 and np.allclose(np.delete(cos.ravel(), 1 * n_h + 5), 1.0)
+    assert ref.tolist() == [[0, 0], [0, 1]]
+    _, none = oracle.query_similarity(q, prev, n_kv, -1.0)   # cos >= -1: nothing is below -1
+    assert not none.any()
+    _, everything = oracle.query_similarity(q, prev, n_kv, 1.5)
+    assert everything.all()
+    # the flag needs a strict drop below tau: cos == tau is kept
+    c = float(cos[1, 5])
+    _, at = oracle.query_similarity(q, prev, n_kv, c)
+    assert at[1, 1] == 0
+
+
+def _spec_case(seed, S=200, n_h=4, n_kv=2, d=16, k=12, n_keep=4):
+    rng = np.random.default_rng(seed)
+    kk = rng.standard_normal((1, n_kv, S, d)).astype(np.float32)
+    vv = rng.standard_normal((1, n_kv, S, d)).astype(np.float32)
+    q0 = rng.standard_normal((1, n_h, d)).astype(np.float32)
+    q1 = rng.standard_normal((1, n_h, d)).astype(np.float32)   # unrelated: selections differ
+    return kk, vv, q0, q1, dict(seq_lens=np.array([S], np.int32), k_budget=k, n_keep=n_keep, pool=1)
+
+
+def test_speculative_step_uses_previous_selection_unless_corrected():
+    kk, vv, q0, q1, kw = _spec_case(21)
+    first = oracle.speculative_step(q0, None, kk, vv, None, tau=0.9, **kw)
+    assert first["refresh"].all()                                  # the first step selects fresh
+    assert np.array_equal(first["idx"], first["next_sel"][0])
+    prev = first["next_sel"]
+    fresh = oracle.speculative_step(q1, q0, kk, vv, prev, tau=2.0, **kw)     # tau > 1: correct all
+    stale = oracle.speculative_step(q1, q0, kk, vv, prev, tau=-2.0, **kw)    # tau < -1: reuse all
+    assert fresh["refresh"].all() and not stale["refresh"].any()
+    assert np.array_equal(fresh["idx"], fresh["next_sel"][0])
+    assert np.array_equal(stale["idx"], prev[0]) and np.array_equal(stale["count"], prev[1])
+    assert not np.array_equal(fresh["idx"], stale["idx"])
+    # reused or not, the next step always gets the selection made with q1
+    assert np.array_equal(stale["next_sel"][0], fresh["next_sel"][0])
+    # attention over the reused subset equals attention over the full cache restricted
+    # to prev's kept tokens (torch, float64): the output follows the selection used
+    for res, idx in ((stale, prev[0]), (fresh, fresh["next_sel"][0])):
+        q = torch.from_numpy(q1).double()
+        for g in range(kk.shape[1]):
+            keep = torch.zeros(kk.shape[2], dtype=torch.bool)
+            keep[torch.from_numpy(idx[0, g][idx[0, g] >= 0].astype(np.int64))] = True
+            kf = torch.from_numpy(kk[0, g]).double()[None, None]
+            vf = torch.from_numpy(vv[0, g]).double()[None, None]
+            for h in range(g * 2, g * 2 + 2):
+                ref = F.scaled_dot_product_attention(q[0, h][None, None, None], kf, vf,
+                                                     attn_mask=keep[None, None, None])
+                assert np.allclose(res["out"][0, h], ref[0, 0, 0].numpy(), atol=1e-12)
+
+
+def test_speculative_step_corrects_per_kv_head():
+    kk, vv, q0, q1, kw = _spec_case(22)
+    prev = oracle.speculative_step(q0, None, kk, vv, None, tau=0.9, **kw)["next_sel"]
+    mixed = q0.copy()
+    mixed[0, 3] = q1[0, 3]                           # only query head 3 (KV head 1) drifts
+    res = oracle.speculative_step(mixed, q0, kk, vv, prev, tau=0.9, **kw)
+    assert res["refresh"].tolist() == [[0, 1]]
+    assert np.array_equal(res["idx"][0, 0], prev[0][0, 0])
+    assert np.array_equal(res["idx"][0, 1], res["next_sel"][0][0, 1])
+    # an explicit decision overrides the similarity
+    forced = oracle.speculative_step(mixed, q0, kk, vv, prev, tau=0.9, refresh=np.array([[1, 0]]), **kw)
+    assert np.array_equal(forced["idx"][0, 0], forced["next_sel"][0][0, 0])
+    assert np.array_equal(forced["idx"][0, 1], prev[0][0, 1])
