@@ -13,6 +13,9 @@
  *                       the original positions
  *   kvc_decode_attn     GQA decode attention of one query per head over the
  *                       compacted cache
+ *   kvc_query_similarity  cosine of the queries of two adjacent decode steps and
+ *                       the KV heads whose selection is redone before attention
+ *                       (speculative retrieval with fine-grained correction)
  *
  * Pages these calls follow (cited by title and section):
  *   [FastKV]   "FastKV: Decoupling of Context Reduction and KV Cache Compression for
@@ -28,7 +31,9 @@
  *              scoring, keep a subset of past keys and values).
  *   [FreeKV]   "FreeKV: Boosting KV Cache Retrieval for Efficient LLM Inference",
  *              technical summary section 2.A (select a subset with the current
- *              query, then attend over it, at every decode step).
+ *              query, then attend over it, at every decode step; speculative
+ *              retrieval reuses the previous step's subset and fine-grained
+ *              correction redoes the selection of the heads whose query drifted).
  *
  * Conventions for every call:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
@@ -64,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -92,6 +97,11 @@ typedef struct kvc_dims {
     int32_t n_kv;             /* KV heads; query head h reads KV head h / (n_h / n_kv)       */
     int32_t d_h;              /* head width: 64 or 128                                       */
     int32_t dtype;            /* kvc_dtype of Q, K, V and the decode output                  */
+    const int32_t *unit_mask; /* device int32[B][n_kv] or NULL (every unit).  kvc_score_window
+                                 and kvc_select_topk skip unit (b, g) when its entry is 0 and
+                                 leave its outputs as they were (FreeKV 2.A: selection runs
+                                 again only for the heads that need correction); not allowed
+                                 with KVC_SELECT_SHARED_HEADS; kvc_decode_attn ignores it     */
 } kvc_dims;
 
 /* kvc_select_topk flag: one selection per sequence from the float sum of the
@@ -186,20 +196,23 @@ kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores, int32_t k,
  *   pos_out[b][h][j] = src_pos[b][idx[b][h'][j]]  (idx itself when src_pos is NULL)
  * where h' = h when idx_heads == heads and h' = 0 when idx_heads == 1 (one list
  * shared by every head).  Rows j >= count are not written; their pos_out is -1.
- * An index outside [0, s_max) copies nothing and gets pos_out -1.
+ * An index outside [0, s_max) copies nothing and gets pos_out -1.  With unit_mask,
+ * a list whose entry is 0 is skipped: its dst rows and pos_out are left as they were.
  *
  * src0, src1   [B][heads][s_max][row_bytes]; src1 may be NULL (then dst1 must be NULL)
  * src_pos      [B][s_max] int32 or NULL
  * idx          [B][idx_heads][cap] int32; count [B][idx_heads] int32
  * dst0, dst1   [B][heads][cap][row_bytes]
  * pos_out      [B][heads][cap] int32 or NULL
+ * unit_mask    [B][idx_heads] int32 or NULL (every list is copied)
  * row_bytes    a multiple of 16; row_bytes/16 a power of two or a multiple of 256;
  *              every row pointer 16-byte aligned
  */
 kvc_status kvc_gather_compact(int32_t batch, int32_t heads, int32_t s_max, int32_t row_bytes,
                               const void *src0, const void *src1, const int32_t *src_pos,
                               const int32_t *idx, const int32_t *count, int32_t idx_heads,
-                              int32_t cap, void *dst0, void *dst1, int32_t *pos_out, void *stream);
+                              int32_t cap, void *dst0, void *dst1, int32_t *pos_out,
+                              const int32_t *unit_mask, void *stream);
 
 /*
  * kvc_decode_attn -- GQA decode attention over the compacted cache (FreeKV 2.A:
@@ -225,6 +238,33 @@ size_t kvc_decode_attn_workspace(const kvc_dims *dims, int32_t cap);
 kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const void *kc, const void *vc,
                            const int32_t *count, int32_t cap, float scale, void *out, float *lse,
                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kvc_query_similarity -- which KV heads must select again before attention at this
+ * decode step (FreeKV, technical summary 2.A).  Queries of adjacent steps are very
+ * similar, so a step may attend over the subset selected with the previous step's
+ * query (speculative retrieval); where the similarity of a head's two queries falls
+ * below a threshold tau, the selection is redone for that head first (fine-grained
+ * correction).  Selection is per KV head, so a KV head is corrected as soon as one
+ * of its query heads drifted.
+ *
+ * For each (b, h), g = h / (n_h/n_kv):
+ *   cos[b][h] = <q_cur[b][h], q_prev[b][h]> / (|q_cur[b][h]| |q_prev[b][h]|),
+ *               0 when either norm is 0 (sums in double, rounded to float)
+ *   refresh[b][g] = 1 iff cos[b][h] < tau (compared in double) for some h of g, else 0
+ *   keep[b][g] = 1 - refresh[b][g]
+ * refresh (keep) is a unit_mask for the calls that redo (skip) the selection.
+ *
+ * dims           batch, n_h, n_kv, d_h and dtype are used
+ * q_cur, q_prev  [B][n_h][d_h] dtype, 16-byte aligned
+ * tau            any finite value: tau > 1 corrects every head, tau <= -1 none
+ * cos            [B][n_h] float or NULL
+ * refresh        [B][n_kv] int32
+ * keep           [B][n_kv] int32 or NULL
+ * No workspace.
+ */
+kvc_status kvc_query_similarity(const kvc_dims *dims, const void *q_cur, const void *q_prev, double tau,
+                                float *cos, int32_t *refresh, int32_t *keep, void *stream);
 
 #ifdef __cplusplus
 }

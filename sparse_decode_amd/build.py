@@ -34,9 +34,18 @@ COMMON_FLAGS = [
 ]
 
 
+# The C ABI layer validates host arguments, NaN included: it keeps IEEE semantics
+# (under -fno-honor-nans a comparison may assume its operand is not NaN).
+KERNEL_ONLY_FLAGS = ("-fno-honor-nans", "-mno-amdgpu-ieee")
+HOST_CHECKED_SOURCES = ("kvc_api.hip",)
+
+
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
+    flags = COMMON_FLAGS
+    if os.path.basename(src) in HOST_CHECKED_SOURCES:
+        flags = [f for f in COMMON_FLAGS if f not in KERNEL_ONLY_FLAGS]
+    cmd = [HIPCC, *flags, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, res.stdout, res.stderr))

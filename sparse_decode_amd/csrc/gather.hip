@@ -26,13 +26,14 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     const int32_t *__restrict__ src_pos, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ count, int heads, int idx_heads, int s_max, int vpr, int tpr_log2,
     int cap, int rows_per_block, u32x4 *__restrict__ dst0, u32x4 *__restrict__ dst1,
-    int32_t *__restrict__ pos_out)
+    int32_t *__restrict__ pos_out, const int32_t *__restrict__ mask)
 {
     __shared__ int rows[kMaxBlockRows];
     const int unit = blockIdx.y;
     const int b = unit / heads;
     const int h = unit - b * heads;
     const int list = b * idx_heads + (idx_heads == 1 ? 0 : h);
+    if (mask && !mask[list]) return;
     const int r0 = blockIdx.x * rows_per_block;
     const int r1 = min(r0 + rows_per_block, cap);
     const int32_t *lidx = idx + (size_t)list * cap;
@@ -88,7 +89,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
 hipError_t launch_gather(int batch, int heads, int s_max, int row_bytes, const void *src0,
                          const void *src1, const int32_t *src_pos, const int32_t *idx,
                          const int32_t *count, int idx_heads, int cap, void *dst0, void *dst1,
-                         int32_t *pos_out, const DeviceInfo &dev, hipStream_t stream)
+                         int32_t *pos_out, const int32_t *unit_mask, const DeviceInfo &dev,
+                         hipStream_t stream)
 {
     const int vpr = row_bytes / 16;
     int tpr_log2 = 0;
@@ -108,7 +110,7 @@ hipError_t launch_gather(int batch, int heads, int s_max, int row_bytes, const v
     dim3 grid((unsigned)((cap + rpb - 1) / rpb), (unsigned)units);
     hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(kGatherThreads), 0, stream,
                        (const u32x4 *)src0, (const u32x4 *)src1, src_pos, idx, count, heads, idx_heads,
-                       s_max, vpr, tpr_log2, cap, (int)rpb, (u32x4 *)dst0, (u32x4 *)dst1, pos_out);
+                       s_max, vpr, tpr_log2, cap, (int)rpb, (u32x4 *)dst0, (u32x4 *)dst1, pos_out, unit_mask);
     return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // to the gfx950 kernels.  No exception crosses this layer.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
 #include <mutex>
 
 #include "kvc.h"
@@ -124,7 +125,7 @@ KVC_EXPORT kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, 
                                           dims->dtype == KVC_BF16, w, (flags & KVC_SCORE_GENERIC) != 0, kPlanCus);
     hipError_t e = kvc::launch_score(dims->batch, dims->s_max, dims->seq_lens, dims->n_h, dims->n_kv, dims->d_h,
                                      dims->dtype == KVC_BF16, q_win, k, w, window_in_cache != 0, n_keep,
-                                     pool_kernel, sc, raw, pooled, ws, plan, (hipStream_t)stream);
+                                     pool_kernel, sc, raw, pooled, dims->unit_mask, ws, plan, (hipStream_t)stream);
     return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
@@ -137,6 +138,7 @@ static kvc_status select_args(const kvc_dims *d, int32_t k, int32_t n_keep, int3
     if ((long)d->batch * d->n_kv > kMaxUnits) return KVC_ERR_INVALID_ARG;
     if (k < 0 || n_keep < 0 || (long)k + n_keep < 1 || (long)k + n_keep > (1L << 30)) return KVC_ERR_INVALID_ARG;
     if (flags & ~KVC_SELECT_SHARED_HEADS) return KVC_ERR_INVALID_ARG;
+    if ((flags & KVC_SELECT_SHARED_HEADS) && d->unit_mask) return KVC_ERR_INVALID_ARG;
     return KVC_OK;
 }
 
@@ -159,7 +161,7 @@ KVC_EXPORT kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores,
     kvc::DeviceInfo dev;
     if (kvc::device_info(&dev) != hipSuccess) return KVC_ERR_HIP;
     hipError_t e = kvc::launch_select(dims->batch, dims->n_kv, dims->s_max, dims->seq_lens, scores, k, n_keep,
-                                      shared, idx, count, ws, dev, (hipStream_t)stream);
+                                      shared, idx, count, dims->unit_mask, ws, dev, (hipStream_t)stream);
     return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
@@ -168,7 +170,8 @@ KVC_EXPORT kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores,
 KVC_EXPORT kvc_status kvc_gather_compact(int32_t batch, int32_t heads, int32_t s_max, int32_t row_bytes,
                                          const void *src0, const void *src1, const int32_t *src_pos,
                                          const int32_t *idx, const int32_t *count, int32_t idx_heads, int32_t cap,
-                                         void *dst0, void *dst1, int32_t *pos_out, void *stream)
+                                         void *dst0, void *dst1, int32_t *pos_out, const int32_t *unit_mask,
+                                         void *stream)
 {
     if (batch < 1 || heads < 1 || s_max < 1 || cap < 1 || row_bytes < 16) return KVC_ERR_INVALID_ARG;
     if ((long)batch * heads > kMaxUnits) return KVC_ERR_INVALID_ARG;
@@ -184,7 +187,7 @@ KVC_EXPORT kvc_status kvc_gather_compact(int32_t batch, int32_t heads, int32_t s
     kvc::DeviceInfo dev;
     if (kvc::device_info(&dev) != hipSuccess) return KVC_ERR_HIP;
     hipError_t e = kvc::launch_gather(batch, heads, s_max, row_bytes, src0, src1, src_pos, idx, count, idx_heads,
-                                      cap, dst0, dst1, pos_out, dev, (hipStream_t)stream);
+                                      cap, dst0, dst1, pos_out, unit_mask, dev, (hipStream_t)stream);
     return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
@@ -211,5 +214,22 @@ KVC_EXPORT kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const
     const float sc = scale == 0.f ? 1.0f / sqrtf((float)dims->d_h) : scale;
     hipError_t e = kvc::launch_decode(dims->batch, dims->n_h, dims->n_kv, dims->d_h, dims->dtype == KVC_BF16, q,
                                       kc, vc, count, cap, sc, out, lse, ws, plan, (hipStream_t)stream);
+    return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------- query similarity
+
+KVC_EXPORT kvc_status kvc_query_similarity(const kvc_dims *dims, const void *q_cur, const void *q_prev, double tau,
+                                           float *cos, int32_t *refresh, int32_t *keep, void *stream)
+{
+    kvc_status st = check_dims(dims, false);
+    if (st != KVC_OK) return st;
+    if (!q_cur || !q_prev || !refresh) return KVC_ERR_INVALID_ARG;
+    uint64_t tau_bits;
+    memcpy(&tau_bits, &tau, sizeof tau_bits);
+    if (((tau_bits >> 52) & 0x7ff) == 0x7ff) return KVC_ERR_INVALID_ARG;   // inf or NaN (bit test: NaN-free flags)
+    if (!aligned16(q_cur) || !aligned16(q_prev)) return KVC_ERR_INVALID_ARG;
+    hipError_t e = kvc::launch_similarity(dims->batch, dims->n_h, dims->n_kv, dims->d_h, dims->dtype == KVC_BF16,
+                                          q_cur, q_prev, tau, cos, refresh, keep, (hipStream_t)stream);
     return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }

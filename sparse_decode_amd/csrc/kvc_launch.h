@@ -20,7 +20,8 @@ hipError_t device_info(DeviceInfo *out);
 hipError_t launch_gather(int batch, int heads, int s_max, int row_bytes, const void *src0,
                          const void *src1, const int32_t *src_pos, const int32_t *idx,
                          const int32_t *count, int idx_heads, int cap, void *dst0, void *dst1,
-                         int32_t *pos_out, const DeviceInfo &dev, hipStream_t stream);
+                         int32_t *pos_out, const int32_t *unit_mask, const DeviceInfo &dev,
+                         hipStream_t stream);
 
 // ---- decode -------------------------------------------------------------------------
 struct DecodePlan {
@@ -39,8 +40,8 @@ hipError_t launch_decode(int batch, int n_h, int n_kv, int d_h, bool bf16, const
 // ---- select -------------------------------------------------------------------------
 size_t select_ws_bytes(int batch, int n_kv, int s_max, int n_keep, bool shared);
 hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
-                         int k, int n_keep, bool shared, int32_t *idx, int32_t *count, void *ws,
-                         const DeviceInfo &dev, hipStream_t stream);
+                         int k, int n_keep, bool shared, int32_t *idx, int32_t *count,
+                         const int32_t *unit_mask, void *ws, const DeviceInfo &dev, hipStream_t stream);
 
 // ---- score --------------------------------------------------------------------------
 struct ScorePlan {
@@ -56,7 +57,12 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
                      bool generic, int cus);
 hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, int n_kv, int d_h,
                         bool bf16, const void *q_win, const void *k, int w, bool window_in_cache,
-                        int n_keep, int pool, float scale, float *raw, float *pooled, void *ws,
-                        const ScorePlan &plan, hipStream_t stream);
+                        int n_keep, int pool, float scale, float *raw, float *pooled,
+                        const int32_t *unit_mask, void *ws, const ScorePlan &plan, hipStream_t stream);
+
+// ---- query similarity ---------------------------------------------------------------
+hipError_t launch_similarity(int batch, int n_h, int n_kv, int d_h, bool bf16, const void *q_cur,
+                             const void *q_prev, double tau, float *cos, int32_t *refresh, int32_t *keep,
+                             hipStream_t stream);
 
 }  // namespace kvc

@@ -67,10 +67,12 @@ __device__ __forceinline__ void load_row_f32(const void *base, size_t row, float
 template <bool BF16, int D>
 __global__ __launch_bounds__(kGenThreads) void gen_logits_kernel(
     const void *__restrict__ q_win, const void *__restrict__ k, const int32_t *__restrict__ seq_lens,
-    int s_max, int n_h, int n_kv, int w, int wic, int R, int unit0, float scale, float *__restrict__ logits)
+    int s_max, int n_h, int n_kv, int w, int wic, int R, int unit0, float scale, const int32_t *__restrict__ mask,
+    float *__restrict__ logits)
 {
     __shared__ float qs[kGenRowsLds][D];
     const int u = unit0 + blockIdx.y;
+    if (mask && !mask[u]) return;
     const int b = u / n_kv;
     const int g = u - b * n_kv;
     const int r = n_h / n_kv;
@@ -109,8 +111,10 @@ __global__ __launch_bounds__(kGenThreads) void gen_logits_kernel(
 // Per row: M = max logit, L = sum exp(x - M); fin = (-M*log2e, 1/L), or (0, 0) when
 // the row sees no key.
 __global__ __launch_bounds__(kGenThreads) void gen_rowstats_kernel(const float *__restrict__ logits, int s_max,
-                                                                   int R, float2 *__restrict__ fin)
+                                                                   int R, const int32_t *__restrict__ mask,
+                                                                   float2 *__restrict__ fin)
 {
+    if (mask && !mask[blockIdx.y]) return;
     __shared__ float red_m[kGenThreads / kWave];
     __shared__ double red_l[kGenThreads / kWave];
     const int row = blockIdx.x;
@@ -147,10 +151,12 @@ __global__ __launch_bounds__(kGenThreads) void gen_probsum_kernel(const float *_
                                                                   const float2 *__restrict__ fin,
                                                                   const int32_t *__restrict__ seq_lens,
                                                                   int s_max, int n_kv, int R, int unit0,
+                                                                  const int32_t *__restrict__ mask,
                                                                   float *__restrict__ raw)
 {
     const int ul = blockIdx.y;
     const int u = unit0 + ul;
+    if (mask && !mask[u]) return;
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
     const int t = blockIdx.x * kGenThreads + threadIdx.x;
     if (t >= s_max) return;
@@ -178,10 +184,12 @@ constexpr int kMaxHalf = 31;        // pool kernels up to 63
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restrict__ raw,
                                                             const int32_t *__restrict__ seq_lens, int s_max,
                                                             int n_kv, int n_keep, int half,
+                                                            const int32_t *__restrict__ mask,
                                                             float *__restrict__ pooled)
 {
     __shared__ float tile[kPoolTile + 2 * kMaxHalf];
     const int u = blockIdx.y;
+    if (mask && !mask[u]) return;
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
     const int C = S - n_keep > 0 ? S - n_keep : 0;
     const int t0 = blockIdx.x * kPoolTile;
@@ -245,6 +253,7 @@ struct MfArgs {
     float2 *part;            // pass 1 out: [group][chunk][RT*16] (m, l)
     const float2 *fin;       // pass 2 in:  [group][RT*16] (-M*c, 1/L)
     float *raw;              // pass 2 out: [B*n_kv][s_max]
+    const int32_t *mask;     // [B*n_kv] or null: units with 0 are skipped
 };
 
 // Work decomposition shared by both passes (a work-group is four waves).  Logits come from
@@ -445,6 +454,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int chunk = blockIdx.x;
     const int ul = blockIdx.y;
     const int u = a.unit0 + ul;
+    if (a.mask && !a.mask[u]) return;
     const int b = u / a.n_kv;
     const int g = u - b * a.n_kv;
     const int S = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, b, a.s_max));   // uniform: scalar offsets below
@@ -517,11 +527,13 @@ constexpr int kMergeThreads = 1024;
 
 __global__ __launch_bounds__(kMergeThreads) void mfma_merge_kernel(const float2 *__restrict__ part, int n_chunks,
                                                                     int rpad, int R, float c,
+                                                                    const int32_t *__restrict__ mask,
                                                                     float2 *__restrict__ fin)
 {
     __shared__ float sm_M[kMergeThreads];
     __shared__ double sm_L[kMergeThreads];
     const int ul = blockIdx.x;
+    if (mask && !mask[ul]) return;
     const int slices = kMergeThreads / rpad;
     const int row = threadIdx.x % rpad;
     const int slice = threadIdx.x / rpad;
@@ -616,6 +628,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int chunk = blockIdx.x;
     const int ul = blockIdx.y;
     const int u = a.unit0 + ul;
+    if (a.mask && !a.mask[u]) return;
     const int b = u / a.n_kv;
     const int g = u - b * a.n_kv;
     const int S = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, b, a.s_max));   // uniform: scalar offsets below
@@ -681,7 +694,8 @@ void launch_mfma_group(const MfArgs &a, int group_units, hipStream_t stream)
     dim3 grid(a.n_chunks, group_units);
     hipLaunchKernelGGL((mfma_stats_kernel<D, RT>), grid, dim3(kMfThreads), C::LDS_BYTES, stream, a);
     hipLaunchKernelGGL(mfma_merge_kernel, dim3(group_units), dim3(kMergeThreads), 0, stream,
-                       (const float2 *)a.part, a.n_chunks, RT * 16, a.R, a.c, (float2 *)a.fin);
+                       (const float2 *)a.part, a.n_chunks, RT * 16, a.R, a.c, a.mask ? a.mask + a.unit0 : nullptr,
+                       (float2 *)a.fin);
     hipLaunchKernelGGL((mfma_probsum_kernel<D, RT>), grid, dim3(kMfThreads),
                        C::LDS_BYTES + (size_t)a.chunk_tokens * sizeof(float), stream, a);
 }
@@ -737,8 +751,8 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
 
 hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, int n_kv, int d_h, bool bf16,
                         const void *q_win, const void *k, int w, bool window_in_cache, int n_keep, int pool,
-                        float scale, float *raw, float *pooled, void *ws, const ScorePlan &plan,
-                        hipStream_t stream)
+                        float scale, float *raw, float *pooled, const int32_t *unit_mask, void *ws,
+                        const ScorePlan &plan, hipStream_t stream)
 {
     const int units = batch * n_kv;
     if (plan.mfma) {
@@ -760,6 +774,7 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         a.part = (float2 *)ws;
         a.fin = (const float2 *)((char *)ws + align256((size_t)plan.group_units * plan.n_chunks * rpad * sizeof(float2)));
         a.raw = raw;
+        a.mask = unit_mask;
         for (int u0 = 0; u0 < units; u0 += plan.group_units) {
             const int gu = min(plan.group_units, units - u0);
             a.unit0 = u0;
@@ -773,21 +788,21 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         float2 *fin = (float2 *)((char *)ws + align256((size_t)units * plan.R * s_max * sizeof(float)));
         dim3 gtok((s_max + kGenThreads - 1) / kGenThreads, units);
         if (bf16) {
-            if (d_h == 128) hipLaunchKernelGGL((gen_logits_kernel<true, 128>), gtok, dim3(kGenThreads), 0, stream, q_win, k, seq_lens, s_max, n_h, n_kv, w, window_in_cache ? 1 : 0, plan.R, 0, scale, logits);
-            else hipLaunchKernelGGL((gen_logits_kernel<true, 64>), gtok, dim3(kGenThreads), 0, stream, q_win, k, seq_lens, s_max, n_h, n_kv, w, window_in_cache ? 1 : 0, plan.R, 0, scale, logits);
+            if (d_h == 128) hipLaunchKernelGGL((gen_logits_kernel<true, 128>), gtok, dim3(kGenThreads), 0, stream, q_win, k, seq_lens, s_max, n_h, n_kv, w, window_in_cache ? 1 : 0, plan.R, 0, scale, unit_mask, logits);
+            else hipLaunchKernelGGL((gen_logits_kernel<true, 64>), gtok, dim3(kGenThreads), 0, stream, q_win, k, seq_lens, s_max, n_h, n_kv, w, window_in_cache ? 1 : 0, plan.R, 0, scale, unit_mask, logits);
         } else {
-            if (d_h == 128) hipLaunchKernelGGL((gen_logits_kernel<false, 128>), gtok, dim3(kGenThreads), 0, stream, q_win, k, seq_lens, s_max, n_h, n_kv, w, window_in_cache ? 1 : 0, plan.R, 0, scale, logits);
-            else hipLaunchKernelGGL((gen_logits_kernel<false, 64>), gtok, dim3(kGenThreads), 0, stream, q_win, k, seq_lens, s_max, n_h, n_kv, w, window_in_cache ? 1 : 0, plan.R, 0, scale, logits);
+            if (d_h == 128) hipLaunchKernelGGL((gen_logits_kernel<false, 128>), gtok, dim3(kGenThreads), 0, stream, q_win, k, seq_lens, s_max, n_h, n_kv, w, window_in_cache ? 1 : 0, plan.R, 0, scale, unit_mask, logits);
+            else hipLaunchKernelGGL((gen_logits_kernel<false, 64>), gtok, dim3(kGenThreads), 0, stream, q_win, k, seq_lens, s_max, n_h, n_kv, w, window_in_cache ? 1 : 0, plan.R, 0, scale, unit_mask, logits);
         }
         hipLaunchKernelGGL(gen_rowstats_kernel, dim3(plan.R, units), dim3(kGenThreads), 0, stream, logits, s_max,
-                           plan.R, fin);
+                           plan.R, unit_mask, fin);
         hipLaunchKernelGGL(gen_probsum_kernel, gtok, dim3(kGenThreads), 0, stream, logits, (const float2 *)fin,
-                           seq_lens, s_max, n_kv, plan.R, 0, raw);
+                           seq_lens, s_max, n_kv, plan.R, 0, unit_mask, raw);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(pool_kernel, dim3((s_max + kPoolTile - 1) / kPoolTile, units), dim3(kPoolThreads), 0, stream,
-                       raw, seq_lens, s_max, n_kv, n_keep, pool / 2, pooled);
+                       raw, seq_lens, s_max, n_kv, n_keep, pool / 2, unit_mask, pooled);
     return hipGetLastError();
 }
 

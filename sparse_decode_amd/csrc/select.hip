@@ -76,6 +76,7 @@ struct SelArgs {
     int32_t *sfx3;            // [units][n_chunks][kSfx]: suffix sums of the chunk's H3 part
     int32_t *idx;             // [units][cap]
     int32_t *count;           // [units]
+    const int32_t *mask;      // [units] or null: units with 0 are skipped by every kernel
 };
 
 // Histogram increment with leader aggregation: the lanes whose bin equals the first
@@ -191,6 +192,7 @@ __device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t
     us = unit_shape(a.seq_lens, (int)blockIdx.y / a.H, a.s_max, a.k, a.n_keep);
     t0 = (int)blockIdx.x * kChunk;
     t1 = min(us.C, t0 + kChunk);
+    if (a.mask && !a.mask[blockIdx.y]) return false;
     return us.k_eff > 0 && us.k_eff < us.C && t0 < us.C;
 }
 
@@ -314,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
+    if (a.mask && !a.mask[u]) return;
     const UnitShape us = unit_shape(a.seq_lens, u / a.H, a.s_max, a.k, a.n_keep);
     int32_t *out = a.idx + (size_t)u * a.cap;
     if (j == 0) {
@@ -496,8 +499,8 @@ size_t select_ws_bytes(int batch, int n_kv, int s_max, int n_keep, bool shared)
 }
 
 hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
-                         int k, int n_keep, bool shared, int32_t *idx, int32_t *count, void *ws,
-                         const DeviceInfo &dev, hipStream_t stream)
+                         int k, int n_keep, bool shared, int32_t *idx, int32_t *count,
+                         const int32_t *unit_mask, void *ws, const DeviceInfo &dev, hipStream_t stream)
 {
     (void)dev;
     const SelLayout L = sel_layout(batch, n_kv, s_max, n_keep, shared);
@@ -527,6 +530,7 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
     a.sfx3 = (int32_t *)(w + L.sfx_off);
     a.idx = idx;
     a.count = count;
+    a.mask = shared ? nullptr : unit_mask;
 
     const dim3 grid(L.n_chunks, units);
     hipLaunchKernelGGL(sel_level1_kernel, grid, dim3(kThreads), 0, stream, a);

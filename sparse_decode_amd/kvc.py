@@ -27,13 +27,14 @@ EXPORTED = (
     "kvc_select_topk_workspace", "kvc_select_topk",
     "kvc_gather_compact",
     "kvc_decode_attn_workspace", "kvc_decode_attn",
+    "kvc_query_similarity",
 )
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("s_max", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
                 ("n_h", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("d_h", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("unit_mask", ctypes.c_void_p)]
 
 
 class KvcError(RuntimeError):
@@ -63,9 +64,10 @@ def lib():
                 "kvc_score_window": (I, [D, P, P, I, I, I, I, F, P, P, I, P, Z, P]),
                 "kvc_select_topk_workspace": (Z, [D, I, I, I]),
                 "kvc_select_topk": (I, [D, P, I, I, I, P, P, P, Z, P]),
-                "kvc_gather_compact": (I, [I, I, I, I, P, P, P, P, P, I, I, P, P, P, P]),
+                "kvc_gather_compact": (I, [I, I, I, I, P, P, P, P, P, I, I, P, P, P, P, P]),
                 "kvc_decode_attn_workspace": (Z, [D, I]),
                 "kvc_decode_attn": (I, [D, P, P, P, P, I, F, P, P, P, Z, P]),
+                "kvc_query_similarity": (I, [D, P, P, ctypes.c_double, P, P, P, P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -120,8 +122,20 @@ def _seq_lens(seq_lens, device):
     return torch.as_tensor(seq_lens, dtype=torch.int32).to(device)
 
 
-def make_dims(batch, s_max, n_h, n_kv, d_h, dtype_code, seq_lens=None) -> Dims:
-    return Dims(int(batch), int(s_max), _ptr(seq_lens), int(n_h), int(n_kv), int(d_h), int(dtype_code))
+def _mask(unit_mask, shape, device):
+    if unit_mask is None:
+        return None
+    if not (isinstance(unit_mask, torch.Tensor) and unit_mask.is_cuda and unit_mask.dtype == torch.int32
+            and unit_mask.is_contiguous()):
+        raise ValueError("unit_mask must be a contiguous int32 device tensor")
+    if tuple(unit_mask.shape) != tuple(shape):
+        raise ValueError("unit_mask must have shape %s" % (tuple(shape),))
+    return unit_mask
+
+
+def make_dims(batch, s_max, n_h, n_kv, d_h, dtype_code, seq_lens=None, unit_mask=None) -> Dims:
+    return Dims(int(batch), int(s_max), _ptr(seq_lens), int(n_h), int(n_kv), int(d_h), int(dtype_code),
+                _ptr(unit_mask))
 
 
 # ------------------------------------------------------------------------------- score
@@ -131,8 +145,9 @@ def score_window_workspace(dims: Dims, w: int, flags: int = 0) -> int:
 
 
 def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=None, pool=1, scale=0.0,
-                 generic=False, raw=None, pooled=None, ws=None, stream=None):
-    """kvc_score_window: q_win [B][n_h][w][d_h], k [B][n_kv][s_max][d_h] -> (raw, pooled) fp32."""
+                 generic=False, raw=None, pooled=None, ws=None, unit_mask=None, stream=None):
+    """kvc_score_window: q_win [B][n_h][w][d_h], k [B][n_kv][s_max][d_h] -> (raw, pooled) fp32.
+    With unit_mask ([B][n_kv] int32), units whose entry is 0 are skipped."""
     _dev(q_win, "q_win")
     _dev(k, "k")
     B, n_h, w_, d_h = q_win.shape
@@ -140,7 +155,8 @@ def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=Non
     if w_ != w or k.dtype != q_win.dtype:
         raise ValueError("q_win/k shapes or dtypes disagree")
     sl = _seq_lens(seq_lens, k.device)
-    dims = make_dims(B, s_max, n_h, n_kv, d_h, _dtype_code(k), sl)
+    um = _mask(unit_mask, (B, n_kv), k.device)
+    dims = make_dims(B, s_max, n_h, n_kv, d_h, _dtype_code(k), sl, um)
     flags = KVC_SCORE_GENERIC if generic else 0
     if n_keep is None:
         n_keep = w
@@ -165,14 +181,16 @@ def select_topk_workspace(dims: Dims, k: int, n_keep: int, flags: int = 0) -> in
 
 
 def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=None, count=None, ws=None,
-                stream=None):
-    """kvc_select_topk: scores [B][n_kv][s_max] fp32 -> (idx [B][H][k+n_keep], count [B][H]) int32."""
+                unit_mask=None, stream=None):
+    """kvc_select_topk: scores [B][n_kv][s_max] fp32 -> (idx [B][H][k+n_keep], count [B][H]) int32.
+    With unit_mask ([B][n_kv] int32), units whose entry is 0 are skipped."""
     _dev(scores, "scores")
     if scores.dtype != torch.float32:
         raise TypeError("scores must be float32")
     B, n_kv, s_max = scores.shape
     sl = _seq_lens(seq_lens, scores.device)
-    dims = make_dims(B, s_max, n_kv, n_kv, 128, KVC_F32, sl)
+    um = _mask(unit_mask, (B, n_kv), scores.device)
+    dims = make_dims(B, s_max, n_kv, n_kv, 128, KVC_F32, sl, um)
     flags = KVC_SELECT_SHARED_HEADS if shared_heads else 0
     H = 1 if shared_heads else n_kv
     cap = k + n_keep
@@ -193,8 +211,9 @@ def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=Non
 # ------------------------------------------------------------------------------ gather
 
 def gather_compact(src0, idx, count, *, src1=None, src_pos=None, dst0=None, dst1=None, pos_out=None,
-                   want_pos=True, stream=None):
-    """kvc_gather_compact: src [B][heads][s_max][...] -> dst [B][heads][cap][...] (+ pos_out)."""
+                   want_pos=True, unit_mask=None, stream=None):
+    """kvc_gather_compact: src [B][heads][s_max][...] -> dst [B][heads][cap][...] (+ pos_out).
+    With unit_mask ([B][idx_heads] int32), lists whose entry is 0 are skipped."""
     _dev(src0, "src0")
     _dev(idx, "idx")
     _dev(count, "count")
@@ -212,7 +231,8 @@ def gather_compact(src0, idx, count, *, src1=None, src_pos=None, dst0=None, dst1
         pos_out = torch.empty((B, heads, cap), dtype=torch.int32, device=src0.device)
     st = lib().kvc_gather_compact(int(B), int(heads), int(s_max), int(row_bytes), _ptr(src0), _ptr(src1),
                                   _ptr(src_pos), _ptr(idx), _ptr(count), int(idx_heads), int(cap), _ptr(dst0),
-                                  _ptr(dst1), _ptr(pos_out), _stream(stream))
+                                  _ptr(dst1), _ptr(pos_out), _ptr(_mask(unit_mask, (B, idx_heads), src0.device)),
+                                  _stream(stream))
     _check(st, "kvc_gather_compact")
     return dst0, dst1, pos_out
 
@@ -242,3 +262,27 @@ def decode_attn(q, kc, vc, count, *, scale=0.0, out=None, lse=None, want_lse=Tru
                                _stream(stream))
     _check(st, "kvc_decode_attn")
     return out, lse
+
+
+# ----------------------------------------------------------------------- query similarity
+
+def query_similarity(q_cur, q_prev, n_kv, tau, *, cos=None, refresh=None, keep=None, want_cos=True,
+                     stream=None):
+    """kvc_query_similarity: q_cur, q_prev [B][n_h][d_h] -> (cos [B][n_h] fp32, refresh, keep [B][n_kv] int32)."""
+    _dev(q_cur, "q_cur")
+    _dev(q_prev, "q_prev")
+    if q_cur.shape != q_prev.shape or q_cur.dtype != q_prev.dtype:
+        raise ValueError("q_cur/q_prev shapes or dtypes disagree")
+    B, n_h, d_h = q_cur.shape
+    dims = make_dims(B, 1, n_h, n_kv, d_h, _dtype_code(q_cur))
+    dev = q_cur.device
+    if want_cos and cos is None:
+        cos = torch.empty((B, n_h), dtype=torch.float32, device=dev)
+    if refresh is None:
+        refresh = torch.empty((B, n_kv), dtype=torch.int32, device=dev)
+    if keep is None:
+        keep = torch.empty((B, n_kv), dtype=torch.int32, device=dev)
+    st = lib().kvc_query_similarity(ctypes.byref(dims), _ptr(q_cur), _ptr(q_prev), float(tau), _ptr(cos),
+                                    _ptr(refresh), _ptr(keep), _stream(stream))
+    _check(st, "kvc_query_similarity")
+    return cos, refresh, keep

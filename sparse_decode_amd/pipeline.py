@@ -46,19 +46,19 @@ class LayerPath:
         self.ws_select = torch.zeros(max(256, kvc.select_topk_workspace(sdims, self.k, wl.n_keep)),
                                      dtype=torch.uint8, device=dev)
 
-    def score(self, q_win, k, seq_lens=None):
+    def score(self, q_win, k, seq_lens=None, unit_mask=None):
         wl = self.wl
         return kvc.score_window(q_win, k, wl.w, seq_lens=seq_lens, window_in_cache=wl.window_in_cache,
                                 n_keep=wl.n_keep, pool=wl.pool, raw=self.raw, pooled=self.pooled,
-                                ws=self.ws_score)
+                                ws=self.ws_score, unit_mask=unit_mask)
 
-    def select(self, seq_lens=None):
+    def select(self, seq_lens=None, unit_mask=None):
         return kvc.select_topk(self.pooled, self.k, self.wl.n_keep, seq_lens=seq_lens, idx=self.idx,
-                               count=self.count, ws=self.ws_select)
+                               count=self.count, ws=self.ws_select, unit_mask=unit_mask)
 
-    def gather(self, k, v, src_pos=None):
+    def gather(self, k, v, src_pos=None, unit_mask=None):
         return kvc.gather_compact(k, self.idx, self.count, src1=v, src_pos=src_pos, dst0=self.kc, dst1=self.vc,
-                                  pos_out=self.pos)
+                                  pos_out=self.pos, unit_mask=unit_mask)
 
     def decode(self, q_dec):
         return kvc.decode_attn(q_dec, self.kc, self.vc, self.count, out=self.out, lse=self.lse,
@@ -98,3 +98,66 @@ class TspStep:
         h = hidden.view(hidden.shape[0], 1, hidden.shape[1], hidden.shape[2])
         kvc.gather_compact(h, self.idx, self.count, dst0=self.hidden_out, pos_out=self.pos)
         return self.hidden_out, self.pos
+
+
+class SpeculativeRetrieval:
+    """FreeKV technical summary section 2.A on one GPU: speculative retrieval with
+    fine-grained correction, for a workload whose per-step query re-scores the cache.
+
+    Two compacted caches alternate.  At step i the current one holds the selection
+    made with q_{i-1}; `critical` finds the KV heads whose query drifted (cosine
+    below tau for some query head of the group), redoes score -> select -> gather
+    for those heads only (unit masks), and attends over the current cache.
+    `speculate` then selects with q_i for every head into the other cache, which
+    step i + 1 reuses; it does not depend on step i's attention and may run on a
+    second stream beside it.  `swap` makes the other cache current.  The first
+    step has no previous query: every head is selected before attention.
+    """
+
+    def __init__(self, wl: Workload, tau: float, device="cuda", s_max: int | None = None,
+                 batch: int | None = None):
+        self.wl = wl
+        self.tau = float(tau)
+        self.paths = [LayerPath(wl, device, s_max, batch), LayerPath(wl, device, s_max, batch)]
+        self.cur = 0
+        B, dev = self.paths[0].B, torch.device(device)
+        self.cos = torch.empty((B, wl.n_h), dtype=torch.float32, device=dev)
+        self.refresh = torch.empty((B, wl.n_kv), dtype=torch.int32, device=dev)
+        self.keep = torch.empty((B, wl.n_kv), dtype=torch.int32, device=dev)
+
+    @property
+    def current(self) -> LayerPath:
+        return self.paths[self.cur]
+
+    @property
+    def other(self) -> LayerPath:
+        return self.paths[1 - self.cur]
+
+    def critical(self, q, q_prev, k, v, seq_lens=None):
+        """The work before step i's attention, then the attention itself.
+        q, q_prev [B][n_h][d_h] (q_prev None at the first step)."""
+        p = self.current
+        q_win = q.view(q.shape[0], q.shape[1], 1, q.shape[2])
+        if q_prev is None:
+            self.refresh.fill_(1)
+            self.keep.fill_(0)
+            p.score(q_win, k, seq_lens)
+            p.select(seq_lens)
+            p.gather(k, v)
+        else:
+            kvc.query_similarity(q, q_prev, self.wl.n_kv, self.tau, cos=self.cos, refresh=self.refresh,
+                                 keep=self.keep)
+            p.score(q_win, k, seq_lens, unit_mask=self.refresh)
+            p.select(seq_lens, unit_mask=self.refresh)
+            p.gather(k, v, unit_mask=self.refresh)
+        return p.decode(q)
+
+    def speculate(self, q, k, v, seq_lens=None):
+        """Selection with q for every head into the other cache (used by the next step)."""
+        p = self.other
+        p.score(q.view(q.shape[0], q.shape[1], 1, q.shape[2]), k, seq_lens)
+        p.select(seq_lens)
+        p.gather(k, v)
+
+    def swap(self):
+        self.cur = 1 - self.cur

@@ -143,6 +143,26 @@ def _unit_dirs(wl: Workload, layer: int, n: int, d: int) -> np.ndarray:
     return u / np.linalg.norm(u, axis=1, keepdims=True)
 
 
+def _step_queries(wl: Workload, layer: int, step: int, B: int, device):
+    """The per-step query rows [B][n_h][w][d_h] (fp32) of a workload whose query is
+    not in the cache, and the persistent component (None for iid queries)."""
+    d, nh = wl.d_h, wl.n_h
+    q_win = _randn((B, nh, wl.w, d), seed_for(wl.cfg_id, layer, STREAM_QDEC, step), device)
+    qm = None
+    if wl.query_mode == "persistent":
+        qm = _randn((B, nh, d), seed_for(wl.cfg_id, layer, STREAM_QMEAN), device)
+        q_win = (3.0 * qm[:, :, None, :] + q_win) / math.sqrt(10.0)
+    return q_win, qm
+
+
+def step_query(wl: Workload, layer: int, step: int, device="cpu", batch: int | None = None):
+    """Decode query [B][n_h][d_h] of one step (workload dtype), identical to the q_dec
+    that layer_inputs returns for that step, without drawing the cache again."""
+    B = wl.batch if batch is None else batch
+    q_win, _ = _step_queries(wl, layer, step, B, device)
+    return q_win[:, :, -1, :].to(wl.torch_dtype).contiguous()
+
+
 def layer_inputs(wl: Workload, layer: int = 0, device="cpu", step: int = 0, s_max: int | None = None,
                  batch: int | None = None):
     """Draws one layer's window queries, cache and decode query.
@@ -162,10 +182,7 @@ def layer_inputs(wl: Workload, layer: int = 0, device="cpu", step: int = 0, s_ma
         q_win = _randn((B, nh, wl.w, d), seed_for(wl.cfg_id, layer, STREAM_QWIN), device)
         q_dec = _randn((B, nh, d), seed_for(wl.cfg_id, layer, STREAM_QDEC), device)
     else:
-        q_win = _randn((B, nh, wl.w, d), seed_for(wl.cfg_id, layer, STREAM_QDEC, step), device)
-        if wl.query_mode == "persistent":
-            qm = _randn((B, nh, d), seed_for(wl.cfg_id, layer, STREAM_QMEAN), device)
-            q_win = (3.0 * qm[:, :, None, :] + q_win) / math.sqrt(10.0)
+        q_win, qm = _step_queries(wl, layer, step, B, device)
         q_dec = q_win[:, :, -1, :].clone()
     k = _randn((B, nkv, S, d), seed_for(wl.cfg_id, layer, STREAM_K), device)
     v = _randn((B, nkv, S, d), seed_for(wl.cfg_id, layer, STREAM_V), device)

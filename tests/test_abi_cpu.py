@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvc.lib().kvc_abi_version() == 1
+    assert kvc.lib().kvc_abi_version() == 2
     seen = set()
     for s in range(5):
         txt = kvc.status_str(s)
@@ -122,11 +122,11 @@ def test_select_rejects_invalid_arguments():
 
 def _gather(**kw):
     a = dict(batch=1, heads=8, s_max=1024, row_bytes=256, src0=BAD, src1=BAD, src_pos=None, idx=BAD, count=BAD,
-             idx_heads=8, cap=80, dst0=BAD, dst1=BAD, pos=BAD)
+             idx_heads=8, cap=80, dst0=BAD, dst1=BAD, pos=BAD, mask=None)
     a.update(kw)
     return kvc.lib().kvc_gather_compact(a["batch"], a["heads"], a["s_max"], a["row_bytes"], a["src0"], a["src1"],
                                         a["src_pos"], a["idx"], a["count"], a["idx_heads"], a["cap"], a["dst0"],
-                                        a["dst1"], a["pos"], None)
+                                        a["dst1"], a["pos"], a["mask"], None)
 
 
 def test_gather_rejects_invalid_arguments():
@@ -159,6 +159,7 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(_dims(), q=None) == E
     assert _decode(_dims(), out=None) == E
     assert _decode(_dims(), scale=-2.0) == E
+    assert _decode(_dims(), scale=float("nan")) == E
     assert _decode(_dims(), vc=BAD + 2) == E
     assert _decode(_dims(), ws=None) == W
     assert _decode(_dims(), ws_bytes=16) == W
@@ -171,3 +172,31 @@ def test_valid_call_without_gpu_reports_hip_error():
     assert _select(_dims(), ws=BAD, ws_bytes=kvc.select_topk_workspace(_dims(), 64, 16)) == kvc.KVC_ERR_HIP
     assert _decode(_dims()) == kvc.KVC_ERR_HIP
     assert _score(_dims()) == kvc.KVC_ERR_HIP
+
+
+def _similarity(dims, **kw):
+    a = dict(q_cur=BAD, q_prev=BAD, tau=0.9, cos=BAD, refresh=BAD, keep=None)
+    a.update(kw)
+    return kvc.lib().kvc_query_similarity(ctypes.byref(dims) if dims is not None else None, a["q_cur"], a["q_prev"],
+                                          a["tau"], a["cos"], a["refresh"], a["keep"], None)
+
+
+def test_similarity_rejects_invalid_arguments():
+    E, U = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_UNSUPPORTED
+    assert _similarity(None) == E
+    assert _similarity(_dims(n_kv=5)) == E
+    assert _similarity(_dims(d_h=80)) == U
+    assert _similarity(_dims(), q_cur=None) == E
+    assert _similarity(_dims(), refresh=None) == E
+    assert _similarity(_dims(), q_prev=BAD + 4) == E
+    assert _similarity(_dims(), tau=float("nan")) == E
+    assert _similarity(_dims(), tau=float("inf")) == E
+    # valid arguments reach the launch, which fails without a device
+    assert _similarity(_dims(), tau=-3.0) == kvc.KVC_ERR_HIP
+
+
+def test_shared_head_selection_takes_no_unit_mask():
+    d = _dims()
+    d.unit_mask = BAD
+    assert kvc.select_topk_workspace(d, 64, 16, kvc.KVC_SELECT_SHARED_HEADS) == 0
+    assert _select(d, flags=kvc.KVC_SELECT_SHARED_HEADS) == kvc.KVC_ERR_INVALID_ARG
