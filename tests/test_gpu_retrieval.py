@@ -163,3 +163,45 @@ def test_speculative_schedule_vs_oracle(tau):
         assert all(c == 1.0 for c in corrected)
     else:
         assert corrected[0] == 1.0 and max(corrected[1:]) < 0.5
+
+
+def test_overlapped_schedule_matches_sequential():
+    # the speculative selection on a second stream beside the critical path (events
+    # order the two caches) gives bit-identical attention outputs to running them in turn
+    wl = synth.WORKLOADS[4]
+    steps = 6
+    _say("overlapped schedule", wl.name, "steps", steps)
+    inp = synth.layer_inputs(wl, 0, device=DEV, step=0)
+    k, v = inp["k"], inp["v"]
+    sl = torch.from_numpy(inp["seq_lens"]).to(DEV)
+    qs = [synth.step_query(wl, 0, i, device=DEV) for i in range(steps)]
+    seq = SpeculativeRetrieval(wl, TAU)
+    want = []
+    for i, q in enumerate(qs):
+        seq.critical(q, qs[i - 1] if i else None, k, v, sl)
+        want.append(seq.current.out.clone())
+        seq.speculate(q, k, v, sl)
+        seq.swap()
+    ovl = SpeculativeRetrieval(wl, TAU)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    got, e_c, e_s = [], None, None
+    for i, q in enumerate(qs):
+        if e_s is not None:
+            main.wait_event(e_s)
+        ovl.critical(q, qs[i - 1] if i else None, k, v, sl)
+        got.append(ovl.current.out.clone())
+        e_prev_c, e_c = e_c, torch.cuda.Event()
+        e_c.record(main)
+        with torch.cuda.stream(side):
+            if e_prev_c is not None:
+                side.wait_event(e_prev_c)
+            ovl.speculate(q, k, v, sl)
+            e_s = torch.cuda.Event()
+            e_s.record(side)
+        ovl.swap()
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        assert torch.equal(got[i].view(torch.int16), want[i].view(torch.int16)), "step %d" % i
