@@ -51,6 +51,8 @@ struct ScorePlan {
     int chunk_tokens = 0;      // MFMA path: tokens per work-group
     int n_chunks = 0;
     int group_units = 0;       // KV-head units per pass-1/pass-2 launch pair
+    int logit_rows = 0;        // MFMA path, R <= 16: logits kept per token between the passes
+    size_t logits_off = 0;     // their place in the workspace
     size_t ws_bytes = 0;
 };
 ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16, int w,

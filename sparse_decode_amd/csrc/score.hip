@@ -253,6 +253,8 @@ struct MfArgs {
     float2 *part;            // pass 1 out: [group][chunk][RT*16] (m, l)
     const float2 *fin;       // pass 2 in:  [group][RT*16] (-M*c, 1/L)
     float *raw;              // pass 2 out: [B*n_kv][s_max]
+    float *logits;           // one row block only: pass 1 keeps its logits [B*n_kv][s_max][rs], or null
+    int rs;                  // rows kept per token (R rounded up to 4)
     const int32_t *mask;     // [B*n_kv] or null: units with 0 are skipped
 };
 
@@ -395,7 +397,7 @@ __device__ __forceinline__ void stream_stages(__amdgpu_buffer_rsrc_t kunit, int 
 template <int D, int RT, bool MASK>
 __device__ __forceinline__ void stats_stage(const unsigned char *buf, int st0, int tg, int n, int kg,
                                             const u32x4 (*qb)[Sc<D, RT>::KS], const int *last, float c,
-                                            float *m, double *l)
+                                            float *m, double *l, float *lg, int rs, int S)
 {
     using C = Sc<D, RT>;
     constexpr int NV = 4 * C::PAIR;                      // logits per lane per row block per max
@@ -414,6 +416,16 @@ __device__ __forceinline__ void stats_stage(const unsigned char *buf, int st0, i
                 for (int j = 0; j < 4; ++j) {
                     x[cb][4 * pp + j] = x4[j];
                     if (MASK && st0 + tile * 16 + 4 * kg + j > last[cb]) x[cb][4 * pp + j] = -INFINITY;
+                }
+                if constexpr (RT == 1) {
+                    // few rows: keep the logits (rs floats per token) for pass 2 instead of K
+                    if (lg && n < rs) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int tok = st0 + tile * 16 + 4 * kg + j;
+                            if (tok < S) lg[(size_t)tok * rs + n] = x[cb][4 * pp + j];
+                        }
+                    }
                 }
             }
         }
@@ -475,6 +487,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         last[cb] = a.wic ? min(S - a.w + i, S - 1) : S - 1;
     }
     const int all_vis = a.wic ? S - a.w : S - 1;          // every row sees tokens <= all_vis
+    float *lg = a.logits ? a.logits + (size_t)u * a.s_max * a.rs : nullptr;
     float m[C::CPW];
     double l[C::CPW];
 #pragma unroll
@@ -486,9 +499,9 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         [&](const unsigned char *cur, int st) {
             const int st0 = ch0 + st * C::ST;
             if (st0 + C::ST - 1 <= all_vis)
-                stats_stage<D, RT, false>(cur, st0, tg, n, kg, qb, last, a.c, m, l);
+                stats_stage<D, RT, false>(cur, st0, tg, n, kg, qb, last, a.c, m, l, lg, a.rs, S);
             else
-                stats_stage<D, RT, true>(cur, st0, tg, n, kg, qb, last, a.c, m, l);
+                stats_stage<D, RT, true>(cur, st0, tg, n, kg, qb, last, a.c, m, l, lg, a.rs, S);
         },
         [&](int) {});
     // merge the four lane groups of a row (lanes n, n+16, n+32, n+48), then the token groups
@@ -687,6 +700,46 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
 }
 
+// Pass 2 from the logits pass 1 kept (a single row block of at most 16 rows): per
+// token, raw = sum over rows, in row order, of exp2(x c - M c) / L.  Each thread reads
+// one token's rs consecutive logits; no K is read again.
+constexpr int kLogitThreads = 256;
+
+__global__ __launch_bounds__(kLogitThreads) void logit_probsum_kernel(const float *__restrict__ logits,
+                                                                      const float2 *__restrict__ fin,
+                                                                      const int32_t *__restrict__ seq_lens,
+                                                                      int s_max, int n_kv, int R, int rs, int rpad,
+                                                                      int unit0, float c,
+                                                                      const int32_t *__restrict__ mask,
+                                                                      float *__restrict__ raw)
+{
+    __shared__ float2 f[16];
+    const int ul = blockIdx.y;
+    const int u = unit0 + ul;
+    if (mask && !mask[u]) return;
+    if (threadIdx.x < 16) f[threadIdx.x] = threadIdx.x < R ? fin[(size_t)ul * rpad + threadIdx.x] : make_float2(0.f, 0.f);
+    __syncthreads();
+    const int S = clamp_len(seq_lens, u / n_kv, s_max);
+    const int t = blockIdx.x * kLogitThreads + threadIdx.x;
+    if (t >= s_max) return;
+    float acc = 0.f;
+    if (t < S) {
+        const float4 *x4 = (const float4 *)(logits + ((size_t)u * s_max + t) * rs);
+        float x[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (4 * q < rs) {
+                const float4 v = x4[q];
+                x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (r < R) acc = fmaf(fast_exp2(fmaf(x[r], c, f[r].x)), f[r].y, acc);
+    }
+    raw[(size_t)u * s_max + t] = acc;
+}
+
 template <int D, int RT>
 void launch_mfma_group(const MfArgs &a, int group_units, hipStream_t stream)
 {
@@ -696,8 +749,14 @@ void launch_mfma_group(const MfArgs &a, int group_units, hipStream_t stream)
     hipLaunchKernelGGL(mfma_merge_kernel, dim3(group_units), dim3(kMergeThreads), 0, stream,
                        (const float2 *)a.part, a.n_chunks, RT * 16, a.R, a.c, a.mask ? a.mask + a.unit0 : nullptr,
                        (float2 *)a.fin);
-    hipLaunchKernelGGL((mfma_probsum_kernel<D, RT>), grid, dim3(kMfThreads),
-                       C::LDS_BYTES + (size_t)a.chunk_tokens * sizeof(float), stream, a);
+    if (RT == 1 && a.logits) {
+        const dim3 lgrid((a.s_max + kLogitThreads - 1) / kLogitThreads, group_units);
+        hipLaunchKernelGGL(logit_probsum_kernel, lgrid, dim3(kLogitThreads), 0, stream, (const float *)a.logits,
+                           a.fin, a.seq_lens, a.s_max, a.n_kv, a.R, a.rs, RT * 16, a.unit0, a.c, a.mask, a.raw);
+    } else {
+        hipLaunchKernelGGL((mfma_probsum_kernel<D, RT>), grid, dim3(kMfThreads),
+                           C::LDS_BYTES + (size_t)a.chunk_tokens * sizeof(float), stream, a);
+    }
 }
 
 template <int D>
@@ -741,6 +800,11 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
         p.n_chunks = (s_max + ct_tok - 1) / ct_tok;
         p.ws_bytes = align256((size_t)p.group_units * p.n_chunks * rpad * sizeof(float2)) +
                      align256((size_t)p.group_units * rpad * sizeof(float2)) + 256;
+        // a single row block (R <= 16): pass 1 keeps its logits, 4 * rs bytes per token,
+        // and pass 2 reads those instead of K's 2 * d_h bytes
+        p.logit_rows = rt == 1 ? (p.R + 3) / 4 * 4 : 0;
+        p.logits_off = p.ws_bytes;
+        if (p.logit_rows) p.ws_bytes += align256((size_t)units * s_max * p.logit_rows * sizeof(float));
     } else {
         p.group_units = units;
         p.ws_bytes = align256((size_t)units * p.R * s_max * sizeof(float)) +
@@ -775,6 +839,8 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         a.fin = (const float2 *)((char *)ws + align256((size_t)plan.group_units * plan.n_chunks * rpad * sizeof(float2)));
         a.raw = raw;
         a.mask = unit_mask;
+        a.rs = plan.logit_rows;
+        a.logits = plan.logit_rows ? (float *)((char *)ws + plan.logits_off) : nullptr;
         for (int u0 = 0; u0 < units; u0 += plan.group_units) {
             const int gu = min(plan.group_units, units - u0);
             a.unit0 = u0;
