@@ -114,18 +114,33 @@ def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=Non
     return raw, pooled
 
 
-def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False):
+def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, k_per_unit=None):
     """Per-head top-k (score desc, index asc) + trailing n_keep tokens, ascending.
 
     scores [B][H][s_max] float32.  Returns (idx int32 [B][H_out][k+n_keep], count int32 [B][H_out]).
+    With k_per_unit ([B][H_out]), unit u takes min(k_per_unit[u], k) candidates (clamped at 0)
+    and its row keeps the width k + n_keep, -1 padded (per-layer budgets, Tutorial
+    "Compresser un cache existant": PyramidKV gives layers different cache budgets).
     """
     scores = _f32(scores)
     B, H, s_max = scores.shape
     H_out = 1 if shared_heads else H
     cap = k + n_keep
+    sl = _i32(seq_lens)
+    if k_per_unit is not None:
+        ku = np.clip(np.asarray(k_per_unit, np.int64).reshape(B, H_out), 0, k)
+        idx = np.full((B, H_out, cap), -1, np.int32)
+        count = np.empty((B, H_out), np.int32)
+        for b in range(B):
+            slb = None if sl is None else sl[b:b + 1]
+            for h in range(H_out):
+                src = scores[b:b + 1] if shared_heads else scores[b:b + 1, h:h + 1]
+                i1, c1 = select_topk(src, int(ku[b, h]), n_keep, seq_lens=slb, shared_heads=shared_heads)
+                idx[b, h, :i1.shape[-1]] = i1[0, 0]
+                count[b, h] = c1[0, 0]
+        return idx, count
     idx = np.empty((B, H_out, cap), np.int32)
     count = np.empty((B, H_out), np.int32)
-    sl = _i32(seq_lens)
     _load().kvo_select_topk(B, H, s_max, _ptr(sl), _ptr(scores), int(k), int(n_keep),
                             int(bool(shared_heads)), _ptr(idx), _ptr(count))
     return idx, count

@@ -522,3 +522,35 @@ def test_speculative_step_corrects_per_kv_head():
     forced = oracle.speculative_step(mixed, q0, kk, vv, prev, tau=0.9, refresh=np.array([[1, 0]]), **kw)
     assert np.array_equal(forced["idx"][0, 0], forced["next_sel"][0][0, 0])
     assert np.array_equal(forced["idx"][0, 1], prev[0][0, 1])
+
+
+# ----------------------------------------------------------------------------------
+# Budgets that differ per unit (Tutorial, "Compresser un cache existant": PyramidKV)
+# ----------------------------------------------------------------------------------
+def test_select_per_unit_budgets_bruteforce():
+    rng = np.random.default_rng(41)
+    B, H, S, n_keep = 2, 3, 11, 2
+    sc = (rng.integers(0, 6, (B, H, S)) / 5.0).astype(np.float32)      # many exact ties
+    sl = np.array([S, 8], np.int32)
+    ku = np.array([[0, 3, 9], [2, 5, 1]], np.int32)                      # 9 > C for both sequences
+    k = 6
+    idx, cnt = oracle.select_topk(sc, k, n_keep, seq_lens=sl, k_per_unit=ku)
+    for b in range(B):
+        S_b = int(sl[b])
+        C = S_b - n_keep
+        for h in range(H):
+            k_eff = min(int(ku[b, h]), k, C)
+            # brute force: the lexicographically best k_eff-subset under (score desc, index asc)
+            best = None
+            for sub in itertools.combinations(range(C), k_eff):
+                key = sorted(((-float(sc[b, h, t]), t) for t in sub))
+                if best is None or key < best[0]:
+                    best = (key, sub)
+            want = sorted(best[1]) + list(range(C, S_b))
+            n = int(cnt[b, h])
+            assert n == len(want) and idx[b, h, :n].tolist() == want
+            assert np.all(idx[b, h, n:] == -1)
+    # a uniform budget array is the scalar budget
+    u_idx, u_cnt = oracle.select_topk(sc, 4, n_keep, seq_lens=sl, k_per_unit=np.full((B, H), 4, np.int32))
+    s_idx, s_cnt = oracle.select_topk(sc, 4, n_keep, seq_lens=sl)
+    assert np.array_equal(u_idx, s_idx) and np.array_equal(u_cnt, s_cnt)
