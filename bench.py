@@ -304,13 +304,65 @@ def main():
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.no_retrieval:
-        print("[bench] speculative retrieval on ragged_b16", file=sys.stderr, flush=True)
+        print("[bench] per-layer budgets", file=sys.stderr, flush=True)
         del g_step, g_layer_step, g_fold, g_call
+        res["pyramid_budgets"] = measure_pyramid(wl, L, B, QW, K, V, QD, sl_all, dev, args.steps)
+        print("[bench] speculative retrieval on ragged_b16", file=sys.stderr, flush=True)
         res["speculative_retrieval"] = measure_retrieval(dev, 64, 5)
     print(json.dumps(res), flush=True)
 
 
 RETRIEVAL_TAU = 0.85
+PYRAMID_BETA = 0.5
+
+
+def measure_pyramid(wl, L, B, QW, K, V, QD, sl_all, dev, steps):
+    """The folded step with per-layer budgets (PyramidKV-style, mean budget k): layer l
+    keeps pyramid_budgets(k, L)[l] + n_keep tokens per KV head; one select call over all
+    layers takes the budgets as a per-unit array."""
+    import torch
+
+    from sparse_decode_amd import kvc, synth
+    from sparse_decode_amd.pipeline import LayerPath
+    budgets = synth.pyramid_budgets(wl.k, L, PYRAMID_BETA)
+    kmax = max(budgets)
+    path = LayerPath(wl, device=dev, batch=L * B, k=kmax)
+    # unit (l * B + b, g) takes layer l's budget
+    kpu = (torch.tensor(budgets, dtype=torch.int32, device=dev).repeat_interleave(B)[:, None]
+           .expand(L * B, wl.n_kv).contiguous())
+    outs = torch.empty((L, B, wl.n_h, wl.d_h), dtype=wl.torch_dtype, device=dev)
+
+    def step():
+        path.score(QW, K, sl_all)
+        path.select(sl_all, k_per_unit=kpu)
+        path.gather(K, V)
+        for l in range(L):
+            sl = slice(l * B, (l + 1) * B)
+            kvc.decode_attn(QD[l], path.kc[sl], path.vc[sl], path.count[sl], out=outs[l], ws=path.ws_decode)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    mean_S = float(np.mean(sl_all.cpu().numpy()))
+    nbytes = 0.0
+    for l in range(L):
+        by = layer_bytes(wl, mean_S, budgets[l] + wl.n_keep)
+        nbytes += by["score"] + by["select"] + by["gather"] + by["decode"]
+    del g
+    return {"schedule": "linear from (1+beta) k to (1-beta) k over the layers, mean k", "beta": PYRAMID_BETA,
+            "k_first_layer": budgets[0], "k_last_layer": budgets[-1], "k_mean": round(sum(budgets) / L, 2),
+            "ms_per_step": round(ms, 4), "value_GBps": round(nbytes / (ms * 1e-3) / 1e9, 2)}
 
 
 def measure_retrieval(dev, steps, reps):

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -160,15 +160,18 @@ kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void 
  * plus the always-kept trailing tokens (FastKV 2.A), in ascending original order.
  *
  * For each unit (b, g) (or b alone with KVC_SELECT_SHARED_HEADS, score = float sum
- * over g in head order), with C = max(0, S_b - n_keep) candidates [0, C):
- *   k_eff = min(k, C); the first k_eff candidates in the total order
+ * over g in head order), with C = max(0, S_b - n_keep) candidates [0, C) and the
+ * unit's budget k_u = k, or k_per_unit[u] clamped to [0, k] (PyramidKV-style budgets
+ * that differ per layer or head: Tutorial, "Compresser un cache existant"):
+ *   k_eff = min(k_u, C); the first k_eff candidates in the total order
  *   (score descending, index ascending) are selected;
  *   idx[0 .. k_eff) = those indices ascending; idx[k_eff ..) = C, C+1, ..., S_b - 1;
  *   count = k_eff + (S_b - C); idx entries past count are -1.
  *
  * scores [B][n_kv][s_max] float (the pooled output of kvc_score_window); must not
  *        hold NaN; -0.0 and +0.0 are equal
- * k, n_keep  >= 0, cap = k + n_keep >= 1
+ * k, n_keep  >= 0, cap = k + n_keep >= 1 (k: the largest budget)
+ * k_per_unit  [B][H] int32 or NULL (every unit takes k)
  * idx    [B][H][k + n_keep] int32, H = n_kv, or 1 with KVC_SELECT_SHARED_HEADS
  * count  [B][H] int32
  * ws     at least kvc_select_topk_workspace(dims, k, n_keep, flags) bytes, 16-byte
@@ -182,7 +185,7 @@ kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void 
  */
 size_t kvc_select_topk_workspace(const kvc_dims *dims, int32_t k, int32_t n_keep, int32_t flags);
 kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores, int32_t k, int32_t n_keep,
-                           int32_t flags, int32_t *idx, int32_t *count,
+                           int32_t flags, const int32_t *k_per_unit, int32_t *idx, int32_t *count,
                            void *ws, size_t ws_bytes, void *stream);
 
 /*

@@ -149,8 +149,8 @@ KVC_EXPORT size_t kvc_select_topk_workspace(const kvc_dims *dims, int32_t k, int
 }
 
 KVC_EXPORT kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores, int32_t k, int32_t n_keep,
-                                      int32_t flags, int32_t *idx, int32_t *count, void *ws, size_t ws_bytes,
-                                      void *stream)
+                                      int32_t flags, const int32_t *k_per_unit, int32_t *idx, int32_t *count,
+                                      void *ws, size_t ws_bytes, void *stream)
 {
     kvc_status st = select_args(dims, k, n_keep, flags);
     if (st != KVC_OK) return st;
@@ -161,7 +161,8 @@ KVC_EXPORT kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores,
     kvc::DeviceInfo dev;
     if (kvc::device_info(&dev) != hipSuccess) return KVC_ERR_HIP;
     hipError_t e = kvc::launch_select(dims->batch, dims->n_kv, dims->s_max, dims->seq_lens, scores, k, n_keep,
-                                      shared, idx, count, dims->unit_mask, ws, dev, (hipStream_t)stream);
+                                      shared, idx, count, dims->unit_mask, k_per_unit, ws, dev,
+                                      (hipStream_t)stream);
     return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 

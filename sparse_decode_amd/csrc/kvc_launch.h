@@ -41,7 +41,8 @@ hipError_t launch_decode(int batch, int n_h, int n_kv, int d_h, bool bf16, const
 size_t select_ws_bytes(int batch, int n_kv, int s_max, int n_keep, bool shared);
 hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
                          int k, int n_keep, bool shared, int32_t *idx, int32_t *count,
-                         const int32_t *unit_mask, void *ws, const DeviceInfo &dev, hipStream_t stream);
+                         const int32_t *unit_mask, const int32_t *k_per_unit, void *ws,
+                         const DeviceInfo &dev, hipStream_t stream);
 
 // ---- score --------------------------------------------------------------------------
 struct ScorePlan {

@@ -77,7 +77,16 @@ struct SelArgs {
     int32_t *idx;             // [units][cap]
     int32_t *count;           // [units]
     const int32_t *mask;      // [units] or null: units with 0 are skipped by every kernel
+    const int32_t *kpu;       // [units] or null: the unit's budget, clamped to [0, k]
 };
+
+// The unit's budget: its own entry of kpu (clamped to [0, k]) or k.
+__device__ __forceinline__ int unit_budget(const SelArgs &a, int u)
+{
+    if (!a.kpu) return a.k;
+    const int v = a.kpu[u];
+    return v < 0 ? 0 : (v > a.k ? a.k : v);
+}
 
 // Histogram increment with leader aggregation: the lanes whose bin equals the first
 // active lane's bin add their count with one atomic (neighbouring tokens often share
@@ -189,7 +198,7 @@ __device__ __forceinline__ bool chunk_valid(const ChunkKeys &ck, int q)
 // The work-group's unit and chunk; false when the chunk has nothing to histogram.
 __device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t0, int &t1)
 {
-    us = unit_shape(a.seq_lens, (int)blockIdx.y / a.H, a.s_max, a.k, a.n_keep);
+    us = unit_shape(a.seq_lens, (int)blockIdx.y / a.H, a.s_max, unit_budget(a, blockIdx.y), a.n_keep);
     t0 = (int)blockIdx.x * kChunk;
     t1 = min(us.C, t0 + kChunk);
     if (a.mask && !a.mask[blockIdx.y]) return false;
@@ -317,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
     if (a.mask && !a.mask[u]) return;
-    const UnitShape us = unit_shape(a.seq_lens, u / a.H, a.s_max, a.k, a.n_keep);
+    const UnitShape us = unit_shape(a.seq_lens, u / a.H, a.s_max, unit_budget(a, u), a.n_keep);
     int32_t *out = a.idx + (size_t)u * a.cap;
     if (j == 0) {
         // the always-kept trailing tokens, the -1 padding and the count
@@ -500,7 +509,8 @@ size_t select_ws_bytes(int batch, int n_kv, int s_max, int n_keep, bool shared)
 
 hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
                          int k, int n_keep, bool shared, int32_t *idx, int32_t *count,
-                         const int32_t *unit_mask, void *ws, const DeviceInfo &dev, hipStream_t stream)
+                         const int32_t *unit_mask, const int32_t *k_per_unit, void *ws, const DeviceInfo &dev,
+                         hipStream_t stream)
 {
     (void)dev;
     const SelLayout L = sel_layout(batch, n_kv, s_max, n_keep, shared);
@@ -531,6 +541,7 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
     a.idx = idx;
     a.count = count;
     a.mask = shared ? nullptr : unit_mask;
+    a.kpu = k_per_unit;
 
     const dim3 grid(L.n_chunks, units);
     hipLaunchKernelGGL(sel_level1_kernel, grid, dim3(kThreads), 0, stream, a);

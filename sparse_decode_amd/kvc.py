@@ -63,7 +63,7 @@ def lib():
                 "kvc_score_window_workspace": (Z, [D, I, I]),
                 "kvc_score_window": (I, [D, P, P, I, I, I, I, F, P, P, I, P, Z, P]),
                 "kvc_select_topk_workspace": (Z, [D, I, I, I]),
-                "kvc_select_topk": (I, [D, P, I, I, I, P, P, P, Z, P]),
+                "kvc_select_topk": (I, [D, P, I, I, I, P, P, P, P, Z, P]),
                 "kvc_gather_compact": (I, [I, I, I, I, P, P, P, P, P, I, I, P, P, P, P, P]),
                 "kvc_decode_attn_workspace": (Z, [D, I]),
                 "kvc_decode_attn": (I, [D, P, P, P, P, I, F, P, P, P, Z, P]),
@@ -122,14 +122,15 @@ def _seq_lens(seq_lens, device):
     return torch.as_tensor(seq_lens, dtype=torch.int32).to(device)
 
 
-def _mask(unit_mask, shape, device):
+def _mask(unit_mask, shape, device, name="unit_mask"):
+    """A per-unit int32 device array (unit mask or budgets) of the given shape, or None."""
     if unit_mask is None:
         return None
     if not (isinstance(unit_mask, torch.Tensor) and unit_mask.is_cuda and unit_mask.dtype == torch.int32
             and unit_mask.is_contiguous()):
-        raise ValueError("unit_mask must be a contiguous int32 device tensor")
+        raise ValueError("%s must be a contiguous int32 device tensor" % name)
     if tuple(unit_mask.shape) != tuple(shape):
-        raise ValueError("unit_mask must have shape %s" % (tuple(shape),))
+        raise ValueError("%s must have shape %s" % (name, tuple(shape)))
     return unit_mask
 
 
@@ -181,9 +182,10 @@ def select_topk_workspace(dims: Dims, k: int, n_keep: int, flags: int = 0) -> in
 
 
 def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=None, count=None, ws=None,
-                unit_mask=None, stream=None):
+                unit_mask=None, k_per_unit=None, stream=None):
     """kvc_select_topk: scores [B][n_kv][s_max] fp32 -> (idx [B][H][k+n_keep], count [B][H]) int32.
-    With unit_mask ([B][n_kv] int32), units whose entry is 0 are skipped."""
+    With unit_mask ([B][n_kv] int32), units whose entry is 0 are skipped; with k_per_unit
+    ([B][H] int32 device tensor), unit u takes min(k_per_unit[u], k) candidates."""
     _dev(scores, "scores")
     if scores.dtype != torch.float32:
         raise TypeError("scores must be float32")
@@ -201,9 +203,10 @@ def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=Non
     need = select_topk_workspace(dims, k, n_keep, flags)
     if ws is None and need:
         ws = torch.zeros(need, dtype=torch.uint8, device=scores.device)
-    st = lib().kvc_select_topk(ctypes.byref(dims), _ptr(scores), int(k), int(n_keep), flags, _ptr(idx),
-                               _ptr(count), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                               _stream(stream))
+    kpu = _mask(k_per_unit, (B, H), scores.device, "k_per_unit")
+    st = lib().kvc_select_topk(ctypes.byref(dims), _ptr(scores), int(k), int(n_keep), flags, _ptr(kpu),
+                               _ptr(idx), _ptr(count), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "kvc_select_topk")
     return idx, count
 

@@ -52,9 +52,9 @@ class LayerPath:
                                 n_keep=wl.n_keep, pool=wl.pool, raw=self.raw, pooled=self.pooled,
                                 ws=self.ws_score, unit_mask=unit_mask)
 
-    def select(self, seq_lens=None, unit_mask=None):
+    def select(self, seq_lens=None, unit_mask=None, k_per_unit=None):
         return kvc.select_topk(self.pooled, self.k, self.wl.n_keep, seq_lens=seq_lens, idx=self.idx,
-                               count=self.count, ws=self.ws_select, unit_mask=unit_mask)
+                               count=self.count, ws=self.ws_select, unit_mask=unit_mask, k_per_unit=k_per_unit)
 
     def gather(self, k, v, src_pos=None, unit_mask=None):
         return kvc.gather_compact(k, self.idx, self.count, src1=v, src_pos=src_pos, dst0=self.kc, dst1=self.vc,

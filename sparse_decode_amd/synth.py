@@ -107,6 +107,16 @@ def budget_from_rate(rate: float, s: int) -> int:
     return int(math.ceil(rate * s - 1e-9))
 
 
+def pyramid_budgets(k: int, layers: int, beta: float = 0.5) -> list[int]:
+    """Per-layer budgets that fall linearly from (1 + beta) k at the first layer to
+    (1 - beta) k at the last, rounded, so that their mean is k (a PyramidKV-style
+    schedule: the Tutorial, "Compresser un cache existant", gives layers different
+    budgets; the shape of the schedule is this reading's)."""
+    if layers == 1:
+        return [k]
+    return [int(round(k * (1.0 + beta * (1.0 - 2.0 * l / (layers - 1))))) for l in range(layers)]
+
+
 def seed_for(cfg_id: int, layer: int, stream: int, step: int = 0) -> int:
     return ((cfg_id * 1000 + layer) * 1000 + step) * 10 + stream
 

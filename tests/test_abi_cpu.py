@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvc.lib().kvc_abi_version() == 2
+    assert kvc.lib().kvc_abi_version() == 3
     seen = set()
     for s in range(5):
         txt = kvc.status_str(s)
@@ -101,7 +101,7 @@ def test_workspace_queries():
 
 def _select(dims, k=64, n_keep=16, flags=0, scores=BAD, idx=BAD, count=BAD, ws=None, ws_bytes=0):
     return kvc.lib().kvc_select_topk(ctypes.byref(dims) if dims is not None else None, scores, k, n_keep, flags,
-                                     idx, count, ws, ws_bytes, None)
+                                     None, idx, count, ws, ws_bytes, None)
 
 
 def test_select_rejects_invalid_arguments():

@@ -310,3 +310,20 @@ def test_score_then_select_matches_oracle_rule():
     idx, cnt = kvc.select_topk(pooled, 256, 32, seq_lens=sl)
     ri, rc = oracle.select_topk(rpooled, 256, 32, seq_lens=sl)
     check_selection(idx, cnt, ri, rc, rpooled, sl, 256, 32)
+
+
+def test_select_per_unit_budgets():
+    # budgets that differ per unit (Tutorial "Compresser un cache existant": PyramidKV),
+    # clamped to [0, k]; each unit matches the oracle with its own budget
+    _say("select per-unit budgets")
+    rng = np.random.default_rng(77)
+    B, H, s_max, k, n_keep = 3, 8, 20000, 1500, 32
+    sc = rng.random((B, H, s_max)).astype(np.float32) ** 3
+    sc[1, 2] = (rng.integers(0, 40, s_max) / 39.0).astype(np.float32)       # exact ties
+    sl = np.array([s_max, 12345, 900], np.int32)
+    ku = rng.integers(0, k + 1, (B, H)).astype(np.int32)
+    ku[0, 0], ku[0, 1], ku[2, 3] = 0, k + 500, -4                              # none, clamped to k, clamped to 0
+    idx, cnt = kvc.select_topk(torch.from_numpy(sc).to(DEV), k, n_keep, seq_lens=sl,
+                               k_per_unit=torch.from_numpy(ku).to(DEV))
+    ri, rc = oracle.select_topk(sc, k, n_keep, seq_lens=sl, k_per_unit=ku)
+    assert np.array_equal(host(idx), ri) and np.array_equal(host(cnt), rc)
