@@ -11,6 +11,7 @@ from .ref import (  # noqa: F401
     gather,
     query_similarity,
     score_window,
+    select_core,
     select_topk,
     set_threads,
     speculative_step,

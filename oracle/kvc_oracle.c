@@ -339,3 +339,52 @@ KVO_API void kvo_query_similarity(int B, int n_h, int n_kv, int d_h, const float
         }
     }
 }
+
+/*
+ * Role-based retention (CASK, "Core" and "Scratch" tokens): core tokens are always
+ * kept; the budget k applies to the scratch tokens only.  The n_keep trailing tokens
+ * stay kept as in kvo_select_topk.
+ *
+ * scores [B][H][s_max] float; core [B][s_max] uint8, nonzero = core token (a role of
+ * the token, shared by every head of the sequence).
+ * With C = max(0, S_b - n_keep), Core = {t < C : core[b][t]}, Scratch = [0, C) \ Core:
+ *   k_eff = min(k, |Scratch|); Sel = the first k_eff scratch tokens in the order
+ *   (score desc, index asc); idx = sort_asc(Sel u Core) ++ [C, S_b);
+ *   count = k_eff + |Core| + (S_b - C); idx rows have width cap, -1 past count
+ *   (cap >= k + |Core| + n_keep is the caller's: the first cap entries are written).
+ */
+KVO_API void kvo_select_core(int B, int H, int s_max, const int32_t *seq_lens, const float *scores,
+                             const uint8_t *core, int k, int n_keep, int cap, int32_t *idx, int32_t *count)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < H; ++h) {
+            const int S = seq_len_of(seq_lens, b, s_max);
+            const int C = S - n_keep > 0 ? S - n_keep : 0;
+            kvo_item *items = (kvo_item *)malloc(((size_t)C + 1) * sizeof(kvo_item));
+            int32_t *keep = (int32_t *)malloc(((size_t)S + 1) * sizeof(int32_t));
+            int n_scratch = 0, n_keep_list = 0;
+            for (int t = 0; t < C; ++t) {
+                if (core[(size_t)b * s_max + t]) {
+                    keep[n_keep_list++] = t;            /* core: always kept */
+                } else {
+                    items[n_scratch].key = scores[((size_t)b * H + h) * s_max + t];
+                    items[n_scratch].t = t;
+                    ++n_scratch;
+                }
+            }
+            const int k_eff = k < n_scratch ? k : n_scratch;
+            qsort(items, (size_t)n_scratch, sizeof(kvo_item), by_score_desc_index_asc);
+            for (int j = 0; j < k_eff; ++j) keep[n_keep_list++] = items[j].t;
+            qsort(keep, (size_t)n_keep_list, sizeof(int32_t), by_int_asc);
+            for (int t = C; t < S; ++t) keep[n_keep_list++] = t;
+            int32_t *out = idx + ((size_t)b * H + h) * cap;
+            const int n = n_keep_list < cap ? n_keep_list : cap;
+            for (int j = 0; j < n; ++j) out[j] = keep[j];
+            for (int j = n; j < cap; ++j) out[j] = -1;
+            count[(size_t)b * H + h] = n_keep_list;
+            free(items);
+            free(keep);
+        }
+    }
+}

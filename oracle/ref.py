@@ -55,6 +55,8 @@ def _load():
             lib.kvo_gather.argtypes = [I, I, I, I, P, P, P, P, I, P, P]
             lib.kvo_decode.restype = None
             lib.kvo_decode.argtypes = [I, I, I, I, P, P, P, P, I, ctypes.c_double, P, P]
+            lib.kvo_select_core.restype = None
+            lib.kvo_select_core.argtypes = [I, I, I, P, P, P, I, I, I, P, P]
             lib.kvo_query_similarity.restype = None
             lib.kvo_query_similarity.argtypes = [I, I, I, I, P, P, ctypes.c_double, P, P]
             _lib = lib
@@ -251,3 +253,24 @@ def speculative_step(q_cur, q_prev, k, v, prev_sel, *, seq_lens, k_budget, n_kee
     out, lse = decode(q_cur, kc, vc, use_cnt, scale=scale)
     return dict(out=out, lse=lse, refresh=ref, cos=cos, idx=use_idx, count=use_cnt,
                 next_sel=(sel_idx, sel_cnt), pooled=pooled)
+
+
+def select_core(scores, core, k, n_keep, *, seq_lens=None, cap=None):
+    """CASK role-based retention: core tokens always kept, the budget k over the
+    scratch tokens only (score desc, index asc), the n_keep trailing tokens kept.
+
+    scores [B][H][s_max] float32, core [B][s_max] (nonzero = core).  Returns
+    (idx int32 [B][H][cap], count int32 [B][H]); cap defaults to k + s_max.
+    """
+    scores = _f32(scores)
+    B, H, s_max = scores.shape
+    core = np.ascontiguousarray(np.asarray(core) != 0, dtype=np.uint8)
+    assert core.shape == (B, s_max)
+    if cap is None:
+        cap = k + s_max
+    idx = np.empty((B, H, cap), np.int32)
+    count = np.empty((B, H), np.int32)
+    sl = _i32(seq_lens)
+    _load().kvo_select_core(B, H, s_max, _ptr(sl), _ptr(scores), _ptr(core), int(k), int(n_keep), int(cap),
+                            _ptr(idx), _ptr(count))
+    return idx, count

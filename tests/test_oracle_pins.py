@@ -554,3 +554,41 @@ def test_select_per_unit_budgets_bruteforce():
     u_idx, u_cnt = oracle.select_topk(sc, 4, n_keep, seq_lens=sl, k_per_unit=np.full((B, H), 4, np.int32))
     s_idx, s_cnt = oracle.select_topk(sc, 4, n_keep, seq_lens=sl)
     assert np.array_equal(u_idx, s_idx) and np.array_equal(u_cnt, s_cnt)
+
+
+# ----------------------------------------------------------------------------------
+# Role-based retention: core tokens always kept, the budget over scratch (CASK)
+# ----------------------------------------------------------------------------------
+def test_select_core_bruteforce_and_special_cases():
+    rng = np.random.default_rng(51)
+    B, H, S, n_keep = 2, 2, 12, 2
+    sc = (rng.integers(0, 5, (B, H, S)) / 4.0).astype(np.float32)       # exact ties
+    core = (rng.random((B, S)) < 0.3).astype(np.uint8)
+    core[0, S - 1] = 1                                                    # a core token inside the window
+    sl = np.array([S, 9], np.int32)
+    for k in (0, 2, 4, 20):
+        idx, cnt = oracle.select_core(sc, core, k, n_keep, seq_lens=sl)
+        for b in range(B):
+            S_b = int(sl[b])
+            C = S_b - n_keep
+            cores = [t for t in range(C) if core[b, t]]
+            scratch = [t for t in range(C) if not core[b, t]]
+            for h in range(H):
+                k_eff = min(k, len(scratch))
+                best = None
+                for sub in itertools.combinations(scratch, k_eff):
+                    key = sorted((-float(sc[b, h, t]), t) for t in sub)
+                    if best is None or key < best[0]:
+                        best = (key, sub)
+                want = sorted(set(best[1]) | set(cores)) + list(range(C, S_b))
+                n = int(cnt[b, h])
+                assert n == len(want) and idx[b, h, :n].tolist() == want, (k, b, h)
+                assert np.all(idx[b, h, n:] == -1)
+    # no core token: the plain selection; every token core: everything kept
+    none = np.zeros((B, S), np.uint8)
+    c_idx, c_cnt = oracle.select_core(sc, none, 3, n_keep, seq_lens=sl, cap=3 + n_keep)
+    p_idx, p_cnt = oracle.select_topk(sc, 3, n_keep, seq_lens=sl)
+    assert np.array_equal(c_idx, p_idx) and np.array_equal(c_cnt, p_cnt)
+    a_idx, a_cnt = oracle.select_core(sc, np.ones((B, S), np.uint8), 3, n_keep, seq_lens=sl)
+    for b in range(B):
+        assert a_cnt[0 if b == 0 else 1, 0] == sl[b] and a_idx[b, 0, :sl[b]].tolist() == list(range(sl[b]))
