@@ -307,6 +307,8 @@ def main():
         print("[bench] per-layer budgets", file=sys.stderr, flush=True)
         del g_step, g_layer_step, g_fold, g_call
         res["pyramid_budgets"] = measure_pyramid(wl, L, B, QW, K, V, QD, sl_all, dev, args.steps)
+        print("[bench] role-based retention", file=sys.stderr, flush=True)
+        res["core_retention"] = measure_core(wl, fold, sl_all, us["select"], dev, args.steps)
         print("[bench] speculative retrieval on ragged_b16", file=sys.stderr, flush=True)
         res["speculative_retrieval"] = measure_retrieval(dev, 64, 5)
     print(json.dumps(res), flush=True)
@@ -314,6 +316,53 @@ def main():
 
 RETRIEVAL_TAU = 0.85
 PYRAMID_BETA = 0.5
+CORE_BLOCK, CORE_FRAC = 64, 0.05
+
+
+def measure_core(wl, fold, sl_all, select_us, dev, steps):
+    """Role-based retention (CASK core/scratch) over every layer in one call: the pooled
+    scores of the folded step, a seeded role mask (5 % of the candidates, in 64-token
+    blocks, are core), budget k over the scratch tokens; against the plain selection."""
+    import torch
+
+    from sparse_decode_amd import kvc
+    LB, nkv, S = fold.pooled.shape
+    rng = np.random.Generator(np.random.PCG64([wl.cfg_id, 0x636f7265]))
+    nblk = (S - wl.n_keep) // CORE_BLOCK
+    core = np.zeros((LB, S), np.uint8)
+    for r in range(LB):
+        for blk in rng.choice(nblk, int(round(CORE_FRAC * nblk)), replace=False):
+            core[r, blk * CORE_BLOCK:(blk + 1) * CORE_BLOCK] = 1
+    core_dev = torch.from_numpy(core).to(dev)
+    core_cap = int(core.sum(axis=1).max())
+    cap = wl.k + core_cap + wl.n_keep
+    idx = torch.empty((LB, nkv, cap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((LB, nkv), dtype=torch.int32, device=dev)
+    dims = kvc.make_dims(LB, S, nkv, nkv, 128, kvc.KVC_F32)
+    ws = torch.zeros(kvc.select_core_workspace(dims, wl.n_keep), dtype=torch.uint8, device=dev)
+
+    def call():
+        kvc.select_core(fold.pooled, core_dev, wl.k, core_cap, wl.n_keep, seq_lens=sl_all, idx=idx, count=cnt,
+                        ws=ws)
+
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / steps / (LB // wl.batch)
+    del g
+    return {"core_frac": CORE_FRAC, "core_block": CORE_BLOCK, "core_tokens_per_seq": int(core.sum(axis=1).mean()),
+            "k_scratch": wl.k, "mean_kept": round(float(cnt.float().mean()), 1),
+            "us_per_layer": round(us, 3), "plain_select_us_per_layer": round(select_us, 3)}
 
 
 def measure_pyramid(wl, L, B, QW, K, V, QD, sl_all, dev, steps):

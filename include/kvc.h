@@ -9,6 +9,8 @@
  *                       heads of each GQA group, then max-pooled in 1-D
  *   kvc_select_topk     per-KV-head top-k under a retention budget, plus the
  *                       trailing window, lower index first on equal scores
+ *   kvc_select_core     the same with role-based retention: core tokens always
+ *                       kept, the budget over the scratch tokens (CASK)
  *   kvc_gather_compact  copy of the kept rows into a compacted cache that keeps
  *                       the original positions
  *   kvc_decode_attn     GQA decode attention of one query per head over the
@@ -186,6 +188,34 @@ kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void 
 size_t kvc_select_topk_workspace(const kvc_dims *dims, int32_t k, int32_t n_keep, int32_t flags);
 kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores, int32_t k, int32_t n_keep,
                            int32_t flags, const int32_t *k_per_unit, int32_t *idx, int32_t *count,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kvc_select_core -- role-based retention (CASK: "Core" tokens, which carry the
+ * reasoning state, are always kept; "Scratch" tokens are the target of compression):
+ * the budget k applies to the scratch tokens only.
+ *
+ * For each unit (b, g), with C = max(0, S_b - n_keep), Core = {t < C : core[b][t] != 0},
+ * Scratch = [0, C) minus Core:
+ *   k_eff = min(k, |Scratch|); Sel = the first k_eff scratch tokens in the order
+ *   (score descending, index ascending);
+ *   idx = ascending(Sel u Core), then C, C+1, ..., S_b - 1; -1 padded
+ *   count = k_eff + |Core| + (S_b - C)
+ * |Core| <= core_cap is the caller's contract; a unit with more core candidates keeps
+ * the k + core_cap lowest-indexed of them and no scratch token.
+ *
+ * scores  [B][n_kv][s_max] float, finite (the pooled output of kvc_score_window)
+ * core    [B][s_max] uint8 role of each token, shared by the heads of a sequence
+ * k, core_cap, n_keep >= 0, k + core_cap + n_keep >= 1
+ * idx     [B][n_kv][k + core_cap + n_keep] int32; count [B][n_kv] int32
+ * dims->unit_mask is honoured as in kvc_select_topk
+ * ws      at least kvc_select_core_workspace(dims, n_keep) bytes, 16-byte aligned,
+ *         zero-filled before first use; its first part is a kvc_select_topk workspace
+ *         (same reuse rule: calls with the same batch and n_kv), then scratch
+ */
+size_t kvc_select_core_workspace(const kvc_dims *dims, int32_t n_keep);
+kvc_status kvc_select_core(const kvc_dims *dims, const float *scores, const uint8_t *core, int32_t k,
+                           int32_t core_cap, int32_t n_keep, int32_t *idx, int32_t *count,
                            void *ws, size_t ws_bytes, void *stream);
 
 /*

@@ -166,6 +166,31 @@ KVC_EXPORT kvc_status kvc_select_topk(const kvc_dims *dims, const float *scores,
     return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
+KVC_EXPORT size_t kvc_select_core_workspace(const kvc_dims *dims, int32_t n_keep)
+{
+    if (!dims || dims->batch < 1 || dims->s_max < 1 || dims->n_kv < 1 || n_keep < 0) return 0;
+    if ((long)dims->batch * dims->n_kv > kMaxUnits) return 0;
+    return kvc::select_core_ws_bytes(dims->batch, dims->n_kv, dims->s_max, n_keep);
+}
+
+KVC_EXPORT kvc_status kvc_select_core(const kvc_dims *dims, const float *scores, const uint8_t *core, int32_t k,
+                                      int32_t core_cap, int32_t n_keep, int32_t *idx, int32_t *count, void *ws,
+                                      size_t ws_bytes, void *stream)
+{
+    if (k < 0 || core_cap < 0 || (long)k + core_cap > (1L << 29)) return KVC_ERR_INVALID_ARG;
+    kvc_status st = select_args(dims, k + core_cap, n_keep, 0);
+    if (st != KVC_OK) return st;
+    if (!scores || !core || !idx || !count) return KVC_ERR_INVALID_ARG;
+    const size_t need = kvc::select_core_ws_bytes(dims->batch, dims->n_kv, dims->s_max, n_keep);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return KVC_ERR_WORKSPACE;
+    kvc::DeviceInfo dev;
+    if (kvc::device_info(&dev) != hipSuccess) return KVC_ERR_HIP;
+    hipError_t e = kvc::launch_select_core(dims->batch, dims->n_kv, dims->s_max, dims->seq_lens, scores, core, k,
+                                           core_cap, n_keep, idx, count, dims->unit_mask, ws, dev,
+                                           (hipStream_t)stream);
+    return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
 // --------------------------------------------------------------------------------- gather
 
 KVC_EXPORT kvc_status kvc_gather_compact(int32_t batch, int32_t heads, int32_t s_max, int32_t row_bytes,

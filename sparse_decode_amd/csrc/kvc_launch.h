@@ -44,6 +44,12 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
                          const int32_t *unit_mask, const int32_t *k_per_unit, void *ws,
                          const DeviceInfo &dev, hipStream_t stream);
 
+// role-based retention (core tokens always kept, the budget over the others)
+size_t select_core_ws_bytes(int batch, int n_kv, int s_max, int n_keep);
+hipError_t launch_select_core(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
+                              const uint8_t *core, int k, int core_cap, int n_keep, int32_t *idx, int32_t *count,
+                              const int32_t *unit_mask, void *ws, const DeviceInfo &dev, hipStream_t stream);
+
 // ---- score --------------------------------------------------------------------------
 struct ScorePlan {
     bool mfma = false;

@@ -465,6 +465,56 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const float *__restrict__
     out[(size_t)b * s_max + t] = s;
 }
 
+// ---------------------------------------------------------------- role-based retention
+// CASK's core tokens are always kept and the budget applies to the scratch tokens: a
+// core candidate's score becomes +inf (the largest key), and the unit's budget grows
+// by its number of core candidates, so the ordinary selection of k + |core| keys takes
+// every core token plus the best k scratch tokens.  One work-group per (2048-token
+// chunk, unit) writes the masked scores and counts the chunk's core candidates.
+__global__ __launch_bounds__(kThreads) void core_scores_kernel(const float *__restrict__ scores,
+                                                               const uint8_t *__restrict__ core,
+                                                               const int32_t *__restrict__ seq_lens, int H,
+                                                               int s_max, int n_keep, int n_chunks,
+                                                               const int32_t *__restrict__ mask,
+                                                               float *__restrict__ masked,
+                                                               int32_t *__restrict__ chunk_core)
+{
+    __shared__ int wave_n[kWaves];
+    const int u = blockIdx.y;
+    if (mask && !mask[u]) return;
+    const int b = u / H;
+    const int S = clamp_len(seq_lens, b, s_max);
+    const int C = S - n_keep > 0 ? S - n_keep : 0;
+    const int t0 = blockIdx.x * kChunk;
+    int n = 0;
+    for (int t = t0 + threadIdx.x; t < min(t0 + kChunk, s_max); t += kThreads) {
+        const bool c = t < C && core[(size_t)b * s_max + t] != 0;
+        n += c;
+        masked[(size_t)u * s_max + t] = c ? INFINITY : scores[(size_t)u * s_max + t];
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) n += __shfl_xor(n, o, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) wave_n[threadIdx.x >> 6] = n;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int tot = 0;
+        for (int w = 0; w < kWaves; ++w) tot += wave_n[w];
+        chunk_core[(size_t)u * n_chunks + blockIdx.x] = tot;
+    }
+}
+
+// budget[u] = k + min(|core candidates of u|, core_cap)
+__global__ __launch_bounds__(256) void core_budget_kernel(const int32_t *__restrict__ chunk_core, int units,
+                                                          int n_chunks, int k, int core_cap,
+                                                          int32_t *__restrict__ budget)
+{
+    const int u = blockIdx.x * 256 + threadIdx.x;
+    if (u >= units) return;
+    int n = 0;
+    for (int j = 0; j < n_chunks; ++j) n += chunk_core[(size_t)u * n_chunks + j];
+    budget[u] = k + (n < core_cap ? n : core_cap);
+}
+
 struct SelLayout {
     int n_chunks;
     size_t sum_off, hist_off, done_off, above_off, sfx_off, bytes;
@@ -505,6 +555,53 @@ static_assert(kHistInts % 4 == 0 && kSfx % 4 == 0 && kB1 % 4 == 0, "16-byte alig
 size_t select_ws_bytes(int batch, int n_kv, int s_max, int n_keep, bool shared)
 {
     return sel_layout(batch, n_kv, s_max, n_keep, shared).bytes;
+}
+
+// [selection workspace][masked scores][per-chunk core counts][budgets]
+struct CoreLayout {
+    size_t masked_off, chunk_off, budget_off, bytes;
+    int n_chunks;
+};
+
+static CoreLayout core_layout(int batch, int n_kv, int s_max, int n_keep)
+{
+    CoreLayout L;
+    const size_t units = (size_t)batch * n_kv;
+    L.n_chunks = (s_max + kChunk - 1) / kChunk;
+    size_t off = align256(select_ws_bytes(batch, n_kv, s_max, n_keep, false));
+    L.masked_off = off;
+    off += align256(units * s_max * sizeof(float));
+    L.chunk_off = off;
+    off += align256(units * L.n_chunks * sizeof(int32_t));
+    L.budget_off = off;
+    off += align256(units * sizeof(int32_t));
+    L.bytes = off;
+    return L;
+}
+
+size_t select_core_ws_bytes(int batch, int n_kv, int s_max, int n_keep)
+{
+    return core_layout(batch, n_kv, s_max, n_keep).bytes;
+}
+
+hipError_t launch_select_core(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,
+                              const uint8_t *core, int k, int core_cap, int n_keep, int32_t *idx, int32_t *count,
+                              const int32_t *unit_mask, void *ws, const DeviceInfo &dev, hipStream_t stream)
+{
+    const CoreLayout L = core_layout(batch, n_kv, s_max, n_keep);
+    char *w = (char *)ws;
+    float *masked = (float *)(w + L.masked_off);
+    int32_t *chunk_core = (int32_t *)(w + L.chunk_off);
+    int32_t *budget = (int32_t *)(w + L.budget_off);
+    const int units = batch * n_kv;
+    hipLaunchKernelGGL(core_scores_kernel, dim3(L.n_chunks, units), dim3(kThreads), 0, stream, scores, core,
+                       seq_lens, n_kv, s_max, n_keep, L.n_chunks, unit_mask, masked, chunk_core);
+    hipLaunchKernelGGL(core_budget_kernel, dim3((units + 255) / 256), dim3(256), 0, stream, chunk_core, units,
+                       L.n_chunks, k, core_cap, budget);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_select(batch, n_kv, s_max, seq_lens, masked, k + core_cap, n_keep, false, idx, count, unit_mask,
+                         budget, ws, dev, stream);
 }
 
 hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens, const float *scores,

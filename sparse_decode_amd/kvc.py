@@ -25,6 +25,7 @@ EXPORTED = (
     "kvc_abi_version", "kvc_status_str",
     "kvc_score_window_workspace", "kvc_score_window",
     "kvc_select_topk_workspace", "kvc_select_topk",
+    "kvc_select_core_workspace", "kvc_select_core",
     "kvc_gather_compact",
     "kvc_decode_attn_workspace", "kvc_decode_attn",
     "kvc_query_similarity",
@@ -64,6 +65,8 @@ def lib():
                 "kvc_score_window": (I, [D, P, P, I, I, I, I, F, P, P, I, P, Z, P]),
                 "kvc_select_topk_workspace": (Z, [D, I, I, I]),
                 "kvc_select_topk": (I, [D, P, I, I, I, P, P, P, P, Z, P]),
+                "kvc_select_core_workspace": (Z, [D, I]),
+                "kvc_select_core": (I, [D, P, P, I, I, I, P, P, P, Z, P]),
                 "kvc_gather_compact": (I, [I, I, I, I, P, P, P, P, P, I, I, P, P, P, P, P]),
                 "kvc_decode_attn_workspace": (Z, [D, I]),
                 "kvc_decode_attn": (I, [D, P, P, P, P, I, F, P, P, P, Z, P]),
@@ -208,6 +211,38 @@ def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=Non
                                _ptr(idx), _ptr(count), _ptr(ws),
                                0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "kvc_select_topk")
+    return idx, count
+
+
+def select_core_workspace(dims: Dims, n_keep: int) -> int:
+    return int(lib().kvc_select_core_workspace(ctypes.byref(dims), int(n_keep)))
+
+
+def select_core(scores, core, k, core_cap, n_keep, *, seq_lens=None, idx=None, count=None, ws=None,
+                unit_mask=None, stream=None):
+    """kvc_select_core: scores [B][n_kv][s_max] fp32, core [B][s_max] uint8 ->
+    (idx [B][n_kv][k+core_cap+n_keep], count [B][n_kv]) int32."""
+    _dev(scores, "scores")
+    _dev(core, "core")
+    if scores.dtype != torch.float32 or core.dtype != torch.uint8:
+        raise TypeError("scores must be float32 and core uint8")
+    B, n_kv, s_max = scores.shape
+    if tuple(core.shape) != (B, s_max):
+        raise ValueError("core must have shape (B, s_max)")
+    sl = _seq_lens(seq_lens, scores.device)
+    um = _mask(unit_mask, (B, n_kv), scores.device)
+    dims = make_dims(B, s_max, n_kv, n_kv, 128, KVC_F32, sl, um)
+    cap = k + core_cap + n_keep
+    if idx is None:
+        idx = torch.empty((B, n_kv, cap), dtype=torch.int32, device=scores.device)
+    if count is None:
+        count = torch.empty((B, n_kv), dtype=torch.int32, device=scores.device)
+    need = select_core_workspace(dims, n_keep)
+    if ws is None:
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=scores.device)
+    st = lib().kvc_select_core(ctypes.byref(dims), _ptr(scores), _ptr(core), int(k), int(core_cap), int(n_keep),
+                               _ptr(idx), _ptr(count), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kvc_select_core")
     return idx, count
 
 

@@ -200,3 +200,27 @@ def test_shared_head_selection_takes_no_unit_mask():
     d.unit_mask = BAD
     assert kvc.select_topk_workspace(d, 64, 16, kvc.KVC_SELECT_SHARED_HEADS) == 0
     assert _select(d, flags=kvc.KVC_SELECT_SHARED_HEADS) == kvc.KVC_ERR_INVALID_ARG
+
+
+def _select_core(dims, k=64, core_cap=32, n_keep=16, scores=BAD, core=BAD, idx=BAD, count=BAD, ws=BAD,
+                 ws_bytes=1 << 40):
+    return kvc.lib().kvc_select_core(ctypes.byref(dims) if dims is not None else None, scores, core, k, core_cap,
+                                     n_keep, idx, count, ws, ws_bytes, None)
+
+
+def test_select_core_rejects_invalid_arguments():
+    E, W = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_WORKSPACE
+    assert _select_core(None) == E
+    assert _select_core(_dims(batch=0)) == E
+    assert _select_core(_dims(), k=-1) == E
+    assert _select_core(_dims(), core_cap=-1) == E
+    assert _select_core(_dims(), k=0, core_cap=0, n_keep=0) == E
+    assert _select_core(_dims(), core=None) == E
+    assert _select_core(_dims(), idx=None) == E
+    assert _select_core(_dims(), ws=None) == W
+    need = kvc.select_core_workspace(_dims(), 16)
+    assert need > kvc.select_topk_workspace(_dims(), 64, 16)
+    assert _select_core(_dims(), ws_bytes=need - 1) == W
+    assert kvc.select_core_workspace(_dims(), -1) == 0
+    # valid arguments reach the launch, which fails without a device
+    assert _select_core(_dims(), ws_bytes=need) == kvc.KVC_ERR_HIP

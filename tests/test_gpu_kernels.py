@@ -327,3 +327,44 @@ def test_select_per_unit_budgets():
                                k_per_unit=torch.from_numpy(ku).to(DEV))
     ri, rc = oracle.select_topk(sc, k, n_keep, seq_lens=sl, k_per_unit=ku)
     assert np.array_equal(host(idx), ri) and np.array_equal(host(cnt), rc)
+
+
+@pytest.mark.parametrize("s_max", [3000, 32768])
+def test_select_core_vs_oracle(s_max):
+    # CASK role-based retention: core tokens kept, the budget over the scratch tokens
+    _say("select core", s_max)
+    rng = np.random.default_rng(s_max + 5)
+    B, H, k, core_cap, n_keep = 3, 8, 700, 600, 32
+    sc = (rng.random((B, H, s_max)) ** 2).astype(np.float32)
+    sc[0, 1] = (rng.integers(0, 30, s_max) / 29.0).astype(np.float32)          # exact ties
+    core = (rng.random((B, s_max)) < 0.012).astype(np.uint8)
+    core[2, :] = 0                                                                # no core token
+    sl = np.array([s_max, max(1, s_max // 3), s_max - 7], np.int32)
+    idx, cnt = kvc.select_core(torch.from_numpy(sc).to(DEV), torch.from_numpy(core).to(DEV), k, core_cap, n_keep,
+                               seq_lens=sl)
+    ri, rc = oracle.select_core(sc, core, k, n_keep, seq_lens=sl, cap=k + core_cap + n_keep)
+    n_core = [int(core[b, :max(0, sl[b] - n_keep)].sum()) for b in range(B)]
+    assert max(n_core) <= core_cap
+    assert np.array_equal(host(cnt), rc) and np.array_equal(host(idx), ri)
+    # every core candidate is kept
+    gi = host(idx)
+    for b in range(B):
+        cores = np.nonzero(core[b, :max(0, sl[b] - n_keep)])[0]
+        for h in range(H):
+            assert np.isin(cores, gi[b, h]).all()
+
+
+def test_select_core_over_cap_keeps_lowest_core_tokens():
+    # the documented clamp: more core candidates than core_cap keep the k + core_cap
+    # lowest-indexed core tokens and no scratch token
+    _say("select core over cap")
+    s_max, k, core_cap, n_keep = 4096, 10, 20, 8
+    rng = np.random.default_rng(3)
+    sc = rng.random((1, 2, s_max)).astype(np.float32)
+    core = np.zeros((1, s_max), np.uint8)
+    core[0, 100:200] = 1
+    idx, cnt = kvc.select_core(torch.from_numpy(sc).to(DEV), torch.from_numpy(core).to(DEV), k, core_cap, n_keep)
+    gi, gc = host(idx), host(cnt)
+    want = list(range(100, 100 + k + core_cap)) + list(range(s_max - n_keep, s_max))
+    for h in range(2):
+        assert gc[0, h] == len(want) and gi[0, h].tolist() == want
