@@ -5,9 +5,13 @@ import this package.  It shares no code with the HIP implementation in
 ``sparse_decode_amd`` and never imports it.
 """
 from .ref import (  # noqa: F401
+    block_landmarks,
+    block_retrieval,
+    block_scores,
     build,
     cache_bytes,
     decode,
+    expand_blocks,
     gather,
     query_similarity,
     score_window,

@@ -388,3 +388,89 @@ KVO_API void kvo_select_core(int B, int H, int s_max, const int32_t *seq_lens, c
         }
     }
 }
+
+/*
+ * Landmark-guided block selection (xKV, section 2.3 "Reconstruction Selective": the
+ * tokens most relevant to the current query are found by a block selection guided by
+ * landmarks, as in ShadowKV).  The cache of each KV head is cut into blocks of `block`
+ * consecutive tokens; a block's landmark is the mean of its keys; a block's score is
+ * the group's attention logit for its landmark; the best blocks are kept whole.
+ */
+
+/* landmarks [B][n_kv][n_blk][d_h], n_blk = ceil(s_max / block): the mean of the keys
+ * t < S_b of each block (0 for a block with none), in double, rounded to float. */
+KVO_API void kvo_block_landmarks(int B, int n_kv, int s_max, int d_h, const int32_t *seq_lens,
+                                 const float *k, int block, float *landmarks)
+{
+    const int n_blk = (s_max + block - 1) / block;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < n_kv; ++g) {
+            const int S = seq_len_of(seq_lens, b, s_max);
+            for (int j = 0; j < n_blk; ++j) {
+                float *lm = landmarks + (((size_t)b * n_kv + g) * n_blk + j) * d_h;
+                const int t0 = j * block;
+                const int t1 = t0 + block < S ? t0 + block : S;
+                for (int d = 0; d < d_h; ++d) {
+                    double s = 0.0;
+                    for (int t = t0; t < t1; ++t) s += (double)k[(((size_t)b * n_kv + g) * s_max + t) * d_h + d];
+                    lm[d] = t1 > t0 ? (float)(s / (double)(t1 - t0)) : 0.0f;
+                }
+            }
+        }
+    }
+}
+
+/* scores [B][n_kv][n_blk] = scale * sum over the query heads h of KV head g of
+ * <q[b][h], landmark[b][g][j]> (in double, rounded to float) for the candidate blocks
+ * j < cand[b] = floor(max(0, S_b - n_keep) / block), 0 elsewhere. */
+KVO_API void kvo_block_scores(int B, int n_h, int n_kv, int s_max, int d_h, const int32_t *seq_lens,
+                              const float *q, const float *landmarks, int block, int n_keep, double scale,
+                              float *scores, int32_t *cand)
+{
+    const int r = n_h / n_kv;
+    const int n_blk = (s_max + block - 1) / block;
+    for (int b = 0; b < B; ++b) {
+        const int S = seq_len_of(seq_lens, b, s_max);
+        const int C = S - n_keep > 0 ? S - n_keep : 0;
+        cand[b] = C / block;
+        for (int g = 0; g < n_kv; ++g) {
+            for (int j = 0; j < n_blk; ++j) {
+                double s = 0.0;
+                if (j < cand[b]) {
+                    const float *lm = landmarks + (((size_t)b * n_kv + g) * n_blk + j) * d_h;
+                    for (int h = g * r; h < (g + 1) * r; ++h) {
+                        const float *qh = q + ((size_t)b * n_h + h) * d_h;
+                        for (int d = 0; d < d_h; ++d) s += (double)qh[d] * (double)lm[d];
+                    }
+                }
+                scores[((size_t)b * n_kv + g) * n_blk + j] = (float)(scale * s);
+            }
+        }
+    }
+}
+
+/* Token list of the kept blocks: for unit u, the count_blk[u] selected blocks (their
+ * indices ascending in idx_blk) expand to their `block` tokens each, in order, then the
+ * tail [cand * block, S_b) that is not a candidate block is kept; -1 past count. */
+KVO_API void kvo_expand_blocks(int B, int H, int s_max, const int32_t *seq_lens, int block, int n_keep,
+                               const int32_t *idx_blk, const int32_t *count_blk, int cap_blk,
+                               int32_t *idx, int32_t *count, int cap)
+{
+    for (int b = 0; b < B; ++b) {
+        const int S = seq_len_of(seq_lens, b, s_max);
+        const int C = S - n_keep > 0 ? S - n_keep : 0;
+        const int tail0 = (C / block) * block;
+        for (int h = 0; h < H; ++h) {
+            const size_t u = (size_t)b * H + h;
+            int n = 0;
+            for (int j = 0; j < count_blk[u]; ++j)
+                for (int i = 0; i < block; ++i)
+                    if (n < cap) idx[u * cap + n++] = idx_blk[u * cap_blk + j] * block + i;
+            for (int t = tail0; t < S; ++t)
+                if (n < cap) idx[u * cap + n++] = t;
+            count[u] = n;
+            for (int j = n; j < cap; ++j) idx[u * cap + j] = -1;
+        }
+    }
+}

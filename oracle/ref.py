@@ -55,6 +55,12 @@ def _load():
             lib.kvo_gather.argtypes = [I, I, I, I, P, P, P, P, I, P, P]
             lib.kvo_decode.restype = None
             lib.kvo_decode.argtypes = [I, I, I, I, P, P, P, P, I, ctypes.c_double, P, P]
+            lib.kvo_block_landmarks.restype = None
+            lib.kvo_block_landmarks.argtypes = [I, I, I, I, P, P, I, P]
+            lib.kvo_block_scores.restype = None
+            lib.kvo_block_scores.argtypes = [I, I, I, I, I, P, P, P, I, I, ctypes.c_double, P, P]
+            lib.kvo_expand_blocks.restype = None
+            lib.kvo_expand_blocks.argtypes = [I, I, I, P, I, I, P, P, I, P, P, I]
             lib.kvo_select_core.restype = None
             lib.kvo_select_core.argtypes = [I, I, I, P, P, P, I, I, I, P, P]
             lib.kvo_query_similarity.restype = None
@@ -274,3 +280,60 @@ def select_core(scores, core, k, n_keep, *, seq_lens=None, cap=None):
     _load().kvo_select_core(B, H, s_max, _ptr(sl), _ptr(scores), _ptr(core), int(k), int(n_keep), int(cap),
                             _ptr(idx), _ptr(count))
     return idx, count
+
+
+def block_landmarks(k, block, *, seq_lens=None):
+    """xKV 2.3 / ShadowKV-style landmarks: the mean key of each block of `block`
+    tokens, k [B][n_kv][s_max][d_h] float32 -> [B][n_kv][ceil(s_max/block)][d_h]."""
+    k = _f32(k)
+    B, n_kv, s_max, d_h = k.shape
+    n_blk = (s_max + block - 1) // block
+    lm = np.zeros((B, n_kv, n_blk, d_h), np.float32)
+    _load().kvo_block_landmarks(B, n_kv, s_max, d_h, _ptr(_i32(seq_lens)), _ptr(k), int(block), _ptr(lm))
+    return lm
+
+
+def block_scores(q, landmarks, block, n_keep, s_max, *, seq_lens=None, scale=None):
+    """Group logit of each candidate block's landmark: q [B][n_h][d_h] float32.
+    Returns (scores [B][n_kv][n_blk] float32, cand int32 [B] candidate blocks)."""
+    q = _f32(q)
+    landmarks = _f32(landmarks)
+    B, n_h, d_h = q.shape
+    _, n_kv, n_blk, _ = landmarks.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    sc = np.zeros((B, n_kv, n_blk), np.float32)
+    cand = np.zeros(B, np.int32)
+    _load().kvo_block_scores(B, n_h, n_kv, int(s_max), d_h, _ptr(_i32(seq_lens)), _ptr(q), _ptr(landmarks),
+                             int(block), int(n_keep), float(scale), _ptr(sc), _ptr(cand))
+    return sc, cand
+
+
+def expand_blocks(idx_blk, count_blk, block, n_keep, s_max, cap, *, seq_lens=None):
+    """Token indices of the kept blocks, then the tail after the last candidate block."""
+    idx_blk = _i32(idx_blk)
+    count_blk = _i32(count_blk)
+    B, H, cap_blk = idx_blk.shape
+    idx = np.empty((B, H, cap), np.int32)
+    count = np.empty((B, H), np.int32)
+    _load().kvo_expand_blocks(B, H, int(s_max), _ptr(_i32(seq_lens)), int(block), int(n_keep), _ptr(idx_blk),
+                              _ptr(count_blk), cap_blk, _ptr(idx), _ptr(count), int(cap))
+    return idx, count
+
+
+def block_retrieval(q, k, v, k_blocks, block, n_keep, *, seq_lens=None, scale=None):
+    """One decode step of landmark-guided block selection: landmarks -> block scores ->
+    top k_blocks blocks (score desc, block index asc) -> their tokens plus the tail ->
+    gather -> attention.  Returns a dict with out/lse (float64), idx/count (tokens),
+    block scores and the candidate block counts."""
+    B, n_kv, s_max, d_h = k.shape
+    lm = block_landmarks(k, block, seq_lens=seq_lens)
+    sc, cand = block_scores(q, lm, block, n_keep, s_max, seq_lens=seq_lens, scale=scale)
+    bi, bc = select_topk(sc, k_blocks, 0, seq_lens=cand)
+    cap = k_blocks * block + n_keep + block - 1
+    idx, cnt = expand_blocks(bi, bc, block, n_keep, s_max, cap, seq_lens=seq_lens)
+    kc, _ = gather(k, idx, cnt)
+    vc, _ = gather(v, idx, cnt)
+    out, lse = decode(q, kc, vc, cnt, scale=scale)
+    return dict(out=out, lse=lse, idx=idx, count=cnt, block_scores=sc, cand=cand, landmarks=lm,
+                block_idx=bi, block_count=bc)

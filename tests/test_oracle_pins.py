@@ -592,3 +592,84 @@ def test_select_core_bruteforce_and_special_cases():
     a_idx, a_cnt = oracle.select_core(sc, np.ones((B, S), np.uint8), 3, n_keep, seq_lens=sl)
     for b in range(B):
         assert a_cnt[0 if b == 0 else 1, 0] == sl[b] and a_idx[b, 0, :sl[b]].tolist() == list(range(sl[b]))
+
+
+# ----------------------------------------------------------------------------------
+# Landmark-guided block selection (xKV section 2.3, ShadowKV-style landmarks)
+# ----------------------------------------------------------------------------------
+def test_block_landmarks_closed_forms():
+    B, n_kv, S, d, blk = 2, 2, 37, 4, 8
+    a = np.array([1.0, -2.0, 0.5, 3.0], np.float32)
+    t = np.arange(S, dtype=np.float32)
+    k = np.broadcast_to(t[None, None, :, None] * a, (B, n_kv, S, d)).astype(np.float32).copy()
+    sl = np.array([S, 20], np.int32)
+    lm = oracle.block_landmarks(k, blk, seq_lens=sl)
+    assert lm.shape == (B, n_kv, 5, d)
+    for b in range(B):
+        S_b = int(sl[b])
+        for j in range(5):
+            lo, hi = j * blk, min(j * blk + blk, S_b)
+            want = ((lo + hi - 1) / 2.0) * a if hi > lo else np.zeros(d)   # mean of an arithmetic run
+            assert np.allclose(lm[b, 0, j], want, atol=1e-6), (b, j)
+    # the landmarks, weighted by their block sizes, add up to the sum of the keys
+    rng = np.random.default_rng(61)
+    k2 = rng.standard_normal((1, 1, 45, 8)).astype(np.float32)
+    lm2 = oracle.block_landmarks(k2, 7)
+    sizes = np.array([7] * 6 + [3], np.float64)
+    assert np.allclose((lm2[0, 0].astype(np.float64) * sizes[:, None]).sum(0), k2[0, 0].astype(np.float64).sum(0),
+                       atol=1e-5)
+
+
+def test_block_scores_and_expansion():
+    rng = np.random.default_rng(62)
+    B, n_h, n_kv, S, d, blk, n_keep = 2, 4, 2, 50, 8, 4, 6
+    lm = rng.standard_normal((B, n_kv, (S + blk - 1) // blk, d)).astype(np.float32)
+    q = rng.standard_normal((B, n_h, d)).astype(np.float32)
+    sl = np.array([S, 17], np.int32)
+    sc, cand = oracle.block_scores(q, lm, blk, n_keep, S, seq_lens=sl, scale=0.5)
+    assert cand.tolist() == [(S - n_keep) // blk, (17 - n_keep) // blk]
+    # linear in the queries; identical group queries give r times one head's logit
+    sc2, _ = oracle.block_scores(2.0 * q, lm, blk, n_keep, S, seq_lens=sl, scale=0.5)
+    assert np.allclose(sc2, 2.0 * sc, rtol=1e-6, atol=1e-6)
+    qs = np.repeat(q[:, ::2], 2, axis=1)                          # heads 2g and 2g+1 equal
+    sc3, _ = oracle.block_scores(qs, lm, blk, n_keep, S, seq_lens=sl, scale=0.5)
+    j = 3
+    assert np.isclose(sc3[0, 1, j], 2 * 0.5 * float(np.dot(q[0, 2].astype(np.float64), lm[0, 1, j])), rtol=1e-6)
+    assert np.all(sc[1, :, cand[1]:] == 0)
+    # expansion: blocks 1 and 4 of unit (0, 0), block 0 of unit (1, 1); the tail follows
+    idx_blk = np.full((B, n_kv, 3), -1, np.int32)
+    cnt_blk = np.array([[2, 0], [0, 1]], np.int32)
+    idx_blk[0, 0, :2] = [1, 4]
+    idx_blk[1, 1, :1] = [0]
+    idx, cnt = oracle.expand_blocks(idx_blk, cnt_blk, blk, n_keep, S, 30, seq_lens=sl)
+    tail0 = (S - n_keep) // blk * blk
+    assert idx[0, 0, :cnt[0, 0]].tolist() == [4, 5, 6, 7, 16, 17, 18, 19] + list(range(tail0, S))
+    assert idx[0, 1, :cnt[0, 1]].tolist() == list(range(tail0, S))
+    assert idx[1, 1, :cnt[1, 1]].tolist() == [0, 1, 2, 3] + list(range(8, 17))
+    assert np.all(idx[1, 1, cnt[1, 1]:] == -1)
+
+
+def test_block_retrieval_special_cases():
+    rng = np.random.default_rng(63)
+    B, n_h, n_kv, S, d, n_keep = 1, 4, 2, 40, 16, 4
+    k = rng.standard_normal((B, n_kv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, n_kv, S, d)).astype(np.float32)
+    q = rng.standard_normal((B, n_h, d)).astype(np.float32)
+    # block size 1: the landmark is the key, so the kept tokens are the top k of the
+    # group's logit sum (torch float64 einsum) plus the trailing n_keep
+    res = oracle.block_retrieval(q, k, v, 7, 1, n_keep)
+    logit = torch.einsum("ghd,gtd->gt", torch.from_numpy(q[0]).double().view(n_kv, 2, d),
+                         torch.from_numpy(k[0]).double()) / math.sqrt(d)
+    for g in range(n_kv):
+        order = sorted(range(S - n_keep), key=lambda t: (-float(logit[g, t]), t))[:7]
+        want = sorted(order) + list(range(S - n_keep, S))
+        assert res["idx"][0, g, :res["count"][0, g]].tolist() == want
+    # every block kept: attention over the whole cache (torch scaled_dot_product_attention)
+    full = oracle.block_retrieval(q, k, v, 100, 8, n_keep)
+    assert np.all(full["count"] == S)
+    for h in range(n_h):
+        g = h // 2
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[0, h]).double()[None, None, None],
+                                             torch.from_numpy(k[0, g]).double()[None, None],
+                                             torch.from_numpy(v[0, g]).double()[None, None])
+        assert np.allclose(full["out"][0, h], ref[0, 0, 0].numpy(), atol=1e-12)
