@@ -315,6 +315,7 @@ def main():
 
 
 RETRIEVAL_TAU = 0.85
+BLOCK_TOKENS = 16
 PYRAMID_BETA = 0.5
 CORE_BLOCK, CORE_FRAC = 64, 0.05
 
@@ -426,11 +427,14 @@ def measure_retrieval(dev, steps, reps):
                    attention over the previous step's selection for the other heads
       overlapped   critical on the launch stream and the speculative selection for the
                    next step on a second stream beside it
+      blocks       landmark-guided block selection (xKV 2.3): block scores from the block
+                   landmarks (built once, timed apart), top k/16 blocks of 16 tokens,
+                   their tokens gathered, attention
     """
     import torch
 
     from sparse_decode_amd import synth
-    from sparse_decode_amd.pipeline import LayerPath, SpeculativeRetrieval
+    from sparse_decode_amd.pipeline import BlockRetrieval, LayerPath, SpeculativeRetrieval
     wl = synth.by_name("ragged_b16")
     inp = synth.layer_inputs(wl, 0, device=dev, step=0)
     k, v = inp["k"], inp["v"]
@@ -439,6 +443,14 @@ def measure_retrieval(dev, steps, reps):
     B, nh, d = qs[0].shape
     base = LayerPath(wl, device=dev)
     spec = SpeculativeRetrieval(wl, RETRIEVAL_TAU, device=dev)
+    blk = BlockRetrieval(wl, BLOCK_TOKENS, wl.k // BLOCK_TOKENS, device=dev)
+
+    def blocks():
+        for q in qs:
+            blk.step(q, k, v, sl)
+
+    def landmarks():
+        blk.prepare(k, sl)
 
     def reselect():
         for q in qs:
@@ -495,7 +507,9 @@ def measure_retrieval(dev, steps, reps):
         return g
 
     out = {}
-    for name, fn in (("reselect", reselect), ("critical", critical), ("overlapped", overlapped)):
+    landmarks()
+    for name, fn in (("reselect", reselect), ("critical", critical), ("overlapped", overlapped),
+                     ("blocks", blocks), ("landmarks_once", landmarks)):
         g = graph_of(fn)
         g.replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -505,12 +519,16 @@ def measure_retrieval(dev, steps, reps):
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        out[name] = 1000.0 * e0.elapsed_time(e1) / reps / steps
+        out[name] = 1000.0 * e0.elapsed_time(e1) / reps / (1 if name == "landmarks_once" else steps)
         del g
     return {"workload": wl.name, "steps": steps, "tau": RETRIEVAL_TAU,
             "corrected_kv_head_frac": round(frac, 4),
-            "us_per_step": {n: round(t, 2) for n, t in out.items()},
+            "us_per_step": {n: round(t, 2) for n, t in out.items() if n in ("reselect", "critical", "overlapped")},
             "critical_path_speedup": round(out["reselect"] / out["critical"], 3),
+            "block_selection": {"block": BLOCK_TOKENS, "k_blocks": wl.k // BLOCK_TOKENS,
+                                "us_per_step": round(out["blocks"], 2),
+                                "landmarks_us_once": round(out["landmarks_once"], 2),
+                                "speedup_vs_reselect": round(out["reselect"] / out["blocks"], 3)},
             "step_speedup_overlapped": round(out["reselect"] / out["overlapped"], 3),
             "timing": "HIP graph of all steps per schedule, replayed between HIP events on the launch stream"}
 

@@ -15,6 +15,10 @@
  *                       the original positions
  *   kvc_decode_attn     GQA decode attention of one query per head over the
  *                       compacted cache
+ *   kvc_block_landmarks, kvc_block_scores, kvc_expand_blocks
+ *                       landmark-guided block selection (xKV, ShadowKV-style):
+ *                       block means of K, the group's logit per block, kept blocks
+ *                       back to token indices (the block top-k is kvc_select_topk)
  *   kvc_query_similarity  cosine of the queries of two adjacent decode steps and
  *                       the KV heads whose selection is redone before attention
  *                       (speculative retrieval with fine-grained correction)
@@ -31,6 +35,10 @@
  *              appended after S cached tokens; keep original positions after
  *              eviction) and "Compresser un cache existant" (observation-window
  *              scoring, keep a subset of past keys and values).
+ *   [xKV]      "xKV: Compression de Cache KV Inter-couche par Extraction de Vecteurs
+ *              Singuliers Alignes", section 2.3 (Reconstruction Selective: a sparse
+ *              subset of tokens found by landmark-guided block selection, as in
+ *              ShadowKV; the low-rank reconstruction itself is not part of this path).
  *   [FreeKV]   "FreeKV: Boosting KV Cache Retrieval for Efficient LLM Inference",
  *              technical summary section 2.A (select a subset with the current
  *              query, then attend over it, at every decode step; speculative
@@ -271,6 +279,33 @@ size_t kvc_decode_attn_workspace(const kvc_dims *dims, int32_t cap);
 kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const void *kc, const void *vc,
                            const int32_t *count, int32_t cap, float scale, void *out, float *lse,
                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Landmark-guided block selection (xKV 2.3).  The cache of each KV head is cut into
+ * n_blk = ceil(s_max / block) blocks of `block` tokens.
+ *
+ * kvc_block_landmarks: landmarks[b][g][j] = mean of k[b][g][t] over the block's tokens
+ *   t < S_b (0 for a block with none), summed in token order in double, rounded to float.
+ *   k [B][n_kv][s_max][d_h] dtype; landmarks [B][n_kv][n_blk][d_h] float.
+ * kvc_block_scores: for the candidate blocks j < cand[b] = floor(max(0, S_b - n_keep) /
+ *   block): scores[b][g][j] = scale * sum over the query heads h of g, then over d, of
+ *   q[b][h][d] * landmarks[b][g][j][d] (exact products added in that order in double,
+ *   rounded to float); 0 for the other blocks.  scale 0 selects 1/sqrt(d_h) (in double);
+ *   q [B][n_h][d_h] dtype; scores [B][n_kv][n_blk] float; cand [B] int32.
+ *   Select the blocks with kvc_select_topk(dims with s_max = n_blk, seq_lens = cand,
+ *   k = blocks to keep, n_keep = 0).
+ * kvc_expand_blocks: for unit u = (b, h): the count_blk[u] kept blocks (ascending in
+ *   idx_blk) give tokens idx_blk[u][j] * block + i at position j * block + i, then the
+ *   tail [cand[b] * block, S_b) (the trailing tokens that start no candidate block);
+ *   -1 past count; count[u] = min(cap, count_blk[u] * block + S_b - cand[b] * block).
+ *   cap = k_blocks * block + n_keep + block - 1 holds every case.
+ */
+kvc_status kvc_block_landmarks(const kvc_dims *dims, const void *k, int32_t block, float *landmarks, void *stream);
+kvc_status kvc_block_scores(const kvc_dims *dims, const void *q, const float *landmarks, int32_t block,
+                            int32_t n_keep, float scale, float *scores, int32_t *cand, void *stream);
+kvc_status kvc_expand_blocks(int32_t batch, int32_t heads, int32_t s_max, const int32_t *seq_lens, int32_t block,
+                             int32_t n_keep, const int32_t *idx_blocks, const int32_t *count_blocks,
+                             int32_t cap_blocks, int32_t *idx, int32_t *count, int32_t cap, void *stream);
 
 /*
  * kvc_query_similarity -- which KV heads must select again before attention at this

@@ -259,3 +259,48 @@ KVC_EXPORT kvc_status kvc_query_similarity(const kvc_dims *dims, const void *q_c
                                           q_cur, q_prev, tau, cos, refresh, keep, (hipStream_t)stream);
     return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
+
+// ------------------------------------------------------------------- block selection
+
+KVC_EXPORT kvc_status kvc_block_landmarks(const kvc_dims *dims, const void *k, int32_t block, float *landmarks,
+                                          void *stream)
+{
+    kvc_status st = check_dims(dims, true);
+    if (st != KVC_OK) return st;
+    if (!k || !landmarks || block < 1 || block > dims->s_max) return KVC_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(landmarks)) return KVC_ERR_INVALID_ARG;
+    hipError_t e = kvc::launch_block_landmarks(dims->batch, dims->n_kv, dims->s_max, dims->d_h,
+                                               dims->dtype == KVC_BF16, dims->seq_lens, k, block, landmarks,
+                                               (hipStream_t)stream);
+    return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+KVC_EXPORT kvc_status kvc_block_scores(const kvc_dims *dims, const void *q, const float *landmarks, int32_t block,
+                                       int32_t n_keep, float scale, float *scores, int32_t *cand, void *stream)
+{
+    kvc_status st = check_dims(dims, true);
+    if (st != KVC_OK) return st;
+    if (!q || !landmarks || !scores || !cand || block < 1 || block > dims->s_max || n_keep < 0)
+        return KVC_ERR_INVALID_ARG;
+    if (!(scale >= 0.f) || scale > 1e30f) return KVC_ERR_INVALID_ARG;
+    if (!aligned16(landmarks)) return KVC_ERR_INVALID_ARG;
+    const double sc = scale == 0.f ? 1.0 / sqrt((double)dims->d_h) : (double)scale;
+    hipError_t e = kvc::launch_block_scores(dims->batch, dims->n_h, dims->n_kv, dims->d_h, dims->dtype == KVC_BF16,
+                                            dims->s_max, dims->seq_lens, q, landmarks, block, n_keep, sc, scores,
+                                            cand, (hipStream_t)stream);
+    return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+KVC_EXPORT kvc_status kvc_expand_blocks(int32_t batch, int32_t heads, int32_t s_max, const int32_t *seq_lens,
+                                        int32_t block, int32_t n_keep, const int32_t *idx_blocks,
+                                        const int32_t *count_blocks, int32_t cap_blocks, int32_t *idx,
+                                        int32_t *count, int32_t cap, void *stream)
+{
+    if (batch < 1 || heads < 1 || s_max < 1 || block < 1 || n_keep < 0 || cap_blocks < 1 || cap < 1)
+        return KVC_ERR_INVALID_ARG;
+    if ((long)batch * heads > kMaxUnits || cap > (1 << 30)) return KVC_ERR_INVALID_ARG;
+    if (!idx_blocks || !count_blocks || !idx || !count) return KVC_ERR_INVALID_ARG;
+    hipError_t e = kvc::launch_expand_blocks(batch, heads, s_max, seq_lens, block, n_keep, idx_blocks, count_blocks,
+                                             cap_blocks, idx, count, cap, (hipStream_t)stream);
+    return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}

@@ -69,6 +69,16 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
                         int n_keep, int pool, float scale, float *raw, float *pooled,
                         const int32_t *unit_mask, void *ws, const ScorePlan &plan, hipStream_t stream);
 
+// ---- landmark-guided block selection ------------------------------------------------
+hipError_t launch_block_landmarks(int batch, int n_kv, int s_max, int d_h, bool bf16, const int32_t *seq_lens,
+                                  const void *k, int block, float *landmarks, hipStream_t stream);
+hipError_t launch_block_scores(int batch, int n_h, int n_kv, int d_h, bool bf16, int s_max, const int32_t *seq_lens,
+                               const void *q, const float *landmarks, int block, int n_keep, double scale,
+                               float *scores, int32_t *cand, hipStream_t stream);
+hipError_t launch_expand_blocks(int batch, int heads, int s_max, const int32_t *seq_lens, int block, int n_keep,
+                                const int32_t *idx_blk, const int32_t *count_blk, int cap_blk, int32_t *idx,
+                                int32_t *count, int cap, hipStream_t stream);
+
 // ---- query similarity ---------------------------------------------------------------
 hipError_t launch_similarity(int batch, int n_h, int n_kv, int d_h, bool bf16, const void *q_cur,
                              const void *q_prev, double tau, float *cos, int32_t *refresh, int32_t *keep,

@@ -29,6 +29,7 @@ EXPORTED = (
     "kvc_gather_compact",
     "kvc_decode_attn_workspace", "kvc_decode_attn",
     "kvc_query_similarity",
+    "kvc_block_landmarks", "kvc_block_scores", "kvc_expand_blocks",
 )
 
 
@@ -71,6 +72,9 @@ def lib():
                 "kvc_decode_attn_workspace": (Z, [D, I]),
                 "kvc_decode_attn": (I, [D, P, P, P, P, I, F, P, P, P, Z, P]),
                 "kvc_query_similarity": (I, [D, P, P, ctypes.c_double, P, P, P, P]),
+                "kvc_block_landmarks": (I, [D, P, I, P, P]),
+                "kvc_block_scores": (I, [D, P, P, I, I, F, P, P, P]),
+                "kvc_expand_blocks": (I, [I, I, I, P, I, I, P, P, I, P, P, I, P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -324,3 +328,55 @@ def query_similarity(q_cur, q_prev, n_kv, tau, *, cos=None, refresh=None, keep=N
                                     _ptr(refresh), _ptr(keep), _stream(stream))
     _check(st, "kvc_query_similarity")
     return cos, refresh, keep
+
+
+# ------------------------------------------------------- landmark-guided block selection
+
+def block_landmarks(k, block, *, seq_lens=None, out=None, stream=None):
+    """kvc_block_landmarks: k [B][n_kv][s_max][d_h] -> mean keys [B][n_kv][ceil(s_max/block)][d_h] fp32."""
+    _dev(k, "k")
+    B, n_kv, s_max, d_h = k.shape
+    n_blk = (s_max + block - 1) // block
+    sl = _seq_lens(seq_lens, k.device)
+    dims = make_dims(B, s_max, n_kv, n_kv, d_h, _dtype_code(k), sl)
+    if out is None:
+        out = torch.empty((B, n_kv, n_blk, d_h), dtype=torch.float32, device=k.device)
+    st = lib().kvc_block_landmarks(ctypes.byref(dims), _ptr(k), int(block), _ptr(out), _stream(stream))
+    _check(st, "kvc_block_landmarks")
+    return out
+
+
+def block_scores(q, landmarks, block, n_keep, s_max, *, seq_lens=None, scale=0.0, scores=None, cand=None,
+                 stream=None):
+    """kvc_block_scores: q [B][n_h][d_h], landmarks -> (scores [B][n_kv][n_blk] fp32, cand [B] int32)."""
+    _dev(q, "q")
+    _dev(landmarks, "landmarks")
+    B, n_h, d_h = q.shape
+    _, n_kv, n_blk, _ = landmarks.shape
+    sl = _seq_lens(seq_lens, q.device)
+    dims = make_dims(B, s_max, n_h, n_kv, d_h, _dtype_code(q), sl)
+    if scores is None:
+        scores = torch.empty((B, n_kv, n_blk), dtype=torch.float32, device=q.device)
+    if cand is None:
+        cand = torch.empty((B,), dtype=torch.int32, device=q.device)
+    st = lib().kvc_block_scores(ctypes.byref(dims), _ptr(q), _ptr(landmarks), int(block), int(n_keep), float(scale),
+                                _ptr(scores), _ptr(cand), _stream(stream))
+    _check(st, "kvc_block_scores")
+    return scores, cand
+
+
+def expand_blocks(idx_blocks, count_blocks, block, n_keep, s_max, cap, *, seq_lens=None, idx=None, count=None,
+                  stream=None):
+    """kvc_expand_blocks: kept blocks [B][H][cap_blocks] -> token indices [B][H][cap], count [B][H]."""
+    _dev(idx_blocks, "idx_blocks")
+    _dev(count_blocks, "count_blocks")
+    B, H, cap_blk = idx_blocks.shape
+    sl = _seq_lens(seq_lens, idx_blocks.device)
+    if idx is None:
+        idx = torch.empty((B, H, cap), dtype=torch.int32, device=idx_blocks.device)
+    if count is None:
+        count = torch.empty((B, H), dtype=torch.int32, device=idx_blocks.device)
+    st = lib().kvc_expand_blocks(int(B), int(H), int(s_max), _ptr(sl), int(block), int(n_keep), _ptr(idx_blocks),
+                                 _ptr(count_blocks), int(cap_blk), _ptr(idx), _ptr(count), int(cap), _stream(stream))
+    _check(st, "kvc_expand_blocks")
+    return idx, count

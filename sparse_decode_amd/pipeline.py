@@ -161,3 +161,56 @@ class SpeculativeRetrieval:
 
     def swap(self):
         self.cur = 1 - self.cur
+
+
+class BlockRetrieval:
+    """xKV section 2.3 selective reconstruction's token choice on one GPU: landmark-
+    guided block selection (ShadowKV-style).  `prepare` builds the block landmarks of
+    the cache once; `step` scores the blocks with the step's query, keeps the best
+    k_blocks blocks of every KV head (plus the trailing tokens that start no candidate
+    block), gathers their rows and attends over them."""
+
+    def __init__(self, wl: Workload, block: int, k_blocks: int, device="cuda", s_max: int | None = None,
+                 batch: int | None = None):
+        self.wl = wl
+        self.block = int(block)
+        self.k_blocks = int(k_blocks)
+        dev = torch.device(device)
+        self.B = wl.batch if batch is None else batch
+        self.S = wl.s_max if s_max is None else s_max
+        B, S, nkv, nh, d = self.B, self.S, wl.n_kv, wl.n_h, wl.d_h
+        self.n_blk = (S + self.block - 1) // self.block
+        self.cap = self.k_blocks * self.block + wl.n_keep + self.block - 1
+        self.landmarks = torch.empty((B, nkv, self.n_blk, d), dtype=torch.float32, device=dev)
+        self.scores = torch.empty((B, nkv, self.n_blk), dtype=torch.float32, device=dev)
+        self.cand = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.bidx = torch.empty((B, nkv, self.k_blocks), dtype=torch.int32, device=dev)
+        self.bcount = torch.empty((B, nkv), dtype=torch.int32, device=dev)
+        self.idx = torch.empty((B, nkv, self.cap), dtype=torch.int32, device=dev)
+        self.count = torch.empty((B, nkv), dtype=torch.int32, device=dev)
+        dt = wl.torch_dtype
+        self.kc = torch.empty((B, nkv, self.cap, d), dtype=dt, device=dev)
+        self.vc = torch.empty((B, nkv, self.cap, d), dtype=dt, device=dev)
+        self.pos = torch.empty((B, nkv, self.cap), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, nh, d), dtype=dt, device=dev)
+        self.lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
+        sdims = kvc.make_dims(B, self.n_blk, nkv, nkv, 128, kvc.KVC_F32)
+        self.ws_select = torch.zeros(max(256, kvc.select_topk_workspace(sdims, self.k_blocks, 0)),
+                                     dtype=torch.uint8, device=dev)
+        dims = kvc.make_dims(B, S, nh, nkv, d, kvc.KVC_BF16 if wl.dtype == "bf16" else kvc.KVC_F32)
+        self.ws_decode = torch.zeros(max(256, kvc.decode_attn_workspace(dims, self.cap)), dtype=torch.uint8,
+                                     device=dev)
+
+    def prepare(self, k, seq_lens=None):
+        return kvc.block_landmarks(k, self.block, seq_lens=seq_lens, out=self.landmarks)
+
+    def step(self, q, k, v, seq_lens=None):
+        wl = self.wl
+        kvc.block_scores(q, self.landmarks, self.block, wl.n_keep, self.S, seq_lens=seq_lens, scores=self.scores,
+                         cand=self.cand)
+        kvc.select_topk(self.scores, self.k_blocks, 0, seq_lens=self.cand, idx=self.bidx, count=self.bcount,
+                        ws=self.ws_select)
+        kvc.expand_blocks(self.bidx, self.bcount, self.block, wl.n_keep, self.S, self.cap, seq_lens=seq_lens,
+                          idx=self.idx, count=self.count)
+        kvc.gather_compact(k, self.idx, self.count, src1=v, dst0=self.kc, dst1=self.vc, pos_out=self.pos)
+        return kvc.decode_attn(q, self.kc, self.vc, self.count, out=self.out, lse=self.lse, ws=self.ws_decode)

@@ -224,3 +224,24 @@ def test_select_core_rejects_invalid_arguments():
     assert kvc.select_core_workspace(_dims(), -1) == 0
     # valid arguments reach the launch, which fails without a device
     assert _select_core(_dims(), ws_bytes=need) == kvc.KVC_ERR_HIP
+
+
+def test_block_selection_rejects_invalid_arguments():
+    E, U = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_UNSUPPORTED
+    L = kvc.lib()
+    d = _dims()
+    assert L.kvc_block_landmarks(None, BAD, 16, BAD, None) == E
+    assert L.kvc_block_landmarks(ctypes.byref(d), None, 16, BAD, None) == E
+    assert L.kvc_block_landmarks(ctypes.byref(d), BAD, 0, BAD, None) == E
+    assert L.kvc_block_landmarks(ctypes.byref(d), BAD, 2048, BAD, None) == E     # block > s_max
+    assert L.kvc_block_landmarks(ctypes.byref(_dims(d_h=80)), BAD, 16, BAD, None) == U
+    assert L.kvc_block_scores(ctypes.byref(d), BAD, BAD, 16, 32, 0.0, BAD, None, None) == E   # no cand
+    assert L.kvc_block_scores(ctypes.byref(d), BAD, BAD, 16, -1, 0.0, BAD, BAD, None) == E
+    assert L.kvc_block_scores(ctypes.byref(d), BAD, BAD, 16, 32, float("nan"), BAD, BAD, None) == E
+    assert L.kvc_expand_blocks(1, 8, 1024, None, 16, 32, BAD, BAD, 0, BAD, BAD, 80, None) == E
+    assert L.kvc_expand_blocks(1, 8, 1024, None, 0, 32, BAD, BAD, 4, BAD, BAD, 80, None) == E
+    assert L.kvc_expand_blocks(1, 8, 1024, None, 16, 32, None, BAD, 4, BAD, BAD, 80, None) == E
+    # valid arguments reach the launch, which fails without a device
+    assert L.kvc_block_landmarks(ctypes.byref(d), BAD, 16, BAD, None) == kvc.KVC_ERR_HIP
+    assert L.kvc_block_scores(ctypes.byref(d), BAD, BAD, 16, 32, 0.0, BAD, BAD, None) == kvc.KVC_ERR_HIP
+    assert L.kvc_expand_blocks(1, 8, 1024, None, 16, 32, BAD, BAD, 4, BAD, BAD, 80, None) == kvc.KVC_ERR_HIP
