@@ -103,12 +103,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
     const int r = a.r;
     const int heads = min(RH, r - hc * RH);  // query heads of this chunk
 
-    int n = a.count[unit];
-    n = n < 0 ? 0 : (n > a.cap ? a.cap : n);
+    // ---- phase 1: this split.  Its first rows are requested before the count is
+    // known (rows below cap are in bounds) and zeroed past the count once it arrives,
+    // so count, rows and queries share one round trip.
     const int s0 = split * a.split_tokens;
-    const int s1 = min(s0 + a.split_tokens, n);
-
-    // ---- phase 1: this split
+    const int s1c = min(s0 + a.split_tokens, a.cap);
     constexpr int step = G;                 // token rows per work-group step
     const u32x4 *krow = (const u32x4 *)a.kc + (size_t)unit * a.cap * VPR + li;
     const u32x4 *vrow = (const u32x4 *)a.vc + (size_t)unit * a.cap * VPR + li;
@@ -117,9 +116,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
 #pragma unroll
     for (int q = 0; q < kUnroll; ++q) {
         const int tq = t + q * step;
-        kv[q] = tq < s1 ? ld_stream(krow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
-        vv[q] = tq < s1 ? ld_stream(vrow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
+        kv[q] = tq < s1c ? ld_stream(krow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
+        vv[q] = tq < s1c ? ld_stream(vrow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
     }
+    int n = a.count[unit];
+    n = n < 0 ? 0 : (n > a.cap ? a.cap : n);
+    const int s1 = min(s0 + a.split_tokens, n);
     // queries of this chunk of the group, pre-scaled into log2 units
     float qf[RH][E];
     const int h_first = g * r + hc * RH;
@@ -133,6 +135,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) qf[j][e] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) {
+        if (t + q * step >= s1) {           // past the count: those rows may hold any bits
+            kv[q] = u32x4{0u, 0u, 0u, 0u};
+            vv[q] = u32x4{0u, 0u, 0u, 0u};
         }
     }
     float m[RH], l[RH], o[RH][E];
@@ -274,7 +283,7 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 // for up to G * kMergeBatch splits); the split weights exp2(m_s - M) go to LDS, the
 // kMergeThreads / D thread groups fold their strided subsets of the splits and the
 // groups are added in group order.
-constexpr int kMergeBatch = 16;
+constexpr int kMergeBatch = 32;
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float *__restrict__ part_o,
