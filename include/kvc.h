@@ -146,7 +146,8 @@ const char *kvc_status_str(kvc_status status);
  *
  * q_win      [B][n_h][w][d_h] dtype      window queries
  * k          [B][n_kv][s_max][d_h] dtype  keys
- * w          1 <= w <= 1024, and (n_h/n_kv)*w <= 1024
+ * w          1 <= w <= 1024, and (n_h/n_kv)*w <= 1024; s_max <= 2^22 (else
+ *            KVC_ERR_UNSUPPORTED)
  * pool_kernel odd, 1 <= p <= 63 (1: no pooling)
  * scale      > 0; 0 means 1/sqrt(d_h)
  * raw        [B][n_kv][s_max] float, written (required)

@@ -86,6 +86,7 @@ static kvc_status score_args(const kvc_dims *d, int32_t w, int32_t flags)
     kvc_status st = check_dims(d, true);
     if (st != KVC_OK) return st;
     if (w < 1 || w > 1024 || (long)(d->n_h / d->n_kv) * w > 1024) return KVC_ERR_INVALID_ARG;
+    if (d->s_max > (1 << 22)) return KVC_ERR_UNSUPPORTED;      // byte offsets within a unit fit 31 bits
     if (flags & ~KVC_SCORE_GENERIC) return KVC_ERR_INVALID_ARG;
     return KVC_OK;
 }

@@ -289,10 +289,10 @@ struct Sc {
     static_assert(LOADS >= 1 && ST * VPR % kMfThreads == 0, "stage must split evenly over the threads");
 
     // Coalesced loads of one stage through a buffer resource over the unit's S cached
-    // rows: the stage's first row is a scalar offset, each thread's part a constant
-    // vector offset (no per-load address arithmetic), and rows at or past S read as
-    // zero (the hardware range check).  KEEP: ordinary loads, which leave K in the
-    // caches for the second pass; else loads hinted as streamed (K's last use).
+    // rows: every offset is a vector offset (the range check covers the vector and
+    // instruction offsets, so the stage's first row is added there, not as a scalar
+    // offset), and rows at or past S read as zero.  KEEP: ordinary loads, which leave
+    // K in the caches for the second pass; else loads hinted as streamed (K's last use).
     template <bool KEEP>
     __device__ static void load_stage(__amdgpu_buffer_rsrc_t rsrc, int st0, u32x4 *reg)
     {
@@ -301,7 +301,7 @@ struct Sc {
             const int gid = i * kMfThreads + threadIdx.x;
             const int row = gid / VPR, col = gid - row * VPR;
             reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                rsrc, row * (2 * D) + col * 16, __builtin_amdgcn_readfirstlane(st0 * (2 * D)), KEEP ? 0 : kAuxNt));
+                rsrc, (st0 + row) * (2 * D) + col * 16, 0, KEEP ? 0 : kAuxNt));
         }
     }
 

@@ -87,6 +87,7 @@ def test_workspace_queries():
     big = kvc.score_window_workspace(_dims(s_max=131072), 32)
     assert 0 < small <= big
     gen = kvc.score_window_workspace(_dims(s_max=4096), 32, kvc.KVC_SCORE_GENERIC)
+    assert kvc.score_window_workspace(_dims(s_max=(1 << 22) + 1), 32) == 0
     assert gen >= 32 * 4 * 4096 * 4 * 8     # stored logits
     plain = kvc.select_topk_workspace(d, 64, 16)
     assert plain >= 8 * 5120 * 4                  # three radix histograms (2048 + 2048 + 1024) per unit

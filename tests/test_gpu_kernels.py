@@ -304,6 +304,33 @@ def test_score_short_sequences():
     _score_case(4, 8, 2, 128, 256, 32, np.array([20, 0, 1, 256], np.int32), seed=6, generic=True)
 
 
+def test_score_row_padding_and_ragged_units():
+    # many chunks per unit, a ragged last chunk, units shorter than a chunk and of zero length
+    _score_case(4, 32, 8, 128, 20000, 32, np.array([20000, 19999, 257, 0], np.int32), seed=11, planted=30)
+    # R = 80 (rows 80..127 of the row tile are padding), the query not in the cache
+    _score_case(2, 10, 2, 128, 3000, 16, np.array([3000, 1000], np.int32), wic=False, seed=12)
+    # R = 96, rows that see no key (S < w), S = 1
+    _score_case(3, 12, 4, 128, 600, 32, np.array([20, 1, 600], np.int32), seed=13, pool=3)
+
+
+def test_score_unit_mask():
+    # units whose mask entry is 0 keep what raw/pooled held; the others match the full call
+    B, n_h, n_kv, d, s_max, w = 2, 32, 8, 128, 5000, 32
+    sl = np.array([5000, 3100], np.int32)
+    _say("score unit mask", B, n_h, n_kv, d, s_max, w, list(sl))
+    q = _randn((B, n_h, w, d), 300)
+    k = _randn((B, n_kv, s_max, d), 301)
+    full_raw, full_pooled = kvc.score_window(q, k, w, seq_lens=sl, n_keep=w, pool=7)
+    mask = torch.from_numpy(np.random.default_rng(3).integers(0, 2, (B, n_kv)).astype(np.int32)).to(DEV)
+    raw = torch.full((B, n_kv, s_max), -7.0, device=DEV)
+    pooled = torch.full((B, n_kv, s_max), -9.0, device=DEV)
+    kvc.score_window(q, k, w, seq_lens=sl, n_keep=w, pool=7, raw=raw, pooled=pooled, unit_mask=mask)
+    torch.cuda.synchronize()
+    on = mask.bool()
+    assert torch.equal(raw[on], full_raw[on]) and torch.equal(pooled[on], full_pooled[on])
+    assert bool((raw[~on] == -7.0).all()) and bool((pooled[~on] == -9.0).all())
+
+
 def test_score_then_select_matches_oracle_rule():
     sl = np.array([4000], np.int32)
     q, k, raw, pooled, rpooled = _score_case(1, 32, 8, 128, 4000, 32, sl, planted=40, seed=7)
