@@ -176,46 +176,100 @@ __global__ __launch_bounds__(kGenThreads) void gen_probsum_kernel(const float *_
 // Pooling: centred max of raw over the candidate region (shared by both paths)
 // ====================================================================================
 constexpr int kPoolThreads = 256;
-constexpr int kPoolTile = 1024;     // tokens per work-group
+constexpr int kPoolTile = 4096;     // tokens per work-group, 16 per thread
 constexpr int kMaxHalf = 31;        // pool kernels up to 63
 
+__device__ __forceinline__ float pool_at(const float *tile, int base, int t, int half, int C, int S)
+{
+    if (t < C) {
+        const int lo = t - half < 0 ? 0 : t - half;
+        const int hi = t + half > C - 1 ? C - 1 : t + half;
+        float v = tile[lo - base];
+        for (int x = lo + 1; x <= hi; ++x) v = fmaxf(v, tile[x - base]);
+        return v;
+    }
+    return t < S ? tile[t - base] : 0.f;
+}
+
 // One work-group per kPoolTile tokens of a unit: the tile and its halo are staged in
-// LDS once (coalesced), then each output is the max over its window.
+// LDS once (coalesced), then each output is the max over its window.  VEC (rows of a
+// multiple of 4 floats): every thread moves 4 consecutive tokens per 16-byte load and
+// store, four of them in flight.
+template <bool VEC>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restrict__ raw,
                                                             const int32_t *__restrict__ seq_lens, int s_max,
                                                             int n_kv, int n_keep, int half,
                                                             const int32_t *__restrict__ mask,
                                                             float *__restrict__ pooled)
 {
-    __shared__ float tile[kPoolTile + 2 * kMaxHalf];
+    // VEC: 2 kMaxHalf + 2 slots (left halo, then 16-byte alignment), the body, the right halo
+    __shared__ __attribute__((aligned(16))) float tile[2 * kMaxHalf + 2 + kPoolTile + kMaxHalf + 1];
     const int u = blockIdx.y;
     if (mask && !mask[u]) return;
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
     const int C = S - n_keep > 0 ? S - n_keep : 0;
     const int t0 = blockIdx.x * kPoolTile;
     const float *rw = raw + (size_t)u * s_max;
-    const int base = t0 - half;                          // tile[i] holds raw[base + i]
-    for (int i = threadIdx.x; i < kPoolTile + 2 * half; i += kPoolThreads) {
-        const int t = base + i;
-        tile[i] = (t >= 0 && t < s_max) ? rw[t] : 0.f;
-    }
-    __syncthreads();
     float *out = pooled + (size_t)u * s_max;
+    const int tid = threadIdx.x;
+    if constexpr (VEC) {
+        // the body starts 16-byte aligned 64 slots in; the halos (at most 31 tokens each
+        // side) are read one by one
+        float4 v[kPoolTile / kPoolThreads / 4];
 #pragma unroll
-    for (int q = 0; q < kPoolTile / kPoolThreads; ++q) {
-        const int t = t0 + q * kPoolThreads + (int)threadIdx.x;
-        if (t >= s_max) break;
-        float v;
-        if (t < C) {
-            const int lo = t - half < 0 ? 0 : t - half;
-            const int hi = t + half > C - 1 ? C - 1 : t + half;
-            v = tile[lo - base];
-            for (int x = lo + 1; x <= hi; ++x) v = fmaxf(v, tile[x - base]);
-        } else {
-            v = t < S ? tile[t - base] : 0.f;
+        for (int i = 0; i < kPoolTile / kPoolThreads / 4; ++i) {
+            const int t = t0 + 4 * (i * kPoolThreads + tid);
+            v[i] = t < s_max ? *(const float4 *)(rw + t) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        out[t] = v;
+        float *body = tile + 2 * kMaxHalf + 2;              // 16-byte aligned: 64 floats in
+        const int base = t0 - (2 * kMaxHalf + 2);           // tile[i] holds raw[base + i]
+        if (tid < half) {
+            const int t = t0 - half + tid;
+            tile[t - base] = t >= 0 ? rw[t] : 0.f;
+        } else if (tid < 2 * half) {
+            const int t = t0 + kPoolTile + (tid - half);
+            tile[t - base] = t < s_max ? rw[t] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kPoolTile / kPoolThreads / 4; ++i) *(float4 *)(body + 4 * (i * kPoolThreads + tid)) = v[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPoolTile / kPoolThreads / 4; ++i) {
+            const int t = t0 + 4 * (i * kPoolThreads + tid);
+            if (t >= s_max) break;
+            float4 o;
+            o.x = pool_at(tile, base, t, half, C, S);
+            o.y = pool_at(tile, base, t + 1, half, C, S);
+            o.z = pool_at(tile, base, t + 2, half, C, S);
+            o.w = pool_at(tile, base, t + 3, half, C, S);
+            *(float4 *)(out + t) = o;
+        }
+    } else {
+        const int base = t0 - half;                          // tile[i] holds raw[base + i]
+        for (int i = tid; i < kPoolTile + 2 * half; i += kPoolThreads) {
+            const int t = base + i;
+            tile[i] = (t >= 0 && t < s_max) ? rw[t] : 0.f;
+        }
+        __syncthreads();
+        for (int q = 0; q < kPoolTile / kPoolThreads; ++q) {
+            const int t = t0 + q * kPoolThreads + tid;
+            if (t >= s_max) break;
+            out[t] = pool_at(tile, base, t, half, C, S);
+        }
     }
+}
+
+void launch_pool(const float *raw, const int32_t *seq_lens, int s_max, int units, int n_kv, int n_keep, int half,
+                 const int32_t *mask, float *pooled, hipStream_t stream)
+{
+    const dim3 grid((s_max + kPoolTile - 1) / kPoolTile, units);
+    const bool vec = s_max % 4 == 0 && ((uintptr_t)raw & 15) == 0 && ((uintptr_t)pooled & 15) == 0;
+    if (vec)
+        hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep,
+                           half, mask, pooled);
+    else
+        hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv,
+                           n_keep, half, mask, pooled);
 }
 
 // ====================================================================================
@@ -867,8 +921,7 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(pool_kernel, dim3((s_max + kPoolTile - 1) / kPoolTile, units), dim3(kPoolThreads), 0, stream,
-                       raw, seq_lens, s_max, n_kv, n_keep, pool / 2, unit_mask, pooled);
+    launch_pool(raw, seq_lens, s_max, units, n_kv, n_keep, pool / 2, unit_mask, pooled, stream);
     return hipGetLastError();
 }
 
