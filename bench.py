@@ -225,6 +225,25 @@ def main():
         us_layer[n] = 1000.0 * timed(g_call[n].replay, args.steps) / L
     eager_ms = timed(step_folded, max(1, args.steps // 4))
 
+    # one decode call over every layer's compacted cache (the layers folded into the
+    # batch: the shape of a batch-L decode step of one layer), against the per-layer calls
+    def decode_all():
+        kvc.decode_attn(QD.view(L * B, nh, d), fold.kc, fold.vc, fold.count, out=outs.view(L * B, nh, d),
+                        lse=lses.view(L * B, nh), ws=fold.ws_decode)
+    g_dec_all = capture(decode_all)
+    g_dec_all.replay()
+    dec_all_us = 1000.0 * timed(g_dec_all.replay, args.steps)
+    del g_dec_all
+
+    # plain device copy of 1 GiB (torch's copy kernel): the bandwidth a read + write stream
+    # reaches on this device, as context for the HBM fractions
+    cp_a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cp_b = torch.empty_like(cp_a)
+    cp_b.copy_(cp_a)
+    copy_ms = timed(lambda: cp_b.copy_(cp_a), 5)
+    copy_gbps = 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9
+    del cp_a, cp_b
+
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         bcp = torch.empty_like(a)
@@ -301,6 +320,15 @@ def main():
         "eager_ms_per_step": round(eager_ms, 4),
         "timing": "HIP graph replays between HIP events on the launch stream",
         "score_mfma_frac_algorithmic": round(by["flops_score"] / (us["score"] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "decode_all_layers_one_call": {
+            "us": round(dec_all_us, 3), "GBps": round(L * by["decode"] / (dec_all_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(L * by["decode"] / (dec_all_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "kvc_decode_attn over the %d layers' compacted caches folded into the batch (%d sequences x %d "
+                    "KV heads): the kernel at a batch-%d decode's size; per_layer_us.decode is the one-layer call"
+                    % (L, L * B, nkv, L * B)},
+        "copy_probe": {"GBps": round(copy_gbps, 1), "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
+                       "what": "torch device copy of 1 GiB, read + write bytes / time (HIP events, 5 copies)"},
+        "per_layer_frac_of_copy": {n: round(gbps[n] / copy_gbps, 4) for n in names},
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.no_retrieval:

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kGenThreads) void gen_probsum_kernel(const float *_
 // Pooling: centred max of raw over the candidate region (shared by both paths)
 // ====================================================================================
 constexpr int kPoolThreads = 256;
-constexpr int kPoolTile = 4096;     // tokens per work-group, 16 per thread
+constexpr int kPoolTile = 1024;     // tokens per work-group, 4 per thread
 constexpr int kMaxHalf = 31;        // pool kernels up to 63
 
 __device__ __forceinline__ float pool_at(const float *tile, int base, int t, int half, int C, int S)
@@ -192,18 +192,21 @@ __device__ __forceinline__ float pool_at(const float *tile, int base, int t, int
 }
 
 // One work-group per kPoolTile tokens of a unit: the tile and its halo are staged in
-// LDS once (coalesced), then each output is the max over its window.  VEC (rows of a
-// multiple of 4 floats): every thread moves 4 consecutive tokens per 16-byte load and
-// store, four of them in flight.
-template <bool VEC>
+// LDS once (coalesced), then each output is the max over its window.  Each thread
+// owns 4 consecutive tokens (one 16-byte load and store when a row is a multiple of 4
+// floats).  HALF >= 0 is the half-width known at compile time: where the 4 windows
+// lie inside [0, C), the thread reads the 4 + 2 HALF values once into registers and
+// takes the 4 maxima there; elsewhere, and for HALF < 0, every window is walked.
+template <bool VEC, int HALF>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restrict__ raw,
                                                             const int32_t *__restrict__ seq_lens, int s_max,
                                                             int n_kv, int n_keep, int half,
                                                             const int32_t *__restrict__ mask,
                                                             float *__restrict__ pooled)
 {
-    // VEC: 2 kMaxHalf + 2 slots (left halo, then 16-byte alignment), the body, the right halo
+    // 2 kMaxHalf + 2 slots (left halo, then 16-byte alignment), the body, the right halo
     __shared__ __attribute__((aligned(16))) float tile[2 * kMaxHalf + 2 + kPoolTile + kMaxHalf + 1];
+    if constexpr (HALF >= 0) half = HALF;
     const int u = blockIdx.y;
     if (mask && !mask[u]) return;
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
@@ -212,50 +215,61 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restr
     const float *rw = raw + (size_t)u * s_max;
     float *out = pooled + (size_t)u * s_max;
     const int tid = threadIdx.x;
+    const int base = t0 - (2 * kMaxHalf + 2);               // tile[i] holds raw[base + i]
+    float *body = tile + 2 * kMaxHalf + 2;                  // 16-byte aligned: 64 floats in
+    const int t = t0 + 4 * tid;                             // this thread's 4 tokens
     if constexpr (VEC) {
-        // the body starts 16-byte aligned 64 slots in; the halos (at most 31 tokens each
-        // side) are read one by one
-        float4 v[kPoolTile / kPoolThreads / 4];
+        *(float4 *)(body + 4 * tid) = t < s_max ? *(const float4 *)(rw + t) : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
 #pragma unroll
-        for (int i = 0; i < kPoolTile / kPoolThreads / 4; ++i) {
-            const int t = t0 + 4 * (i * kPoolThreads + tid);
-            v[i] = t < s_max ? *(const float4 *)(rw + t) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        float *body = tile + 2 * kMaxHalf + 2;              // 16-byte aligned: 64 floats in
-        const int base = t0 - (2 * kMaxHalf + 2);           // tile[i] holds raw[base + i]
-        if (tid < half) {
-            const int t = t0 - half + tid;
-            tile[t - base] = t >= 0 ? rw[t] : 0.f;
-        } else if (tid < 2 * half) {
-            const int t = t0 + kPoolTile + (tid - half);
-            tile[t - base] = t < s_max ? rw[t] : 0.f;
-        }
+        for (int k = 0; k < 4; ++k) body[4 * tid + k] = t + k < s_max ? rw[t + k] : 0.f;
+    }
+    if (tid < half) {
+        const int th = t0 - half + tid;
+        tile[th - base] = th >= 0 ? rw[th] : 0.f;
+    } else if (tid < 2 * half) {
+        const int th = t0 + kPoolTile + (tid - half);
+        tile[th - base] = th < s_max ? rw[th] : 0.f;
+    }
+    __syncthreads();
+    if (t >= s_max) return;
+    float o[4];
+    if (HALF >= 0 && t - HALF >= 0 && t + 3 + HALF <= C - 1) {
+        // the 4 windows are whole: [t - HALF, t + 3 + HALF] inside [0, C)
+        constexpr int NW = HALF >= 0 ? 4 + 2 * HALF : 1;
+        float win[NW];
 #pragma unroll
-        for (int i = 0; i < kPoolTile / kPoolThreads / 4; ++i) *(float4 *)(body + 4 * (i * kPoolThreads + tid)) = v[i];
-        __syncthreads();
+        for (int i = 0; i < NW; ++i) win[i] = tile[t - HALF + i - base];
 #pragma unroll
-        for (int i = 0; i < kPoolTile / kPoolThreads / 4; ++i) {
-            const int t = t0 + 4 * (i * kPoolThreads + tid);
-            if (t >= s_max) break;
-            float4 o;
-            o.x = pool_at(tile, base, t, half, C, S);
-            o.y = pool_at(tile, base, t + 1, half, C, S);
-            o.z = pool_at(tile, base, t + 2, half, C, S);
-            o.w = pool_at(tile, base, t + 3, half, C, S);
-            *(float4 *)(out + t) = o;
+        for (int k = 0; k < 4; ++k) {                      // token t + k: win[k .. k + 2 HALF]
+            float v = win[k];
+#pragma unroll
+            for (int i = k + 1; i <= k + 2 * HALF; ++i) v = fmaxf(v, win[i]);
+            o[k] = v;
         }
     } else {
-        const int base = t0 - half;                          // tile[i] holds raw[base + i]
-        for (int i = tid; i < kPoolTile + 2 * half; i += kPoolThreads) {
-            const int t = base + i;
-            tile[i] = (t >= 0 && t < s_max) ? rw[t] : 0.f;
-        }
-        __syncthreads();
-        for (int q = 0; q < kPoolTile / kPoolThreads; ++q) {
-            const int t = t0 + q * kPoolThreads + tid;
-            if (t >= s_max) break;
-            out[t] = pool_at(tile, base, t, half, C, S);
-        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = pool_at(tile, base, t + k, half, C, S);
+    }
+    if constexpr (VEC) {
+        *(float4 *)(out + t) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (t + k < s_max) out[t + k] = o[k];
+    }
+}
+
+template <bool VEC>
+void launch_pool_vec(dim3 grid, const float *raw, const int32_t *seq_lens, int s_max, int n_kv, int n_keep, int half,
+                     const int32_t *mask, float *pooled, hipStream_t stream)
+{
+    switch (half) {
+    case 0: hipLaunchKernelGGL((pool_kernel<VEC, 0>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
+    case 1: hipLaunchKernelGGL((pool_kernel<VEC, 1>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
+    case 2: hipLaunchKernelGGL((pool_kernel<VEC, 2>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
+    case 3: hipLaunchKernelGGL((pool_kernel<VEC, 3>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
+    default: hipLaunchKernelGGL((pool_kernel<VEC, -1>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
     }
 }
 
@@ -263,13 +277,10 @@ void launch_pool(const float *raw, const int32_t *seq_lens, int s_max, int units
                  const int32_t *mask, float *pooled, hipStream_t stream)
 {
     const dim3 grid((s_max + kPoolTile - 1) / kPoolTile, units);
-    const bool vec = s_max % 4 == 0 && ((uintptr_t)raw & 15) == 0 && ((uintptr_t)pooled & 15) == 0;
-    if (vec)
-        hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep,
-                           half, mask, pooled);
+    if (s_max % 4 == 0 && ((uintptr_t)raw & 15) == 0 && ((uintptr_t)pooled & 15) == 0)
+        launch_pool_vec<true>(grid, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, stream);
     else
-        hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv,
-                           n_keep, half, mask, pooled);
+        launch_pool_vec<false>(grid, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, stream);
 }
 
 // ====================================================================================

@@ -331,6 +331,22 @@ def test_score_unit_mask():
     assert bool((raw[~on] == -7.0).all()) and bool((pooled[~on] == -9.0).all())
 
 
+@pytest.mark.parametrize("s_max", [2999, 3000])
+def test_pool_kernel_widths(s_max):
+    # every compiled window (pool 1, 3, 5, 7 specialised, 9 and 63 walked), rows of a
+    # multiple of 4 floats and not, candidate regions ending inside and at a tile edge
+    sl = np.array([s_max, 1024 + 40, 17, 2048 + 32], np.int32)
+    q = _randn((4, 8, 8, 64), 400)
+    k = _randn((4, 2, s_max, 64), 401)
+    for pool in (1, 3, 5, 7, 9, 63):
+        for n_keep in (0, 8, 40):
+            _say("pool", s_max, pool, n_keep)
+            raw, pooled = kvc.score_window(q, k, 8, seq_lens=sl, n_keep=n_keep, pool=pool)
+            torch.cuda.synchronize()
+            _, want = _pool_np(host(raw), sl, n_keep, pool)
+            assert np.array_equal(host(pooled), want), (pool, n_keep)
+
+
 def test_score_then_select_matches_oracle_rule():
     sl = np.array([4000], np.int32)
     q, k, raw, pooled, rpooled = _score_case(1, 32, 8, 128, 4000, 32, sl, planted=40, seed=7)
