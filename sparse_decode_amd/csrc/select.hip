@@ -452,6 +452,148 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     }
 }
 
+// ------------------------------------------------------------- one work-group per unit
+// When a unit has at most 32768 candidates and there are enough units to occupy the
+// chip, one work-group of 512 threads holds all of a unit's candidates in registers
+// (16 bytes per load, every load in flight at once) and runs the three radix levels
+// and the ordered write in LDS: one launch, every key read once.  (A CU keeps only so
+// many loads in flight, so with few units the chunked kernels, which spread a unit
+// over many CUs, finish first.)  The levels, the tie rule and the output are those of
+// the chunked kernels above.
+constexpr int kUnitThreads = 512;
+
+// Bin of the k_rem-th largest key of an LDS histogram (summed over its copies) and the
+// number of keys above that bin; thread i owns bins NB-1-i*per down to NB-per-i*per.
+template <int NB>
+__device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan, Digit *out)
+{
+    constexpr int per = NB / kUnitThreads;
+    const int top = NB - 1 - (int)threadIdx.x * per;
+    int c[per], cnt = 0;
+#pragma unroll
+    for (int p = 0; p < per; ++p) {
+        int s = 0;
+#pragma unroll
+        for (int cc = 0; cc < kCopies; ++cc) s += h[cc][top - p];
+        c[p] = s;
+        cnt += s;
+    }
+    int tot;
+    int above = block_exclusive_scan(cnt, scan, &tot);
+#pragma unroll
+    for (int p = 0; p < per; ++p) {
+        if (above < k_rem && above + c[p] >= k_rem) *out = Digit{top - p, above};
+        above += c[p];
+    }
+    __syncthreads();
+    const Digit d = *out;
+    // the histogram is free again: clear it for the next level
+    for (int i = threadIdx.x; i < kCopies * kB1 / 4; i += kUnitThreads)
+        reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
+    __syncthreads();
+    return d;
+}
+
+// Thread i holds the K = 4 NQ consecutive candidates [K i, K i + K), so one block
+// scan orders the write.  VEC: rows of a multiple of 4 floats, 16-byte loads.
+template <int NQ, bool VEC>
+__global__ __launch_bounds__(kUnitThreads) void sel_unit_kernel(SelArgs a)
+{
+    constexpr int K = 4 * NQ;
+    __shared__ int h[kCopies][kB1];
+    __shared__ int scan[16];
+    __shared__ Digit dg;
+    const int u = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (a.mask && !a.mask[u]) return;
+    const UnitShape us = unit_shape(a.seq_lens, u / a.H, a.s_max, unit_budget(a, u), a.n_keep);
+    int32_t *out = a.idx + (size_t)u * a.cap;
+    // the always-kept trailing tokens, the -1 padding and the count
+    const int nw = us.S - us.C;
+    for (int i = tid; i < nw; i += kUnitThreads) out[us.k_eff + i] = us.C + i;
+    for (int i = us.k_eff + nw + tid; i < a.cap; i += kUnitThreads) out[i] = -1;
+    if (tid == 0) a.count[u] = us.k_eff + nw;
+    if (us.k_eff == 0) return;
+    if (us.k_eff == us.C) {
+        for (int t = tid; t < us.C; t += kUnitThreads) out[t] = t;
+        return;
+    }
+    const float *sc = a.scores + (size_t)u * a.s_max;
+    const int t0 = K * tid;
+    uint32_t key[K];
+    {
+        float v[K];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int t = t0 + 4 * q;
+            if constexpr (VEC) {
+                // t < C <= s_max and s_max % 4 == 0: the whole vector is inside the row
+                const float4 x = t < us.C ? *(const float4 *)(sc + t) : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[4 * q] = x.x;
+                v[4 * q + 1] = x.y;
+                v[4 * q + 2] = x.z;
+                v[4 * q + 3] = x.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * q + e] = t + e < us.C ? sc[t + e] : 0.f;
+            }
+        }
+        // past the candidates the key is 0, below every key of a non-NaN score: the
+        // histograms may count those slots, since the k_eff-th largest key (k_eff < C)
+        // and the counts above its bins do not change; the write checks validity
+#pragma unroll
+        for (int i = 0; i < K; ++i) key[i] = t0 + i < us.C ? order_key(v[i]) : 0u;
+    }
+    for (int i = tid; i < kCopies * kB1 / 4; i += kUnitThreads)
+        reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
+    __syncthreads();
+    int *hc = h[tid & (kCopies - 1)];
+
+    // level 1: key bits [21, 32)
+#pragma unroll
+    for (int i = 0; i < K; ++i) hist_add(hc, h[0], (int)(key[i] >> 21));
+    __syncthreads();
+    const Digit d1 = unit_digit<kB1>(h, us.k_eff, scan, &dg);
+    // level 2: bits [10, 21) of the keys in bin d1
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        if ((int)(key[i] >> 21) == d1.digit) hist_add(hc, h[0], (int)((key[i] >> 10) & (kB2 - 1)));
+    __syncthreads();
+    const Digit d2 = unit_digit<kB2>(h, us.k_eff - d1.above, scan, &dg);
+    // level 3: bits [0, 10) of the keys with prefix (d1, d2)
+    const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        if ((key[i] >> 10) == pre2) hist_add(hc, h[0], (int)(key[i] & (kB3 - 1)));
+    __syncthreads();
+    const Digit d3 = unit_digit<kB3>(h, us.k_eff - d1.above - d2.above, scan, &dg);
+    const uint32_t T = (pre2 << 10) | (uint32_t)d3.digit;
+    const int ties = us.k_eff - d1.above - d2.above - d3.above;     // keys == T to take, lowest index first
+
+    // ordered write: one block scan of (keys > T, keys == T) per thread
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        const bool ok = t0 + i < us.C;
+        gt += ok && key[i] > T;
+        eq += ok && key[i] == T;
+    }
+    int tot;
+    const int before = block_exclusive_scan(gt | (eq << 16), scan, &tot);
+    int eq_before = before >> 16;
+    int pos = (before & 0xffff) + min(ties, eq_before);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        if (t0 + i >= us.C) break;
+        bool sel = key[i] > T;
+        if (key[i] == T) sel = eq_before++ < ties;
+        if (sel) {
+            if (pos < us.k_eff) out[pos] = t0 + i;                    // never past the budget
+            ++pos;
+        }
+    }
+}
+
 // TSP score: float sum over KV heads in head order (one selection per sequence).
 __global__ __launch_bounds__(256) void head_sum_kernel(const float *__restrict__ scores, int n_kv, int s_max,
                                                        float *__restrict__ out)
@@ -609,7 +751,6 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
                          const int32_t *unit_mask, const int32_t *k_per_unit, void *ws, const DeviceInfo &dev,
                          hipStream_t stream)
 {
-    (void)dev;
     const SelLayout L = sel_layout(batch, n_kv, s_max, n_keep, shared);
     char *w = (char *)ws;
     SelArgs a;
@@ -640,6 +781,23 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
     a.mask = shared ? nullptr : unit_mask;
     a.kpu = k_per_unit;
 
+    const long c_max = (long)s_max - n_keep;
+    if (c_max <= 32768 && units >= dev.cus / 2) {
+        // every unit's candidates fit one work-group's registers, and the units fill the chip
+        const bool vec = s_max % 4 == 0 && ((uintptr_t)a.scores & 15) == 0;
+        const dim3 g1(units), b1(kUnitThreads);
+        if (c_max <= 8192) {
+            if (vec) hipLaunchKernelGGL((sel_unit_kernel<4, true>), g1, b1, 0, stream, a);
+            else hipLaunchKernelGGL((sel_unit_kernel<4, false>), g1, b1, 0, stream, a);
+        } else if (c_max <= 16384) {
+            if (vec) hipLaunchKernelGGL((sel_unit_kernel<8, true>), g1, b1, 0, stream, a);
+            else hipLaunchKernelGGL((sel_unit_kernel<8, false>), g1, b1, 0, stream, a);
+        } else {
+            if (vec) hipLaunchKernelGGL((sel_unit_kernel<16, true>), g1, b1, 0, stream, a);
+            else hipLaunchKernelGGL((sel_unit_kernel<16, false>), g1, b1, 0, stream, a);
+        }
+        return hipGetLastError();
+    }
     const dim3 grid(L.n_chunks, units);
     hipLaunchKernelGGL(sel_level1_kernel, grid, dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(sel_level2_kernel, grid, dim3(kThreads), 0, stream, a);

@@ -195,6 +195,51 @@ def test_select_bitexact_continuous(s_max):
         _select_case(sc, sl, k, 32)
 
 
+@pytest.mark.parametrize("s_max", [3001, 4096, 16000, 32768])
+def test_select_many_units(s_max):
+    # 256 units (half the CUs of the chip or more): every unit's candidates go to one
+    # work-group when they fit (s_max - n_keep <= 32768); rows of a multiple of 4 floats
+    # and not, ties, ragged lengths, per-unit budgets and a unit mask
+    _say("select many units", s_max)
+    rng = np.random.default_rng(s_max + 1)
+    B, H = 32, 8
+    sc = rng.random((B, H, s_max)).astype(np.float32) ** 4
+    sc[::3] = (rng.integers(0, 60, (sc[::3].shape)) / 59.0).astype(np.float32)      # many exact ties
+    sc[1, 2] = 0.25                                                                   # all equal
+    sl = rng.integers(1, s_max + 1, B).astype(np.int32)
+    sl[0], sl[1], sl[2] = s_max, 0, 20
+    for k, n_keep in ((1, 0), (s_max // 16, 32), (s_max // 2, 8)):
+        _select_case(sc, sl, k, n_keep)
+    k, n_keep = s_max // 10, 32
+    ku = rng.integers(0, k + 1, (B, H)).astype(np.int32)
+    ku[0, 0], ku[3, 3] = k + 7, -1
+    sc_t = torch.from_numpy(sc).to(DEV)
+    idx, cnt = kvc.select_topk(sc_t, k, n_keep, seq_lens=sl, k_per_unit=torch.from_numpy(ku).to(DEV))
+    ri, rc = oracle.select_topk(sc, k, n_keep, seq_lens=sl, k_per_unit=ku)
+    assert np.array_equal(host(idx), ri) and np.array_equal(host(cnt), rc)
+    mask = torch.from_numpy(rng.integers(0, 2, (B, H)).astype(np.int32)).to(DEV)
+    idx2 = torch.full_like(idx, -5)
+    cnt2 = torch.full_like(cnt, -5)
+    kvc.select_topk(sc_t, k, n_keep, seq_lens=sl, k_per_unit=torch.from_numpy(ku).to(DEV), idx=idx2, count=cnt2,
+                    unit_mask=mask)
+    torch.cuda.synchronize()
+    on = mask.bool()
+    assert torch.equal(idx2[on], idx[on]) and torch.equal(cnt2[on], cnt[on])
+    assert bool((idx2[~on] == -5).all()) and bool((cnt2[~on] == -5).all())
+
+
+def test_select_shared_heads_many_sequences():
+    # one selection per sequence for 128 sequences (the head-summed scores take the
+    # one-work-group-per-unit kernel)
+    _say("select shared many")
+    rng = np.random.default_rng(21)
+    B, H, s_max = 128, 4, 5000
+    sc = rng.random((B, H, s_max)).astype(np.float32) * 1e-3
+    sc[5] = 1e-3
+    sl = rng.integers(0, s_max + 1, B).astype(np.int32)
+    _select_case(sc, sl, 1000, 32, shared=True)
+
+
 def test_select_shared_heads_and_degenerate():
     _say("select shared")
     rng = np.random.default_rng(5)
