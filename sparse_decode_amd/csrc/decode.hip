@@ -104,10 +104,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
     const int heads = min(RH, r - hc * RH);  // query heads of this chunk
 
     // ---- phase 1: this split.  Its first rows are requested before the count is
-    // known (rows below cap are in bounds) and zeroed past the count once it arrives,
-    // so count, rows and queries share one round trip.
+    // known and zeroed past the count once it arrives, so count, rows and queries
+    // share one round trip.  Every load is unconditional (row indices clamped below
+    // cap, head indices to the chunk's last head) and out-of-range values are dropped
+    // afterwards: a load under a branch would be waited for inside it.
     const int s0 = split * a.split_tokens;
-    const int s1c = min(s0 + a.split_tokens, a.cap);
     constexpr int step = G;                 // token rows per work-group step
     const u32x4 *krow = (const u32x4 *)a.kc + (size_t)unit * a.cap * VPR + li;
     const u32x4 *vrow = (const u32x4 *)a.vc + (size_t)unit * a.cap * VPR + li;
@@ -115,27 +116,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
     int t = s0 + grp;
 #pragma unroll
     for (int q = 0; q < kUnroll; ++q) {
-        const int tq = t + q * step;
-        kv[q] = tq < s1c ? ld_stream(krow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
-        vv[q] = tq < s1c ? ld_stream(vrow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
+        const int tq = min(t + q * step, a.cap - 1);
+        kv[q] = ld_stream(krow + (size_t)tq * VPR);
+        vv[q] = ld_stream(vrow + (size_t)tq * VPR);
     }
     int n = a.count[unit];
+    // queries of this chunk of the group
+    const int h_first = g * r + hc * RH;
+    u32x4 qv[RH];
+#pragma unroll
+    for (int j = 0; j < RH; ++j) qv[j] = *((const u32x4 *)a.q + ((size_t)(b * a.n_h + h_first + min(j, heads - 1))) * VPR + li);
+    // the rows count as used here, unconditionally: otherwise the compiler moves their
+    // loads under the branch on the count below, a round trip later
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) asm volatile("" ::"v"(kv[q]), "v"(vv[q]));
     n = n < 0 ? 0 : (n > a.cap ? a.cap : n);
     const int s1 = min(s0 + a.split_tokens, n);
-    // queries of this chunk of the group, pre-scaled into log2 units
+    // pre-scaled into log2 units; heads past the chunk's end are zero
     float qf[RH][E];
-    const int h_first = g * r + hc * RH;
 #pragma unroll
     for (int j = 0; j < RH; ++j) {
-        if (j < heads) {
-            const u32x4 v = *((const u32x4 *)a.q + ((size_t)(b * a.n_h + h_first + j)) * VPR + li);
-            RV::unpack(v, qf[j]);
+        RV::unpack(qv[j], qf[j]);
 #pragma unroll
-            for (int e = 0; e < E; ++e) qf[j][e] *= a.c;
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) qf[j][e] = 0.f;
-        }
+        for (int e = 0; e < E; ++e) qf[j][e] = j < heads ? qf[j][e] * a.c : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < kUnroll; ++q) {
@@ -160,9 +163,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
         if (tn < s1) {                       // next rows, requested before this batch is used
 #pragma unroll
             for (int q = 0; q < kUnroll; ++q) {
-                const int tq = tn + q * step;
-                kn[q] = tq < s1 ? ld_stream(krow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
-                vn[q] = tq < s1 ? ld_stream(vrow + (size_t)tq * VPR) : u32x4{0u, 0u, 0u, 0u};
+                const int tq = min(tn + q * step, a.cap - 1);   // rows past s1 are masked below
+                kn[q] = ld_stream(krow + (size_t)tq * VPR);
+                vn[q] = ld_stream(vrow + (size_t)tq * VPR);
             }
         }
         float x[kUnroll][RH];
@@ -210,9 +213,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
         }
         if (tn < s1) {
 #pragma unroll
-            for (int q = 0; q < kUnroll; ++q) {
-                kv[q] = kn[q];
-                vv[q] = vn[q];
+            for (int q = 0; q < kUnroll; ++q) {       // rows past the count may hold any bits
+                const bool in = tn + q * step < s1;
+                kv[q] = in ? kn[q] : u32x4{0u, 0u, 0u, 0u};
+                vv[q] = in ? vn[q] : u32x4{0u, 0u, 0u, 0u};
             }
         }
     }
