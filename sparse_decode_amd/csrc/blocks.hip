@@ -38,8 +38,8 @@ __global__ __launch_bounds__(kBlkThreads) void block_landmarks_kernel(const u32x
                                                                       int n_blk, float *__restrict__ landmarks)
 {
     constexpr int E = BF16 ? 8 : 4;                 // elements per vector
-    const long gid = (long)blockIdx.x * kBlkThreads + threadIdx.x;
-    const int u = blockIdx.y;
+    const long gid = (long)kvc_bid_x() * kBlkThreads + kvc_tid();
+    const int u = kvc_bid_y();
     if (gid >= (long)n_blk * vpr) return;
     const int j = (int)(gid / vpr), c = (int)(gid - (long)j * vpr);
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
@@ -69,10 +69,10 @@ __global__ __launch_bounds__(kBlkThreads) void block_scores_kernel(const void *_
                                                                    int32_t *__restrict__ cand)
 {
     extern __shared__ double qs[];                  // the group's queries [r][d_h]
-    const int u = blockIdx.y;
+    const int u = kvc_bid_y();
     const int b = u / n_kv, g = u - b * n_kv;
     const int r = n_h / n_kv;
-    for (int x = threadIdx.x; x < r * d_h; x += kBlkThreads) {
+    for (int x = kvc_tid(); x < r * d_h; x += kBlkThreads) {
         const size_t off = ((size_t)b * n_h + g * r) * d_h + x;
         qs[x] = BF16 ? (double)bf16_to_f32(((const uint16_t *)q)[off]) : (double)((const float *)q)[off];
     }
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kBlkThreads) void block_scores_kernel(const void *_
     const int S = clamp_len(seq_lens, b, s_max);
     const int C = S - n_keep > 0 ? S - n_keep : 0;
     const int nc = C / block;
-    const int j = blockIdx.x * kBlkThreads + threadIdx.x;
+    const int j = kvc_bid_x() * kBlkThreads + kvc_tid();
     if (g == 0 && j == 0) cand[b] = nc;
     if (j >= n_blk) return;
     double s = 0.0;
@@ -109,8 +109,8 @@ __global__ __launch_bounds__(kBlkThreads) void expand_blocks_kernel(const int32_
                                                                     int cap, int32_t *__restrict__ idx,
                                                                     int32_t *__restrict__ count)
 {
-    const int u = blockIdx.y;
-    const int p = blockIdx.x * kBlkThreads + threadIdx.x;
+    const int u = kvc_bid_y();
+    const int p = kvc_bid_x() * kBlkThreads + kvc_tid();
     const int S = clamp_len(seq_lens, u / H, s_max);
     const int C = S - n_keep > 0 ? S - n_keep : 0;
     const int tail0 = (C / block) * block;

@@ -89,12 +89,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
     __shared__ float sm_w[G][RH];
     __shared__ float sm_M[RH];
 
-    const int split = blockIdx.x;
-    const int unit = blockIdx.y;            // b * n_kv + g
-    const int hc = blockIdx.z;
+    const int split = kvc_bid_x();
+    const int unit = kvc_bid_y();            // b * n_kv + g
+    const int hc = kvc_bid_z();
     const int b = unit / a.n_kv;
     const int g = unit - b * a.n_kv;
-    const int tid = threadIdx.x;
+    const int tid = kvc_tid();
     const int lane = tid & (kWave - 1);
     const int wv = tid >> 6;
     const int li = lane % LPT;
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
         kv[q] = ld_stream(krow + (size_t)tq * VPR);
         vv[q] = ld_stream(vrow + (size_t)tq * VPR);
     }
-    int n = a.count[unit];
+    int n = ld_uniform(a.count, unit);
     // queries of this chunk of the group
     const int h_first = g * r + hc * RH;
     u32x4 qv[RH];
@@ -262,7 +262,7 @@ __device__ __forceinline__ float block_max(float v, float *red)
 {
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, shfl_xor_f(v, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    if ((kvc_tid() & 63) == 0) red[kvc_tid() >> 6] = v;
     __syncthreads();
     float r = red[0];
     for (int i = 1; i < kMergeThreads / kWave; ++i) r = fmaxf(r, red[i]);
@@ -274,7 +274,7 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 {
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) v += shfl_xor_f(v, o);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    if ((kvc_tid() & 63) == 0) red[kvc_tid() >> 6] = v;
     __syncthreads();
     float r = red[0];
     for (int i = 1; i < kMergeThreads / kWave; ++i) r += red[i];
@@ -300,14 +300,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     __shared__ float sw[kMaxSplits];
     __shared__ float red[kMergeThreads / kWave];
     __shared__ float so[G][D];
-    const int bh = blockIdx.x;              // b * n_h + h
+    const int bh = kvc_bid_x();              // b * n_h + h
     const int b = bh / n_h;
     const int h = bh - b * n_h;
     const int g = h / r;
     const int hl = h - g * r;
     const size_t base = ((size_t)(b * n_kv + g) * r + hl) * n_splits;
-    const int d = threadIdx.x % D;
-    const int grp = threadIdx.x / D;
+    const int d = kvc_tid() % D;
+    const int grp = kvc_tid() / D;
     float v[kMergeBatch];
 #pragma unroll
     for (int q = 0; q < kMergeBatch; ++q) {
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     float2 ml[MLPT];
 #pragma unroll
     for (int i = 0; i < MLPT; ++i) {
-        const int s = (int)threadIdx.x + i * kMergeThreads;
+        const int s = (int)kvc_tid() + i * kMergeThreads;
         ml[i] = s < n_splits ? part_ml[base + s] : make_float2(-INFINITY, 0.f);
     }
     float mloc = -INFINITY;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     float lloc = 0.f;
 #pragma unroll
     for (int i = 0; i < MLPT; ++i) {
-        const int s = (int)threadIdx.x + i * kMergeThreads;
+        const int s = (int)kvc_tid() + i * kMergeThreads;
         const float wgt = (M == -INFINITY || ml[i].x == -INFINITY) ? 0.f : fast_exp2(ml[i].x - M);
         if (s < n_splits) sw[s] = wgt;
         lloc += wgt * ml[i].y;

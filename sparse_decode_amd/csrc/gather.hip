@@ -16,8 +16,8 @@ constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 8;
 constexpr int kMaxBlockRows = 4096;     // rows per work-group (their indices sit in LDS)
 
-// Work-group (blockIdx.x, blockIdx.y) copies rows [blockIdx.x * rows_per_block, ...)
-// of unit blockIdx.y = b * heads + h.  The block's source rows are resolved once
+// Work-group (kvc_bid_x(), kvc_bid_y()) copies rows [kvc_bid_x() * rows_per_block, ...)
+// of unit kvc_bid_y() = b * heads + h.  The block's source rows are resolved once
 // into LDS (one dependent round trip), then every thread keeps kGatherUnroll rows
 // of 16-byte loads (times two with src1) in flight.  tpr threads share one row (a
 // power of two <= 256); a row wider than 256 vectors is walked in strides of 256.
@@ -29,19 +29,19 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     int32_t *__restrict__ pos_out, const int32_t *__restrict__ mask)
 {
     __shared__ int rows[kMaxBlockRows];
-    const int unit = blockIdx.y;
+    const int unit = kvc_bid_y();
     const int b = unit / heads;
     const int h = unit - b * heads;
     const int list = b * idx_heads + (idx_heads == 1 ? 0 : h);
-    if (mask && !mask[list]) return;
-    const int r0 = blockIdx.x * rows_per_block;
+    if (mask && !ld_uniform(mask, list)) return;
+    const int r0 = kvc_bid_x() * rows_per_block;
     const int r1 = min(r0 + rows_per_block, cap);
     const int32_t *lidx = idx + (size_t)list * cap;
     int n = count[list];
     n = n < 0 ? 0 : (n > cap ? cap : n);
 
     // source row of every output row of the block, -1 where nothing is copied
-    for (int j = r0 + (int)threadIdx.x; j < r1; j += kGatherThreads) {
+    for (int j = r0 + (int)kvc_tid(); j < r1; j += kGatherThreads) {
         const int t = lidx[j];
         const bool ok = j < n && t >= 0 && t < s_max;
         rows[j - r0] = ok ? t : -1;
@@ -51,8 +51,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
 
     const int tpr = 1 << tpr_log2;
     const int rows_per_iter = kGatherThreads >> tpr_log2;
-    const int sub = threadIdx.x >> tpr_log2;
-    const int col0 = threadIdx.x & (tpr - 1);
+    const int sub = kvc_tid() >> tpr_log2;
+    const int col0 = kvc_tid() & (tpr - 1);
     const size_t src_unit = (size_t)unit * s_max * vpr;
     const size_t dst_unit = (size_t)unit * cap * vpr;
     const int m = min(r1, n) - r0;                       // rows of this block that are copied

@@ -7,6 +7,16 @@
 
 namespace kvc {
 
+// Work-item and work-group indices read from the hardware registers.  The kernels are
+// built with IEEE mode off and the device library's index functions with it on, so
+// the library's versions are not inlined: every kernel would call out for them and
+// get per-lane results back, hiding that a work-group index is uniform.
+__device__ __forceinline__ unsigned kvc_tid() { return __builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ unsigned kvc_bid_x() { return __builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ unsigned kvc_bid_y() { return __builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ unsigned kvc_bid_z() { return __builtin_amdgcn_workgroup_id_z(); }
+__device__ __forceinline__ unsigned kvc_bdim_x() { return __builtin_amdgcn_workgroup_size_x(); }
+
 constexpr int kWave = 64;
 
 // Native 16-byte vector (HIP's uint4 is a struct; clang builtins want a vector type).
@@ -58,16 +68,26 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
+// p[i] for a wave-uniform i, through the scalar data cache (the constant address
+// space): for arrays that no work-group of the running kernel writes (lengths, masks,
+// budgets, counts from an earlier kernel), so the load takes no vector memory round
+// trip ahead of the kernel's streaming loads.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T *p, int i)
+{
+    return ((const __attribute__((address_space(4))) T *)p)[i];
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t *seq_lens, int b, int s_max)
 {
-    int s = seq_lens ? seq_lens[b] : s_max;
+    int s = seq_lens ? ld_uniform(seq_lens, b) : s_max;
     return s < 0 ? 0 : (s > s_max ? s_max : s);
 }
 
 // Inclusive prefix sum across one 64-lane wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v)
 {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = kvc_tid() & (kWave - 1);
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
         int u = __shfl_up(v, o, kWave);
@@ -76,16 +96,16 @@ __device__ __forceinline__ int wave_inclusive_scan(int v)
     return v;
 }
 
-// Exclusive prefix sum across the work-group (blockDim.x a multiple of 64, at most
+// Exclusive prefix sum across the work-group (kvc_bdim_x() a multiple of 64, at most
 // 1024).  `scratch` holds at least 16 ints of LDS.  Returns the exclusive prefix and
 // writes the group total to *total.  Every wave adds the wave totals it needs itself
 // (broadcast LDS reads), so there is no serial pass.  Contains barriers: call from
 // every thread.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *total)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
+    const int lane = kvc_tid() & (kWave - 1);
+    const int wid = kvc_tid() >> 6;
+    const int nw = kvc_bdim_x() >> 6;
     const int inc = wave_inclusive_scan(v);
     if (lane == kWave - 1) scratch[wid] = inc;
     __syncthreads();

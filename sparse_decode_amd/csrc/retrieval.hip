@@ -35,10 +35,10 @@ __global__ __launch_bounds__(kWave) void similarity_kernel(const void *__restric
                                                            int32_t *__restrict__ refresh, int32_t *__restrict__ keep)
 {
     constexpr int EPL = D / kWave;          // elements per lane
-    const int g = blockIdx.x;
-    const int b = blockIdx.y;
+    const int g = kvc_bid_x();
+    const int b = kvc_bid_y();
     const int r = n_h / n_kv;
-    const int lane = threadIdx.x;
+    const int lane = kvc_tid();
     int drifted = 0;
     for (int j = 0; j < r; ++j) {
         const int h = g * r + j;

@@ -71,21 +71,21 @@ __global__ __launch_bounds__(kGenThreads) void gen_logits_kernel(
     float *__restrict__ logits)
 {
     __shared__ float qs[kGenRowsLds][D];
-    const int u = unit0 + blockIdx.y;
-    if (mask && !mask[u]) return;
+    const int u = unit0 + kvc_bid_y();
+    if (mask && !ld_uniform(mask, u)) return;
     const int b = u / n_kv;
     const int g = u - b * n_kv;
     const int r = n_h / n_kv;
     const int S = clamp_len(seq_lens, b, s_max);
-    const int t = blockIdx.x * kGenThreads + threadIdx.x;
+    const int t = kvc_bid_x() * kGenThreads + kvc_tid();
     float kr[D];
     if (t < S) load_row_f32<BF16, D>(k, (size_t)u * s_max + t, kr);
     const size_t qrow0 = (size_t)(b * n_h + g * r) * w;     // the R rows are contiguous
-    float *lg = logits + (size_t)blockIdx.y * R * s_max;
+    float *lg = logits + (size_t)kvc_bid_y() * R * s_max;
     for (int r0 = 0; r0 < R; r0 += kGenRowsLds) {
         const int nr = min(kGenRowsLds, R - r0);
         __syncthreads();
-        for (int x = threadIdx.x; x < nr * D; x += kGenThreads) {
+        for (int x = kvc_tid(); x < nr * D; x += kGenThreads) {
             const int rr = x / D, d = x - rr * D;
             const size_t off = (qrow0 + r0 + rr) * D + d;
             qs[rr][d] = BF16 ? bf16_to_f32(((const uint16_t *)q_win)[off]) : ((const float *)q_win)[off];
@@ -114,32 +114,32 @@ __global__ __launch_bounds__(kGenThreads) void gen_rowstats_kernel(const float *
                                                                    int R, const int32_t *__restrict__ mask,
                                                                    float2 *__restrict__ fin)
 {
-    if (mask && !mask[blockIdx.y]) return;
+    if (mask && !ld_uniform(mask, kvc_bid_y())) return;
     __shared__ float red_m[kGenThreads / kWave];
     __shared__ double red_l[kGenThreads / kWave];
-    const int row = blockIdx.x;
-    const int ul = blockIdx.y;
+    const int row = kvc_bid_x();
+    const int ul = kvc_bid_y();
     const float *lg = logits + ((size_t)ul * R + row) * s_max;
     float m = -INFINITY;
-    for (int t = threadIdx.x; t < s_max; t += kGenThreads) m = fmaxf(m, lg[t]);
+    for (int t = kvc_tid(); t < s_max; t += kGenThreads) m = fmaxf(m, lg[t]);
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
-    if ((threadIdx.x & 63) == 0) red_m[threadIdx.x >> 6] = m;
+    if ((kvc_tid() & 63) == 0) red_m[kvc_tid() >> 6] = m;
     __syncthreads();
     m = red_m[0];
     for (int i = 1; i < kGenThreads / kWave; ++i) m = fmaxf(m, red_m[i]);
     if (m == -INFINITY) {
-        if (threadIdx.x == 0) fin[(size_t)ul * R + row] = make_float2(0.f, 0.f);
+        if (kvc_tid() == 0) fin[(size_t)ul * R + row] = make_float2(0.f, 0.f);
         return;
     }
     const float nmc = -m * kLog2e;
     double sd = 0.0;
-    for (int t = threadIdx.x; t < s_max; t += kGenThreads) sd += (double)fast_exp2(fmaf(lg[t], kLog2e, nmc));
+    for (int t = kvc_tid(); t < s_max; t += kGenThreads) sd += (double)fast_exp2(fmaf(lg[t], kLog2e, nmc));
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) sd += __shfl_xor(sd, o, kWave);
-    if ((threadIdx.x & 63) == 0) red_l[threadIdx.x >> 6] = sd;
+    if ((kvc_tid() & 63) == 0) red_l[kvc_tid() >> 6] = sd;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (kvc_tid() == 0) {
         double L = 0.0;
         for (int i = 0; i < kGenThreads / kWave; ++i) L += red_l[i];
         fin[(size_t)ul * R + row] = make_float2(nmc, (float)(1.0 / L));
@@ -154,11 +154,11 @@ __global__ __launch_bounds__(kGenThreads) void gen_probsum_kernel(const float *_
                                                                   const int32_t *__restrict__ mask,
                                                                   float *__restrict__ raw)
 {
-    const int ul = blockIdx.y;
+    const int ul = kvc_bid_y();
     const int u = unit0 + ul;
-    if (mask && !mask[u]) return;
+    if (mask && !ld_uniform(mask, u)) return;
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
-    const int t = blockIdx.x * kGenThreads + threadIdx.x;
+    const int t = kvc_bid_x() * kGenThreads + kvc_tid();
     if (t >= s_max) return;
     float acc = 0.f;
     if (t < S) {
@@ -207,14 +207,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restr
     // 2 kMaxHalf + 2 slots (left halo, then 16-byte alignment), the body, the right halo
     __shared__ __attribute__((aligned(16))) float tile[2 * kMaxHalf + 2 + kPoolTile + kMaxHalf + 1];
     if constexpr (HALF >= 0) half = HALF;
-    const int u = blockIdx.y;
-    if (mask && !mask[u]) return;
+    const int u = kvc_bid_y();
+    if (mask && !ld_uniform(mask, u)) return;
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
     const int C = S - n_keep > 0 ? S - n_keep : 0;
-    const int t0 = blockIdx.x * kPoolTile;
+    const int t0 = kvc_bid_x() * kPoolTile;
     const float *rw = raw + (size_t)u * s_max;
     float *out = pooled + (size_t)u * s_max;
-    const int tid = threadIdx.x;
+    const int tid = kvc_tid();
     const int base = t0 - (2 * kMaxHalf + 2);               // tile[i] holds raw[base + i]
     float *body = tile + 2 * kMaxHalf + 2;                  // 16-byte aligned: 64 floats in
     const int t = t0 + 4 * tid;                             // this thread's 4 tokens
@@ -363,7 +363,7 @@ struct Sc {
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int gid = i * kMfThreads + threadIdx.x;
+            const int gid = i * kMfThreads + kvc_tid();
             const int row = gid / VPR, col = gid - row * VPR;
             reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                 rsrc, (st0 + row) * (2 * D) + col * 16, 0, KEEP ? 0 : kAuxNt));
@@ -374,7 +374,7 @@ struct Sc {
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int gid = i * kMfThreads + threadIdx.x;
+            const int gid = i * kMfThreads + kvc_tid();
             const int row = gid / VPR, col = gid - row * VPR;
             *(u32x4 *)(buf + row * ROWB + col * 16) = reg[i];
         }
@@ -528,14 +528,14 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     __shared__ float sm_m[C::TG][RT * 16];
     __shared__ float sm_l[C::TG][RT * 16];
 
-    const int chunk = blockIdx.x;
-    const int ul = blockIdx.y;
+    const int chunk = kvc_bid_x();
+    const int ul = kvc_bid_y();
     const int u = a.unit0 + ul;
-    if (a.mask && !a.mask[u]) return;
+    if (a.mask && !ld_uniform(a.mask, u)) return;
     const int b = u / a.n_kv;
     const int g = u - b * a.n_kv;
     const int S = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, b, a.s_max));   // uniform: scalar offsets below
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = kvc_tid() & 63, wv = kvc_tid() >> 6;
     const int n = lane & 15, kg = lane >> 4;
     const int wr = wv % C::WPR, tg = wv / C::WPR;
     const __amdgpu_buffer_rsrc_t kunit = buffer_rsrc(a.k + (size_t)u * a.s_max * D, S * (2 * D));
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         }
     }
     __syncthreads();
-    for (int row = threadIdx.x; row < RT * 16; row += kMfThreads) {
+    for (int row = kvc_tid(); row < RT * 16; row += kMfThreads) {
         float Mx = -INFINITY;
         for (int t2 = 0; t2 < C::TG; ++t2) Mx = fmaxf(Mx, sm_m[t2][row]);
         float L = 0.f;
@@ -610,11 +610,11 @@ __global__ __launch_bounds__(kMergeThreads) void mfma_merge_kernel(const float2 
 {
     __shared__ float sm_M[kMergeThreads];
     __shared__ double sm_L[kMergeThreads];
-    const int ul = blockIdx.x;
-    if (mask && !mask[ul]) return;
+    const int ul = kvc_bid_x();
+    if (mask && !ld_uniform(mask, ul)) return;
     const int slices = kMergeThreads / rpad;
-    const int row = threadIdx.x % rpad;
-    const int slice = threadIdx.x / rpad;
+    const int row = kvc_tid() % rpad;
+    const int slice = kvc_tid() / rpad;
     const float2 *p = part + (size_t)ul * n_chunks * rpad + row;
     float Mx = -INFINITY;
     double L = 0.0;
@@ -636,8 +636,8 @@ __global__ __launch_bounds__(kMergeThreads) void mfma_merge_kernel(const float2 
             }
         }
     }
-    sm_M[threadIdx.x] = Mx;
-    sm_L[threadIdx.x] = L;
+    sm_M[kvc_tid()] = Mx;
+    sm_L[kvc_tid()] = L;
     __syncthreads();
     if (slice != 0) return;
     float Mt = -INFINITY;
@@ -703,14 +703,14 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     float *rawbuf = (float *)(lds + C::LDS_BYTES);       // the chunk's scores, written once at the end
     __shared__ float red[2][C::WPR * C::ST];
 
-    const int chunk = blockIdx.x;
-    const int ul = blockIdx.y;
+    const int chunk = kvc_bid_x();
+    const int ul = kvc_bid_y();
     const int u = a.unit0 + ul;
-    if (a.mask && !a.mask[u]) return;
+    if (a.mask && !ld_uniform(a.mask, u)) return;
     const int b = u / a.n_kv;
     const int g = u - b * a.n_kv;
     const int S = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, b, a.s_max));   // uniform: scalar offsets below
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = kvc_tid() & 63, wv = kvc_tid() >> 6;
     const int n = lane & 15, kg = lane >> 4;
     const int wr = wv % C::WPR, tg = wv / C::WPR;
     const __amdgpu_buffer_rsrc_t kunit = buffer_rsrc(a.k + (size_t)u * a.s_max * D, S * (2 * D));
@@ -751,7 +751,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
             // add the row slices of this stage in order; red[st & 1] is rewritten two
             // steps later
             const float *rd = red[st & 1];
-            for (int t = threadIdx.x; t < C::ST; t += kMfThreads) {
+            for (int t = kvc_tid(); t < C::ST; t += kMfThreads) {
                 float v = 0.f;
                 for (int r2 = 0; r2 < C::WPR; ++r2) v += rd[r2 * C::ST + t];
                 rawbuf[st * C::ST + t] = v;
@@ -759,7 +759,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         });
     __syncthreads();
     // the chunk's scores, 0 past the cached length
-    for (int t = threadIdx.x; ch0 + t < ch1; t += kMfThreads) {
+    for (int t = kvc_tid(); ch0 + t < ch1; t += kMfThreads) {
         const int tok = ch0 + t;
         rawu[tok] = (tok < S && t < n_st * C::ST) ? rawbuf[t] : 0.f;
     }
@@ -779,13 +779,13 @@ __global__ __launch_bounds__(kLogitThreads) void logit_probsum_kernel(const floa
                                                                       float *__restrict__ raw)
 {
     __shared__ float2 f[16];
-    const int ul = blockIdx.y;
+    const int ul = kvc_bid_y();
     const int u = unit0 + ul;
-    if (mask && !mask[u]) return;
-    if (threadIdx.x < 16) f[threadIdx.x] = threadIdx.x < R ? fin[(size_t)ul * rpad + threadIdx.x] : make_float2(0.f, 0.f);
+    if (mask && !ld_uniform(mask, u)) return;
+    if (kvc_tid() < 16) f[kvc_tid()] = kvc_tid() < R ? fin[(size_t)ul * rpad + kvc_tid()] : make_float2(0.f, 0.f);
     __syncthreads();
     const int S = clamp_len(seq_lens, u / n_kv, s_max);
-    const int t = blockIdx.x * kLogitThreads + threadIdx.x;
+    const int t = kvc_bid_x() * kLogitThreads + kvc_tid();
     if (t >= s_max) return;
     float acc = 0.f;
     if (t < S) {

@@ -84,7 +84,7 @@ struct SelArgs {
 __device__ __forceinline__ int unit_budget(const SelArgs &a, int u)
 {
     if (!a.kpu) return a.k;
-    const int v = a.kpu[u];
+    const int v = ld_uniform(a.kpu, u);
     return v < 0 ? 0 : (v > a.k ? a.k : v);
 }
 
@@ -93,7 +93,7 @@ __device__ __forceinline__ int unit_budget(const SelArgs &a, int u)
 // a bin); the others add into their own histogram copy.
 __device__ __forceinline__ void hist_add(int *h_copy, int *h_lead, int bin)
 {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = kvc_tid() & (kWave - 1);
     const int lead = __builtin_amdgcn_readfirstlane(bin);
     const unsigned long long act = __ballot(1);
     const unsigned long long m = __ballot(bin == lead);
@@ -106,7 +106,7 @@ __device__ __forceinline__ void hist_add(int *h_copy, int *h_lead, int bin)
 
 __device__ __forceinline__ void lds_clear(int (*h)[kB1])
 {
-    for (int i = threadIdx.x; i < kCopies * kB1 / 4; i += kThreads)
+    for (int i = kvc_tid(); i < kCopies * kB1 / 4; i += kThreads)
         reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
 }
 
@@ -114,7 +114,7 @@ __device__ __forceinline__ void lds_clear(int (*h)[kB1])
 template <int NB>
 __device__ __forceinline__ void flush_hist(int (*h)[kB1], int32_t *g)
 {
-    for (int b = threadIdx.x; b < NB; b += kThreads) {
+    for (int b = kvc_tid(); b < NB; b += kThreads) {
         int s = 0;
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) s += h[c][b];
@@ -132,7 +132,7 @@ template <int NB>
 __device__ __forceinline__ void load_bins(const int32_t *__restrict__ g, int (&c)[NB / kThreads])
 {
     constexpr int per = NB / kThreads;
-    const int top = NB - 1 - (int)threadIdx.x * per;
+    const int top = NB - 1 - (int)kvc_tid() * per;
     const int4 *g4 = reinterpret_cast<const int4 *>(g + top - per + 1);
 #pragma unroll
     for (int v = 0; v < per / 4; ++v) {
@@ -150,7 +150,7 @@ template <int NB>
 __device__ __forceinline__ Digit find_digit(const int (&c)[NB / kThreads], int k_rem, int *scan, Digit *out)
 {
     constexpr int per = NB / kThreads;
-    const int top = NB - 1 - (int)threadIdx.x * per;
+    const int top = NB - 1 - (int)kvc_tid() * per;
     int cnt = 0;
 #pragma unroll
     for (int p = 0; p < per; ++p) cnt += c[p];
@@ -182,7 +182,7 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ sc, int t0,
     float v[kKeysPerThread];
 #pragma unroll
     for (int q = 0; q < kKeysPerThread; ++q) {
-        const int t = t0 + (int)threadIdx.x + q * kThreads;
+        const int t = t0 + (int)kvc_tid() + q * kThreads;
         v[q] = t < t1 ? sc[t] : 0.f;
     }
 #pragma unroll
@@ -191,24 +191,24 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ sc, int t0,
 
 __device__ __forceinline__ bool chunk_valid(const ChunkKeys &ck, int q)
 {
-    return ck.t0 + (int)threadIdx.x + q * kThreads < ck.t1;
+    return ck.t0 + (int)kvc_tid() + q * kThreads < ck.t1;
 }
 
 // ------------------------------------------------------------------------------ kernels
 // The work-group's unit and chunk; false when the chunk has nothing to histogram.
 __device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t0, int &t1)
 {
-    us = unit_shape(a.seq_lens, (int)blockIdx.y / a.H, a.s_max, unit_budget(a, blockIdx.y), a.n_keep);
-    t0 = (int)blockIdx.x * kChunk;
+    us = unit_shape(a.seq_lens, (int)kvc_bid_y() / a.H, a.s_max, unit_budget(a, kvc_bid_y()), a.n_keep);
+    t0 = (int)kvc_bid_x() * kChunk;
     t1 = min(us.C, t0 + kChunk);
-    if (a.mask && !a.mask[blockIdx.y]) return false;
+    if (a.mask && !ld_uniform(a.mask, kvc_bid_y())) return false;
     return us.k_eff > 0 && us.k_eff < us.C && t0 < us.C;
 }
 
 __global__ __launch_bounds__(kThreads) void sel_level1_kernel(SelArgs a)
 {
     __shared__ int h[kCopies][kB1];
-    const int u = blockIdx.y;
+    const int u = kvc_bid_y();
     UnitShape us;
     int t0, t1;
     if (!chunk_of(a, us, t0, t1)) return;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void sel_level1_kernel(SelArgs a)
     load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
     lds_clear(h);
     __syncthreads();
-    int *hc = h[threadIdx.x & (kCopies - 1)];
+    int *hc = h[kvc_tid() & (kCopies - 1)];
 #pragma unroll
     for (int q = 0; q < kKeysPerThread; ++q)
         if (chunk_valid(ck, q)) hist_add(hc, h[0], (int)(ck.key[q] >> 21));
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void sel_level2_kernel(SelArgs a)
     __shared__ int h[kCopies][kB1];
     __shared__ int scan[16];
     __shared__ Digit dg;
-    const int u = blockIdx.y;
+    const int u = kvc_bid_y();
     UnitShape us;
     int t0, t1;
     if (!chunk_of(a, us, t0, t1)) return;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void sel_level2_kernel(SelArgs a)
     load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
     lds_clear(h);
     const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
-    int *hc = h[threadIdx.x & (kCopies - 1)];
+    int *hc = h[kvc_tid() & (kCopies - 1)];
 #pragma unroll
     for (int q = 0; q < kKeysPerThread; ++q)
         if (chunk_valid(ck, q) && (int)(ck.key[q] >> 21) == d1.digit)
@@ -255,12 +255,12 @@ __global__ __launch_bounds__(kThreads) void sel_level3_kernel(SelArgs a)
     __shared__ int scan[16];
     __shared__ int wave_above[kWaves];
     __shared__ Digit dg;
-    const int u = blockIdx.y;
-    const int j = blockIdx.x;
+    const int u = kvc_bid_y();
+    const int j = kvc_bid_x();
     UnitShape us;
     int t0, t1;
     if (!chunk_of(a, us, t0, t1)) return;
-    const int tid = threadIdx.x;
+    const int tid = kvc_tid();
     const int lane = tid & (kWave - 1);
     const int32_t *H = a.hist + (size_t)u * kHistInts;
     int c1[kB1 / kThreads], c2[kB2 / kThreads];
@@ -320,12 +320,12 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     __shared__ Digit dg;
     __shared__ int wave_gt[kWaves], wave_eq[kWaves];
     __shared__ int chunk_take, is_last;
-    const int u = blockIdx.y;
-    const int j = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int u = kvc_bid_y();
+    const int j = kvc_bid_x();
+    const int tid = kvc_tid();
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
-    if (a.mask && !a.mask[u]) return;
+    if (a.mask && !ld_uniform(a.mask, u)) return;
     const UnitShape us = unit_shape(a.seq_lens, u / a.H, a.s_max, unit_budget(a, u), a.n_keep);
     int32_t *out = a.idx + (size_t)u * a.cap;
     if (j == 0) {
@@ -468,7 +468,7 @@ template <int NB>
 __device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan, Digit *out)
 {
     constexpr int per = NB / kUnitThreads;
-    const int top = NB - 1 - (int)threadIdx.x * per;
+    const int top = NB - 1 - (int)kvc_tid() * per;
     int c[per], cnt = 0;
 #pragma unroll
     for (int p = 0; p < per; ++p) {
@@ -488,7 +488,7 @@ __device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan,
     __syncthreads();
     const Digit d = *out;
     // the histogram is free again: clear it for the next level
-    for (int i = threadIdx.x; i < kCopies * kB1 / 4; i += kUnitThreads)
+    for (int i = kvc_tid(); i < kCopies * kB1 / 4; i += kUnitThreads)
         reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
     __syncthreads();
     return d;
@@ -503,9 +503,9 @@ __global__ __launch_bounds__(kUnitThreads) void sel_unit_kernel(SelArgs a)
     __shared__ int h[kCopies][kB1];
     __shared__ int scan[16];
     __shared__ Digit dg;
-    const int u = blockIdx.x;
-    const int tid = threadIdx.x;
-    if (a.mask && !a.mask[u]) return;
+    const int u = kvc_bid_x();
+    const int tid = kvc_tid();
+    if (a.mask && !ld_uniform(a.mask, u)) return;
     const UnitShape us = unit_shape(a.seq_lens, u / a.H, a.s_max, unit_budget(a, u), a.n_keep);
     int32_t *out = a.idx + (size_t)u * a.cap;
     // the always-kept trailing tokens, the -1 padding and the count
@@ -598,8 +598,8 @@ __global__ __launch_bounds__(kUnitThreads) void sel_unit_kernel(SelArgs a)
 __global__ __launch_bounds__(256) void head_sum_kernel(const float *__restrict__ scores, int n_kv, int s_max,
                                                        float *__restrict__ out)
 {
-    const int b = blockIdx.y;
-    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int b = kvc_bid_y();
+    const int t = kvc_bid_x() * 256 + kvc_tid();
     if (t >= s_max) return;
     const float *p = scores + (size_t)b * n_kv * s_max + t;
     float s = 0.f;
@@ -622,26 +622,26 @@ __global__ __launch_bounds__(kThreads) void core_scores_kernel(const float *__re
                                                                int32_t *__restrict__ chunk_core)
 {
     __shared__ int wave_n[kWaves];
-    const int u = blockIdx.y;
-    if (mask && !mask[u]) return;
+    const int u = kvc_bid_y();
+    if (mask && !ld_uniform(mask, u)) return;
     const int b = u / H;
     const int S = clamp_len(seq_lens, b, s_max);
     const int C = S - n_keep > 0 ? S - n_keep : 0;
-    const int t0 = blockIdx.x * kChunk;
+    const int t0 = kvc_bid_x() * kChunk;
     int n = 0;
-    for (int t = t0 + threadIdx.x; t < min(t0 + kChunk, s_max); t += kThreads) {
+    for (int t = t0 + kvc_tid(); t < min(t0 + kChunk, s_max); t += kThreads) {
         const bool c = t < C && core[(size_t)b * s_max + t] != 0;
         n += c;
         masked[(size_t)u * s_max + t] = c ? INFINITY : scores[(size_t)u * s_max + t];
     }
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) n += __shfl_xor(n, o, kWave);
-    if ((threadIdx.x & (kWave - 1)) == 0) wave_n[threadIdx.x >> 6] = n;
+    if ((kvc_tid() & (kWave - 1)) == 0) wave_n[kvc_tid() >> 6] = n;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (kvc_tid() == 0) {
         int tot = 0;
         for (int w = 0; w < kWaves; ++w) tot += wave_n[w];
-        chunk_core[(size_t)u * n_chunks + blockIdx.x] = tot;
+        chunk_core[(size_t)u * n_chunks + kvc_bid_x()] = tot;
     }
 }
 
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(256) void core_budget_kernel(const int32_t *__restr
                                                           int n_chunks, int k, int core_cap,
                                                           int32_t *__restrict__ budget)
 {
-    const int u = blockIdx.x * 256 + threadIdx.x;
+    const int u = kvc_bid_x() * 256 + kvc_tid();
     if (u >= units) return;
     int n = 0;
     for (int j = 0; j < n_chunks; ++j) n += chunk_core[(size_t)u * n_chunks + j];
