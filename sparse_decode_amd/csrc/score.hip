@@ -618,15 +618,17 @@ __global__ __launch_bounds__(kMergeThreads) void mfma_merge_kernel(const float2 
     const float2 *p = part + (size_t)ul * n_chunks * rpad + row;
     float Mx = -INFINITY;
     double L = 0.0;
-    for (int ch0 = slice; slice < slices && ch0 < n_chunks; ch0 += 8 * slices) {
-        float2 v[8];
+    constexpr int kBatch = 16;              // chunk partials requested together per thread
+    for (int ch0 = slice; slice < slices && ch0 < n_chunks; ch0 += kBatch * slices) {
+        float2 v[kBatch];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int ch = ch0 + q * slices;
-            v[q] = ch < n_chunks ? p[(size_t)ch * rpad] : make_float2(-INFINITY, 0.f);
+        for (int q = 0; q < kBatch; ++q) {
+            const int ch = min(ch0 + q * slices, n_chunks - 1);      // unconditional: one round trip
+            v[q] = p[(size_t)ch * rpad];
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < kBatch; ++q) {
+            if (ch0 + q * slices >= n_chunks) continue;
             if (v[q].x == -INFINITY) continue;
             if (v[q].x > Mx) {
                 L = L * (double)fast_exp2((Mx - v[q].x) * c) + (double)v[q].y;
