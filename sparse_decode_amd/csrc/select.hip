@@ -462,9 +462,10 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
 // the chunked kernels above.
 constexpr int kUnitThreads = 512;
 
-// Bin of the k_rem-th largest key of an LDS histogram (summed over its copies) and the
-// number of keys above that bin; thread i owns bins NB-1-i*per down to NB-per-i*per.
-template <int NB>
+// Bin of the k_rem-th largest key of an LDS histogram (summed over its first NC
+// copies) and the number of keys above that bin; thread i owns bins NB-1-i*per down to
+// NB-per-i*per.
+template <int NB, int NC>
 __device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan, Digit *out)
 {
     constexpr int per = NB / kUnitThreads;
@@ -474,7 +475,7 @@ __device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan,
     for (int p = 0; p < per; ++p) {
         int s = 0;
 #pragma unroll
-        for (int cc = 0; cc < kCopies; ++cc) s += h[cc][top - p];
+        for (int cc = 0; cc < NC; ++cc) s += h[cc][top - p];
         c[p] = s;
         cnt += s;
     }
@@ -487,9 +488,8 @@ __device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan,
     }
     __syncthreads();
     const Digit d = *out;
-    // the histogram is free again: clear it for the next level
-    for (int i = kvc_tid(); i < kCopies * kB1 / 4; i += kUnitThreads)
-        reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
+    // the histogram is free again: clear the copy the next levels use
+    for (int i = kvc_tid(); i < kB1 / 4; i += kUnitThreads) reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
     __syncthreads();
     return d;
 }
@@ -553,20 +553,21 @@ __global__ __launch_bounds__(kUnitThreads) void sel_unit_kernel(SelArgs a)
 #pragma unroll
     for (int i = 0; i < K; ++i) hist_add(hc, h[0], (int)(key[i] >> 21));
     __syncthreads();
-    const Digit d1 = unit_digit<kB1>(h, us.k_eff, scan, &dg);
-    // level 2: bits [10, 21) of the keys in bin d1
+    const Digit d1 = unit_digit<kB1, kCopies>(h, us.k_eff, scan, &dg);
+    // level 2: bits [10, 21) of the keys in bin d1.  Those spread over many bins, so
+    // plain LDS atomics into one copy beat the wave-level aggregation here.
 #pragma unroll
     for (int i = 0; i < K; ++i)
-        if ((int)(key[i] >> 21) == d1.digit) hist_add(hc, h[0], (int)((key[i] >> 10) & (kB2 - 1)));
+        if ((int)(key[i] >> 21) == d1.digit) atomicAdd(&h[0][(key[i] >> 10) & (kB2 - 1)], 1);
     __syncthreads();
-    const Digit d2 = unit_digit<kB2>(h, us.k_eff - d1.above, scan, &dg);
+    const Digit d2 = unit_digit<kB2, 1>(h, us.k_eff - d1.above, scan, &dg);
     // level 3: bits [0, 10) of the keys with prefix (d1, d2)
     const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
 #pragma unroll
     for (int i = 0; i < K; ++i)
-        if ((key[i] >> 10) == pre2) hist_add(hc, h[0], (int)(key[i] & (kB3 - 1)));
+        if ((key[i] >> 10) == pre2) atomicAdd(&h[0][key[i] & (kB3 - 1)], 1);
     __syncthreads();
-    const Digit d3 = unit_digit<kB3>(h, us.k_eff - d1.above - d2.above, scan, &dg);
+    const Digit d3 = unit_digit<kB3, 1>(h, us.k_eff - d1.above - d2.above, scan, &dg);
     const uint32_t T = (pre2 << 10) | (uint32_t)d3.digit;
     const int ties = us.k_eff - d1.above - d2.above - d3.above;     // keys == T to take, lowest index first
 
