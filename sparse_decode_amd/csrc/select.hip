@@ -9,8 +9,9 @@
 // the selected set is every key > T plus the lowest-indexed keys == T, written in
 // index order.  One work-group alone streams a unit's keys far below the chip's
 // bandwidth (a CU keeps only so many cache lines in flight), so every pass is spread
-// over the unit's chunks of 2048 keys (one work-group each, every key loaded once
-// into registers) and the levels meet through per-unit histograms in global memory:
+// over the unit's chunks of 2048 keys, or 8192 when the call has at least 1024 such
+// larger chunks (one work-group each, every key loaded once into registers), and the
+// levels meet through per-unit histograms in global memory:
 //
 //   level1  grid (chunks, units): histogram of the top 11 bits of the chunk's keys,
 //           added into the unit histogram H1
@@ -41,8 +42,12 @@ constexpr int kHistInts = kB1 + kB2 + kB3;
 constexpr int kSfx = kB3 + 4;       // suffix sums [0, kB3] of one chunk, padded
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk = 2048;        // candidates per work-group
-constexpr int kKeysPerThread = kChunk / kThreads;
+// Candidates per work-group of the chunked kernels: kThreads * KPT, KPT = 8 (2048) or,
+// when the call has many chunks anyway, 32 (8192): fewer work-groups, each reading the
+// unit histograms and scanning them once for four times as many keys.
+constexpr int kKptSmall = 8;
+constexpr int kKptLarge = 32;
+constexpr int kCoreChunk = 2048;    // tokens per work-group of the core-mask kernel
 constexpr int kCopies = 4;          // LDS histogram copies, picked by lane & 3
 
 __device__ __forceinline__ uint32_t order_key(float f)
@@ -167,37 +172,42 @@ __device__ __forceinline__ Digit find_digit(const int (&c)[NB / kThreads], int k
     return d;
 }
 
-// A chunk is kChunk consecutive candidates; thread i holds keys t0 + i + q * kThreads
-// (q < kKeysPerThread), loaded once.  Slots past the chunk's end hold key 0 and are
-// masked by `valid`.
+// A chunk is KPT * kThreads consecutive candidates; thread i holds keys
+// t0 + i + q * kThreads (q < KPT), loaded once.  Slots past the chunk's end hold key 0
+// and are masked by `valid`.
+template <int KPT>
 struct ChunkKeys {
-    uint32_t key[kKeysPerThread];
+    uint32_t key[KPT];
     int t0, t1;
 };
 
-__device__ __forceinline__ void load_chunk(const float *__restrict__ sc, int t0, int t1, ChunkKeys &ck)
+template <int KPT>
+__device__ __forceinline__ void load_chunk(const float *__restrict__ sc, int t0, int t1, ChunkKeys<KPT> &ck)
 {
     ck.t0 = t0;
     ck.t1 = t1;
-    float v[kKeysPerThread];
+    float v[KPT];
 #pragma unroll
-    for (int q = 0; q < kKeysPerThread; ++q) {
+    for (int q = 0; q < KPT; ++q) {
         const int t = t0 + (int)kvc_tid() + q * kThreads;
         v[q] = t < t1 ? sc[t] : 0.f;
     }
 #pragma unroll
-    for (int q = 0; q < kKeysPerThread; ++q) ck.key[q] = order_key(v[q]);
+    for (int q = 0; q < KPT; ++q) ck.key[q] = order_key(v[q]);
 }
 
-__device__ __forceinline__ bool chunk_valid(const ChunkKeys &ck, int q)
+template <int KPT>
+__device__ __forceinline__ bool chunk_valid(const ChunkKeys<KPT> &ck, int q)
 {
     return ck.t0 + (int)kvc_tid() + q * kThreads < ck.t1;
 }
 
 // ------------------------------------------------------------------------------ kernels
 // The work-group's unit and chunk; false when the chunk has nothing to histogram.
+template <int KPT>
 __device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t0, int &t1)
 {
+    constexpr int kChunk = KPT * kThreads;
     us = unit_shape(a.seq_lens, (int)kvc_bid_y() / a.H, a.s_max, unit_budget(a, kvc_bid_y()), a.n_keep);
     t0 = (int)kvc_bid_x() * kChunk;
     t1 = min(us.C, t0 + kChunk);
@@ -205,25 +215,27 @@ __device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t
     return us.k_eff > 0 && us.k_eff < us.C && t0 < us.C;
 }
 
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void sel_level1_kernel(SelArgs a)
 {
     __shared__ int h[kCopies][kB1];
     const int u = kvc_bid_y();
     UnitShape us;
     int t0, t1;
-    if (!chunk_of(a, us, t0, t1)) return;
-    ChunkKeys ck;
+    if (!chunk_of<KPT>(a, us, t0, t1)) return;
+    ChunkKeys<KPT> ck;
     load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
     lds_clear(h);
     __syncthreads();
     int *hc = h[kvc_tid() & (kCopies - 1)];
 #pragma unroll
-    for (int q = 0; q < kKeysPerThread; ++q)
+    for (int q = 0; q < KPT; ++q)
         if (chunk_valid(ck, q)) hist_add(hc, h[0], (int)(ck.key[q] >> 21));
     __syncthreads();
     flush_hist<kB1>(h, a.hist + (size_t)u * kHistInts);
 }
 
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void sel_level2_kernel(SelArgs a)
 {
     __shared__ int h[kCopies][kB1];
@@ -232,23 +244,24 @@ __global__ __launch_bounds__(kThreads) void sel_level2_kernel(SelArgs a)
     const int u = kvc_bid_y();
     UnitShape us;
     int t0, t1;
-    if (!chunk_of(a, us, t0, t1)) return;
+    if (!chunk_of<KPT>(a, us, t0, t1)) return;
     const int32_t *H = a.hist + (size_t)u * kHistInts;
     int c1[kB1 / kThreads];
     load_bins<kB1>(H, c1);
-    ChunkKeys ck;
+    ChunkKeys<KPT> ck;
     load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
     lds_clear(h);
     const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
     int *hc = h[kvc_tid() & (kCopies - 1)];
 #pragma unroll
-    for (int q = 0; q < kKeysPerThread; ++q)
+    for (int q = 0; q < KPT; ++q)
         if (chunk_valid(ck, q) && (int)(ck.key[q] >> 21) == d1.digit)
             hist_add(hc, h[0], (int)((ck.key[q] >> 10) & (kB2 - 1)));
     __syncthreads();
     flush_hist<kB2>(h, a.hist + (size_t)u * kHistInts + kB1);
 }
 
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void sel_level3_kernel(SelArgs a)
 {
     __shared__ int h[kCopies][kB1];
@@ -259,14 +272,14 @@ __global__ __launch_bounds__(kThreads) void sel_level3_kernel(SelArgs a)
     const int j = kvc_bid_x();
     UnitShape us;
     int t0, t1;
-    if (!chunk_of(a, us, t0, t1)) return;
+    if (!chunk_of<KPT>(a, us, t0, t1)) return;
     const int tid = kvc_tid();
     const int lane = tid & (kWave - 1);
     const int32_t *H = a.hist + (size_t)u * kHistInts;
     int c1[kB1 / kThreads], c2[kB2 / kThreads];
     load_bins<kB1>(H, c1);
     load_bins<kB2>(H + kB1, c2);
-    ChunkKeys ck;
+    ChunkKeys<KPT> ck;
     load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
     lds_clear(h);
     const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
@@ -275,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void sel_level3_kernel(SelArgs a)
     int *hc = h[tid & (kCopies - 1)];
     int above = 0;                                       // keys whose top 22 bits exceed pre2
 #pragma unroll
-    for (int q = 0; q < kKeysPerThread; ++q) {
+    for (int q = 0; q < KPT; ++q) {
         if (!chunk_valid(ck, q)) continue;
         const uint32_t k22 = ck.key[q] >> 10;
         above += k22 > pre2;
@@ -314,8 +327,10 @@ __global__ __launch_bounds__(kThreads) void sel_level3_kernel(SelArgs a)
     }
 }
 
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
 {
+    constexpr int kChunk = KPT * kThreads;
     __shared__ int scan[16];
     __shared__ Digit dg;
     __shared__ int wave_gt[kWaves], wave_eq[kWaves];
@@ -351,16 +366,16 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     load_bins<kB1>(H, c1);
     load_bins<kB2>(H + kB1, c2);
     load_bins<kB3>(H + kB1 + kB2, c3);
-    uint32_t key[kKeysPerThread];
+    uint32_t key[KPT];
     {
-        float v[kKeysPerThread];
+        float v[KPT];
 #pragma unroll
-        for (int q = 0; q < kKeysPerThread; ++q) {
+        for (int q = 0; q < KPT; ++q) {
             const int t = w0 + lane + q * kWave;
             v[q] = t < t1 ? sc[t] : 0.f;
         }
 #pragma unroll
-        for (int q = 0; q < kKeysPerThread; ++q) key[q] = order_key(v[q]);
+        for (int q = 0; q < KPT; ++q) key[q] = order_key(v[q]);
     }
     const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
     const Digit d2 = find_digit<kB2>(c2, us.k_eff - d1.above, scan, &dg);
@@ -412,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     // ordered compaction: per-wave counts, then ballots give in-wave prefix counts
     int gt = 0, eq = 0;
 #pragma unroll
-    for (int q = 0; q < kKeysPerThread; ++q) {
+    for (int q = 0; q < KPT; ++q) {
         const bool ok = w0 + lane + q * kWave < t1;
         gt += ok && key[q] > T;
         eq += ok && key[q] == T;
@@ -436,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     }
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-    for (int q = 0; q < kKeysPerThread; ++q) {
+    for (int q = 0; q < KPT; ++q) {
         const int t = w0 + lane + q * kWave;
         const bool ok = t < t1;
         const bool is_gt = ok && key[q] > T;
@@ -628,9 +643,9 @@ __global__ __launch_bounds__(kThreads) void core_scores_kernel(const float *__re
     const int b = u / H;
     const int S = clamp_len(seq_lens, b, s_max);
     const int C = S - n_keep > 0 ? S - n_keep : 0;
-    const int t0 = kvc_bid_x() * kChunk;
+    const int t0 = kvc_bid_x() * kCoreChunk;
     int n = 0;
-    for (int t = t0 + kvc_tid(); t < min(t0 + kChunk, s_max); t += kThreads) {
+    for (int t = t0 + kvc_tid(); t < min(t0 + kCoreChunk, s_max); t += kThreads) {
         const bool c = t < C && core[(size_t)b * s_max + t] != 0;
         n += c;
         masked[(size_t)u * s_max + t] = c ? INFINITY : scores[(size_t)u * s_max + t];
@@ -659,6 +674,7 @@ __global__ __launch_bounds__(256) void core_budget_kernel(const int32_t *__restr
 }
 
 struct SelLayout {
+    int kpt;                  // keys per thread of the chunked kernels
     int n_chunks;
     size_t sum_off, hist_off, done_off, above_off, sfx_off, bytes;
 };
@@ -674,7 +690,10 @@ SelLayout sel_layout(int batch, int n_kv, int s_max, int n_keep, bool shared)
     SelLayout L;
     const long units = shared ? batch : (long)batch * n_kv;
     const long c_max = s_max - n_keep > 1 ? (long)s_max - n_keep : 1;
-    L.n_chunks = (int)((c_max + kChunk - 1) / kChunk);
+    const long big = kKptLarge * kThreads;
+    L.kpt = units * ((c_max + big - 1) / big) >= 1024 ? kKptLarge : kKptSmall;
+    const long chunk = (long)L.kpt * kThreads;
+    L.n_chunks = (int)((c_max + chunk - 1) / chunk);
     size_t off = 0;
     L.done_off = off;
     off += align256((size_t)units * sizeof(int32_t));
@@ -690,7 +709,8 @@ SelLayout sel_layout(int batch, int n_kv, int s_max, int n_keep, bool shared)
     return L;
 }
 
-static_assert(kChunk == kKeysPerThread * kThreads && kChunk % (kWaves * kWave) == 0, "chunk shape");
+static_assert((kKptSmall * kThreads) % (kWaves * kWave) == 0 && (kKptLarge * kThreads) % (kWaves * kWave) == 0,
+              "chunk shape");
 static_assert(kHistInts % 4 == 0 && kSfx % 4 == 0 && kB1 % 4 == 0, "16-byte aligned histogram parts");
 
 }  // namespace
@@ -710,7 +730,7 @@ static CoreLayout core_layout(int batch, int n_kv, int s_max, int n_keep)
 {
     CoreLayout L;
     const size_t units = (size_t)batch * n_kv;
-    L.n_chunks = (s_max + kChunk - 1) / kChunk;
+    L.n_chunks = (s_max + kCoreChunk - 1) / kCoreChunk;
     size_t off = align256(select_ws_bytes(batch, n_kv, s_max, n_keep, false));
     L.masked_off = off;
     off += align256(units * s_max * sizeof(float));
@@ -800,10 +820,17 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
         return hipGetLastError();
     }
     const dim3 grid(L.n_chunks, units);
-    hipLaunchKernelGGL(sel_level1_kernel, grid, dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(sel_level2_kernel, grid, dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(sel_level3_kernel, grid, dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(sel_write_kernel, grid, dim3(kThreads), 0, stream, a);
+    if (L.kpt == kKptLarge) {
+        hipLaunchKernelGGL(sel_level1_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_level2_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_level3_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_write_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(sel_level1_kernel<kKptSmall>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_level2_kernel<kKptSmall>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_level3_kernel<kKptSmall>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_write_kernel<kKptSmall>, grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -195,14 +195,15 @@ def test_select_bitexact_continuous(s_max):
         _select_case(sc, sl, k, 32)
 
 
-@pytest.mark.parametrize("s_max", [3001, 4096, 16000, 32768])
+@pytest.mark.parametrize("s_max", [3001, 4096, 16000, 32768, 70000])
 def test_select_many_units(s_max):
-    # 256 units (half the CUs of the chip or more): every unit's candidates go to one
-    # work-group when they fit (s_max - n_keep <= 32768); rows of a multiple of 4 floats
-    # and not, ties, ragged lengths, per-unit budgets and a unit mask
+    # many units: every unit's candidates go to one work-group when they fit
+    # (s_max - n_keep <= 32768); past that, 128 units of 70000 tokens take the chunked
+    # kernels with 8192-key chunks.  Rows of a multiple of 4 floats and not, ties,
+    # ragged lengths, per-unit budgets and a unit mask.
     _say("select many units", s_max)
     rng = np.random.default_rng(s_max + 1)
-    B, H = 32, 8
+    B, H = (32, 8) if s_max <= 32768 else (16, 8)
     sc = rng.random((B, H, s_max)).astype(np.float32) ** 4
     sc[::3] = (rng.integers(0, 60, (sc[::3].shape)) / 59.0).astype(np.float32)      # many exact ties
     sc[1, 2] = 0.25                                                                   # all equal
