@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-retrieval", action="store_true",
                     help="skip the speculative-retrieval schedules on the batched ragged workload")
+    ap.add_argument("--tsp", action="store_true",
+                    help="also time the token-selective-propagation workload mha_tsp (64K-token MHA cache, "
+                         "selection shared over heads at layer 16, later layers over the kept tokens)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling PMC byte counters)")
     return ap.parse_args()
@@ -339,6 +342,9 @@ def main():
         res["core_retention"] = measure_core(wl, fold, sl_all, us["select"], dev, args.steps)
         print("[bench] speculative retrieval on ragged_b16", file=sys.stderr, flush=True)
         res["speculative_retrieval"] = measure_retrieval(dev, 64, 5)
+    if args.tsp:
+        print("[bench] token-selective propagation on mha_tsp", file=sys.stderr, flush=True)
+        res["tsp"] = measure_tsp(dev, args.steps)
     print(json.dumps(res), flush=True)
 
 
@@ -346,6 +352,98 @@ RETRIEVAL_TAU = 0.85
 BLOCK_TOKENS = 16
 PYRAMID_BETA = 0.5
 CORE_BLOCK, CORE_FRAC = 64, 0.05
+
+
+def measure_tsp(dev, steps):
+    """FastKV's token-selective propagation on mha_tsp (B=2, 32 MHA heads, S=65536): one
+    decode-step's compression schedule layer by layer, since the layers after the TSP
+    layer run over its selection.  Layers 0-16 run score -> select -> gather -> decode
+    over S tokens; at layer 16 one selection per sequence from the head-summed scores
+    (20 % of S, plus the window) gathers the hidden states; layers 17-31 run over the
+    S' = 13108 + 32 kept tokens with their original positions.  Every layer at S reuses
+    one layer's 2 x 1 GiB of K/V (each far above the 256 MB MALL), likewise at S'."""
+    import torch
+
+    from sparse_decode_amd import kvc, synth
+    from sparse_decode_amd.pipeline import LayerPath, TspStep
+    wl = synth.by_name("mha_tsp")
+    k_tsp = synth.budget_from_rate(wl.tsp_rate, wl.s_max)
+    s2 = k_tsp + wl.n_keep
+    full = synth.layer_inputs(wl, 0, device=dev)
+    late = synth.layer_inputs(wl, wl.tsp_layer + 1, device=dev, s_max=s2)
+    hidden = synth.hidden_states(wl, device=dev)
+    sl = torch.from_numpy(full["seq_lens"]).to(dev)
+    sl2 = torch.from_numpy(late["seq_lens"]).to(dev)
+    path = LayerPath(wl, device=dev)
+    path2 = LayerPath(wl, device=dev, s_max=s2)
+    tsp = TspStep(wl, k_tsp, device=dev)
+    src_pos = torch.zeros((wl.batch, s2), dtype=torch.int32, device=dev)
+
+    def full_layer():
+        path.run(full["q_win"], full["k"], full["v"], full["q_dec"], sl)
+
+    def tsp_step():
+        tsp.run(path.pooled, hidden)
+        src_pos.copy_(tsp.pos[:, 0, :])
+
+    def late_layer():
+        path2.run(late["q_win"], late["k"], late["v"], late["q_dec"], sl2, src_pos=src_pos)
+
+    def step():
+        for _ in range(wl.tsp_layer + 1):
+            full_layer()
+        tsp_step()
+        for _ in range(wl.tsp_layer + 1, wl.layers):
+            late_layer()
+
+    def capture(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g, reps):
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    full_layer()
+    tsp_step()
+    torch.cuda.synchronize()
+    ms_step = timed(capture(step), max(2, steps // 2))
+    us_full = 1000.0 * timed(capture(full_layer), steps)
+    us_tsp = 1000.0 * timed(capture(tsp_step), steps)
+    us_late = 1000.0 * timed(capture(late_layer), steps)
+    by_full = layer_bytes(wl, float(np.mean(full["seq_lens"])), path.cap)
+    by_late = layer_bytes(wl, float(np.mean(late["seq_lens"])), path2.cap)
+    lb_full = by_full["score"] + by_full["select"] + by_full["gather"] + by_full["decode"]
+    lb_late = by_late["score"] + by_late["select"] + by_late["gather"] + by_late["decode"]
+    # TSP: head-summed scores read once, kept hidden rows read and written, idx / pos
+    tsp_bytes = wl.batch * (wl.n_kv * wl.s_max * 4 + 2 * s2 * wl.hidden * wl.elem_bytes + 3 * 4 * s2)
+    step_bytes = (wl.tsp_layer + 1) * lb_full + tsp_bytes + (wl.layers - wl.tsp_layer - 1) * lb_late
+    del full, late, hidden
+    return {"workload": wl.name, "layers": wl.layers, "tsp_layer": wl.tsp_layer, "k_tsp": k_tsp, "s_after": s2,
+            "k_per_layer": wl.k, "ms_per_step": round(ms_step, 4),
+            "value_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+            "us_per_layer_at_S": round(us_full, 2), "us_tsp_select_and_hidden_gather": round(us_tsp, 2),
+            "us_per_layer_after": round(us_late, 2),
+            "tsp_GBps": round(tsp_bytes / (us_tsp * 1e-6) / 1e9, 1),
+            "timing": "HIP graph per schedule (whole step, one layer at S, the TSP step, one later layer), "
+                      "replays between HIP events"}
 
 
 def measure_core(wl, fold, sl_all, select_us, dev, steps):

@@ -9,7 +9,7 @@
 // the selected set is every key > T plus the lowest-indexed keys == T, written in
 // index order.  One work-group alone streams a unit's keys far below the chip's
 // bandwidth (a CU keeps only so many cache lines in flight), so every pass is spread
-// over the unit's chunks of 2048 keys, or 8192 when the call has at least 1024 such
+// over the unit's chunks of 2048 keys, or 8192 when the call has at least 512 such
 // larger chunks (one work-group each, every key loaded once into registers), and the
 // levels meet through per-unit histograms in global memory:
 //
@@ -691,7 +691,7 @@ SelLayout sel_layout(int batch, int n_kv, int s_max, int n_keep, bool shared)
     const long units = shared ? batch : (long)batch * n_kv;
     const long c_max = s_max - n_keep > 1 ? (long)s_max - n_keep : 1;
     const long big = kKptLarge * kThreads;
-    L.kpt = units * ((c_max + big - 1) / big) >= 1024 ? kKptLarge : kKptSmall;
+    L.kpt = units * ((c_max + big - 1) / big) >= 512 ? kKptLarge : kKptSmall;
     const long chunk = (long)L.kpt * kThreads;
     L.n_chunks = (int)((c_max + chunk - 1) / chunk);
     size_t off = 0;
