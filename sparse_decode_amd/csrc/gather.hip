@@ -13,7 +13,7 @@ namespace kvc {
 namespace {
 
 constexpr int kGatherThreads = 256;
-constexpr int kGatherUnroll = 8;
+constexpr int kGatherUnroll = 2;   // rows per thread in flight (measured: 2 beats 4 and 8)
 constexpr int kMaxBlockRows = 4096;     // rows per work-group (their indices sit in LDS)
 
 // Work-group (kvc_bid_x(), kvc_bid_y()) copies rows [kvc_bid_x() * rows_per_block, ...)
