@@ -343,7 +343,7 @@ struct Sc {
     static constexpr int CPW = RT / WPR;                 // row blocks per wave
     static constexpr int TG = kMfWaves / WPR;            // token groups
     static constexpr int ST = 16 * (TG > 2 ? TG : 2);    // tokens per stage (8 KB at d_h = 128)
-    static constexpr int P = RT == 8 ? 3 : 4;            // stages in flight (register ring)
+    static constexpr int P = RT == 8 ? 2 : 4;            // stages in flight (register ring; 2 measured best at RT = 8)
     static constexpr int TPG = ST / 16 / TG;             // 16-token tiles per group per stage
     static constexpr int ROWB = 2 * D + 16;              // LDS bytes per row
     static constexpr int VPR = D / 8;                    // 16-byte vectors per row
