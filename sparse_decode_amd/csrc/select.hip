@@ -618,8 +618,17 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const float *__restrict__
     const int t = kvc_bid_x() * 256 + kvc_tid();
     if (t >= s_max) return;
     const float *p = scores + (size_t)b * n_kv * s_max + t;
+    // eight heads' scores requested together, then added in head order
     float s = 0.f;
-    for (int g = 0; g < n_kv; ++g) s += p[(size_t)g * s_max];
+    int g0 = 0;
+    for (; g0 + 8 <= n_kv; g0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = p[(size_t)(g0 + i) * s_max];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; g0 < n_kv; ++g0) s += p[(size_t)g0 * s_max];
     out[(size_t)b * s_max + t] = s;
 }
 
