@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kBlkThreads) void block_landmarks_kernel(const u32x
 // One thread per (unit, block): scale * sum over the group's query heads, then over d,
 // of q * landmark, in double, for the candidate blocks j < floor((S_b - n_keep) / block);
 // 0 elsewhere.  Unit (b, 0)'s block-0 thread also writes the candidate block count.
-template <bool BF16>
+template <bool BF16, int D>
 __global__ __launch_bounds__(kBlkThreads) void block_scores_kernel(const void *__restrict__ q,
                                                                    const float *__restrict__ landmarks,
                                                                    const int32_t *__restrict__ seq_lens,
@@ -85,15 +85,20 @@ __global__ __launch_bounds__(kBlkThreads) void block_scores_kernel(const void *_
     if (j >= n_blk) return;
     double s = 0.0;
     if (j < nc) {
-        const float4 *lm = (const float4 *)(landmarks + ((size_t)u * n_blk + j) * d_h);
+        // the landmark row is read once (every load in flight together) and reused for
+        // every query head; the sum keeps the h-then-d order
+        const float4 *lm = (const float4 *)(landmarks + ((size_t)u * n_blk + j) * D);
+        float4 l[D / 4];
+#pragma unroll
+        for (int d4 = 0; d4 < D / 4; ++d4) l[d4] = lm[d4];
         for (int h = 0; h < r; ++h) {
-            const double *qh = qs + h * d_h;
-            for (int d4 = 0; d4 < d_h / 4; ++d4) {
-                const float4 l = lm[d4];
-                s += qh[4 * d4] * (double)l.x;
-                s += qh[4 * d4 + 1] * (double)l.y;
-                s += qh[4 * d4 + 2] * (double)l.z;
-                s += qh[4 * d4 + 3] * (double)l.w;
+            const double *qh = qs + h * D;
+#pragma unroll
+            for (int d4 = 0; d4 < D / 4; ++d4) {
+                s += qh[4 * d4] * (double)l[d4].x;
+                s += qh[4 * d4 + 1] * (double)l[d4].y;
+                s += qh[4 * d4 + 2] * (double)l[d4].z;
+                s += qh[4 * d4 + 3] * (double)l[d4].w;
             }
         }
     }
@@ -150,12 +155,18 @@ hipError_t launch_block_scores(int batch, int n_h, int n_kv, int d_h, bool bf16,
     const int n_blk = (s_max + block - 1) / block;
     const dim3 grid((n_blk + kBlkThreads - 1) / kBlkThreads, batch * n_kv);
     const size_t lds = (size_t)(n_h / n_kv) * d_h * sizeof(double);
-    if (bf16)
-        hipLaunchKernelGGL(block_scores_kernel<true>, grid, dim3(kBlkThreads), lds, stream, q, landmarks, seq_lens,
-                           n_h, n_kv, d_h, s_max, block, n_keep, n_blk, scale, scores, cand);
+    if (bf16 && d_h == 128)
+        hipLaunchKernelGGL((block_scores_kernel<true, 128>), grid, dim3(kBlkThreads), lds, stream, q, landmarks,
+                           seq_lens, n_h, n_kv, d_h, s_max, block, n_keep, n_blk, scale, scores, cand);
+    else if (bf16)
+        hipLaunchKernelGGL((block_scores_kernel<true, 64>), grid, dim3(kBlkThreads), lds, stream, q, landmarks,
+                           seq_lens, n_h, n_kv, d_h, s_max, block, n_keep, n_blk, scale, scores, cand);
+    else if (d_h == 128)
+        hipLaunchKernelGGL((block_scores_kernel<false, 128>), grid, dim3(kBlkThreads), lds, stream, q, landmarks,
+                           seq_lens, n_h, n_kv, d_h, s_max, block, n_keep, n_blk, scale, scores, cand);
     else
-        hipLaunchKernelGGL(block_scores_kernel<false>, grid, dim3(kBlkThreads), lds, stream, q, landmarks, seq_lens,
-                           n_h, n_kv, d_h, s_max, block, n_keep, n_blk, scale, scores, cand);
+        hipLaunchKernelGGL((block_scores_kernel<false, 64>), grid, dim3(kBlkThreads), lds, stream, q, landmarks,
+                           seq_lens, n_h, n_kv, d_h, s_max, block, n_keep, n_blk, scale, scores, cand);
     return hipGetLastError();
 }
 
