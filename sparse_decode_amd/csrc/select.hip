@@ -654,10 +654,24 @@ __global__ __launch_bounds__(kThreads) void core_scores_kernel(const float *__re
     const int C = S - n_keep > 0 ? S - n_keep : 0;
     const int t0 = kvc_bid_x() * kCoreChunk;
     int n = 0;
-    for (int t = t0 + kvc_tid(); t < min(t0 + kCoreChunk, s_max); t += kThreads) {
-        const bool c = t < C && core[(size_t)b * s_max + t] != 0;
+    // every load of the thread's kCoreChunk / kThreads tokens goes out before the first
+    // use (indices clamped into the row; the stores check the range)
+    constexpr int kPer = kCoreChunk / kThreads;
+    float sc[kPer];
+    uint8_t cr[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int t = min(t0 + (int)kvc_tid() + i * kThreads, s_max - 1);
+        sc[i] = scores[(size_t)u * s_max + t];
+        cr[i] = core[(size_t)b * s_max + t];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int t = t0 + (int)kvc_tid() + i * kThreads;
+        if (t >= s_max) break;
+        const bool c = t < C && cr[i] != 0;
         n += c;
-        masked[(size_t)u * s_max + t] = c ? INFINITY : scores[(size_t)u * s_max + t];
+        masked[(size_t)u * s_max + t] = c ? INFINITY : sc[i];
     }
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) n += __shfl_xor(n, o, kWave);
