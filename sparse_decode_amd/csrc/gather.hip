@@ -64,13 +64,15 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
             t[u] = j < m ? rows[j] : -1;
         }
         for (int c = col0; c < vpr; c += tpr) {
+            // every load is unconditional (an absent row reads row 0 of the unit, which
+            // exists) so that all of them are in flight before the first store; a load
+            // under a branch would be waited for inside it
             u32x4 a[kGatherUnroll], bb[kGatherUnroll];
 #pragma unroll
             for (int u = 0; u < kGatherUnroll; ++u) {
-                if (t[u] >= 0) {
-                    a[u] = ld_stream(src0 + src_unit + (size_t)t[u] * vpr + c);
-                    if (src1) bb[u] = ld_stream(src1 + src_unit + (size_t)t[u] * vpr + c);
-                }
+                const int tr = t[u] >= 0 ? t[u] : 0;
+                a[u] = ld_stream(src0 + src_unit + (size_t)tr * vpr + c);
+                if (src1) bb[u] = ld_stream(src1 + src_unit + (size_t)tr * vpr + c);
             }
 #pragma unroll
             for (int u = 0; u < kGatherUnroll; ++u) {
