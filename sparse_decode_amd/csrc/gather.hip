@@ -13,14 +13,14 @@ namespace kvc {
 namespace {
 
 constexpr int kGatherThreads = 256;
-constexpr int kGatherUnroll = 2;   // rows per thread in flight (measured: 2 beats 4 and 8)
 constexpr int kMaxBlockRows = 4096;     // rows per work-group (their indices sit in LDS)
 
 // Work-group (kvc_bid_x(), kvc_bid_y()) copies rows [kvc_bid_x() * rows_per_block, ...)
 // of unit kvc_bid_y() = b * heads + h.  The block's source rows are resolved once
-// into LDS (one dependent round trip), then every thread keeps kGatherUnroll rows
-// of 16-byte loads (times two with src1) in flight.  tpr threads share one row (a
-// power of two <= 256); a row wider than 256 vectors is walked in strides of 256.
+// into LDS (one dependent round trip), then every thread keeps U rows of 16-byte
+// loads (times two with src1) in flight.  tpr threads share one row (a power of two
+// <= 256); a row wider than 256 vectors is walked in strides of 256.
+template <int U>
 __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     const u32x4 *__restrict__ src0, const u32x4 *__restrict__ src1,
     const int32_t *__restrict__ src_pos, const int32_t *__restrict__ idx,
@@ -56,10 +56,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
     const size_t src_unit = (size_t)unit * s_max * vpr;
     const size_t dst_unit = (size_t)unit * cap * vpr;
     const int m = min(r1, n) - r0;                       // rows of this block that are copied
-    for (int j0 = sub; j0 < m; j0 += rows_per_iter * kGatherUnroll) {
-        int t[kGatherUnroll];
+    for (int j0 = sub; j0 < m; j0 += rows_per_iter * U) {
+        int t[U];
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int j = j0 + u * rows_per_iter;
             t[u] = j < m ? rows[j] : -1;
         }
@@ -67,15 +67,15 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(
             // every load is unconditional (an absent row reads row 0 of the unit, which
             // exists) so that all of them are in flight before the first store; a load
             // under a branch would be waited for inside it
-            u32x4 a[kGatherUnroll], bb[kGatherUnroll];
+            u32x4 a[U], bb[U];
 #pragma unroll
-            for (int u = 0; u < kGatherUnroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int tr = t[u] >= 0 ? t[u] : 0;
                 a[u] = ld_stream(src0 + src_unit + (size_t)tr * vpr + c);
                 if (src1) bb[u] = ld_stream(src1 + src_unit + (size_t)tr * vpr + c);
             }
 #pragma unroll
-            for (int u = 0; u < kGatherUnroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 if (t[u] >= 0) {
                     const size_t o = dst_unit + (size_t)(r0 + j0 + u * rows_per_iter) * vpr + c;
                     dst0[o] = a[u];
@@ -110,9 +110,16 @@ hipError_t launch_gather(int batch, int heads, int s_max, int row_bytes, const v
     if (rpb > cap) rpb = cap;
     if (rpb < 1) rpb = 1;
     dim3 grid((unsigned)((cap + rpb - 1) / rpb), (unsigned)units);
-    hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(kGatherThreads), 0, stream,
-                       (const u32x4 *)src0, (const u32x4 *)src1, src_pos, idx, count, heads, idx_heads,
-                       s_max, vpr, tpr_log2, cap, (int)rpb, (u32x4 *)dst0, (u32x4 *)dst1, pos_out, unit_mask);
+    // two loads in flight per thread: one row of K and V, or two rows of one tensor
+    // (measured against 4 and 8 rows per thread)
+    if (src1)
+        hipLaunchKernelGGL(gather_rows_kernel<1>, grid, dim3(kGatherThreads), 0, stream,
+                           (const u32x4 *)src0, (const u32x4 *)src1, src_pos, idx, count, heads, idx_heads,
+                           s_max, vpr, tpr_log2, cap, (int)rpb, (u32x4 *)dst0, (u32x4 *)dst1, pos_out, unit_mask);
+    else
+        hipLaunchKernelGGL(gather_rows_kernel<2>, grid, dim3(kGatherThreads), 0, stream,
+                           (const u32x4 *)src0, (const u32x4 *)src1, src_pos, idx, count, heads, idx_heads,
+                           s_max, vpr, tpr_log2, cap, (int)rpb, (u32x4 *)dst0, (u32x4 *)dst1, pos_out, unit_mask);
     return hipGetLastError();
 }
 
