@@ -325,6 +325,13 @@ def test_score_gqa_ragged(generic):
     _score_case(2, 32, 8, 128, 2500, 32, np.array([2500, 1337], np.int32), generic=generic, planted=20)
 
 
+def test_score_mqa():
+    # one KV head for every query head: R = 8 * 16 = 128 rows (the MFMA path's largest
+    # row count), and R = 16 * 16 = 256 with d_h = 64 (the generic path)
+    _score_case(1, 8, 1, 128, 2100, 16, np.array([2100], np.int32), seed=5, planted=12)
+    _score_case(2, 16, 1, 64, 900, 16, np.array([900, 517], np.int32), seed=6)
+
+
 def test_score_mha_and_d64():
     _score_case(1, 4, 4, 128, 3001, 32, np.array([3001], np.int32), seed=1)           # R = 32
     _score_case(2, 8, 4, 64, 1500, 32, np.array([1500, 700], np.int32), seed=2)       # d = 64, R = 64
