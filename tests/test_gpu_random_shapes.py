@@ -2,7 +2,8 @@
 against the CPU oracle: odd sequence lengths, empty and ragged sequences, MQA to
 MHA groupings (including a group of 3 query heads), both head sizes, bf16 and fp32,
 queries in or out of the cache, every pool width the workloads use and budgets from
-window-only to dense."""
+window-only to dense.  Then the selection alone on scores full of exact ties, at
+unit counts and row lengths that take each of its kernel paths."""
 import sys
 
 import numpy as np
@@ -97,3 +98,36 @@ def test_random_shape_path(seed):
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.decode(host(q), host(kc), host(vc), gc)
     assert_decode_close(out, ref_out, c["bf16"])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_selection_ties(seed):
+    # selection alone at up to 512 units and 70000 keys (the per-unit kernel and both
+    # chunk sizes of the chunked kernels), with scores on few levels so that exact ties
+    # are everywhere; per-KV-head, shared over heads, and with per-unit budgets
+    rng = np.random.default_rng(7000 + seed)
+    n_kv = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 65))
+    s_max = int(rng.choice([int(rng.integers(1, 5000)), int(rng.integers(5000, 34000)),
+                            int(rng.integers(34000, 70000))]))
+    B = max(1, min(B, 8_000_000 // (n_kv * s_max)))
+    n_keep = int(rng.integers(0, 64))
+    k = int(rng.integers(0 if n_keep else 1, min(s_max, 4096) + 1))
+    lens = rng.integers(0, s_max + 1, B).astype(np.int32)
+    lens[0] = s_max
+    levels = int(rng.choice([3, 50, 1000, 1 << 20]))
+    sc_np = (rng.integers(0, levels, (B, n_kv, s_max)).astype(np.float32) / levels) ** 2
+    print("[case] seed", seed, dict(B=B, n_kv=n_kv, s_max=s_max, k=k, n_keep=n_keep, levels=levels), flush=True)
+    sc = torch.from_numpy(sc_np).to(DEV)
+    for shared in (False, True):
+        idx, cnt = kvc.select_topk(sc, k, n_keep, seq_lens=lens, shared_heads=shared)
+        torch.cuda.synchronize()
+        ri, rc = oracle.select_topk(sc_np, k, n_keep, seq_lens=lens, shared_heads=shared)
+        assert np.array_equal(host(cnt), rc)
+        assert np.array_equal(host(idx), ri)
+    kpu = rng.integers(0, k + 1, (B, n_kv)).astype(np.int32)
+    idx, cnt = kvc.select_topk(sc, k, n_keep, seq_lens=lens, k_per_unit=torch.from_numpy(kpu).to(DEV))
+    torch.cuda.synchronize()
+    ri, rc = oracle.select_topk(sc_np, k, n_keep, seq_lens=lens, k_per_unit=kpu)
+    assert np.array_equal(host(cnt), rc)
+    assert np.array_equal(host(idx), ri)
