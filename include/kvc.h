@@ -114,8 +114,8 @@ typedef struct kvc_dims {
                                  with KVC_SELECT_SHARED_HEADS; kvc_decode_attn ignores it     */
 } kvc_dims;
 
-/* kvc_select_topk flag: one selection per sequence from the float sum of the
- * pooled scores over all KV heads, added in head order (FastKV 2.A: the tokens
+/* kvc_select_topk flag: one selection per sequence from the sum of the pooled
+ * scores over all KV heads, added in double and rounded to float (FastKV 2.A: the tokens
  * chosen at the propagation layer are the same for every head). */
 #define KVC_SELECT_SHARED_HEADS 1
 
@@ -167,11 +167,22 @@ kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void 
                             void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * kvc_score_window_plan -- the launch configuration kvc_score_window takes for these
+ * arguments (it depends on the shapes only), for tests and profiling:
+ *   out[0]  1 when the bf16 MFMA kernels run, 0 for the portable kernels
+ *   out[1]  MFMA path: blocks of 16 window rows per KV head (1, 2, 4 or 8), else 0
+ *   out[2]  MFMA path: tokens per work-group of each pass, else 0
+ *   out[3]  MFMA path: work-groups per KV head of each pass, else 0
+ * out  int32[4], host memory.  Same argument checks as kvc_score_window_workspace.
+ */
+kvc_status kvc_score_window_plan(const kvc_dims *dims, int32_t w, int32_t flags, int32_t *out);
+
+/*
  * kvc_select_topk -- per-KV-head selection under the retention budget (FastKV 2.B),
  * plus the always-kept trailing tokens (FastKV 2.A), in ascending original order.
  *
- * For each unit (b, g) (or b alone with KVC_SELECT_SHARED_HEADS, score = float sum
- * over g in head order), with C = max(0, S_b - n_keep) candidates [0, C) and the
+ * For each unit (b, g) (or b alone with KVC_SELECT_SHARED_HEADS, score = the sum
+ * over g, in double, rounded to float), with C = max(0, S_b - n_keep) candidates [0, C) and the
  * unit's budget k_u = k, or k_per_unit[u] clamped to [0, k] (PyramidKV-style budgets
  * that differ per layer or head: Tutorial, "Compresser un cache existant"):
  *   k_eff = min(k_u, C); the first k_eff candidates in the total order

@@ -36,8 +36,8 @@
  * Arithmetic: logits, softmax and probability sums in double; the window score is
  * rounded to float once at the end.  Pooling and selection compare those float
  * scores exactly (the decision is taken in the precision the scores are stored
- * in), and the head-shared (TSP) score is the float sum over KV heads in head
- * order.  Decode attention is accumulated in double.
+ * in), and the head-shared (TSP) score is the sum over KV heads in double.  Decode
+ * attention is accumulated in double.
  */
 #include <math.h>
 #include <stdint.h>
@@ -157,7 +157,7 @@ KVO_API void kvo_score_window(int B, int s_max, const int32_t *seq_lens, int n_h
 }
 
 typedef struct {
-    float key;
+    double key; /* a float score widened exactly, or the double head sum (TSP) */
     int32_t t;
 } kvo_item;
 
@@ -182,7 +182,9 @@ static int by_int_asc(const void *pa, const void *pb)
  * reutilisation ...": keep the original positions).
  *
  * scores [B][H][s_max] float; shared_heads != 0 selects one set per sequence from
- *        the float sum over the H heads, added in head order (TSP, FastKV 2.A).
+ *        the sum over the H heads (TSP, FastKV 2.A: one token set is propagated for
+ *        every head), taken in double (every addend is exact in double, and the sum's
+ *        rounding error stays far below the spacing of the float scores).
  * idx    [B][H_out][k + n_keep], H_out = shared_heads ? 1 : H; -1 past count
  * count  [B][H_out] = min(k, C) + (S_b - C), C = max(0, S_b - n_keep)
  */
@@ -199,12 +201,12 @@ KVO_API void kvo_select_topk(int B, int H, int s_max, const int32_t *seq_lens, c
             const int k_eff = k < cand_end ? k : cand_end;
             kvo_item *items = (kvo_item *)malloc(((size_t)cand_end + 1) * sizeof(kvo_item));
             for (int t = 0; t < cand_end; ++t) {
-                float s;
+                double s;
                 if (shared_heads) {
-                    s = 0.0f;
-                    for (int g = 0; g < H; ++g) s += scores[((size_t)b * H + g) * s_max + t];
+                    s = 0.0;
+                    for (int g = 0; g < H; ++g) s += (double)scores[((size_t)b * H + g) * s_max + t];
                 } else {
-                    s = scores[((size_t)b * H + h) * s_max + t];
+                    s = (double)scores[((size_t)b * H + h) * s_max + t];
                 }
                 items[t].key = s;
                 items[t].t = t;
@@ -350,12 +352,17 @@ KVO_API void kvo_query_similarity(int B, int n_h, int n_kv, int d_h, const float
  * With C = max(0, S_b - n_keep), Core = {t < C : core[b][t]}, Scratch = [0, C) \ Core:
  *   k_eff = min(k, |Scratch|); Sel = the first k_eff scratch tokens in the order
  *   (score desc, index asc); idx = sort_asc(Sel u Core) ++ [C, S_b);
- *   count = k_eff + |Core| + (S_b - C); idx rows have width cap, -1 past count
- *   (cap >= k + |Core| + n_keep is the caller's: the first cap entries are written).
+ *   count = k_eff + |Core| + (S_b - C); -1 past count.
+ * The output holds cap = k + core_cap + n_keep indices per unit.  When the caller's
+ * core_cap is smaller than |Core| the candidates cannot all fit: the unit then keeps
+ * the first k + core_cap candidates of the list "Core by ascending index, then Scratch
+ * in the selection order" (every core token while they fit, the best scratch tokens
+ * in what is left), so count never exceeds cap.  Otherwise this is the rule above.
  */
 KVO_API void kvo_select_core(int B, int H, int s_max, const int32_t *seq_lens, const float *scores,
-                             const uint8_t *core, int k, int n_keep, int cap, int32_t *idx, int32_t *count)
+                             const uint8_t *core, int k, int core_cap, int n_keep, int32_t *idx, int32_t *count)
 {
+    const int cap = k + core_cap + n_keep;
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b) {
         for (int h = 0; h < H; ++h) {
@@ -363,26 +370,28 @@ KVO_API void kvo_select_core(int B, int H, int s_max, const int32_t *seq_lens, c
             const int C = S - n_keep > 0 ? S - n_keep : 0;
             kvo_item *items = (kvo_item *)malloc(((size_t)C + 1) * sizeof(kvo_item));
             int32_t *keep = (int32_t *)malloc(((size_t)S + 1) * sizeof(int32_t));
-            int n_scratch = 0, n_keep_list = 0;
+            int n_scratch = 0, n_core = 0;
             for (int t = 0; t < C; ++t) {
                 if (core[(size_t)b * s_max + t]) {
-                    keep[n_keep_list++] = t;            /* core: always kept */
+                    keep[n_core++] = t;                 /* core: always kept (ascending) */
                 } else {
-                    items[n_scratch].key = scores[((size_t)b * H + h) * s_max + t];
+                    items[n_scratch].key = (double)scores[((size_t)b * H + h) * s_max + t];
                     items[n_scratch].t = t;
                     ++n_scratch;
                 }
             }
-            const int k_eff = k < n_scratch ? k : n_scratch;
             qsort(items, (size_t)n_scratch, sizeof(kvo_item), by_score_desc_index_asc);
-            for (int j = 0; j < k_eff; ++j) keep[n_keep_list++] = items[j].t;
-            qsort(keep, (size_t)n_keep_list, sizeof(int32_t), by_int_asc);
-            for (int t = C; t < S; ++t) keep[n_keep_list++] = t;
+            const int k_eff = k < n_scratch ? k : n_scratch;
+            int n_cand = n_core + k_eff;                /* the rule's kept candidates */
+            if (n_cand > k + core_cap) n_cand = k + core_cap;   /* what the output can hold */
+            int n = n_core < n_cand ? n_core : n_cand;  /* core first, lowest index first */
+            for (int j = 0; n < n_cand; ++j) keep[n++] = items[j].t;
+            qsort(keep, (size_t)n, sizeof(int32_t), by_int_asc);
+            for (int t = C; t < S; ++t) keep[n++] = t;
             int32_t *out = idx + ((size_t)b * H + h) * cap;
-            const int n = n_keep_list < cap ? n_keep_list : cap;
             for (int j = 0; j < n; ++j) out[j] = keep[j];
             for (int j = n; j < cap; ++j) out[j] = -1;
-            count[(size_t)b * H + h] = n_keep_list;
+            count[(size_t)b * H + h] = n;
             free(items);
             free(keep);
         }

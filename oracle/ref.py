@@ -261,23 +261,27 @@ def speculative_step(q_cur, q_prev, k, v, prev_sel, *, seq_lens, k_budget, n_kee
                 next_sel=(sel_idx, sel_cnt), pooled=pooled)
 
 
-def select_core(scores, core, k, n_keep, *, seq_lens=None, cap=None):
+def select_core(scores, core, k, n_keep, *, seq_lens=None, core_cap=None):
     """CASK role-based retention: core tokens always kept, the budget k over the
     scratch tokens only (score desc, index asc), the n_keep trailing tokens kept.
 
     scores [B][H][s_max] float32, core [B][s_max] (nonzero = core).  Returns
-    (idx int32 [B][H][cap], count int32 [B][H]); cap defaults to k + s_max.
+    (idx int32 [B][H][k + core_cap + n_keep], count int32 [B][H]).  core_cap is the
+    room the caller leaves for core tokens (default s_max: always enough); a unit
+    with more core candidates keeps the first k + core_cap candidates of the list
+    "core by ascending index, then scratch in the selection order".
     """
     scores = _f32(scores)
     B, H, s_max = scores.shape
     core = np.ascontiguousarray(np.asarray(core) != 0, dtype=np.uint8)
     assert core.shape == (B, s_max)
-    if cap is None:
-        cap = k + s_max
+    if core_cap is None:
+        core_cap = s_max
+    cap = k + core_cap + n_keep
     idx = np.empty((B, H, cap), np.int32)
     count = np.empty((B, H), np.int32)
     sl = _i32(seq_lens)
-    _load().kvo_select_core(B, H, s_max, _ptr(sl), _ptr(scores), _ptr(core), int(k), int(n_keep), int(cap),
+    _load().kvo_select_core(B, H, s_max, _ptr(sl), _ptr(scores), _ptr(core), int(k), int(core_cap), int(n_keep),
                             _ptr(idx), _ptr(count))
     return idx, count
 

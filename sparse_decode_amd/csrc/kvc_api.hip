@@ -108,6 +108,20 @@ KVC_EXPORT size_t kvc_score_window_workspace(const kvc_dims *dims, int32_t w, in
     return score_ws(dims, w, flags, kPlanCus);
 }
 
+KVC_EXPORT kvc_status kvc_score_window_plan(const kvc_dims *dims, int32_t w, int32_t flags, int32_t *out)
+{
+    kvc_status st = score_args(dims, w, flags);
+    if (st != KVC_OK) return st;
+    if (!out) return KVC_ERR_INVALID_ARG;
+    const kvc::ScorePlan p = kvc::plan_score(dims->batch, dims->s_max, dims->n_h, dims->n_kv, dims->d_h,
+                                             dims->dtype == KVC_BF16, w, (flags & KVC_SCORE_GENERIC) != 0, kPlanCus);
+    out[0] = p.mfma ? 1 : 0;
+    out[1] = p.mfma ? p.rt : 0;
+    out[2] = p.mfma ? p.chunk_tokens : 0;
+    out[3] = p.mfma ? p.n_chunks : 0;
+    return KVC_OK;
+}
+
 KVC_EXPORT kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void *k, int32_t w,
                                        int32_t window_in_cache, int32_t n_keep, int32_t pool_kernel,
                                        float scale, float *raw, float *pooled, int32_t flags, void *ws,

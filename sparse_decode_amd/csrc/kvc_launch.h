@@ -54,6 +54,7 @@ hipError_t launch_select_core(int batch, int n_kv, int s_max, const int32_t *seq
 struct ScorePlan {
     bool mfma = false;
     int R = 0;                 // rows per KV head: (n_h / n_kv) * w
+    int rt = 0;                // MFMA path: blocks of 16 rows (1, 2, 4 or 8)
     int tiles_per_wave = 1;    // MFMA path: 32-token tiles per wave per chunk
     int chunk_tokens = 0;      // MFMA path: tokens per work-group
     int n_chunks = 0;

@@ -849,6 +849,7 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
     p.mfma = !generic && bf16 && (d_h == 64 || d_h == 128) && p.R <= 128;
     if (p.mfma) {
         const int rt = p.R <= 16 ? 1 : (p.R <= 32 ? 2 : (p.R <= 64 ? 4 : 8));
+        p.rt = rt;
         const int rpad = rt * 16;
         // every unit in one launch: the second pass streams K from HBM again either
         // way (measured: keeping a group's K within the MALL size does not make the
@@ -887,7 +888,7 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
 {
     const int units = batch * n_kv;
     if (plan.mfma) {
-        const int rt = plan.R <= 16 ? 1 : (plan.R <= 32 ? 2 : (plan.R <= 64 ? 4 : 8));
+        const int rt = plan.rt;
         const int rpad = rt * 16;
         MfArgs a;
         a.q_win = (const uint16_t *)q_win;

@@ -610,7 +610,8 @@ __global__ __launch_bounds__(kUnitThreads) void sel_unit_kernel(SelArgs a)
     }
 }
 
-// TSP score: float sum over KV heads in head order (one selection per sequence).
+// TSP score: the sum over KV heads (one selection per sequence), added in double and
+// rounded to float once, so the selection key is the exact sum correctly rounded.
 __global__ __launch_bounds__(256) void head_sum_kernel(const float *__restrict__ scores, int n_kv, int s_max,
                                                        float *__restrict__ out)
 {
@@ -618,18 +619,18 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const float *__restrict__
     const int t = kvc_bid_x() * 256 + kvc_tid();
     if (t >= s_max) return;
     const float *p = scores + (size_t)b * n_kv * s_max + t;
-    // eight heads' scores requested together, then added in head order
-    float s = 0.f;
+    // eight heads' scores requested together, then added
+    double s = 0.0;
     int g0 = 0;
     for (; g0 + 8 <= n_kv; g0 += 8) {
         float v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = p[(size_t)(g0 + i) * s_max];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s += v[i];
+        for (int i = 0; i < 8; ++i) s += (double)v[i];
     }
-    for (; g0 < n_kv; ++g0) s += p[(size_t)g0 * s_max];
-    out[(size_t)b * s_max + t] = s;
+    for (; g0 < n_kv; ++g0) s += (double)p[(size_t)g0 * s_max];
+    out[(size_t)b * s_max + t] = (float)s;
 }
 
 // ---------------------------------------------------------------- role-based retention

@@ -7,7 +7,9 @@ if the library is not built, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 import threading
 
@@ -23,7 +25,7 @@ KVC_SCORE_GENERIC = 1
 
 EXPORTED = (
     "kvc_abi_version", "kvc_status_str",
-    "kvc_score_window_workspace", "kvc_score_window",
+    "kvc_score_window_workspace", "kvc_score_window", "kvc_score_window_plan",
     "kvc_select_topk_workspace", "kvc_select_topk",
     "kvc_select_core_workspace", "kvc_select_core",
     "kvc_gather_compact",
@@ -64,6 +66,7 @@ def lib():
                 "kvc_status_str": (ctypes.c_char_p, [I]),
                 "kvc_score_window_workspace": (Z, [D, I, I]),
                 "kvc_score_window": (I, [D, P, P, I, I, I, I, F, P, P, I, P, Z, P]),
+                "kvc_score_window_plan": (I, [D, I, I, P]),
                 "kvc_select_topk_workspace": (Z, [D, I, I, I]),
                 "kvc_select_topk": (I, [D, P, I, I, I, P, P, P, P, Z, P]),
                 "kvc_select_core_workspace": (Z, [D, I]),
@@ -113,10 +116,27 @@ def _dev(t: torch.Tensor, name: str):
     return t
 
 
-def _stream(stream):
-    if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+def _stream():
+    """The hipStream_t of the launch: torch's current stream (which on_stream sets)."""
+    return torch.cuda.current_stream().cuda_stream
+
+
+def on_stream(fn):
+    """Runs a binding call with its ``stream=`` argument (a torch.cuda.Stream) made
+    torch's current stream, so that the temporaries the call allocates or fills
+    (workspaces, outputs, host-to-device copies of lengths) are ordered on the same
+    stream as its kernels and released to that stream's pool."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            ctx = contextlib.nullcontext()
+        elif isinstance(stream, torch.cuda.Stream):
+            ctx = torch.cuda.stream(stream)
+        else:
+            raise TypeError("stream must be a torch.cuda.Stream")
+        with ctx:
+            return fn(*args, **kw)
+    return call
 
 
 def _seq_lens(seq_lens, device):
@@ -152,8 +172,16 @@ def score_window_workspace(dims: Dims, w: int, flags: int = 0) -> int:
     return int(lib().kvc_score_window_workspace(ctypes.byref(dims), int(w), int(flags)))
 
 
+def score_window_plan(dims: Dims, w: int, flags: int = 0) -> dict:
+    """kvc_score_window_plan: the launch configuration of kvc_score_window for dims."""
+    out = (ctypes.c_int32 * 4)()
+    _check(lib().kvc_score_window_plan(ctypes.byref(dims), int(w), int(flags), out), "kvc_score_window_plan")
+    return {"mfma": bool(out[0]), "rt": int(out[1]), "chunk_tokens": int(out[2]), "chunks_per_unit": int(out[3])}
+
+
+@on_stream
 def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=None, pool=1, scale=0.0,
-                 generic=False, raw=None, pooled=None, ws=None, unit_mask=None, stream=None):
+                 generic=False, raw=None, pooled=None, ws=None, unit_mask=None):
     """kvc_score_window: q_win [B][n_h][w][d_h], k [B][n_kv][s_max][d_h] -> (raw, pooled) fp32.
     With unit_mask ([B][n_kv] int32), units whose entry is 0 are skipped."""
     _dev(q_win, "q_win")
@@ -177,7 +205,7 @@ def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=Non
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=k.device)
     st = lib().kvc_score_window(ctypes.byref(dims), _ptr(q_win), _ptr(k), int(w), int(bool(window_in_cache)),
                                 int(n_keep), int(pool), float(scale), _ptr(raw), _ptr(pooled), flags,
-                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream())
     _check(st, "kvc_score_window")
     return raw, pooled
 
@@ -188,8 +216,9 @@ def select_topk_workspace(dims: Dims, k: int, n_keep: int, flags: int = 0) -> in
     return int(lib().kvc_select_topk_workspace(ctypes.byref(dims), int(k), int(n_keep), int(flags)))
 
 
+@on_stream
 def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=None, count=None, ws=None,
-                unit_mask=None, k_per_unit=None, stream=None):
+                unit_mask=None, k_per_unit=None):
     """kvc_select_topk: scores [B][n_kv][s_max] fp32 -> (idx [B][H][k+n_keep], count [B][H]) int32.
     With unit_mask ([B][n_kv] int32), units whose entry is 0 are skipped; with k_per_unit
     ([B][H] int32 device tensor), unit u takes min(k_per_unit[u], k) candidates."""
@@ -213,7 +242,7 @@ def select_topk(scores, k, n_keep, *, seq_lens=None, shared_heads=False, idx=Non
     kpu = _mask(k_per_unit, (B, H), scores.device, "k_per_unit")
     st = lib().kvc_select_topk(ctypes.byref(dims), _ptr(scores), int(k), int(n_keep), flags, _ptr(kpu),
                                _ptr(idx), _ptr(count), _ptr(ws),
-                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check(st, "kvc_select_topk")
     return idx, count
 
@@ -222,8 +251,9 @@ def select_core_workspace(dims: Dims, n_keep: int) -> int:
     return int(lib().kvc_select_core_workspace(ctypes.byref(dims), int(n_keep)))
 
 
+@on_stream
 def select_core(scores, core, k, core_cap, n_keep, *, seq_lens=None, idx=None, count=None, ws=None,
-                unit_mask=None, stream=None):
+                unit_mask=None):
     """kvc_select_core: scores [B][n_kv][s_max] fp32, core [B][s_max] uint8 ->
     (idx [B][n_kv][k+core_cap+n_keep], count [B][n_kv]) int32."""
     _dev(scores, "scores")
@@ -245,15 +275,16 @@ def select_core(scores, core, k, core_cap, n_keep, *, seq_lens=None, idx=None, c
     if ws is None:
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=scores.device)
     st = lib().kvc_select_core(ctypes.byref(dims), _ptr(scores), _ptr(core), int(k), int(core_cap), int(n_keep),
-                               _ptr(idx), _ptr(count), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+                               _ptr(idx), _ptr(count), _ptr(ws), ws.numel() * ws.element_size(), _stream())
     _check(st, "kvc_select_core")
     return idx, count
 
 
 # ------------------------------------------------------------------------------ gather
 
+@on_stream
 def gather_compact(src0, idx, count, *, src1=None, src_pos=None, dst0=None, dst1=None, pos_out=None,
-                   want_pos=True, unit_mask=None, stream=None):
+                   want_pos=True, unit_mask=None):
     """kvc_gather_compact: src [B][heads][s_max][...] -> dst [B][heads][cap][...] (+ pos_out).
     With unit_mask ([B][idx_heads] int32), lists whose entry is 0 are skipped."""
     _dev(src0, "src0")
@@ -274,7 +305,7 @@ def gather_compact(src0, idx, count, *, src1=None, src_pos=None, dst0=None, dst1
     st = lib().kvc_gather_compact(int(B), int(heads), int(s_max), int(row_bytes), _ptr(src0), _ptr(src1),
                                   _ptr(src_pos), _ptr(idx), _ptr(count), int(idx_heads), int(cap), _ptr(dst0),
                                   _ptr(dst1), _ptr(pos_out), _ptr(_mask(unit_mask, (B, idx_heads), src0.device)),
-                                  _stream(stream))
+                                  _stream())
     _check(st, "kvc_gather_compact")
     return dst0, dst1, pos_out
 
@@ -285,7 +316,8 @@ def decode_attn_workspace(dims: Dims, cap: int) -> int:
     return int(lib().kvc_decode_attn_workspace(ctypes.byref(dims), int(cap)))
 
 
-def decode_attn(q, kc, vc, count, *, scale=0.0, out=None, lse=None, want_lse=True, ws=None, stream=None):
+@on_stream
+def decode_attn(q, kc, vc, count, *, scale=0.0, out=None, lse=None, want_lse=True, ws=None):
     """kvc_decode_attn: q [B][n_h][d_h], kc/vc [B][n_kv][cap][d_h] -> (out [B][n_h][d_h], lse [B][n_h])."""
     for t, nm in ((q, "q"), (kc, "kc"), (vc, "vc"), (count, "count")):
         _dev(t, nm)
@@ -301,15 +333,15 @@ def decode_attn(q, kc, vc, count, *, scale=0.0, out=None, lse=None, want_lse=Tru
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     st = lib().kvc_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(kc), _ptr(vc), _ptr(count), int(cap),
                                float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
-                               _stream(stream))
+                               _stream())
     _check(st, "kvc_decode_attn")
     return out, lse
 
 
 # ----------------------------------------------------------------------- query similarity
 
-def query_similarity(q_cur, q_prev, n_kv, tau, *, cos=None, refresh=None, keep=None, want_cos=True,
-                     stream=None):
+@on_stream
+def query_similarity(q_cur, q_prev, n_kv, tau, *, cos=None, refresh=None, keep=None, want_cos=True):
     """kvc_query_similarity: q_cur, q_prev [B][n_h][d_h] -> (cos [B][n_h] fp32, refresh, keep [B][n_kv] int32)."""
     _dev(q_cur, "q_cur")
     _dev(q_prev, "q_prev")
@@ -325,14 +357,15 @@ def query_similarity(q_cur, q_prev, n_kv, tau, *, cos=None, refresh=None, keep=N
     if keep is None:
         keep = torch.empty((B, n_kv), dtype=torch.int32, device=dev)
     st = lib().kvc_query_similarity(ctypes.byref(dims), _ptr(q_cur), _ptr(q_prev), float(tau), _ptr(cos),
-                                    _ptr(refresh), _ptr(keep), _stream(stream))
+                                    _ptr(refresh), _ptr(keep), _stream())
     _check(st, "kvc_query_similarity")
     return cos, refresh, keep
 
 
 # ------------------------------------------------------- landmark-guided block selection
 
-def block_landmarks(k, block, *, seq_lens=None, out=None, stream=None):
+@on_stream
+def block_landmarks(k, block, *, seq_lens=None, out=None):
     """kvc_block_landmarks: k [B][n_kv][s_max][d_h] -> mean keys [B][n_kv][ceil(s_max/block)][d_h] fp32."""
     _dev(k, "k")
     B, n_kv, s_max, d_h = k.shape
@@ -341,13 +374,13 @@ def block_landmarks(k, block, *, seq_lens=None, out=None, stream=None):
     dims = make_dims(B, s_max, n_kv, n_kv, d_h, _dtype_code(k), sl)
     if out is None:
         out = torch.empty((B, n_kv, n_blk, d_h), dtype=torch.float32, device=k.device)
-    st = lib().kvc_block_landmarks(ctypes.byref(dims), _ptr(k), int(block), _ptr(out), _stream(stream))
+    st = lib().kvc_block_landmarks(ctypes.byref(dims), _ptr(k), int(block), _ptr(out), _stream())
     _check(st, "kvc_block_landmarks")
     return out
 
 
-def block_scores(q, landmarks, block, n_keep, s_max, *, seq_lens=None, scale=0.0, scores=None, cand=None,
-                 stream=None):
+@on_stream
+def block_scores(q, landmarks, block, n_keep, s_max, *, seq_lens=None, scale=0.0, scores=None, cand=None):
     """kvc_block_scores: q [B][n_h][d_h], landmarks -> (scores [B][n_kv][n_blk] fp32, cand [B] int32)."""
     _dev(q, "q")
     _dev(landmarks, "landmarks")
@@ -360,13 +393,13 @@ def block_scores(q, landmarks, block, n_keep, s_max, *, seq_lens=None, scale=0.0
     if cand is None:
         cand = torch.empty((B,), dtype=torch.int32, device=q.device)
     st = lib().kvc_block_scores(ctypes.byref(dims), _ptr(q), _ptr(landmarks), int(block), int(n_keep), float(scale),
-                                _ptr(scores), _ptr(cand), _stream(stream))
+                                _ptr(scores), _ptr(cand), _stream())
     _check(st, "kvc_block_scores")
     return scores, cand
 
 
-def expand_blocks(idx_blocks, count_blocks, block, n_keep, s_max, cap, *, seq_lens=None, idx=None, count=None,
-                  stream=None):
+@on_stream
+def expand_blocks(idx_blocks, count_blocks, block, n_keep, s_max, cap, *, seq_lens=None, idx=None, count=None):
     """kvc_expand_blocks: kept blocks [B][H][cap_blocks] -> token indices [B][H][cap], count [B][H]."""
     _dev(idx_blocks, "idx_blocks")
     _dev(count_blocks, "count_blocks")
@@ -377,6 +410,6 @@ def expand_blocks(idx_blocks, count_blocks, block, n_keep, s_max, cap, *, seq_le
     if count is None:
         count = torch.empty((B, H), dtype=torch.int32, device=idx_blocks.device)
     st = lib().kvc_expand_blocks(int(B), int(H), int(s_max), _ptr(sl), int(block), int(n_keep), _ptr(idx_blocks),
-                                 _ptr(count_blocks), int(cap_blk), _ptr(idx), _ptr(count), int(cap), _stream(stream))
+                                 _ptr(count_blocks), int(cap_blk), _ptr(idx), _ptr(count), int(cap), _stream())
     _check(st, "kvc_expand_blocks")
     return idx, count

@@ -77,9 +77,7 @@ def check_selection(gpu_idx, gpu_count, ref_idx, ref_count, ref_scores, seq_lens
             chosen = sel[:k_eff]
             assert chosen.size == 0 or (chosen.min() >= 0 and chosen.max() < C)
             if shared:
-                s = np.zeros(sc.shape[-1], np.float32)
-                for g in range(sc.shape[1]):
-                    s = (s + sc[b, g]).astype(np.float32)
+                s = sc[b].astype(np.float64).sum(axis=0)      # the oracle's exact head sum
             else:
                 s = sc[b, h]
             mask = np.zeros(C, bool)

@@ -246,3 +246,23 @@ def test_block_selection_rejects_invalid_arguments():
     assert L.kvc_block_landmarks(ctypes.byref(d), BAD, 16, BAD, None) == kvc.KVC_ERR_HIP
     assert L.kvc_block_scores(ctypes.byref(d), BAD, BAD, 16, 32, 0.0, BAD, BAD, None) == kvc.KVC_ERR_HIP
     assert L.kvc_expand_blocks(1, 8, 1024, None, 16, 32, BAD, BAD, 4, BAD, BAD, 80, None) == kvc.KVC_ERR_HIP
+
+
+def test_score_plan_query():
+    # the launch configuration depends on the shapes only (host logic, no GPU)
+    E = kvc.KVC_ERR_INVALID_ARG
+    cfg2_fold = kvc.score_window_plan(_dims(batch=32, s_max=32768), 32)
+    assert cfg2_fold == {"mfma": True, "rt": 8, "chunk_tokens": 2048, "chunks_per_unit": 16}
+    one_layer = kvc.score_window_plan(_dims(batch=1, s_max=32768), 32)
+    assert one_layer["rt"] == 8 and one_layer["chunk_tokens"] == 256 and one_layer["chunks_per_unit"] == 128
+    mha = kvc.score_window_plan(_dims(batch=2, s_max=65536, n_h=32, n_kv=32), 32)
+    assert mha["rt"] == 2 and mha["chunk_tokens"] * mha["chunks_per_unit"] >= 65536
+    one_query = kvc.score_window_plan(_dims(batch=16, s_max=16384), 1)
+    assert one_query["rt"] == 1
+    assert kvc.score_window_plan(_dims(dtype_code=kvc.KVC_F32), 32)["mfma"] is False
+    assert kvc.score_window_plan(_dims(), 32, kvc.KVC_SCORE_GENERIC)["mfma"] is False
+    out = (ctypes.c_int32 * 4)()
+    assert kvc.lib().kvc_score_window_plan(None, 32, 0, out) == E
+    assert kvc.lib().kvc_score_window_plan(ctypes.byref(_dims()), 0, 0, out) == E
+    assert kvc.lib().kvc_score_window_plan(ctypes.byref(_dims()), 32, 0, None) == E
+

@@ -98,34 +98,71 @@ def test_cfg2_llama3_8b_32k():
     _layer_parity(wl, 31, check_planted=False)
 
 
-def test_cfg2_layers_folded_into_batch():
-    # compressing an existing cache of several layers in one call: the layers are
-    # independent units of the batch; every layer must match the oracle on its own
-    wl = synth.WORKLOADS[2]
-    layers = (0, 7, 31)
-    _say(wl.name, "layers", layers, "in one call")
-    inps = [synth.layer_inputs(wl, l, device="cuda") for l in layers]
-    q = torch.cat([x["q_win"] for x in inps]).contiguous()
-    k = torch.cat([x["k"] for x in inps]).contiguous()
-    v = torch.cat([x["v"] for x in inps]).contiguous()
-    sl = np.concatenate([x["seq_lens"] for x in inps])
-    sl_dev = torch.from_numpy(sl).cuda()
-    path = LayerPath(wl, batch=len(layers))
-    path.score(q, k, sl_dev)
+def _folded_parity(wl, layers, sampled, want_plan):
+    """Compresses the cache of several layers in one call each of score, select and
+    gather (the layers folded into the batch, as the benchmark's step does), checks
+    that the score call takes the launch configuration the benchmark times, then:
+    every layer's selection equals the oracle's selection over the GPU's own pooled
+    scores bit for bit, and on the sampled layers the raw and pooled scores, the
+    selection and the gathered rows match the oracle on the layer's inputs."""
+    L, B = len(layers), wl.batch
+    _say(wl.name, "%d layers in one call, sampled" % L, sampled)
+    S, d = wl.s_max, wl.d_h
+    K = torch.empty((L * B, wl.n_kv, S, d), dtype=wl.torch_dtype, device="cuda")
+    V = torch.empty_like(K)
+    Q = torch.empty((L * B, wl.n_h, wl.w, d), dtype=wl.torch_dtype, device="cuda")
+    sl = None
+    for i, l in enumerate(layers):
+        x = synth.layer_inputs(wl, l, device="cuda")
+        K[i * B:(i + 1) * B].copy_(x["k"])
+        V[i * B:(i + 1) * B].copy_(x["v"])
+        Q[i * B:(i + 1) * B].copy_(x["q_win"])
+        sl = x["seq_lens"]
+        del x
+    sl_all = np.tile(sl, L)
+    sl_dev = torch.from_numpy(sl_all).cuda()
+    path = LayerPath(wl, batch=L * B)
+    dims = kvc.make_dims(L * B, S, wl.n_h, wl.n_kv, d, kvc.KVC_BF16)
+    plan = kvc.score_window_plan(dims, wl.w)
+    _say("  score plan", plan)
+    assert plan == want_plan
+    path.score(Q, K, sl_dev)
     path.select(sl_dev)
-    path.gather(k, v)
+    path.gather(K, V)
     torch.cuda.synchronize()
-    for i, x in enumerate(inps):
-        _say("  layer", layers[i])
+    gp = host(path.pooled)
+    ri, rc = oracle.select_topk(gp, wl.k, wl.n_keep, seq_lens=sl_all)
+    assert np.array_equal(host(path.idx), ri) and np.array_equal(host(path.count), rc)
+    for l in sampled:
+        i = layers.index(l)
+        _say("  layer", l)
+        x = synth.layer_inputs(wl, l, device="cuda")
+        rows = slice(i * B, (i + 1) * B)
         rraw, rpooled = oracle.score_window(host(x["q_win"]), host(x["k"]), wl.w, seq_lens=x["seq_lens"],
                                             window_in_cache=wl.window_in_cache, n_keep=wl.n_keep, pool=wl.pool)
-        assert_scores_close(path.raw[i:i + 1], rraw, "raw")
-        assert_scores_close(path.pooled[i:i + 1], rpooled, "pooled")
+        assert_scores_close(path.raw[rows], rraw, "raw")
+        assert_scores_close(path.pooled[rows], rpooled, "pooled")
         ri, rc = oracle.select_topk(rpooled, wl.k, wl.n_keep, seq_lens=x["seq_lens"])
-        check_selection(path.idx[i:i + 1], path.count[i:i + 1], ri, rc, rpooled, x["seq_lens"], wl.k, wl.n_keep)
-        gi, gc = host(path.idx[i:i + 1]), host(path.count[i:i + 1])
-        ref, _ = oracle.gather(_bits(x["k"]), gi, gc, dst=_bits(path.kc[i:i + 1]))
-        assert np.array_equal(_bits(path.kc[i:i + 1]), ref)
+        check_selection(path.idx[rows], path.count[rows], ri, rc, rpooled, x["seq_lens"], wl.k, wl.n_keep)
+        gi, gc = host(path.idx[rows]), host(path.count[rows])
+        for src, dst in ((x["k"], path.kc[rows]), (x["v"], path.vc[rows])):
+            ref, ref_pos = oracle.gather(_bits(src), gi, gc, dst=_bits(dst))
+            assert np.array_equal(_bits(dst), ref)
+        assert np.array_equal(host(path.pos[rows]), ref_pos)
+        del x
+
+
+def test_cfg2_all_layers_folded_as_timed():
+    # the benchmark's score call: 32 layers x 8 KV heads in one launch, 2048-token
+    # work-groups over 8 blocks of 16 window rows
+    wl = synth.WORKLOADS[2]
+    _folded_parity(wl, list(range(wl.layers)), (0, 15, 31),
+                   {"mfma": True, "rt": 8, "chunk_tokens": 2048, "chunks_per_unit": 16})
+
+
+def test_cfg3_layers_folded():
+    wl = synth.WORKLOADS[3]
+    _folded_parity(wl, [0, 31], (0, 31), {"mfma": True, "rt": 8, "chunk_tokens": 2048, "chunks_per_unit": 64})
 
 
 def test_cfg3_ctx_128k():
@@ -164,3 +201,28 @@ def test_cfg5_mha_tsp():
     s2 = k_tsp + wl.n_keep
     src_pos = gi[:, 0, :].astype(np.int32)
     _layer_parity(wl, wl.tsp_layer + 1, s_max=s2, src_pos=src_pos, check_planted=False)
+
+
+@pytest.mark.parametrize("tsp_layer,tsp_rate", [(8, 0.1), (24, 0.4)])
+def test_cfg5_tsp_other_layer_and_rate(tsp_layer, tsp_rate):
+    # FastKV 2.A/2.B: the propagation layer and the TSP rate are free parameters,
+    # independent of the per-layer KV budget
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS[5], tsp_layer=tsp_layer, tsp_rate=tsp_rate)
+    k_tsp = synth.budget_from_rate(tsp_rate, wl.s_max)
+    inp, path, rpooled = _layer_parity(wl, tsp_layer, check_planted=False)
+    _say("mha_tsp TSP at layer", tsp_layer, "rate", tsp_rate, "k", k_tsp)
+    hidden = synth.hidden_states(wl, device="cuda")
+    tsp = TspStep(wl, k_tsp)
+    hid_out, pos = tsp.run(path.pooled, hidden)
+    torch.cuda.synchronize()
+    ri, rc = oracle.select_topk(rpooled, k_tsp, wl.n_keep, seq_lens=inp["seq_lens"], shared_heads=True)
+    check_selection(tsp.idx, tsp.count, ri, rc, rpooled, inp["seq_lens"], k_tsp, wl.n_keep, shared=True)
+    gi, gc = host(tsp.idx), host(tsp.count)
+    assert np.all(gc == k_tsp + wl.n_keep)
+    ref, ref_pos = oracle.gather(_bits(hidden).reshape(wl.batch, 1, wl.s_max, wl.hidden), gi, gc)
+    assert np.array_equal(_bits(hid_out), ref)
+    assert np.array_equal(host(pos), ref_pos)
+    del hidden, ref
+    s2 = k_tsp + wl.n_keep
+    _layer_parity(wl, tsp_layer + 1, s_max=s2, src_pos=gi[:, 0, :].astype(np.int32), check_planted=False)

@@ -155,12 +155,18 @@ def test_decode_closed_forms():
 # ===================================================================================== select
 
 def _select_case(scores_np, seq_lens, k, n_keep, shared=False, ws=None):
+    """Bit-exact against the oracle; shared over heads, the GPU selects on the head sum
+    rounded to float and the oracle on the exact sum, so there the near-tie rule
+    applies (and bit-exactness where the sums are exact in float)."""
     sc = torch.from_numpy(scores_np).to(DEV)
     idx, cnt = kvc.select_topk(sc, k, n_keep, seq_lens=seq_lens, shared_heads=shared, ws=ws)
     torch.cuda.synchronize()
     ri, rc = oracle.select_topk(scores_np, k, n_keep, seq_lens=seq_lens, shared_heads=shared)
     assert np.array_equal(host(cnt), rc)
-    assert np.array_equal(host(idx), ri)
+    if shared:
+        check_selection(idx, cnt, ri, rc, scores_np, seq_lens, k, n_keep, shared=True)
+    else:
+        assert np.array_equal(host(idx), ri)
 
 
 @pytest.mark.parametrize("s_max", [100, 4096, 32768, 65536])
@@ -247,6 +253,11 @@ def test_select_shared_heads_and_degenerate():
     B, H, s_max = 2, 32, 65536
     sc = rng.random((B, H, s_max)).astype(np.float32) * 1e-3
     _select_case(sc, np.array([s_max, s_max], np.int32), 13108, 32, shared=True)
+    # multiples of 2^-18 below 1 over 32 heads add exactly in float: bit-exact
+    dy = (rng.integers(0, 1 << 18, (B, H, s_max)) / float(1 << 18)).astype(np.float32)
+    idx, cnt = kvc.select_topk(torch.from_numpy(dy).to(DEV), 13108, 32, shared_heads=True)
+    ri, rc = oracle.select_topk(dy, 13108, 32, shared_heads=True)
+    assert np.array_equal(host(idx), ri) and np.array_equal(host(cnt), rc)
     small = rng.random((3, 2, 64)).astype(np.float32)
     _select_case(small, np.array([0, 5, 64], np.int32), 10, 8)     # S_b = 0, S_b < n_keep
     _select_case(small, np.array([64, 64, 64], np.int32), 0, 8)    # k = 0
@@ -438,7 +449,7 @@ def test_select_core_vs_oracle(s_max):
     sl = np.array([s_max, max(1, s_max // 3), s_max - 7], np.int32)
     idx, cnt = kvc.select_core(torch.from_numpy(sc).to(DEV), torch.from_numpy(core).to(DEV), k, core_cap, n_keep,
                                seq_lens=sl)
-    ri, rc = oracle.select_core(sc, core, k, n_keep, seq_lens=sl, cap=k + core_cap + n_keep)
+    ri, rc = oracle.select_core(sc, core, k, n_keep, seq_lens=sl, core_cap=core_cap)
     n_core = [int(core[b, :max(0, sl[b] - n_keep)].sum()) for b in range(B)]
     assert max(n_core) <= core_cap
     assert np.array_equal(host(cnt), rc) and np.array_equal(host(idx), ri)
@@ -450,17 +461,50 @@ def test_select_core_vs_oracle(s_max):
             assert np.isin(cores, gi[b, h]).all()
 
 
-def test_select_core_over_cap_keeps_lowest_core_tokens():
-    # the documented clamp: more core candidates than core_cap keep the k + core_cap
-    # lowest-indexed core tokens and no scratch token
-    _say("select core over cap")
-    s_max, k, core_cap, n_keep = 4096, 10, 20, 8
-    rng = np.random.default_rng(3)
-    sc = rng.random((1, 2, s_max)).astype(np.float32)
-    core = np.zeros((1, s_max), np.uint8)
+@pytest.mark.parametrize("k,core_cap", [(10, 20), (70, 60), (50, 0), (300, 99)])
+def test_select_core_over_capacity_vs_oracle(k, core_cap):
+    # more core candidates (100) than core_cap: the first k + core_cap candidates of
+    # "core by index, then scratch by score" are kept, as the oracle defines it
+    _say("select core over capacity", k, core_cap)
+    s_max, n_keep = 4096, 8
+    rng = np.random.default_rng(3 + k)
+    sc = rng.random((2, 2, s_max)).astype(np.float32)
+    sc[1, 0] = (rng.integers(0, 9, s_max) / 8.0).astype(np.float32)            # exact ties
+    core = np.zeros((2, s_max), np.uint8)
     core[0, 100:200] = 1
-    idx, cnt = kvc.select_core(torch.from_numpy(sc).to(DEV), torch.from_numpy(core).to(DEV), k, core_cap, n_keep)
-    gi, gc = host(idx), host(cnt)
-    want = list(range(100, 100 + k + core_cap)) + list(range(s_max - n_keep, s_max))
-    for h in range(2):
-        assert gc[0, h] == len(want) and gi[0, h].tolist() == want
+    core[1, rng.choice(s_max - n_keep, 100, replace=False)] = 1
+    sl = np.array([s_max, 3001], np.int32)
+    idx, cnt = kvc.select_core(torch.from_numpy(sc).to(DEV), torch.from_numpy(core).to(DEV), k, core_cap, n_keep,
+                               seq_lens=sl)
+    ri, rc = oracle.select_core(sc, core, k, n_keep, seq_lens=sl, core_cap=core_cap)
+    assert np.array_equal(host(cnt), rc) and np.array_equal(host(idx), ri)
+
+
+def test_calls_on_a_side_stream():
+    # stream=: every temporary the binding allocates or fills (workspaces, outputs,
+    # host lengths) is ordered on that stream; results equal the default stream's
+    _say("calls on a side stream")
+    B, n_h, n_kv, S, d, w, k, n_keep = 2, 8, 2, 5000, 128, 16, 300, 16
+    q = _randn((B, n_h, w, d), 91)
+    kk = _randn((B, n_kv, S, d), 92)
+    vv = _randn((B, n_kv, S, d), 93)
+    qd = _randn((B, n_h, d), 94)
+    lens = np.array([S, 3333], np.int32)
+
+    def run(stream):
+        _, pooled = kvc.score_window(q, kk, w, seq_lens=lens, n_keep=n_keep, pool=7, stream=stream)
+        idx, cnt = kvc.select_topk(pooled, k, n_keep, seq_lens=lens, stream=stream)
+        kc, vc, pos = kvc.gather_compact(kk, idx, cnt, src1=vv, stream=stream)
+        out, lse = kvc.decode_attn(qd, kc, vc, cnt, stream=stream)
+        return [t for t in (pooled, idx, cnt, kc, vc, pos, out, lse)]
+
+    ref = run(None)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = run(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    with pytest.raises(TypeError):
+        kvc.decode_attn(qd, got[3], got[4], got[2], stream=123)

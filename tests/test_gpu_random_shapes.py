@@ -119,10 +119,14 @@ def test_random_selection_ties(seed):
     sc_np = (rng.integers(0, levels, (B, n_kv, s_max)).astype(np.float32) / levels) ** 2
     print("[case] seed", seed, dict(B=B, n_kv=n_kv, s_max=s_max, k=k, n_keep=n_keep, levels=levels), flush=True)
     sc = torch.from_numpy(sc_np).to(DEV)
-    for shared in (False, True):
-        idx, cnt = kvc.select_topk(sc, k, n_keep, seq_lens=lens, shared_heads=shared)
+    # shared over heads: dyadic scores (multiples of 2^-20 below 1, at most 8 heads)
+    # add exactly in float, so the GPU's rounded head sum equals the oracle's exact one
+    den = 1 << min(20, max(2, int(levels - 1).bit_length()))
+    dy_np = (rng.integers(0, den, (B, n_kv, s_max)) / den).astype(np.float32)
+    for shared, src_np in ((False, sc_np), (True, dy_np)):
+        idx, cnt = kvc.select_topk(torch.from_numpy(src_np).to(DEV), k, n_keep, seq_lens=lens, shared_heads=shared)
         torch.cuda.synchronize()
-        ri, rc = oracle.select_topk(sc_np, k, n_keep, seq_lens=lens, shared_heads=shared)
+        ri, rc = oracle.select_topk(src_np, k, n_keep, seq_lens=lens, shared_heads=shared)
         assert np.array_equal(host(cnt), rc)
         assert np.array_equal(host(idx), ri)
     kpu = rng.integers(0, k + 1, (B, n_kv)).astype(np.int32)

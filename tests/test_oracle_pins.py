@@ -258,18 +258,59 @@ def test_torch_crosscheck(n_h, n_kv, wic):
     assert torch.allclose(torch.from_numpy(out[0]), ref_out, rtol=1e-12, atol=1e-13)
 
 
-def test_shared_heads_sum_in_float_head_order():
+def test_shared_heads_exact_dyadic_sums():
+    """Scores that are multiples of 2^-8 below 16 add exactly in any float type, so the
+    shared (TSP) score is an integer count of 2^-8 units: the selection is brute-forced
+    on Python integers (no floating point at all), ties and all."""
     rng = np.random.default_rng(31)
-    B, H, S = 2, 5, 64
-    sc = rng.random((B, H, S)).astype(np.float32)
-    idx, count = oracle.select_topk(sc, 10, 4, shared_heads=True)
-    for b in range(B):
-        s = np.zeros(S, np.float32)
-        for g in range(H):
-            s = (s + sc[b, g]).astype(np.float32)
-        order = sorted(range(S - 4), key=lambda t: (-s[t], t))[:10]
-        assert idx[b, 0].tolist() == sorted(order) + list(range(S - 4, S))
-        assert count[b, 0] == 14
+    for B, H, S, k, n_keep, levels in ((2, 5, 64, 10, 4, 7), (1, 32, 300, 57, 32, 3), (3, 8, 129, 0, 8, 50),
+                                       (2, 3, 40, 40, 0, 4), (1, 4, 33, 5, 40, 9)):
+        units = rng.integers(0, levels, size=(B, H, S))
+        sc = (units / 256.0).astype(np.float32)
+        idx, count = oracle.select_topk(sc, k, n_keep, shared_heads=True)
+        assert idx.shape == (B, 1, k + n_keep)
+        for b in range(B):
+            tot = [int(units[b, :, t].sum()) for t in range(S)]
+            C = max(0, S - n_keep)
+            k_eff = min(k, C)
+            best = sorted(range(C), key=lambda t: (-tot[t], t))[:k_eff]
+            want = sorted(best) + list(range(C, S))
+            assert idx[b, 0, :len(want)].tolist() == want
+            assert np.all(idx[b, 0, len(want):] == -1)
+            assert count[b, 0] == len(want)
+
+
+def test_shared_heads_of_identical_heads_equal_per_head_selection():
+    """H identical heads: the summed score is H times each head's, which orders the
+    tokens as one head does, so the shared selection equals the per-head one."""
+    rng = np.random.default_rng(32)
+    for H in (1, 2, 7, 32):
+        one = rng.random((2, 1, 200)).astype(np.float32)
+        one[0, 0, 50:60] = one[0, 0, 10]                       # exact ties too
+        sc = np.repeat(one, H, axis=1)
+        si, sc_count = oracle.select_topk(sc, 37, 16, shared_heads=True)
+        pi, p_count = oracle.select_topk(one, 37, 16)
+        assert np.array_equal(si, pi) and np.array_equal(sc_count, p_count)
+
+
+def test_shared_heads_sum_is_exact_not_float_head_order():
+    """The shared score is the exact sum over heads.  Token 0 holds 1 + 3 * 2^-24
+    spread as 1, 2^-24, 2^-24, 2^-24; token 1 holds 1 + 2^-23 in its first head.
+    Added in float in head order, each 2^-24 is lost (ties to even) and token 1
+    would win; exactly, token 0 is larger and is the one kept."""
+    e = 2.0 ** -24
+    sc = np.zeros((1, 4, 3), np.float32)
+    sc[0, :, 0] = [1.0, e, e, e]
+    sc[0, :, 1] = [1.0 + 2 * e, 0.0, 0.0, 0.0]
+    sc[0, :, 2] = [0.5, 0.0, 0.0, 0.0]
+    f = np.float32(0.0)
+    for g in range(4):
+        f = np.float32(f + sc[0, g, 0])
+    assert f == np.float32(1.0) < sc[0, 0, 1]            # the float head-order sum ranks token 1 first
+    idx, count = oracle.select_topk(sc, 1, 0, shared_heads=True)
+    assert idx.tolist() == [[[0]]] and count.tolist() == [[1]]
+    idx, count = oracle.select_topk(sc, 2, 0, shared_heads=True)
+    assert idx.tolist() == [[[0, 1]]]
 
 
 # ----------------------------------------------------------------------------------
@@ -586,12 +627,49 @@ def test_select_core_bruteforce_and_special_cases():
                 assert np.all(idx[b, h, n:] == -1)
     # no core token: the plain selection; every token core: everything kept
     none = np.zeros((B, S), np.uint8)
-    c_idx, c_cnt = oracle.select_core(sc, none, 3, n_keep, seq_lens=sl, cap=3 + n_keep)
+    c_idx, c_cnt = oracle.select_core(sc, none, 3, n_keep, seq_lens=sl, core_cap=0)
     p_idx, p_cnt = oracle.select_topk(sc, 3, n_keep, seq_lens=sl)
     assert np.array_equal(c_idx, p_idx) and np.array_equal(c_cnt, p_cnt)
     a_idx, a_cnt = oracle.select_core(sc, np.ones((B, S), np.uint8), 3, n_keep, seq_lens=sl)
     for b in range(B):
         assert a_cnt[0 if b == 0 else 1, 0] == sl[b] and a_idx[b, 0, :sl[b]].tolist() == list(range(sl[b]))
+
+
+def test_select_core_over_capacity():
+    """Fewer output slots than the rule needs (core_cap < |Core|): the unit keeps the
+    first k + core_cap candidates of "core by index, then scratch by score".  Pinned
+    through the plain selection (itself brute-forced above): with room for every core
+    token the scratch tokens are the plain top-k over the scratch tokens alone with
+    the budget that is left; without it, the lowest-indexed core tokens."""
+    rng = np.random.default_rng(52)
+    B, H, S, n_keep = 1, 3, 300, 6
+    sc = (rng.integers(0, 40, (B, H, S)) / 39.0).astype(np.float32)
+    core = np.zeros((B, S), np.uint8)
+    core[0, rng.choice(S - n_keep, 50, replace=False)] = 1
+    cores = np.nonzero(core[0, :S - n_keep])[0]
+    window = list(range(S - n_keep, S))
+    big_i, big_c = oracle.select_core(sc, core, 30, n_keep, core_cap=50)
+    for k, core_cap in ((30, 50), (30, 200), (30, 45), (30, 20), (30, 0), (10, 30), (0, 7)):
+        idx, cnt = oracle.select_core(sc, core, k, n_keep, core_cap=core_cap)
+        assert idx.shape == (B, H, k + core_cap + n_keep)
+        room = k + core_cap
+        for h in range(H):
+            n = int(cnt[0, h])
+            got = idx[0, h, :n].tolist()
+            assert np.all(idx[0, h, n:] == -1) and n <= k + core_cap + n_keep
+            if core_cap >= cores.size:
+                # the rule itself: as with ample room
+                if k == 30:
+                    assert got == big_i[0, h, :big_c[0, h]].tolist()
+            if cores.size <= room:
+                left = min(k, room - cores.size)
+                masked = sc.copy()
+                masked[0, :, cores] = -1.0                        # below every scratch score
+                pi, pc = oracle.select_topk(masked[:, h:h + 1], left, n_keep)
+                want = sorted(set(cores.tolist()) | set(pi[0, 0, :left].tolist())) + window
+            else:
+                want = sorted(cores[:room].tolist()) + window
+            assert got == want, (k, core_cap, h)
 
 
 # ----------------------------------------------------------------------------------
