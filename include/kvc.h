@@ -293,6 +293,22 @@ kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const void *kc, 
                            void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * kvc_decode_attn_noalloc -- kvc_decode_attn for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and kernels as kvc_decode_attn, without the
+ * workspace: the split partials go to a static device array of the library, one per
+ * GPU, of 4 MiB (4194304 bytes), held until the process ends.
+ * A shape whose kvc_decode_attn_workspace() exceeds that limit returns
+ * KVC_ERR_WORKSPACE and launches nothing.  The call allocates nothing and needs no
+ * zero-filled memory.  Every call on a GPU uses that GPU's one array: calls that may
+ * overlap on one GPU (other streams, other threads) race and must be ordered by the
+ * caller.
+ */
+kvc_status kvc_decode_attn_noalloc(const kvc_dims *dims, const void *q, const void *kc, const void *vc,
+                                   const int32_t *count, int32_t cap, float scale, void *out, float *lse,
+                                   void *stream);
+
+/*
  * Landmark-guided block selection (xKV 2.3).  The cache of each KV head is cut into
  * n_blk = ceil(s_max / block) blocks of `block` tokens.
  *

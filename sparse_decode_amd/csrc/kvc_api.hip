@@ -258,6 +258,54 @@ KVC_EXPORT kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const
     return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
+// ------------------------------------------------------------ decode without allocation
+// Split partials of kvc_decode_attn_noalloc live in this file-scope device array, one
+// copy per GPU, held until the process ends.  Its host-side name is only a stand-in:
+// host code uses the device address hipGetSymbolAddress returns for the current device.
+static constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The device address of `scratch` on the current device (looked up once per device).
+static hipError_t scratch_ptr(void **out)
+{
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+KVC_EXPORT kvc_status kvc_decode_attn_noalloc(const kvc_dims *dims, const void *q, const void *kc, const void *vc,
+                                              const int32_t *count, int32_t cap, float scale, void *out, float *lse,
+                                              void *stream)
+{
+    kvc_status st = check_dims(dims, false);
+    if (st != KVC_OK) return st;
+    if (cap < 1 || cap > (1 << 30)) return KVC_ERR_INVALID_ARG;
+    if (!q || !kc || !vc || !count || !out) return KVC_ERR_INVALID_ARG;
+    if (!(scale >= 0.f) || scale > 1e30f) return KVC_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(out)) return KVC_ERR_INVALID_ARG;
+    kvc::DecodePlan plan = kvc::plan_decode(dims->batch, dims->n_h, dims->n_kv, dims->d_h, cap, kPlanCus);
+    if (plan.ws_bytes > kNoAllocScratchBytes) return KVC_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (scratch_ptr(&ws) != hipSuccess) return KVC_ERR_HIP;
+    const float sc = scale == 0.f ? 1.0f / sqrtf((float)dims->d_h) : scale;
+    hipError_t e = kvc::launch_decode(dims->batch, dims->n_h, dims->n_kv, dims->d_h, dims->dtype == KVC_BF16, q,
+                                      kc, vc, count, cap, sc, out, lse, ws, plan, (hipStream_t)stream);
+    return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
 // ------------------------------------------------------------------------- query similarity
 
 KVC_EXPORT kvc_status kvc_query_similarity(const kvc_dims *dims, const void *q_cur, const void *q_prev, double tau,

@@ -29,7 +29,7 @@ EXPORTED = (
     "kvc_select_topk_workspace", "kvc_select_topk",
     "kvc_select_core_workspace", "kvc_select_core",
     "kvc_gather_compact",
-    "kvc_decode_attn_workspace", "kvc_decode_attn",
+    "kvc_decode_attn_workspace", "kvc_decode_attn", "kvc_decode_attn_noalloc",
     "kvc_query_similarity",
     "kvc_block_landmarks", "kvc_block_scores", "kvc_expand_blocks",
 )
@@ -74,6 +74,7 @@ def lib():
                 "kvc_gather_compact": (I, [I, I, I, I, P, P, P, P, P, I, I, P, P, P, P, P]),
                 "kvc_decode_attn_workspace": (Z, [D, I]),
                 "kvc_decode_attn": (I, [D, P, P, P, P, I, F, P, P, P, Z, P]),
+                "kvc_decode_attn_noalloc": (I, [D, P, P, P, P, I, F, P, P, P]),
                 "kvc_query_similarity": (I, [D, P, P, ctypes.c_double, P, P, P, P]),
                 "kvc_block_landmarks": (I, [D, P, I, P, P]),
                 "kvc_block_scores": (I, [D, P, P, I, I, F, P, P, P]),
@@ -335,6 +336,24 @@ def decode_attn(q, kc, vc, count, *, scale=0.0, out=None, lse=None, want_lse=Tru
                                float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream())
     _check(st, "kvc_decode_attn")
+    return out, lse
+
+
+DECODE_NOALLOC_LIMIT = 4 << 20   # bytes of the library's static decode scratch, per GPU
+
+
+@on_stream
+def decode_attn_noalloc(q, kc, vc, count, out, lse=None, *, scale=0.0):
+    """kvc_decode_attn_noalloc: decode attention with the library's static scratch
+    (no workspace, nothing allocated here either: out and lse are the caller's)."""
+    for t, nm in ((q, "q"), (kc, "kc"), (vc, "vc"), (count, "count"), (out, "out")):
+        _dev(t, nm)
+    B, n_h, d_h = q.shape
+    _, n_kv, cap, _ = kc.shape
+    dims = make_dims(B, 1, n_h, n_kv, d_h, _dtype_code(q))
+    st = lib().kvc_decode_attn_noalloc(ctypes.byref(dims), _ptr(q), _ptr(kc), _ptr(vc), _ptr(count), int(cap),
+                                       float(scale), _ptr(out), _ptr(lse), _stream())
+    _check(st, "kvc_decode_attn_noalloc")
     return out, lse
 
 

@@ -266,3 +266,18 @@ def test_score_plan_query():
     assert kvc.lib().kvc_score_window_plan(ctypes.byref(_dims()), 0, 0, out) == E
     assert kvc.lib().kvc_score_window_plan(ctypes.byref(_dims()), 32, 0, None) == E
 
+
+def test_decode_noalloc_rejects_invalid_arguments():
+    E, W = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_WORKSPACE
+    L = kvc.lib()
+
+    def call(dims, cap=2080, q=BAD, out=BAD):
+        return L.kvc_decode_attn_noalloc(ctypes.byref(dims) if dims is not None else None, q, BAD, BAD, BAD, cap,
+                                         0.0, out, None, None)
+    assert call(None) == E
+    assert call(_dims(), cap=0) == E
+    assert call(_dims(), q=None) == E
+    assert call(_dims(), out=BAD + 4) == E
+    big = _dims(batch=1024)
+    assert kvc.decode_attn_workspace(big, 128) > kvc.DECODE_NOALLOC_LIMIT
+    assert call(big, cap=128) == W
