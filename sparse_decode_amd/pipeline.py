@@ -214,3 +214,94 @@ class BlockRetrieval:
                           idx=self.idx, count=self.count)
         kvc.gather_compact(k, self.idx, self.count, src1=v, dst0=self.kc, dst1=self.vc, pos_out=self.pos)
         return kvc.decode_attn(q, self.kc, self.vc, self.count, out=self.out, lse=self.lse, ws=self.ws_decode)
+
+
+class TspSchedule:
+    """One decode step of FastKV's layer-by-layer schedule over a whole model's cache
+    (FastKV sections 2.A and 2.B): layers up to and including the propagation layer
+    run score -> select -> gather -> decode over all S cached tokens; at the
+    propagation layer one selection per sequence from the head-summed scores keeps
+    k_tsp tokens plus the window and gathers their hidden states; every later layer
+    runs over those S' = k_tsp + n_keep tokens, its compacted cache keeping their
+    original positions.  The per-layer retention budget (wl.k) and the TSP budget are
+    independent.
+
+    layers   list of per-layer dicts (q_win, k, v, q_dec), one per model layer; the
+             first tsp_layer + 1 hold caches of s_full tokens, the others of s_after
+             tokens (entries may repeat the same tensors)
+    Each layer keeps its own selection and compacted cache (idx, count, kc, vc, pos,
+    out, lse), so a layer's decode reads that layer's cache; score and select scratch
+    is shared by the layers of one length, which run one after another.
+    """
+
+    def __init__(self, wl: Workload, layers, tsp_layer: int, k_tsp: int, seq_full, seq_after, hidden,
+                 device="cuda"):
+        self.wl = wl
+        self.layers = layers
+        self.tsp_layer = int(tsp_layer)
+        self.k_tsp = int(k_tsp)
+        self.s_full = int(layers[0]["k"].shape[2])
+        self.s_after = self.k_tsp + wl.n_keep
+        self.seq_full = seq_full
+        self.seq_after = seq_after
+        self.hidden = hidden
+        dev = torch.device(device)
+        self.full = LayerPath(wl, device=dev, s_max=self.s_full)
+        self.after = LayerPath(wl, device=dev, s_max=self.s_after)
+        self.tsp = TspStep(wl, self.k_tsp, device=dev, s_max=self.s_full)
+        B, nkv, nh, d, cap = wl.batch, wl.n_kv, wl.n_h, wl.d_h, self.full.cap
+        dt = wl.torch_dtype
+        L = len(layers)
+        self.idx = torch.empty((L, B, nkv, cap), dtype=torch.int32, device=dev)
+        self.count = torch.empty((L, B, nkv), dtype=torch.int32, device=dev)
+        self.kc = torch.empty((L, B, nkv, cap, d), dtype=dt, device=dev)
+        self.vc = torch.empty((L, B, nkv, cap, d), dtype=dt, device=dev)
+        self.pos = torch.empty((L, B, nkv, cap), dtype=torch.int32, device=dev)
+        self.out = torch.empty((L, B, nh, d), dtype=dt, device=dev)
+        self.lse = torch.empty((L, B, nh), dtype=torch.float32, device=dev)
+        # the propagation layer's kept original positions, [B][S'], are the later
+        # layers' source positions
+        self.src_pos = self.tsp.pos.view(B, self.s_after)
+
+    def path_of(self, l: int) -> LayerPath:
+        return self.full if l <= self.tsp_layer else self.after
+
+    def seq_of(self, l: int):
+        return self.seq_full if l <= self.tsp_layer else self.seq_after
+
+    def score(self, l: int):
+        x = self.layers[l]
+        self.path_of(l).score(x["q_win"], x["k"], self.seq_of(l))
+
+    def select(self, l: int):
+        p = self.path_of(l)
+        kvc.select_topk(p.pooled, p.k, self.wl.n_keep, seq_lens=self.seq_of(l), idx=self.idx[l],
+                        count=self.count[l], ws=p.ws_select)
+
+    def gather(self, l: int):
+        x = self.layers[l]
+        sp = None if l <= self.tsp_layer else self.src_pos
+        kvc.gather_compact(x["k"], self.idx[l], self.count[l], src1=x["v"], src_pos=sp, dst0=self.kc[l],
+                           dst1=self.vc[l], pos_out=self.pos[l])
+
+    def decode(self, l: int):
+        kvc.decode_attn(self.layers[l]["q_dec"], self.kc[l], self.vc[l], self.count[l], out=self.out[l],
+                        lse=self.lse[l], ws=self.full.ws_decode)
+
+    def propagate(self):
+        """The propagation layer's shared selection and hidden-state gather (its kept
+        original positions are src_pos)."""
+        self.tsp.run(self.full.pooled, self.hidden, self.seq_full)
+
+    def layer(self, l: int):
+        self.score(l)
+        self.select(l)
+        self.gather(l)
+        self.decode(l)
+        if l == self.tsp_layer:
+            self.propagate()
+
+    def step(self):
+        for l in range(len(self.layers)):
+            self.layer(l)
+        return self.out

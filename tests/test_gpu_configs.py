@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from sparse_decode_amd import kvc, synth
-from sparse_decode_amd.pipeline import LayerPath, TspStep
+from sparse_decode_amd.pipeline import LayerPath, TspSchedule, TspStep
 from _parity import assert_decode_close, assert_scores_close, check_selection, host
 
 pytestmark = pytest.mark.gpu
@@ -226,3 +226,46 @@ def test_cfg5_tsp_other_layer_and_rate(tsp_layer, tsp_rate):
     del hidden, ref
     s2 = k_tsp + wl.n_keep
     _layer_parity(wl, tsp_layer + 1, s_max=s2, src_pos=gi[:, 0, :].astype(np.int32), check_planted=False)
+
+
+def test_tsp_schedule_whole_model():
+    # the benchmark's whole-model step (pipeline.TspSchedule) on a 4-layer MHA model of
+    # 4096 tokens, propagation at layer 1 keeping 25 %: every layer's selection,
+    # compacted cache, positions and attention against the oracle, and the propagation
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS[5], layers=4, s_max=4096, tsp_layer=1, tsp_rate=0.25, k=256)
+    k_tsp = synth.budget_from_rate(wl.tsp_rate, wl.s_max)
+    s2 = k_tsp + wl.n_keep
+    _say("tsp schedule", dict(layers=wl.layers, S=wl.s_max, tsp_layer=wl.tsp_layer, k_tsp=k_tsp))
+    xs = [synth.layer_inputs(wl, l, device="cuda", s_max=None if l <= wl.tsp_layer else s2)
+          for l in range(wl.layers)]
+    hidden = synth.hidden_states(wl, device="cuda")
+    seq_full = torch.from_numpy(xs[0]["seq_lens"]).cuda()
+    seq_after = torch.from_numpy(xs[-1]["seq_lens"]).cuda()
+    layers = [{n: x[n] for n in ("q_win", "k", "v", "q_dec")} for x in xs]
+    sched = TspSchedule(wl, layers, wl.tsp_layer, k_tsp, seq_full, seq_after, hidden)
+    sched.step()
+    torch.cuda.synchronize()
+    tsp_pos = host(sched.src_pos).astype(np.int32)
+    for l, x in enumerate(xs):
+        _say("  layer", l)
+        sl = x["seq_lens"]
+        src_pos = None if l <= wl.tsp_layer else tsp_pos
+        _, rpooled = oracle.score_window(host(x["q_win"]), host(x["k"]), wl.w, seq_lens=sl,
+                                         window_in_cache=wl.window_in_cache, n_keep=wl.n_keep, pool=wl.pool)
+        ri, rc = oracle.select_topk(rpooled, wl.k, wl.n_keep, seq_lens=sl)
+        check_selection(sched.idx[l], sched.count[l], ri, rc, rpooled, sl, wl.k, wl.n_keep)
+        gi, gc = host(sched.idx[l]), host(sched.count[l])
+        for src, dst in ((x["k"], sched.kc[l]), (x["v"], sched.vc[l])):
+            ref, ref_pos = oracle.gather(_bits(src), gi, gc, src_pos=src_pos, dst=_bits(dst))
+            assert np.array_equal(_bits(dst), ref)
+        assert np.array_equal(host(sched.pos[l]), ref_pos)
+        ref_out, _ = oracle.decode(host(x["q_dec"]), host(sched.kc[l]), host(sched.vc[l]), gc)
+        assert_decode_close(sched.out[l], ref_out, True)
+        if l == wl.tsp_layer:
+            ti, tc = oracle.select_topk(rpooled, k_tsp, wl.n_keep, seq_lens=sl, shared_heads=True)
+            check_selection(sched.tsp.idx, sched.tsp.count, ti, tc, rpooled, sl, k_tsp, wl.n_keep, shared=True)
+            hi, hc = host(sched.tsp.idx), host(sched.tsp.count)
+            ref, ref_pos = oracle.gather(_bits(hidden).reshape(wl.batch, 1, wl.s_max, wl.hidden), hi, hc)
+            assert np.array_equal(_bits(sched.tsp.hidden_out), ref)
+            assert np.array_equal(tsp_pos, ref_pos[:, 0, :])
