@@ -122,6 +122,10 @@ typedef struct kvc_dims {
 /* kvc_score_window flag: use the portable VALU kernels (any R, d_h, dtype) instead
  * of the bf16 MFMA kernels.  Results agree to the same tolerance; meant for tests. */
 #define KVC_SCORE_GENERIC 1
+/* kvc_score_window flag, for tests: the single-pass kernel does not wait for the row
+ * statistics of any KV head and leaves every item to its follow-up kernel (the path
+ * an item takes when its bounded wait runs out).  Results are identical. */
+#define KVC_SCORE_DEFER_ALL 2
 
 int32_t kvc_abi_version(void);
 const char *kvc_status_str(kvc_status status);
@@ -152,9 +156,12 @@ const char *kvc_status_str(kvc_status status);
  * scale      > 0; 0 means 1/sqrt(d_h)
  * raw        [B][n_kv][s_max] float, written (required)
  * pooled     [B][n_kv][s_max] float, written (required)
- * flags      0 or KVC_SCORE_GENERIC
+ * flags      0, or KVC_SCORE_GENERIC and/or KVC_SCORE_DEFER_ALL
  * ws         at least kvc_score_window_workspace(dims, w, flags) bytes, 16-byte
- *            aligned: per-chunk row statistics (scratch only; any contents)
+ *            aligned, zero-filled before first use: per-item row statistics, and for
+ *            the single-pass kernel per-KV-head arrival counters and a deferred-item
+ *            count (returned to zero by each call that completes); calls with the same
+ *            batch and n_kv may share one workspace without zero-filling it again
  * Arithmetic: fp32 logits (bf16 products are exact), fp32 exp2-based softmax with
  * the row sums accumulated per lane and merged in double; raw agrees with a
  * double-precision evaluation to about 1e-6 relative.  Probabilities below the
@@ -171,9 +178,16 @@ kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void 
  * arguments (it depends on the shapes only), for tests and profiling:
  *   out[0]  1 when the bf16 MFMA kernels run, 0 for the portable kernels
  *   out[1]  MFMA path: blocks of 16 window rows per KV head (1, 2, 4 or 8), else 0
- *   out[2]  MFMA path: tokens per work-group of each pass, else 0
- *   out[3]  MFMA path: work-groups per KV head of each pass, else 0
- * out  int32[4], host memory.  Same argument checks as kvc_score_window_workspace.
+ *   out[2]  MFMA path: tokens per work-group item, else 0
+ *   out[3]  MFMA path: work-group items per KV head, else 0
+ *   out[4]  1 when K is read in a single pass (16 < R <= 32, s_max <= 131072: the row
+ *           statistics are exchanged between the work-groups of a resident grid), 0
+ *           for the two-pass kernels, which a device that cannot hold one work-group
+ *           per 1024-token item of a KV head at once also takes.  Work-groups that
+ *           wait too long for the statistics (two such calls running at the same time
+ *           on other streams, for instance) leave their items to a follow-up kernel
+ *           that re-reads their K: slower, same results
+ * out  int32[5], host memory.  Same argument checks as kvc_score_window_workspace.
  */
 kvc_status kvc_score_window_plan(const kvc_dims *dims, int32_t w, int32_t flags, int32_t *out);
 

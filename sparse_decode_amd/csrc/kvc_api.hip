@@ -87,7 +87,7 @@ static kvc_status score_args(const kvc_dims *d, int32_t w, int32_t flags)
     if (st != KVC_OK) return st;
     if (w < 1 || w > 1024 || (long)(d->n_h / d->n_kv) * w > 1024) return KVC_ERR_INVALID_ARG;
     if (d->s_max > (1 << 22)) return KVC_ERR_UNSUPPORTED;      // byte offsets within a unit fit 31 bits
-    if (flags & ~KVC_SCORE_GENERIC) return KVC_ERR_INVALID_ARG;
+    if (flags & ~(KVC_SCORE_GENERIC | KVC_SCORE_DEFER_ALL)) return KVC_ERR_INVALID_ARG;
     return KVC_OK;
 }
 
@@ -117,8 +117,9 @@ KVC_EXPORT kvc_status kvc_score_window_plan(const kvc_dims *dims, int32_t w, int
                                              dims->dtype == KVC_BF16, w, (flags & KVC_SCORE_GENERIC) != 0, kPlanCus);
     out[0] = p.mfma ? 1 : 0;
     out[1] = p.mfma ? p.rt : 0;
-    out[2] = p.mfma ? p.chunk_tokens : 0;
-    out[3] = p.mfma ? p.n_chunks : 0;
+    out[2] = p.mfma ? (p.single ? p.sp_item : p.chunk_tokens) : 0;
+    out[3] = p.mfma ? (p.single ? p.sp_chunks : p.n_chunks) : 0;
+    out[4] = p.single ? 1 : 0;
     return KVC_OK;
 }
 
@@ -138,6 +139,7 @@ KVC_EXPORT kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, 
     const float sc = scale == 0.f ? 1.0f / sqrtf((float)dims->d_h) : scale;
     kvc::ScorePlan plan = kvc::plan_score(dims->batch, dims->s_max, dims->n_h, dims->n_kv, dims->d_h,
                                           dims->dtype == KVC_BF16, w, (flags & KVC_SCORE_GENERIC) != 0, kPlanCus);
+    if (flags & KVC_SCORE_DEFER_ALL) plan.sp_spin = 0;
     hipError_t e = kvc::launch_score(dims->batch, dims->s_max, dims->seq_lens, dims->n_h, dims->n_kv, dims->d_h,
                                      dims->dtype == KVC_BF16, q_win, k, w, window_in_cache != 0, n_keep,
                                      pool_kernel, sc, raw, pooled, dims->unit_mask, ws, plan, (hipStream_t)stream);

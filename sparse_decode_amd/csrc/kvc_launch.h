@@ -61,6 +61,14 @@ struct ScorePlan {
     int group_units = 0;       // KV-head units per pass-1/pass-2 launch pair
     int logit_rows = 0;        // MFMA path, R <= 16: logits kept per token between the passes
     size_t logits_off = 0;     // their place in the workspace
+    // single-pass MFMA path (R <= 32, S <= 65536): K read once, 256-token items; its
+    // zero-state words open the workspace and the two-pass region (a fallback when too
+    // few work-groups fit the device at once) follows at two_pass_off
+    bool single = false;
+    int sp_chunks = 0;         // items per unit
+    int sp_item = 0;           // tokens per item
+    int sp_spin = 5000;        // bound of an item's wait (100 MHz ticks: 50 us) before it is deferred
+    size_t two_pass_off = 0;
     size_t ws_bytes = 0;
 };
 ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16, int w,

@@ -26,6 +26,8 @@
 // transposed butterfly of DPP lane exchanges.  Both passes evaluate exactly the
 // same MFMA sequence, so their logits are identical.  Exponentials use exp2 with
 // scale * log2(e) folded into one FMA.
+#include <mutex>
+
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -202,8 +204,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restr
                                                             const int32_t *__restrict__ seq_lens, int s_max,
                                                             int n_kv, int n_keep, int half,
                                                             const int32_t *__restrict__ mask,
-                                                            float *__restrict__ pooled)
+                                                            float *__restrict__ pooled, int32_t *reset, int n_reset)
 {
+    // the single-pass kernels' counters go back to zero here, after their last use
+    if (reset && kvc_bid_x() == 0 && kvc_bid_y() == 0)
+        for (int i = kvc_tid(); i < n_reset; i += kPoolThreads) reset[i] = 0;
     // 2 kMaxHalf + 2 slots (left halo, then 16-byte alignment), the body, the right halo
     __shared__ __attribute__((aligned(16))) float tile[2 * kMaxHalf + 2 + kPoolTile + kMaxHalf + 1];
     if constexpr (HALF >= 0) half = HALF;
@@ -262,25 +267,25 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restr
 
 template <bool VEC>
 void launch_pool_vec(dim3 grid, const float *raw, const int32_t *seq_lens, int s_max, int n_kv, int n_keep, int half,
-                     const int32_t *mask, float *pooled, hipStream_t stream)
+                     const int32_t *mask, float *pooled, int32_t *reset, int n_reset, hipStream_t stream)
 {
     switch (half) {
-    case 0: hipLaunchKernelGGL((pool_kernel<VEC, 0>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
-    case 1: hipLaunchKernelGGL((pool_kernel<VEC, 1>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
-    case 2: hipLaunchKernelGGL((pool_kernel<VEC, 2>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
-    case 3: hipLaunchKernelGGL((pool_kernel<VEC, 3>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
-    default: hipLaunchKernelGGL((pool_kernel<VEC, -1>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled); break;
+    case 0: hipLaunchKernelGGL((pool_kernel<VEC, 0>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, reset, n_reset); break;
+    case 1: hipLaunchKernelGGL((pool_kernel<VEC, 1>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, reset, n_reset); break;
+    case 2: hipLaunchKernelGGL((pool_kernel<VEC, 2>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, reset, n_reset); break;
+    case 3: hipLaunchKernelGGL((pool_kernel<VEC, 3>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, reset, n_reset); break;
+    default: hipLaunchKernelGGL((pool_kernel<VEC, -1>), grid, dim3(kPoolThreads), 0, stream, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, reset, n_reset); break;
     }
 }
 
 void launch_pool(const float *raw, const int32_t *seq_lens, int s_max, int units, int n_kv, int n_keep, int half,
-                 const int32_t *mask, float *pooled, hipStream_t stream)
+                 const int32_t *mask, float *pooled, int32_t *reset, int n_reset, hipStream_t stream)
 {
     const dim3 grid((s_max + kPoolTile - 1) / kPoolTile, units);
     if (s_max % 4 == 0 && ((uintptr_t)raw & 15) == 0 && ((uintptr_t)pooled & 15) == 0)
-        launch_pool_vec<true>(grid, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, stream);
+        launch_pool_vec<true>(grid, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, reset, n_reset, stream);
     else
-        launch_pool_vec<false>(grid, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, stream);
+        launch_pool_vec<false>(grid, raw, seq_lens, s_max, n_kv, n_keep, half, mask, pooled, reset, n_reset, stream);
 }
 
 // ====================================================================================
@@ -807,6 +812,557 @@ __global__ __launch_bounds__(kLogitThreads) void logit_probsum_kernel(const floa
     raw[(size_t)u * s_max + t] = acc;
 }
 
+// ====================================================================================
+// Single-pass MFMA path for R <= 32 rows per KV head (MHA or small groups, and the
+// one-query re-scoring of batched decode): K is read once.
+//
+// An item is 1024 consecutive tokens of one unit; each of the four waves of a
+// work-group takes 256 of them (16 tiles of 16 tokens).  K reaches LDS by direct
+// buffer-to-LDS loads, four tiles ahead in a per-wave ring, laid out so that every
+// lane reads back exactly the 16 bytes it loaded as its MFMA operand: no registers
+// hold K in flight and no barrier orders it.  The item's R x 1024 logits stay in
+// registers (query rows on M, tokens on N, as in pass 2 above).
+//
+// A persistent grid of G work-groups takes items j = blockIdx.x, + G, + 2G, ... with
+// G a multiple of the items per unit, so all items of a unit fall in one round and
+// every work-group of a round is resident at once.  For its item a work-group
+//   A  computes the logits, reduces them to the item's per-row (max, sum of exp),
+//      publishes that record and counts the unit's arrival;
+//   B  one round later, once the next item's first K tiles are in flight, waits
+//      until every item of the unit has arrived, merges the unit's records in item
+//      order into the final per-row (M, 1/L), and turns the logits still in registers
+//      into the probability sums of the item's tokens.
+// A never waits and B waits only for items of an earlier round, so the grid cannot
+// deadlock while all of it is resident.  A wait that does not end within a bounded
+// time (a work-group not resident, for instance) puts the item on a deferred list; a
+// follow-up kernel recomputes those items from K once every record is written.
+// Records and arrival counters are written and read with device-scope atomics
+// (coherent across the XCDs' L2 caches); a writer waits for its record stores to
+// complete before the arrival that announces them.
+// ====================================================================================
+constexpr int kSpThreads = 256;
+constexpr int kSpWaves = kSpThreads / kWave;
+constexpr int kSpTiles = 16;                             // 16-token tiles per wave per item
+constexpr int kSpRing = 4;                               // K tiles in flight per wave
+constexpr int kSpItem = 16 * kSpTiles * kSpWaves;        // 1024 tokens
+
+struct SpArgs {
+    const uint16_t *q_win;
+    const uint16_t *k;
+    const int32_t *seq_lens;
+    const int32_t *mask;
+    int s_max, n_h, n_kv, w, wic, R, n_chunks, n_items, G;
+    int spin;                 // bound of a wait, 100 MHz ticks (0: defer every item)
+    int fix_g;                // work-groups of the follow-up kernel
+    float c;                  // scale * log2(e)
+    float *raw;               // [units][s_max]
+    int32_t *arrive;          // [units] items that published their record (zero between calls)
+    int32_t *defer_n;         // deferred items (zero between calls)
+    int32_t *gen;             // [units] bumped once per call when the unit's statistics are final
+    int32_t *defer;           // [n_items]
+    unsigned long long *rec;  // [units][n_chunks][16 RT] packed (m, l) per item and row
+    unsigned long long *fin;  // [units][16 RT] packed final (-M c, 1/L)
+};
+
+__device__ __forceinline__ unsigned long long pack2(float a, float b)
+{
+    return (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+}
+__device__ __forceinline__ float unpack_lo(unsigned long long v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float unpack_hi(unsigned long long v) { return __uint_as_float((uint32_t)(v >> 32)); }
+
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's earlier memory operations (its stores too) have completed.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v)
+{
+    return fmaxf(v, dpp_f<CTRL>(v));
+}
+// Max over the 16 lanes of a row (same pairings as row16_sum).
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = dpp_max<kDppRowMirror>(v);
+    v = dpp_max<kDppHalfMirror>(v);
+    v = dpp_max<kDppXor2>(v);
+    v = dpp_max<kDppXor1>(v);
+    return v;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Waits until at most N vector memory operations of this wave are outstanding (the
+// direct-to-LDS loads of a ring slot have landed once the later ones are all that is
+// left); N is a constant after unrolling.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Waits until this wave's LDS reads have returned (before a ring slot is refilled).
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Work-group barrier that orders LDS accesses only: the direct-to-LDS loads of K stay in
+// flight across it (a full barrier would wait for every outstanding load).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct SpItem {
+    int u, b, g, ch, t0, S;
+    bool active;              // unit not masked and the item holds cached tokens
+    bool zero;                // unit not masked, item past the cached tokens: raw = 0
+};
+
+__device__ __forceinline__ SpItem sp_item(const SpArgs &a, int j)
+{
+    SpItem it;
+    it.u = j / a.n_chunks;
+    it.ch = j - it.u * a.n_chunks;
+    it.b = it.u / a.n_kv;
+    it.g = it.u - it.b * a.n_kv;
+    it.t0 = it.ch * kSpItem;
+    it.S = clamp_len(a.seq_lens, it.b, a.s_max);
+    const bool on = !a.mask || ld_uniform(a.mask, it.u) != 0;
+    it.active = on && it.t0 < it.S;
+    it.zero = on && !it.active && it.t0 < a.s_max;
+    return it;
+}
+
+template <int D, int RT>
+struct Sp {
+    static constexpr int KS = D / 32;
+    static constexpr int ROWS = 16 * RT;
+    static constexpr int QROWB = 2 * D + 16;             // LDS bytes per query row (padded: distinct banks)
+    static constexpr int SLOT = 16 * 2 * D;              // LDS bytes of one wave's tile
+
+    // First token of the wave's share of an item.
+    __device__ static int wave_t0(const SpItem &it, int wv) { return it.t0 + wv * 16 * kSpTiles; }
+
+    // Direct loads of one 16-token tile of the wave's share into its LDS slot.  Every
+    // load instruction reads 1 KB of contiguous rows (64 / CPR whole rows of CPR 16-byte
+    // chunks); lane l's chunk lands at slot + 1024 i + 16 l.  Chunk c of row r is stored
+    // at position c ^ (r % CPR) of the row (an XOR swizzle), so that the 16 lanes reading
+    // one chunk column of 16 rows as an MFMA operand hit distinct banks.  Rows at or past
+    // S read as zero.
+    static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+    __device__ static void load_tile(__amdgpu_buffer_rsrc_t rs, int tb, int n, int kg, unsigned char *slot)
+    {
+        const int l = 16 * kg + n;
+        constexpr int RPI = kWave / CPR;                 // rows per load instruction
+#pragma unroll
+        for (int i = 0; i < 16 / RPI; ++i) {
+            const int row = RPI * i + l / CPR;
+            const int chunk = (l % CPR) ^ (row % CPR);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(slot + i * kWave * 16), 16,
+                                                     (tb + row) * (2 * D) + chunk * 16, 0, 0, kAuxNt);
+        }
+    }
+
+    // This thread's share of the unit's query rows (rows >= R repeat row R - 1; they are
+    // masked out): QV 16-byte vectors, fetched ahead of the item and stored to LDS later.
+    static constexpr int QV = (ROWS * (D / 8) + kSpThreads - 1) / kSpThreads;
+    __device__ static void fetch_q(const SpArgs &a, const SpItem &it, u32x4 *qr)
+    {
+        const int r = a.n_h / a.n_kv;
+        const uint16_t *q0 = a.q_win + (size_t)(it.b * a.n_h + it.g * r) * a.w * D;
+        constexpr int VPR = D / 8;
+#pragma unroll
+        for (int v = 0; v < QV; ++v) {
+            const int i = min((int)kvc_tid() + v * kSpThreads, ROWS * VPR - 1);
+            const int row = i / VPR, col = i - row * VPR;
+            qr[v] = *((const u32x4 *)(q0 + (size_t)min(row, a.R - 1) * D) + col);
+        }
+    }
+    __device__ static void store_q(const u32x4 *qr, unsigned char *q_lds)
+    {
+        constexpr int VPR = D / 8;
+#pragma unroll
+        for (int v = 0; v < QV; ++v) {
+            const int i = (int)kvc_tid() + v * kSpThreads;
+            const int row = i / VPR, col = i - row * VPR;
+            if (i < ROWS * VPR) *(u32x4 *)(q_lds + row * QROWB + col * 16) = qr[v];
+        }
+    }
+
+    // Last visible token of each of this lane's rows (cb*16 + 4 kg + jj); -1 for rows >= R.
+    __device__ static void last_of(const SpArgs &a, const SpItem &it, int kg, int (*last)[4])
+    {
+#pragma unroll
+        for (int cb = 0; cb < RT; ++cb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = cb * 16 + 4 * kg + jj;
+                last[cb][jj] = r >= a.R ? -1 : (a.wic ? min(it.S - a.w + r % a.w, it.S - 1) : it.S - 1);
+            }
+    }
+
+    // Logits of one tile from its LDS slot: lane (kg, n) holds token t = tb + n for rows
+    // cb*16 + 4 kg + jj; invisible (row, token) pairs are -inf.
+    __device__ static void tile_logits(const unsigned char *slot, const unsigned char *q_lds, int tb, int n, int kg,
+                                       const int (*last)[4], float (*lg)[4])
+    {
+        u32x4 kb[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            kb[s] = *(const u32x4 *)(slot + n * (2 * D) + (((4 * s + kg) ^ (n % CPR)) * 16));
+        const int t = tb + n;
+#pragma unroll
+        for (int cb = 0; cb < RT; ++cb) {
+            f32x4_t acc = {};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 qv = *(const u32x4 *)(q_lds + (cb * 16 + n) * QROWB + (4 * s + kg) * 16);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qv), as_bf16x8(kb[s]), acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) lg[cb][jj] = t <= last[cb][jj] ? acc[jj] : -INFINITY;
+        }
+    }
+
+    // The item's raw scores from its logits and the unit's final (-M c, 1/L).
+    __device__ static void finish(const SpArgs &a, const SpItem &it, const float (*lg)[RT][4], const float2 *fin,
+                                  int wv, int n, int kg)
+    {
+        float nmc[RT][4], il[RT][4];
+#pragma unroll
+        for (int cb = 0; cb < RT; ++cb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float2 f = fin[cb * 16 + 4 * kg + jj];
+                nmc[cb][jj] = f.x;
+                il[cb][jj] = f.y;
+            }
+        const int tw = wave_t0(it, wv);
+        float *out = a.raw + (size_t)it.u * a.s_max;
+#pragma unroll
+        for (int p = 0; p < kSpTiles; ++p) {
+            float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < RT; ++cb) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float e = fast_exp2(fmaf(lg[p][cb][jj], a.c, nmc[cb][jj]));   // -inf: 0
+                    if (jj & 1) v1 = fmaf(e, il[cb][jj], v1);
+                    else v0 = fmaf(e, il[cb][jj], v0);
+                }
+            }
+            const float v = v0 + v1;
+            const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+            const float v2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+            const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2), false, false);
+            const float v4 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+            const int t = tw + 16 * p + n;
+            if (kg == 0 && t < a.s_max) out[t] = t < it.S ? v4 : 0.f;
+        }
+    }
+};
+
+// The unit's final per-row (-M c, 1/L) from its items' records, merged in item order
+// (a thread per (row, slice of items), every record load of a thread in flight at
+// once, then the slices in order); left in fin[ROWS] in LDS.  Every thread calls it.
+template <int ROWS>
+__device__ __forceinline__ void sp_merge(const SpArgs &a, int u, int n_u, bool dev, float *mg_m, double *mg_l,
+                                         float2 *fin)
+{
+    constexpr int SL = kSpThreads / ROWS;
+    constexpr int PER = 8;                                // records per thread per batch
+    const int tid = kvc_tid();
+    const int row = tid % ROWS, sl = tid / ROWS;
+    const unsigned long long *rp = a.rec + (size_t)u * a.n_chunks * ROWS + row;
+    float M = -INFINITY;
+    double L = 0.0;
+    for (int c0 = sl; c0 < n_u; c0 += PER * SL) {
+        unsigned long long v[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const unsigned long long *p = rp + (size_t)min(c0 + q * SL, n_u - 1) * ROWS;
+            v[q] = dev ? ld_dev(p) : *p;
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (c0 + q * SL >= n_u) continue;
+            const float m2 = unpack_lo(v[q]), l2 = unpack_hi(v[q]);
+            if (m2 == -INFINITY) continue;
+            if (m2 > M) {
+                L = L * (double)fast_exp2((M - m2) * a.c) + (double)l2;
+                M = m2;
+            } else {
+                L += (double)l2 * (double)fast_exp2((m2 - M) * a.c);
+            }
+        }
+    }
+    mg_m[tid] = M;
+    mg_l[tid] = L;
+    __syncthreads();
+    if (tid < ROWS) {
+        float Mt = -INFINITY;
+        for (int s2 = 0; s2 < SL; ++s2) Mt = fmaxf(Mt, mg_m[s2 * ROWS + tid]);
+        float2 res = make_float2(0.f, 0.f);
+        if (tid < a.R && Mt != -INFINITY) {
+            double Lt = 0.0;
+            for (int s2 = 0; s2 < SL; ++s2) {
+                const float ms = mg_m[s2 * ROWS + tid];
+                if (ms != -INFINITY) Lt += mg_l[s2 * ROWS + tid] * (double)fast_exp2((ms - Mt) * a.c);
+            }
+            if (Lt > 0.0) res = make_float2(-Mt * a.c, (float)(1.0 / Lt));
+        }
+        fin[tid] = res;
+    }
+    __syncthreads();
+}
+
+// The item's 16 tiles of one wave through the ring: before tile P is read, only the
+// loads of the tiles issued after it may still be in flight; once its LDS reads have
+// returned, its slot is refilled with tile P + 4.
+template <int D, int RT, int P>
+__device__ __forceinline__ void sp_tiles(__amdgpu_buffer_rsrc_t rs, unsigned char *const *slot,
+                                         const unsigned char *q_lds, int tw, int n, int kg, const int (*last)[4],
+                                         float (*lg)[RT][4])
+{
+    if constexpr (P < kSpTiles) {
+        using S = Sp<D, RT>;
+        constexpr int later = (P + kSpRing < kSpTiles ? P + kSpRing : kSpTiles) - (P + 1);
+        vm_wait<S::KS * later>();
+        S::tile_logits(slot[P % kSpRing], q_lds, tw + 16 * P, n, kg, last, lg[P]);
+        if constexpr (P + kSpRing < kSpTiles) {
+            lds_reads_done();
+            S::load_tile(rs, tw + 16 * (P + kSpRing), n, kg, slot[P % kSpRing]);
+        }
+        sp_tiles<D, RT, P + 1>(rs, slot, q_lds, tw, n, kg, last, lg);
+    }
+}
+
+template <int D, int RT>
+__global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_single_kernel(SpArgs a)
+{
+    using P = Sp<D, RT>;
+    constexpr int ROWS = P::ROWS;
+    __shared__ __attribute__((aligned(16))) unsigned char ring0[kSpWaves * P::SLOT];
+    __shared__ __attribute__((aligned(16))) unsigned char ring1[kSpWaves * P::SLOT];
+    __shared__ __attribute__((aligned(16))) unsigned char ring2[kSpWaves * P::SLOT];
+    __shared__ __attribute__((aligned(16))) unsigned char ring3[kSpWaves * P::SLOT];
+    __shared__ __attribute__((aligned(16))) unsigned char q_lds[ROWS * P::QROWB];
+    __shared__ float sm_m[kSpWaves][ROWS];
+    __shared__ float sm_l[kSpWaves][ROWS];
+    __shared__ double mg_l[kSpThreads];
+    __shared__ float mg_m[kSpThreads];
+    __shared__ float2 sh_fin[ROWS];
+    __shared__ int sh_int[2];
+
+    const int tid = kvc_tid();
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, kg = lane >> 4;
+    // the wave's four ring slots, one LDS array each so that reading one slot waits only
+    // for the loads into it
+    unsigned char *const slot[kSpRing] = {ring0 + wv * P::SLOT, ring1 + wv * P::SLOT, ring2 + wv * P::SLOT,
+                                          ring3 + wv * P::SLOT};
+
+    float lg[kSpTiles][RT][4];
+    u32x4 qr[P::QV];
+    SpItem prev;
+    prev.active = false;
+    int prev_g0 = 0;          // thread 0: the generation the previous item waits past
+
+    // an item's query rows (to registers) and first ring of K tiles, issued ahead of it;
+    // issued for every item (an inactive one reads unit 0's queries and no K: an empty
+    // range), so that the same number of loads is in flight on every path
+    auto prefetch = [&](const SpItem &x) {
+        SpItem y = x;
+        if (!x.active) {
+            y.u = y.b = y.g = 0;
+            y.t0 = 0;
+        }
+        P::fetch_q(a, y, qr);
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc(a.k + (size_t)y.u * a.s_max * D, x.active ? x.S * (2 * D) : 0);
+#pragma unroll
+        for (int p = 0; p < kSpRing; ++p) P::load_tile(rs, P::wave_t0(y, wv) + 16 * p, n, kg, slot[p]);
+    };
+
+    SpItem it;
+    it.active = false;
+    it.zero = false;
+    if ((int)kvc_bid_x() < a.n_items) it = sp_item(a, kvc_bid_x());
+    prefetch(it);
+    for (int j = kvc_bid_x();; j += a.G) {
+        const bool have = j < a.n_items;
+
+        // ---- B: the previous item, once its unit's statistics are final
+        if (prev.active) {
+            if (tid == 0) {
+                // wait at most a.spin ticks of the 100 MHz real-time counter
+                int ok = 0;
+                const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + (uint64_t)a.spin;
+                for (bool first = true; first || __builtin_amdgcn_s_memrealtime() < t_end; first = false) {
+                    if (a.spin &&
+                        __hip_atomic_load(a.gen + prev.u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != prev_g0) {
+                        ok = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (!ok) {
+                    const int slot_i = __hip_atomic_fetch_add(a.defer_n, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    a.defer[slot_i] = (int)(prev.u * a.n_chunks + prev.ch);
+                }
+                sh_int[0] = ok;
+            }
+            lds_barrier();
+            if (sh_int[0]) {
+                if (tid < ROWS) {
+                    const unsigned long long f = ld_dev(a.fin + (size_t)prev.u * ROWS + tid);
+                    sh_fin[tid] = make_float2(unpack_lo(f), unpack_hi(f));
+                }
+                lds_barrier();
+                P::finish(a, prev, lg, sh_fin, wv, n, kg);
+            }
+        }
+        if (!have) break;
+        if (it.zero) {
+            float *out = a.raw + (size_t)it.u * a.s_max;
+            for (int t = it.t0 + tid; t < it.t0 + kSpItem && t < a.s_max; t += kSpThreads) out[t] = 0.f;
+        }
+        prev = it;
+        const int jn = j + a.G;
+        SpItem nx;
+        nx.active = false;
+        nx.zero = false;
+        if (jn < a.n_items) nx = sp_item(a, jn);
+        if (!it.active) {
+            prefetch(nx);
+            it = nx;
+            continue;
+        }
+
+        // ---- A: this item's logits and per-row statistics, published as its record
+        lds_barrier();                   // no wave still reads the previous item's queries
+        P::store_q(qr, q_lds);
+        lds_barrier();
+        int last[RT][4];
+        P::last_of(a, it, kg, last);
+        {
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.k + (size_t)it.u * a.s_max * D, it.S * (2 * D));
+            sp_tiles<D, RT, 0>(rs, slot, q_lds, P::wave_t0(it, wv), n, kg, last, lg);
+        }
+#pragma unroll
+        for (int cb = 0; cb < RT; ++cb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float m = lg[0][cb][jj];
+#pragma unroll
+                for (int p = 1; p < kSpTiles; ++p) m = fmaxf(m, lg[p][cb][jj]);
+                m = row16_max(m);
+                if (n == 0) sm_m[wv][cb * 16 + 4 * kg + jj] = m;
+            }
+        lds_barrier();
+#pragma unroll
+        for (int cb = 0; cb < RT; ++cb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = cb * 16 + 4 * kg + jj;
+                float m = sm_m[0][r];
+#pragma unroll
+                for (int x = 1; x < kSpWaves; ++x) m = fmaxf(m, sm_m[x][r]);
+                float s0 = 0.f, s1 = 0.f;
+                if (m != -INFINITY) {
+                    const float nm = -m * a.c;
+#pragma unroll
+                    for (int p = 0; p < kSpTiles; p += 2) {
+                        s0 += fast_exp2(fmaf(lg[p][cb][jj], a.c, nm));
+                        s1 += fast_exp2(fmaf(lg[p + 1][cb][jj], a.c, nm));
+                    }
+                }
+                const float s = row16_sum(s0 + s1);
+                if (n == 0) sm_l[wv][r] = s;
+            }
+        lds_barrier();
+        if (tid < ROWS) {
+            float m = sm_m[0][tid];
+            for (int x = 1; x < kSpWaves; ++x) m = fmaxf(m, sm_m[x][tid]);
+            float l = 0.f;
+            for (int x = 0; x < kSpWaves; ++x) l += sm_l[x][tid];
+            st_dev(a.rec + ((size_t)it.u * a.n_chunks + it.ch) * ROWS + tid, pack2(m, l));
+            stores_done();               // nothing else is in flight here
+        }
+        lds_barrier();
+        const int n_u = (it.S + kSpItem - 1) / kSpItem;
+        int g0 = 0, old = 0;
+        if (tid == 0) {
+            // the generation before this item arrives (only the unit's last arrival bumps it)
+            g0 = __hip_atomic_load(a.gen + it.u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __hip_atomic_fetch_add(a.arrive + it.u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // the next item's queries and first K tiles fly from here on, across the previous
+        // item's wait and finish
+        prefetch(nx);
+        if (tid == 0) {
+            prev_g0 = g0;
+            sh_int[1] = old == n_u - 1;
+        }
+        lds_barrier();
+        if (sh_int[1]) {
+            // the unit's last item: merge the records, publish the final statistics
+            sp_merge<ROWS>(a, it.u, n_u, true, mg_m, mg_l, sh_fin);
+            if (tid < ROWS) {
+                st_dev(a.fin + (size_t)it.u * ROWS + tid, pack2(sh_fin[tid].x, sh_fin[tid].y));
+                stores_done();
+            }
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_add(a.gen + it.u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        it = nx;
+    }
+}
+
+// Items whose wait ran out: recomputed from K (the same logits) with the unit's
+// statistics merged from its records, every record being written by now (a kernel
+// boundary later).  Work-group i takes deferred items i, i + grid, ...; the pooling
+// kernel that follows returns the arrival counters and the deferred count to zero.
+template <int D, int RT>
+__global__ __launch_bounds__(kSpThreads) void mfma_single_fixup_kernel(SpArgs a)
+{
+    using P = Sp<D, RT>;
+    constexpr int ROWS = P::ROWS;
+    __shared__ __attribute__((aligned(16))) unsigned char ring0[kSpWaves * P::SLOT];
+    __shared__ __attribute__((aligned(16))) unsigned char q_lds[ROWS * P::QROWB];
+    __shared__ double mg_l[kSpThreads];
+    __shared__ float mg_m[kSpThreads];
+    __shared__ float2 sh_fin[ROWS];
+    const int tid = kvc_tid();
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, kg = lane >> 4;
+    unsigned char *const slot = ring0 + wv * P::SLOT;
+    const int nd = *a.defer_n;
+    for (int i = kvc_bid_x(); i < nd; i += a.fix_g) {
+        const SpItem it = sp_item(a, a.defer[i]);
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.k + (size_t)it.u * a.s_max * D, it.S * (2 * D));
+        const int tw = P::wave_t0(it, wv);
+        float lg[kSpTiles][RT][4];
+        u32x4 qr[P::QV];
+        P::fetch_q(a, it, qr);
+        P::store_q(qr, q_lds);
+        sp_merge<ROWS>(a, it.u, (it.S + kSpItem - 1) / kSpItem, false, mg_m, mg_l, sh_fin);   // orders q_lds too
+        int last[RT][4];
+        P::last_of(a, it, kg, last);
+#pragma unroll
+        for (int p = 0; p < kSpTiles; ++p) {
+            lds_reads_done();
+            P::load_tile(rs, tw + 16 * p, n, kg, slot);
+            vm_wait<0>();
+            P::tile_logits(slot, q_lds, tw + 16 * p, n, kg, last, lg[p]);
+        }
+        P::finish(a, it, lg, sh_fin, wv, n, kg);
+        __syncthreads();
+    }
+}
+
 template <int D, int RT>
 void launch_mfma_group(const MfArgs &a, int group_units, hipStream_t stream)
 {
@@ -838,6 +1394,81 @@ void launch_mfma_group_rt(int rt, const MfArgs &a, int group_units, hipStream_t 
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the single-pass path: the words that must be zero between calls come
+// first and depend on the unit count only.
+struct SpLayout {
+    size_t arrive_off, defer_n_off, gen_off, defer_off, rec_off, fin_off, bytes;
+};
+
+// The arrival counters and the deferred count (units + 1 words, zero between calls)
+// open the workspace; the generation words (any value) follow.
+SpLayout sp_layout(int units, int n_chunks, int rows)
+{
+    SpLayout L;
+    size_t off = 0;
+    L.arrive_off = off;
+    off += (size_t)units * sizeof(int32_t);
+    L.defer_n_off = off;
+    off += sizeof(int32_t);
+    L.gen_off = off;
+    off = align256(off + (size_t)units * sizeof(int32_t));
+    L.defer_off = off;
+    off = align256(off + (size_t)units * n_chunks * sizeof(int32_t));
+    L.rec_off = off;
+    off = align256(off + (size_t)units * n_chunks * rows * sizeof(unsigned long long));
+    L.fin_off = off;
+    off = align256(off + (size_t)units * rows * sizeof(unsigned long long));
+    L.bytes = off;
+    return L;
+}
+
+// Work-groups of the single-pass kernel that fit the current device at once (cached
+// per device and instance).
+template <int D, int RT>
+hipError_t sp_capacity(long *cap)
+{
+    static std::mutex mu;
+    static long cache[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < 64 && cache[dev]) {
+        *cap = cache[dev];
+        return hipSuccess;
+    }
+    DeviceInfo di;
+    if ((e = device_info(&di)) != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(mfma_single_kernel<D, RT>),
+                                                     kSpThreads, 0);
+    if (e != hipSuccess) return e;
+    *cap = (long)nb * di.cus;
+    if (dev >= 0 && dev < 64) cache[dev] = *cap;
+    return hipSuccess;
+}
+
+// Launches the single-pass kernel and its follow-up; *done = false (nothing launched)
+// when a unit's items would not fit one resident round.
+template <int D, int RT>
+hipError_t launch_single(const SpArgs &a0, bool *done, hipStream_t stream)
+{
+    *done = false;
+    long cap = 0;
+    hipError_t e = sp_capacity<D, RT>(&cap);
+    if (e != hipSuccess) return e;
+    if (cap < a0.n_chunks) return hipSuccess;
+    SpArgs a = a0;
+    long G = cap < a.n_items ? cap : a.n_items;
+    G = G / a.n_chunks * a.n_chunks;
+    a.G = (int)G;
+    a.fix_g = (int)G;
+    hipLaunchKernelGGL((mfma_single_kernel<D, RT>), dim3((unsigned)G), dim3(kSpThreads), 0, stream, a);
+    hipLaunchKernelGGL((mfma_single_fixup_kernel<D, RT>), dim3((unsigned)a.fix_g), dim3(kSpThreads), 0, stream, a);
+    *done = true;
+    return hipGetLastError();
+}
 
 }  // namespace
 
@@ -873,6 +1504,21 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
         p.logit_rows = rt == 1 ? (p.R + 3) / 4 * 4 : 0;
         p.logits_off = p.ws_bytes;
         if (p.logit_rows) p.ws_bytes += align256((size_t)units * s_max * p.logit_rows * sizeof(float));
+        const long items = ((long)s_max + kSpItem - 1) / kSpItem;
+        if (rt == 2 && items <= 128) {
+            // one pass over K for 17..32 rows: a resident grid of at least half a
+            // work-group per CU holds a unit's items (at most 128 of 1024 tokens) in one
+            // round.  A single row block (R <= 16) keeps the two-kernel path above, whose
+            // second kernel reads 4 R bytes of logits per token instead of K: measured
+            // faster for one query per head of the batched ragged decode
+            p.single = true;
+            p.sp_chunks = (int)items;
+            p.sp_item = kSpItem;
+            const SpLayout L = sp_layout(units, p.sp_chunks, rpad);
+            p.two_pass_off = L.bytes;
+            p.logits_off += L.bytes;
+            p.ws_bytes += L.bytes;
+        }
     } else {
         p.group_units = units;
         p.ws_bytes = align256((size_t)units * p.R * s_max * sizeof(float)) +
@@ -887,9 +1533,45 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
                         const ScorePlan &plan, hipStream_t stream)
 {
     const int units = batch * n_kv;
-    if (plan.mfma) {
+    void *const ws_base = ws;
+    bool single_done = false;
+    if (plan.mfma && plan.single) {
+        const SpLayout L = sp_layout(units, plan.sp_chunks, plan.rt * 16);
+        char *w8 = (char *)ws;
+        SpArgs a;
+        a.q_win = (const uint16_t *)q_win;
+        a.k = (const uint16_t *)k;
+        a.seq_lens = seq_lens;
+        a.mask = unit_mask;
+        a.s_max = s_max;
+        a.n_h = n_h;
+        a.n_kv = n_kv;
+        a.w = w;
+        a.wic = window_in_cache ? 1 : 0;
+        a.R = plan.R;
+        a.n_chunks = plan.sp_chunks;
+        a.n_items = units * plan.sp_chunks;
+        a.G = 0;
+        a.spin = plan.sp_spin;
+        a.c = scale * kLog2e;
+        a.raw = raw;
+        a.arrive = (int32_t *)(w8 + L.arrive_off);
+        a.defer_n = (int32_t *)(w8 + L.defer_n_off);
+        a.gen = (int32_t *)(w8 + L.gen_off);
+        a.fin = (unsigned long long *)(w8 + L.fin_off);
+        a.defer = (int32_t *)(w8 + L.defer_off);
+        a.rec = (unsigned long long *)(w8 + L.rec_off);
+        hipError_t e;
+        if (d_h == 128) e = plan.rt == 1 ? launch_single<128, 1>(a, &single_done, stream)
+                                         : launch_single<128, 2>(a, &single_done, stream);
+        else e = plan.rt == 1 ? launch_single<64, 1>(a, &single_done, stream)
+                              : launch_single<64, 2>(a, &single_done, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (plan.mfma && !single_done) {
         const int rt = plan.rt;
         const int rpad = rt * 16;
+        ws = (char *)ws + plan.two_pass_off;
         MfArgs a;
         a.q_win = (const uint16_t *)q_win;
         a.k = (const uint16_t *)k;
@@ -908,7 +1590,7 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         a.raw = raw;
         a.mask = unit_mask;
         a.rs = plan.logit_rows;
-        a.logits = plan.logit_rows ? (float *)((char *)ws + plan.logits_off) : nullptr;
+        a.logits = plan.logit_rows ? (float *)((char *)ws + plan.logits_off - plan.two_pass_off) : nullptr;
         for (int u0 = 0; u0 < units; u0 += plan.group_units) {
             const int gu = min(plan.group_units, units - u0);
             a.unit0 = u0;
@@ -917,7 +1599,7 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-    } else {
+    } else if (!plan.mfma) {
         float *logits = (float *)ws;
         float2 *fin = (float2 *)((char *)ws + align256((size_t)units * plan.R * s_max * sizeof(float)));
         dim3 gtok((s_max + kGenThreads - 1) / kGenThreads, units);
@@ -935,7 +1617,10 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    launch_pool(raw, seq_lens, s_max, units, n_kv, n_keep, pool / 2, unit_mask, pooled, stream);
+    // after the single-pass kernels the pooling kernel zeroes their arrival counters and
+    // deferred count (laid out first in the workspace: units + 1 words)
+    int32_t *reset = single_done ? (int32_t *)ws_base : nullptr;
+    launch_pool(raw, seq_lens, s_max, units, n_kv, n_keep, pool / 2, unit_mask, pooled, reset, units + 1, stream);
     return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP
 KVC_F32, KVC_BF16 = 0, 1
 KVC_SELECT_SHARED_HEADS = 1
 KVC_SCORE_GENERIC = 1
+KVC_SCORE_DEFER_ALL = 2
 
 EXPORTED = (
     "kvc_abi_version", "kvc_status_str",
@@ -175,14 +176,15 @@ def score_window_workspace(dims: Dims, w: int, flags: int = 0) -> int:
 
 def score_window_plan(dims: Dims, w: int, flags: int = 0) -> dict:
     """kvc_score_window_plan: the launch configuration of kvc_score_window for dims."""
-    out = (ctypes.c_int32 * 4)()
+    out = (ctypes.c_int32 * 5)()
     _check(lib().kvc_score_window_plan(ctypes.byref(dims), int(w), int(flags), out), "kvc_score_window_plan")
-    return {"mfma": bool(out[0]), "rt": int(out[1]), "chunk_tokens": int(out[2]), "chunks_per_unit": int(out[3])}
+    return {"mfma": bool(out[0]), "rt": int(out[1]), "chunk_tokens": int(out[2]), "chunks_per_unit": int(out[3]),
+            "single_pass": bool(out[4])}
 
 
 @on_stream
 def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=None, pool=1, scale=0.0,
-                 generic=False, raw=None, pooled=None, ws=None, unit_mask=None):
+                 generic=False, defer_all=False, raw=None, pooled=None, ws=None, unit_mask=None):
     """kvc_score_window: q_win [B][n_h][w][d_h], k [B][n_kv][s_max][d_h] -> (raw, pooled) fp32.
     With unit_mask ([B][n_kv] int32), units whose entry is 0 are skipped."""
     _dev(q_win, "q_win")
@@ -194,7 +196,7 @@ def score_window(q_win, k, w, *, seq_lens=None, window_in_cache=True, n_keep=Non
     sl = _seq_lens(seq_lens, k.device)
     um = _mask(unit_mask, (B, n_kv), k.device)
     dims = make_dims(B, s_max, n_h, n_kv, d_h, _dtype_code(k), sl, um)
-    flags = KVC_SCORE_GENERIC if generic else 0
+    flags = (KVC_SCORE_GENERIC if generic else 0) | (KVC_SCORE_DEFER_ALL if defer_all else 0)
     if n_keep is None:
         n_keep = w
     if raw is None:

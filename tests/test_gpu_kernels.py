@@ -395,6 +395,71 @@ def test_score_unit_mask():
     assert bool((raw[~on] == -7.0).all()) and bool((pooled[~on] == -9.0).all())
 
 
+def _plan(B, n_h, n_kv, d, s_max, w):
+    return kvc.score_window_plan(kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16), w)
+
+
+def test_score_single_pass_shapes():
+    # 17..32 rows per KV head read K once (1024-token items exchanging row statistics)
+    cases = [
+        (2, 8, 8, 128, 4097, 32, [4097, 2000], True, 0),        # MHA, R = 32, ragged tail item
+        (3, 8, 8, 128, 1000, 32, [20, 0, 1000], True, 1),        # rows that see no key, an empty unit
+        (2, 8, 8, 64, 3000, 32, [3000, 1024], True, 2),          # d_h = 64, a unit of exactly one item
+        (2, 12, 4, 128, 2600, 8, [2600, 1025], True, 3),         # R = 24: rows 24..31 padding
+        (2, 4, 4, 128, 9000, 32, [9000, 8193], True, 4),         # R = 32, 1024-token items and a tail
+        (4, 16, 8, 128, 3000, 16, [3000, 1, 1023, 2049], False, 5),  # R = 32, queries not in the cache
+    ]
+    for B, n_h, n_kv, d, s_max, w, sl, wic, seed in cases:
+        plan = _plan(B, n_h, n_kv, d, s_max, w)
+        assert plan["single_pass"], plan
+        _score_case(B, n_h, n_kv, d, s_max, w, np.array(sl, np.int32), wic=wic, n_keep=max(w, 8), seed=20 + seed,
+                    planted=10 if s_max > 2000 else 0)
+
+
+def test_score_single_pass_deferred_items():
+    # every item left to the follow-up kernel (forced from the host): identical results
+    B, n_h, n_kv, d, s_max, w = 2, 16, 16, 128, 6000, 32
+    sl = np.array([6000, 3333], np.int32)
+    _say("score single pass, every item deferred")
+    q = _randn((B, n_h, w, d), 310)
+    k = _randn((B, n_kv, s_max, d), 311)
+    dims = kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16)
+    ws = torch.zeros(kvc.score_window_workspace(dims, w), dtype=torch.uint8, device=DEV)
+    raw, pooled = kvc.score_window(q, k, w, seq_lens=sl, n_keep=w, pool=7, ws=ws)
+    raw_d, pooled_d = kvc.score_window(q, k, w, seq_lens=sl, n_keep=w, pool=7, ws=ws, defer_all=True)
+    raw_n, pooled_n = kvc.score_window(q, k, w, seq_lens=sl, n_keep=w, pool=7, ws=ws)   # the count went back to 0
+    torch.cuda.synchronize()
+    assert torch.equal(raw, raw_d) and torch.equal(pooled, pooled_d)
+    assert torch.equal(raw, raw_n) and torch.equal(pooled, pooled_n)
+    rraw, _ = oracle.score_window(host(q), host(k), w, seq_lens=sl, n_keep=w, pool=7)
+    assert_scores_close(raw_d, rraw, "raw")
+
+
+def test_score_single_pass_unit_mask_and_reuse():
+    # masked units are left as they were; one workspace reused by calls of other
+    # lengths and masks (its counters return to zero)
+    B, n_h, n_kv, d, s_max, w = 2, 8, 8, 128, 5000, 32
+    q = _randn((B, n_h, w, d), 320)
+    k = _randn((B, n_kv, s_max, d), 321)
+    dims = kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16)
+    ws = torch.zeros(kvc.score_window_workspace(dims, w), dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(9)
+    for i, sl in enumerate(([5000, 3100], [4000, 5000], [1, 2600])):
+        sl = np.array(sl, np.int32)
+        _say("score single pass mask", i, list(sl))
+        full_raw, full_pooled = kvc.score_window(q, k, w, seq_lens=sl, n_keep=w, pool=7, ws=ws)
+        mask = torch.from_numpy(rng.integers(0, 2, (B, n_kv)).astype(np.int32)).to(DEV)
+        raw = torch.full((B, n_kv, s_max), -7.0, device=DEV)
+        pooled = torch.full((B, n_kv, s_max), -9.0, device=DEV)
+        kvc.score_window(q, k, w, seq_lens=sl, n_keep=w, pool=7, raw=raw, pooled=pooled, unit_mask=mask, ws=ws)
+        torch.cuda.synchronize()
+        on = mask.bool()
+        assert torch.equal(raw[on], full_raw[on]) and torch.equal(pooled[on], full_pooled[on])
+        assert bool((raw[~on] == -7.0).all()) and bool((pooled[~on] == -9.0).all())
+        rraw, _ = oracle.score_window(host(q), host(k), w, seq_lens=sl, n_keep=w, pool=7)
+        assert_scores_close(full_raw, rraw, "raw")
+
+
 @pytest.mark.parametrize("s_max", [2999, 3000])
 def test_pool_kernel_widths(s_max):
     # every compiled window (pool 1, 3, 5, 7 specialised, 9 and 63 walked), rows of a
