@@ -297,8 +297,12 @@ kvc_status kvc_gather_compact(int32_t batch, int32_t heads, int32_t s_max, int32
  * out        [B][n_h][d_h] dtype (bf16: round to nearest even)
  * lse        [B][n_h] float or NULL
  * q, kc, vc and out 16-byte aligned
- * ws         at least kvc_decode_attn_workspace(dims, cap) bytes, 16-byte aligned:
- *            the split partials (scratch only; any contents, no zero-filling needed)
+ * ws         at least kvc_decode_attn_workspace(dims, cap) bytes, 16-byte aligned,
+ *            zero-filled before first use: its first 65536 bytes hold arrival counters
+ *            (one per KV head and chunk of query heads) that every completed call
+ *            leaves at zero, the rest the split partials.  One workspace of the
+ *            largest size needed serves calls of any shape in stream order; calls
+ *            that overlap on one workspace race
  * Splits over t are merged in a fixed order: results are bit-reproducible.
  */
 size_t kvc_decode_attn_workspace(const kvc_dims *dims, int32_t cap);
@@ -307,16 +311,31 @@ kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const void *kc, 
                            void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * kvc_decode_attn_plan -- the launch configuration kvc_decode_attn takes for these
+ * shapes, for tests and profiling:
+ *   out[0]  token splits per KV head (work-groups along t)
+ *   out[1]  tokens per split
+ *   out[2]  query heads per work-group (the rest of a group in further chunks)
+ *   out[3]  1 when the last work-group of a (KV head, chunk) to finish folds the
+ *           splits itself (up to 64 splits for one head per work-group, fewer for
+ *           more heads: 8 for eight heads of 128 elements), 0 when a second kernel does
+ * out  int32[4], host memory.  KVC_ERR_INVALID_ARG for invalid dims, cap < 1 or a
+ * NULL out.
+ */
+kvc_status kvc_decode_attn_plan(const kvc_dims *dims, int32_t cap, int32_t *out);
+
+/*
  * kvc_decode_attn_noalloc -- kvc_decode_attn for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, results and kernels as kvc_decode_attn, without the
  * workspace: the split partials go to a static device array of the library, one per
  * GPU, of 4 MiB (4194304 bytes), held until the process ends.
  * A shape whose kvc_decode_attn_workspace() exceeds that limit returns
- * KVC_ERR_WORKSPACE and launches nothing.  The call allocates nothing and needs no
- * zero-filled memory.  Every call on a GPU uses that GPU's one array: calls that may
- * overlap on one GPU (other streams, other threads) race and must be ordered by the
- * caller.
+ * KVC_ERR_WORKSPACE and launches nothing.  The call allocates nothing; the array is
+ * zero when the library loads and every call leaves its counters at zero, as
+ * kvc_decode_attn does those of its workspace.  Every call on a GPU uses that GPU's
+ * one array: calls that may overlap on one GPU (other streams, other threads) race
+ * and must be ordered by the caller.
  */
 kvc_status kvc_decode_attn_noalloc(const kvc_dims *dims, const void *q, const void *kc, const void *vc,
                                    const int32_t *count, int32_t cap, float scale, void *out, float *lse,

@@ -8,11 +8,14 @@
 // to 8), so the compacted cache is streamed exactly once.  A lane owns 16 bytes of a
 // row (8 bf16 or 4 fp32); a row is spread over d_h/8 (d_h/4) lanes, a lane group.
 // Each lane group keeps an online softmax state (max m, sum l, output o); the groups
-// are folded in group order into the split's partial state, and a second kernel
-// folds the splits in split order (a kernel boundary, rather than a device-wide
-// fence per work-group, makes the partials visible across XCDs).  The result does
-// not depend on scheduling.  Logits are kept in log2 units: q is pre-multiplied by
-// scale * log2(e).
+// are folded in group order into the split's partial state.  The splits of a
+// (KV head, chunk) are folded in split order by whichever of its work-groups arrives
+// last (an arrival counter per chunk; up to kFuseSplits splits), or, for more splits,
+// by a second kernel.  Either way the result does not depend on scheduling.  Logits
+// are kept in log2 units: q is pre-multiplied by scale * log2(e).  The arrival
+// counters open the workspace in a region of fixed size that no partial ever
+// overwrites; the last arrival returns its counter to zero, so one zero-filled
+// workspace serves calls of any shape.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -59,14 +62,143 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float *o, float 
 struct DecArgs {
     const void *q, *kc, *vc;
     const int32_t *count;
-    int cap, n_h, n_kv, r, n_splits, split_tokens;
+    int cap, n_h, n_kv, r, n_splits, split_tokens, head_chunks;
     float c;                  // scale * log2(e)
     float *part_o;            // [units][r][n_splits][D]
     float2 *part_ml;          // [units][r][n_splits] (max, sum) in log2 units
+    int32_t *arrive;          // [units][head_chunks] arrivals, or null: the merge kernel folds
+    void *out;                // [B][n_h][D]
+    float *lse;               // [B][n_h] or null
 };
 
 constexpr int kMaxSplits = 1024;   // longer caches take longer splits
-constexpr int kUnroll = 4;          // token rows in flight per lane group
+constexpr int kFuseSplits = 64;    // at most this many splits are folded by their last arrival
+constexpr int kDecWgPerCu = 2;     // work-groups per CU the split count aims at
+constexpr int kUnroll = 4;          // token rows per lane group and batch (two batches in flight)
+
+// Writes one output element and, for d == 0, the log-sum-exp (natural log).
+template <bool BF16>
+__device__ __forceinline__ void store_out(void *out, float *lse, size_t bh, int D, int d, float M, float L, float O)
+{
+    const float y = (L > 0.f) ? O / L : 0.f;
+    if (BF16)
+        ((uint16_t *)out)[bh * D + d] = f32_to_bf16(y);
+    else
+        ((float *)out)[bh * D + d] = y;
+    if (lse && d == 0) lse[bh] = (L > 0.f) ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+// Split-fold geometry of a chunk of RH heads of D elements: the kDecThreads threads
+// take (head, element) pairs, SG split groups per pair when there are fewer pairs
+// than threads, PPT pairs per thread otherwise.  A thread holds every partial value it
+// folds in registers at once (at most kFoldVals), which bounds the splits a last
+// arrival folds: fold_limit(RH * D) splits, at most kFuseSplits.
+constexpr int kFoldVals = 32;
+__host__ __device__ constexpr int fold_sg(int pt) { return pt >= kDecThreads ? 1 : kDecThreads / pt; }
+__host__ __device__ constexpr int fold_ppt(int pt) { return pt >= kDecThreads ? pt / kDecThreads : 1; }
+__host__ __device__ constexpr int fold_limit(int pt)
+{
+    return kFoldVals * fold_sg(pt) / fold_ppt(pt) < kFuseSplits ? kFoldVals * fold_sg(pt) / fold_ppt(pt) : kFuseSplits;
+}
+
+// The last work-group to arrive for (unit, head chunk) folds the chunk's split
+// partials in split order.  Every load (split maxima and sums, the partial outputs)
+// is issued first, so the fold costs one memory round trip; the maxima and sums go to
+// LDS, where a wave per head forms the weights exp2(m_s - M) and L; each thread folds
+// its pairs' values over its strided subset of the splits and the split groups are
+// added in group order.  `lds` holds at least
+// 2 * RH * n_splits + kDecThreads floats; n_splits <= fold_limit(RH * D).
+template <bool BF16, int D, int RH>
+__device__ void fold_splits(const DecArgs &a, int unit, int hc, int heads, float *lds, float *sM, float *sL)
+{
+    constexpr int PT = RH * D;                // (head, element) pairs
+    constexpr int SG = fold_sg(PT);
+    constexpr int PPT = fold_ppt(PT);
+    constexpr int VPP = kFoldVals / PPT;      // split values per pair and thread
+    constexpr int MLT = (RH * kFuseSplits + kDecThreads - 1) / kDecThreads;
+    static_assert(PT % kDecThreads == 0 || kDecThreads % PT == 0, "pairs and threads");
+    const int NS = a.n_splits;
+    const int tid = kvc_tid();
+    const int lane = tid & (kWave - 1);
+    const int wv = tid >> 6;
+    const int sg = tid / (PT < kDecThreads ? PT : kDecThreads);
+    float *wm = lds;                  // [heads][NS] split maxima, then weights
+    float *wl = lds + RH * NS;        // [heads][NS] split sums
+    float *red = wl + RH * NS;        // [SG][PT] group sums
+    const size_t base = ((size_t)unit * a.r + hc * RH) * NS;    // slot of (head 0, split 0)
+    unsigned long long *ml = (unsigned long long *)a.part_ml;
+    unsigned long long mlv[MLT];
+#pragma unroll
+    for (int i = 0; i < MLT; ++i) {
+        const int x = tid + i * kDecThreads;
+        if (x < heads * NS) mlv[i] = ld_dev(ml + base + x);
+    }
+    float v[PPT][VPP];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int p = PT >= kDecThreads ? tid + i * kDecThreads : tid - sg * PT;
+        const int j = p / D;
+        const float *po = a.part_o + (base + (size_t)j * NS) * D + (p - j * D);
+#pragma unroll
+        for (int q = 0; q < VPP; ++q) {
+            const int s = sg + q * SG;
+            if (j < heads && s < NS) v[i][q] = ld_dev(po + (size_t)s * D);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MLT; ++i) {
+        const int x = tid + i * kDecThreads;
+        if (x < heads * NS) {
+            wm[x] = unpack_lo(mlv[i]);
+            wl[x] = unpack_hi(mlv[i]);
+        }
+    }
+    __syncthreads();
+    for (int j = wv; j < heads; j += kDecWaves) {               // NS <= 64: a split per lane
+        const bool on = lane < NS;
+        const float ms = on ? wm[j * NS + lane] : -INFINITY;
+        float M = ms;
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
+        const float w = (M == -INFINITY || ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+        float L = on ? w * wl[j * NS + lane] : 0.f;
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) L += shfl_xor_f(L, o);
+        if (on) wm[j * NS + lane] = w;
+        if (lane == 0) {
+            sM[j] = M;
+            sL[j] = L;
+        }
+    }
+    __syncthreads();
+    float acc[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int p = PT >= kDecThreads ? tid + i * kDecThreads : tid - sg * PT;
+        const int j = p / D;
+        acc[i] = 0.f;
+#pragma unroll
+        for (int q = 0; q < VPP; ++q) {
+            const int s = sg + q * SG;
+            if (j < heads && s < NS) acc[i] = fmaf(wm[j * NS + s], v[i][q], acc[i]);
+        }
+    }
+    if (SG > 1) {
+        red[sg * PT + (tid - sg * PT)] = acc[0];
+        __syncthreads();
+        if (sg != 0) return;
+        for (int g2 = 1; g2 < SG; ++g2) acc[0] += red[g2 * PT + tid];
+    }
+    const int b = unit / a.n_kv;
+    const int g = unit - b * a.n_kv;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int p = PT >= kDecThreads ? tid + i * kDecThreads : tid;
+        const int j = p / D;
+        const int d = p - j * D;
+        if (j < heads) store_out<BF16>(a.out, a.lse, (size_t)b * a.n_h + g * a.r + hc * RH + j, D, d, sM[j], sL[j], acc[i]);
+    }
+}
 
 // One work-group per (token split, KV head, head chunk) streams the split's K and V
 // rows once (the first rows are requested before the queries) and keeps an online
@@ -240,6 +372,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
         if (g2 == 0) sm_M[j] = M;
     }
     __syncthreads();
+    const bool fuse = a.arrive != nullptr;
     for (int x2 = tid; x2 < heads * D; x2 += kDecThreads) {
         const int j = x2 / D;
         const int d = x2 - j * D;
@@ -249,10 +382,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
             O = fmaf(sm_w[g2][j], sm_o[g2][j][d], O);
         }
         const size_t slot = ((size_t)unit * r + hc * RH + j) * a.n_splits + split;
-        a.part_o[slot * D + d] = O;
-        if (d == 0) a.part_ml[slot] = make_float2(sm_M[j], L);
+        if (fuse) {
+            st_dev(a.part_o + slot * D + d, O);
+            if (d == 0) st_dev((unsigned long long *)a.part_ml + slot, pack2(sm_M[j], L));
+        } else {
+            a.part_o[slot * D + d] = O;
+            if (d == 0) a.part_ml[slot] = make_float2(sm_M[j], L);
+        }
     }
-
+    if (!fuse) return;
+    // count this split's arrival once its partial state has landed; the last arrival folds
+    stores_done();
+    __shared__ int sm_last;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t *cnt = a.arrive + (size_t)unit * a.head_chunks + hc;
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = old == a.n_splits - 1;
+        if (sm_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!sm_last) return;
+    fold_splits<BF16, D, RH>(a, unit, hc, heads, &sm_o[0][0][0], sm_M, &sm_w[0][0]);
 }
 
 constexpr int kMergeThreads = 256;
@@ -320,6 +471,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
         const int s = (int)kvc_tid() + i * kMergeThreads;
         ml[i] = s < n_splits ? part_ml[base + s] : make_float2(-INFINITY, 0.f);
     }
+
     float mloc = -INFINITY;
 #pragma unroll
     for (int i = 0; i < MLPT; ++i) mloc = fmaxf(mloc, ml[i].x);
@@ -356,12 +508,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     if (grp != 0) return;
     float Ot = so[0][d];
     for (int g2 = 1; g2 < G; ++g2) Ot += so[g2][d];
-    const float y = (L > 0.f) ? Ot / L : 0.f;
-    if (BF16)
-        ((uint16_t *)out)[(size_t)bh * D + d] = f32_to_bf16(y);
-    else
-        ((float *)out)[(size_t)bh * D + d] = y;
-    if (lse && d == 0) lse[bh] = (L > 0.f) ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+    store_out<BF16>(out, lse, bh, D, d, M, L, Ot);
 }
 
 template <bool BF16, int D>
@@ -386,9 +533,9 @@ DecodePlan plan_decode(int batch, int n_h, int n_kv, int d_h, int cap, int cus)
     if (p.head_chunk < r && r < 8) p.head_chunk *= 2;   // r = 3, 5, 6, 7 -> next power of two
     p.head_chunks = (r + p.head_chunk - 1) / p.head_chunk;
     const long units = (long)batch * n_kv * p.head_chunks;
-    // about two work-groups per CU, splits of at least 64 tokens (one unrolled
-    // iteration of the work-group), at most kMaxSplits
-    long splits = (2L * cus + units - 1) / units;
+    // about kDecWgPerCu work-groups per CU, splits of a multiple of 64 tokens (one
+    // unrolled iteration of the work-group), at most kMaxSplits
+    long splits = ((long)kDecWgPerCu * cus + units - 1) / units;
     const long max_splits = (cap + 63) / 64;
     if (splits > max_splits) splits = max_splits;
     if (splits > kMaxSplits) splits = kMaxSplits;
@@ -398,9 +545,11 @@ DecodePlan plan_decode(int batch, int n_h, int n_kv, int d_h, int cap, int cus)
     p.split_tokens = (int)tok;
     p.n_splits = (int)((cap + tok - 1) / tok);
     if (p.n_splits < 1) p.n_splits = 1;
+    p.fused = p.n_splits <= fold_limit(p.head_chunk * d_h) && units <= kDecCounters;
     const size_t slots = (size_t)batch * n_kv * r * p.n_splits;
-    p.o_bytes = (slots * (size_t)d_h * sizeof(float) + 255) / 256 * 256;
-    p.ws_bytes = p.o_bytes + slots * sizeof(float2);
+    p.o_off = (size_t)kDecCounters * sizeof(int32_t);
+    p.ml_off = p.o_off + (slots * (size_t)d_h * sizeof(float) + 255) / 256 * 256;
+    p.ws_bytes = p.ml_off + slots * sizeof(float2);
     return p;
 }
 
@@ -420,14 +569,18 @@ hipError_t launch_decode(int batch, int n_h, int n_kv, int d_h, bool bf16, const
     a.n_splits = plan.n_splits;
     a.split_tokens = plan.split_tokens;
     a.c = scale * 1.4426950408889634f;
-    a.part_o = (float *)ws;
-    a.part_ml = (float2 *)((char *)ws + plan.o_bytes);
+    a.head_chunks = plan.head_chunks;
+    a.part_o = (float *)((char *)ws + plan.o_off);
+    a.part_ml = (float2 *)((char *)ws + plan.ml_off);
+    a.arrive = plan.fused ? (int32_t *)ws : nullptr;
+    a.out = out;
+    a.lse = lse;
     const dim3 grid(plan.n_splits, batch * n_kv, plan.head_chunks);
     hipError_t e = bf16 ? (d_h == 128 ? launch_rh<true, 128>(plan.head_chunk, grid, stream, a)
                                       : launch_rh<true, 64>(plan.head_chunk, grid, stream, a))
                         : (d_h == 128 ? launch_rh<false, 128>(plan.head_chunk, grid, stream, a)
                                       : launch_rh<false, 64>(plan.head_chunk, grid, stream, a));
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || plan.fused) return e;
     const dim3 mgrid(batch * n_h);
     if (bf16) {
         if (d_h == 128) hipLaunchKernelGGL((decode_merge_kernel<true, 128>), mgrid, dim3(kMergeThreads), 0, stream, a.part_o, a.part_ml, n_h, n_kv, a.r, a.n_splits, out, lse);

@@ -242,6 +242,19 @@ KVC_EXPORT size_t kvc_decode_attn_workspace(const kvc_dims *dims, int32_t cap)
     return kvc::plan_decode(dims->batch, dims->n_h, dims->n_kv, dims->d_h, cap, kPlanCus).ws_bytes;
 }
 
+KVC_EXPORT kvc_status kvc_decode_attn_plan(const kvc_dims *dims, int32_t cap, int32_t *out)
+{
+    kvc_status st = check_dims(dims, false);
+    if (st != KVC_OK) return st;
+    if (cap < 1 || cap > (1 << 30) || !out) return KVC_ERR_INVALID_ARG;
+    const kvc::DecodePlan p = kvc::plan_decode(dims->batch, dims->n_h, dims->n_kv, dims->d_h, cap, kPlanCus);
+    out[0] = p.n_splits;
+    out[1] = p.split_tokens;
+    out[2] = p.head_chunk;
+    out[3] = p.fused ? 1 : 0;
+    return KVC_OK;
+}
+
 KVC_EXPORT kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const void *kc, const void *vc,
                                       const int32_t *count, int32_t cap, float scale, void *out, float *lse,
                                       void *ws, size_t ws_bytes, void *stream)
@@ -261,9 +274,12 @@ KVC_EXPORT kvc_status kvc_decode_attn(const kvc_dims *dims, const void *q, const
 }
 
 // ------------------------------------------------------------ decode without allocation
-// Split partials of kvc_decode_attn_noalloc live in this file-scope device array, one
-// copy per GPU, held until the process ends.  Its host-side name is only a stand-in:
-// host code uses the device address hipGetSymbolAddress returns for the current device.
+// The workspace of kvc_decode_attn_noalloc (arrival counters, then split partials)
+// lives in this file-scope device array, one copy per GPU, held until the process
+// ends.  It is zero when the library loads and every completed call returns the
+// counters to zero (the last work-group to arrive resets its own), so no call clears
+// it.  Its host-side name is only a stand-in: host code uses the device address
+// hipGetSymbolAddress returns for the current device.
 static constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 

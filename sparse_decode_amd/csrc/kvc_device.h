@@ -1,5 +1,6 @@
 // kvc_device.h -- device-side helpers shared by the gfx950 kernels of the KV-cache
-// compression path: bf16 conversion, 64-lane shuffles and work-group scans.
+// compression path: bf16 conversion, 64-lane shuffles, exchange between work-groups
+// and work-group scans.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,6 +84,37 @@ __device__ __forceinline__ int clamp_len(const int32_t *seq_lens, int b, int s_m
     int s = seq_lens ? ld_uniform(seq_lens, b) : s_max;
     return s < 0 ? 0 : (s > s_max ? s_max : s);
 }
+
+// ---- exchange between the work-groups of one running kernel.  Agent-scope relaxed
+// atomic loads and stores are coherent across the XCDs (they do not hit a stale line
+// of an XCD's own L2); a work-group publishes with st_dev, waits with stores_done()
+// until its stores have completed, and only then counts its arrival atomically, so a
+// work-group that sees the count complete reads every published value with ld_dev.
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p)
+{
+    return __uint_as_float(__hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_dev(float *p, float v)
+{
+    __hip_atomic_store((uint32_t *)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's earlier memory operations (its stores too) have completed.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ unsigned long long pack2(float a, float b)
+{
+    return (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+}
+__device__ __forceinline__ float unpack_lo(unsigned long long v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float unpack_hi(unsigned long long v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
 // Inclusive prefix sum across one 64-lane wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v)

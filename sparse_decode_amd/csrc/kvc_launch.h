@@ -24,12 +24,17 @@ hipError_t launch_gather(int batch, int heads, int s_max, int row_bytes, const v
                          hipStream_t stream);
 
 // ---- decode -------------------------------------------------------------------------
+// Decode workspace: kDecCounters arrival counters (zero between calls), then the
+// split partial outputs and (max, sum) pairs.
+constexpr int kDecCounters = 16384;
 struct DecodePlan {
     int n_splits = 1;
     int split_tokens = 0;
     int head_chunk = 1;        // query heads handled per work-group
     int head_chunks = 1;
-    size_t o_bytes = 0;        // split partial outputs
+    bool fused = false;        // the last work-group of a chunk folds its splits
+    size_t o_off = 0;          // split partial outputs
+    size_t ml_off = 0;         // split (max, sum) pairs
     size_t ws_bytes = 0;
 };
 DecodePlan plan_decode(int batch, int n_h, int n_kv, int d_h, int cap, int cus);
@@ -61,7 +66,7 @@ struct ScorePlan {
     int group_units = 0;       // KV-head units per pass-1/pass-2 launch pair
     int logit_rows = 0;        // MFMA path, R <= 16: logits kept per token between the passes
     size_t logits_off = 0;     // their place in the workspace
-    // single-pass MFMA path (R <= 32, S <= 65536): K read once, 256-token items; its
+    // single-pass MFMA path (16 < R <= 32, S <= 131072): K read once, 1024-token items; its
     // zero-state words open the workspace and the two-pass region (a fallback when too
     // few work-groups fit the device at once) follows at two_pass_off
     bool single = false;

@@ -864,24 +864,6 @@ struct SpArgs {
     unsigned long long *fin;  // [units][16 RT] packed final (-M c, 1/L)
 };
 
-__device__ __forceinline__ unsigned long long pack2(float a, float b)
-{
-    return (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
-}
-__device__ __forceinline__ float unpack_lo(unsigned long long v) { return __uint_as_float((uint32_t)v); }
-__device__ __forceinline__ float unpack_hi(unsigned long long v) { return __uint_as_float((uint32_t)(v >> 32)); }
-
-__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(unsigned long long *p, unsigned long long v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Waits until this thread's earlier memory operations (its stores too) have completed.
-__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float v)
 {

@@ -30,7 +30,7 @@ EXPORTED = (
     "kvc_select_topk_workspace", "kvc_select_topk",
     "kvc_select_core_workspace", "kvc_select_core",
     "kvc_gather_compact",
-    "kvc_decode_attn_workspace", "kvc_decode_attn", "kvc_decode_attn_noalloc",
+    "kvc_decode_attn_workspace", "kvc_decode_attn", "kvc_decode_attn_plan", "kvc_decode_attn_noalloc",
     "kvc_query_similarity",
     "kvc_block_landmarks", "kvc_block_scores", "kvc_expand_blocks",
 )
@@ -75,6 +75,7 @@ def lib():
                 "kvc_gather_compact": (I, [I, I, I, I, P, P, P, P, P, I, I, P, P, P, P, P]),
                 "kvc_decode_attn_workspace": (Z, [D, I]),
                 "kvc_decode_attn": (I, [D, P, P, P, P, I, F, P, P, P, Z, P]),
+                "kvc_decode_attn_plan": (I, [D, I, P]),
                 "kvc_decode_attn_noalloc": (I, [D, P, P, P, P, I, F, P, P, P]),
                 "kvc_query_similarity": (I, [D, P, P, ctypes.c_double, P, P, P, P]),
                 "kvc_block_landmarks": (I, [D, P, I, P, P]),
@@ -317,6 +318,13 @@ def gather_compact(src0, idx, count, *, src1=None, src_pos=None, dst0=None, dst1
 
 def decode_attn_workspace(dims: Dims, cap: int) -> int:
     return int(lib().kvc_decode_attn_workspace(ctypes.byref(dims), int(cap)))
+
+
+def decode_attn_plan(dims: Dims, cap: int) -> dict:
+    """kvc_decode_attn_plan: the launch configuration of kvc_decode_attn for dims and cap."""
+    out = (ctypes.c_int32 * 4)()
+    _check(lib().kvc_decode_attn_plan(ctypes.byref(dims), int(cap), out), "kvc_decode_attn_plan")
+    return {"n_splits": int(out[0]), "split_tokens": int(out[1]), "head_chunk": int(out[2]), "fused": bool(out[3])}
 
 
 @on_stream

@@ -151,6 +151,27 @@ def _decode(dims, cap=80, **kw):
                                      a["count"], cap, a["scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
 
 
+def test_decode_plan_query():
+    # one layer of the 32-layer MHA workload after compaction (1024 + 32 tokens per head)
+    mha = kvc.decode_attn_plan(_dims(batch=2, n_h=32, n_kv=32), 1056)
+    assert mha["fused"] and mha["head_chunk"] == 1 and mha["n_splits"] * mha["split_tokens"] >= 1056
+    # the last arrival folds up to 64 splits of one head, 8 of eight heads (a register
+    # budget per thread); more splits go to the merge kernel
+    assert kvc.decode_attn_plan(_dims(batch=2, n_h=4, n_kv=4), 4096) == \
+        {"n_splits": 64, "split_tokens": 64, "head_chunk": 1, "fused": True}
+    assert kvc.decode_attn_plan(_dims(batch=2, n_h=32, n_kv=4), 4096) == \
+        {"n_splits": 64, "split_tokens": 64, "head_chunk": 8, "fused": False}
+    long_few = kvc.decode_attn_plan(_dims(batch=2, n_h=8, n_kv=1), 9000)
+    assert long_few["n_splits"] > 64 and not long_few["fused"]
+    for p in (mha, long_few):
+        assert p["split_tokens"] % 64 == 0
+    out = (ctypes.c_int32 * 4)()
+    E = kvc.KVC_ERR_INVALID_ARG
+    assert kvc.lib().kvc_decode_attn_plan(None, 80, out) == E
+    assert kvc.lib().kvc_decode_attn_plan(ctypes.byref(_dims()), 0, out) == E
+    assert kvc.lib().kvc_decode_attn_plan(ctypes.byref(_dims()), 80, None) == E
+
+
 def test_decode_rejects_invalid_arguments():
     E, U, W = kvc.KVC_ERR_INVALID_ARG, kvc.KVC_ERR_UNSUPPORTED, kvc.KVC_ERR_WORKSPACE
     assert _decode(None) == E

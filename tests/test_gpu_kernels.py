@@ -89,10 +89,16 @@ def test_gather_bitexact(dtype, d, heads, idx_heads, s_max, cap):
     (torch.bfloat16, 64, 12, 4, 517),        # group of 3
     (torch.float32, 64, 4, 2, 80),
     (torch.float32, 128, 8, 2, 999),
+    (torch.bfloat16, 128, 4, 4, 4096),       # 64 splits of one head folded by the last arrival
+    (torch.bfloat16, 128, 32, 4, 4096),      # 64 splits of 8 heads: the merge kernel folds
+    (torch.bfloat16, 128, 8, 1, 9000),       # 141 splits: the merge kernel folds
+    (torch.float32, 64, 8, 1, 9000),
 ])
 def test_decode_vs_oracle(dtype, d, n_h, n_kv, cap):
     _say("decode", dtype, d, n_h, n_kv, cap)
     B = 2
+    plan = kvc.decode_attn_plan(kvc.make_dims(B, 1, n_h, n_kv, d, kvc.KVC_BF16), cap)
+    assert plan["n_splits"] * plan["split_tokens"] >= cap, plan
     q = _randn((B, n_h, d), 11, dtype)
     kc = _randn((B, n_kv, cap, d), 12, dtype)
     vc = _randn((B, n_kv, cap, d), 13, dtype)
@@ -115,23 +121,35 @@ def test_decode_vs_oracle(dtype, d, n_h, n_kv, cap):
 
 
 def test_decode_workspace_reuse():
-    # one zero-filled workspace, sized for the largest cap, serves calls with the same
-    # batch and heads but other caps and counts (the finish counters reset each call)
+    # one zero-filled workspace, sized for the largest call, serves calls of other
+    # batches, heads, caps and counts, with and without the fused split fold: every call
+    # leaves the arrival counters (the first 64 KiB) at zero, and each result equals
+    # that of a fresh workspace
     _say("decode ws reuse")
-    B, n_h, n_kv, d = 2, 32, 8, 128
-    dims = kvc.make_dims(B, 1, n_h, n_kv, d, kvc.KVC_BF16)
-    ws = torch.zeros(kvc.decode_attn_workspace(dims, 5000), dtype=torch.uint8, device=DEV)
-    q = _randn((B, n_h, d), 21)
-    for cap, seed in [(5000, 1), (2080, 2), (64, 3), (5000, 4), (1, 5)]:
+    d = 128
+    calls = [(2, 32, 8, 5000, 1), (2, 32, 8, 2080, 2), (2, 8, 1, 9000, 3), (4, 32, 32, 1056, 4),
+             (2, 32, 8, 64, 5), (1, 8, 1, 9000, 6), (2, 32, 8, 5000, 7), (2, 32, 8, 1, 8)]
+    need = max(kvc.decode_attn_workspace(kvc.make_dims(B, 1, nh, nkv, d, kvc.KVC_BF16), cap)
+               for B, nh, nkv, cap, _ in calls)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    fused = set()
+    for B, n_h, n_kv, cap, seed in calls:
+        fused.add(kvc.decode_attn_plan(kvc.make_dims(B, 1, n_h, n_kv, d, kvc.KVC_BF16), cap)["fused"])
+        q = _randn((B, n_h, d), 20 + seed)
         kc = _randn((B, n_kv, cap, d), 30 + seed)
         vc = _randn((B, n_kv, cap, d), 40 + seed)
         cnt = np.full((B, n_kv), cap, np.int32)
-        cnt[0, 1] = 0
-        cnt[1, 2] = max(0, cap // 3)
-        out, lse = kvc.decode_attn(q, kc, vc, torch.from_numpy(cnt).to(DEV), ws=ws)
+        cnt[0, min(1, n_kv - 1)] = 0
+        cnt[B - 1, n_kv - 1] = max(0, cap // 3)
+        cnt_d = torch.from_numpy(cnt).to(DEV)
+        out, lse = kvc.decode_attn(q, kc, vc, cnt_d, ws=ws)
+        out_f, lse_f = kvc.decode_attn(q, kc, vc, cnt_d)      # a fresh zero-filled workspace
         torch.cuda.synchronize()
+        assert int(ws[:65536].count_nonzero()) == 0
+        assert torch.equal(out, out_f) and torch.equal(lse, lse_f)
         ref, ref_lse = oracle.decode(host(q), host(kc), host(vc), cnt)
         assert_decode_close(out, ref, True)
+    assert fused == {True, False}
 
 
 def test_decode_closed_forms():
