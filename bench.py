@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads, sweep and next rows")
     ap.add_argument("--profile-call", choices=("score", "decode", "gather", "select"), default=None,
-                    help="only replay one call of one headline layer (for rocprofv3 runs), then a 1 GiB copy")
+                    help="only replay one call of one headline layer (for rocprofv3 runs), then a 1 GiB elementwise kernel")
     ap.add_argument("--calls", type=int, default=10, help="replays of --profile-call")
     return ap.parse_args()
 
@@ -852,8 +852,8 @@ def measure_retrieval(dev, wl, x, qs, flush, args):
 
 def profile_call(args, dev):
     """Replays one call of one headline layer (mha_tsp at S) `--calls` times, then one
-    plain 1 GiB device copy: a short program for rocprofv3 kernel-trace and --pmc runs
-    (the copy calibrates the byte counters)."""
+    elementwise kernel over 1 GiB: a short program for rocprofv3 kernel-trace and --pmc
+    runs (the elementwise kernel calibrates the byte counters)."""
     import torch
 
     from sparse_decode_amd import synth
@@ -868,12 +868,14 @@ def profile_call(args, dev):
     for _ in range(args.calls):
         fn()
     torch.cuda.synchronize()
-    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # calibration: an elementwise kernel that reads 1 GiB and writes 1 GiB (a same-dtype
+    # copy_ would go to the copy engine, which the counters do not see)
+    a = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
-    b.copy_(a)
+    torch.neg(a, out=b)
     torch.cuda.synchronize()
-    print("[bench] profiled %d %s calls of mha_tsp layer 0, then a 1 GiB copy" % (args.calls, args.profile_call),
-          flush=True)
+    print("[bench] profiled %d %s calls of mha_tsp layer 0, then a 1 GiB elementwise negation" %
+          (args.calls, args.profile_call), flush=True)
 
 
 # ------------------------------------------------------------------------------ main

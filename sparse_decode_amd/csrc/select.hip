@@ -468,22 +468,21 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
 }
 
 // ------------------------------------------------------------- one work-group per unit
-// When a unit has at most 32768 candidates and there are enough units to occupy the
-// chip, one work-group of 512 threads holds all of a unit's candidates in registers
-// (16 bytes per load, every load in flight at once) and runs the three radix levels
-// and the ordered write in LDS: one launch, every key read once.  (A CU keeps only so
-// many loads in flight, so with few units the chunked kernels, which spread a unit
-// over many CUs, finish first.)  The levels, the tie rule and the output are those of
-// the chunked kernels above.
-constexpr int kUnitThreads = 512;
-
+// A unit of at most 16384 candidates (32768 when the units fill the chip) is selected
+// by one work-group of NT threads (1024, or 512 with 64 keys each) that holds all of
+// them in registers (16-byte loads, every load in flight at once) and runs the three
+// radix levels and the ordered write in LDS: one launch, every key read once.  Thread i holds K consecutive candidates, so equal keys, which come in
+// runs (plateaus of the max-pooled scores, repeated heavy-hitter scores), meet in one
+// thread: a histogram level adds a run of one bin with one LDS atomic, and the level-1
+// histogram is split over kCopies copies against conflicts between lanes.  The levels,
+// the tie rule and the output are those of the chunked kernels above.
 // Bin of the k_rem-th largest key of an LDS histogram (summed over its first NC
 // copies) and the number of keys above that bin; thread i owns bins NB-1-i*per down to
 // NB-per-i*per.
-template <int NB, int NC>
+template <int NB, int NC, int NT>
 __device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan, Digit *out)
 {
-    constexpr int per = NB / kUnitThreads;
+    constexpr int per = NB / NT;
     const int top = NB - 1 - (int)kvc_tid() * per;
     int c[per], cnt = 0;
 #pragma unroll
@@ -504,15 +503,34 @@ __device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan,
     __syncthreads();
     const Digit d = *out;
     // the histogram is free again: clear the copy the next levels use
-    for (int i = kvc_tid(); i < kB1 / 4; i += kUnitThreads) reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
+    for (int i = kvc_tid(); i < kB1 / 4; i += NT) reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
     __syncthreads();
     return d;
 }
 
-// Thread i holds the K = 4 NQ consecutive candidates [K i, K i + K), so one block
-// scan orders the write.  VEC: rows of a multiple of 4 floats, 16-byte loads.
-template <int NQ, bool VEC>
-__global__ __launch_bounds__(kUnitThreads) void sel_unit_kernel(SelArgs a)
+// Adds the thread's keys to an LDS histogram, a run of equal bins with one atomic:
+// bin_of(i) is the bin of key i, or -1 for a key that does not take part.
+template <int K, typename F>
+__device__ __forceinline__ void run_hist(int *h, F bin_of)
+{
+    int cur = -1, cnt = 0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        const int b = bin_of(i);
+        if (b != cur) {
+            if (cnt) atomicAdd(&h[cur], cnt);
+            cur = b;
+            cnt = 0;
+        }
+        cnt += b >= 0;
+    }
+    if (cnt) atomicAdd(&h[cur], cnt);
+}
+
+// Thread i of NT holds the K = 4 NQ consecutive candidates [K i, K i + K), so block
+// scans order the write.  VEC: rows of a multiple of 4 floats, 16-byte loads.
+template <int NQ, int NT, bool VEC>
+__global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
 {
     constexpr int K = 4 * NQ;
     __shared__ int h[kCopies][kB1];
@@ -525,68 +543,60 @@ __global__ __launch_bounds__(kUnitThreads) void sel_unit_kernel(SelArgs a)
     int32_t *out = a.idx + (size_t)u * a.cap;
     // the always-kept trailing tokens, the -1 padding and the count
     const int nw = us.S - us.C;
-    for (int i = tid; i < nw; i += kUnitThreads) out[us.k_eff + i] = us.C + i;
-    for (int i = us.k_eff + nw + tid; i < a.cap; i += kUnitThreads) out[i] = -1;
+    for (int i = tid; i < nw; i += NT) out[us.k_eff + i] = us.C + i;
+    for (int i = us.k_eff + nw + tid; i < a.cap; i += NT) out[i] = -1;
     if (tid == 0) a.count[u] = us.k_eff + nw;
     if (us.k_eff == 0) return;
     if (us.k_eff == us.C) {
-        for (int t = tid; t < us.C; t += kUnitThreads) out[t] = t;
+        for (int t = tid; t < us.C; t += NT) out[t] = t;
         return;
     }
     const float *sc = a.scores + (size_t)u * a.s_max;
     const int t0 = K * tid;
-    uint32_t key[K];
-    {
-        float v[K];
+    uint32_t key[K];                          // the score bits, then the key in place
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int t = t0 + 4 * q;
-            if constexpr (VEC) {
-                // t < C <= s_max and s_max % 4 == 0: the whole vector is inside the row
-                const float4 x = t < us.C ? *(const float4 *)(sc + t) : make_float4(0.f, 0.f, 0.f, 0.f);
-                v[4 * q] = x.x;
-                v[4 * q + 1] = x.y;
-                v[4 * q + 2] = x.z;
-                v[4 * q + 3] = x.w;
-            } else {
+    for (int q = 0; q < NQ; ++q) {
+        const int t = t0 + 4 * q;
+        if constexpr (VEC) {
+            // t < C <= s_max and s_max % 4 == 0: the whole vector is inside the row
+            const u32x4 x = t < us.C ? *(const u32x4 *)(sc + t) : u32x4{0u, 0u, 0u, 0u};
+            key[4 * q] = x.x;
+            key[4 * q + 1] = x.y;
+            key[4 * q + 2] = x.z;
+            key[4 * q + 3] = x.w;
+        } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * q + e] = t + e < us.C ? sc[t + e] : 0.f;
-            }
+            for (int e = 0; e < 4; ++e) key[4 * q + e] = t + e < us.C ? __float_as_uint(sc[t + e]) : 0u;
         }
-        // past the candidates the key is 0, below every key of a non-NaN score: the
-        // histograms may count those slots, since the k_eff-th largest key (k_eff < C)
-        // and the counts above its bins do not change; the write checks validity
-#pragma unroll
-        for (int i = 0; i < K; ++i) key[i] = t0 + i < us.C ? order_key(v[i]) : 0u;
     }
-    for (int i = tid; i < kCopies * kB1 / 4; i += kUnitThreads)
+    // past the candidates the key is 0, below every key of a non-NaN score: the
+    // histograms may count those slots, since the k_eff-th largest key (k_eff < C) and
+    // the counts above its bins do not change; the write checks validity
+#pragma unroll
+    for (int i = 0; i < K; ++i) key[i] = t0 + i < us.C ? order_key(__uint_as_float(key[i])) : 0u;
+    for (int i = tid; i < kCopies * kB1 / 4; i += NT)
         reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
     __syncthreads();
-    int *hc = h[tid & (kCopies - 1)];
 
-    // level 1: key bits [21, 32)
-#pragma unroll
-    for (int i = 0; i < K; ++i) hist_add(hc, h[0], (int)(key[i] >> 21));
+    // level 1: key bits [21, 32), into the thread's histogram copy
+    run_hist<K>(h[tid & (kCopies - 1)], [&](int i) { return (int)(key[i] >> 21); });
     __syncthreads();
-    const Digit d1 = unit_digit<kB1, kCopies>(h, us.k_eff, scan, &dg);
-    // level 2: bits [10, 21) of the keys in bin d1.  Those spread over many bins, so
-    // plain LDS atomics into one copy beat the wave-level aggregation here.
-#pragma unroll
-    for (int i = 0; i < K; ++i)
-        if ((int)(key[i] >> 21) == d1.digit) atomicAdd(&h[0][(key[i] >> 10) & (kB2 - 1)], 1);
+    const Digit d1 = unit_digit<kB1, kCopies, NT>(h, us.k_eff, scan, &dg);
+    // level 2: bits [10, 21) of the keys in bin d1
+    run_hist<K>(h[0], [&](int i) {
+        return (int)(key[i] >> 21) == d1.digit ? (int)((key[i] >> 10) & (kB2 - 1)) : -1;
+    });
     __syncthreads();
-    const Digit d2 = unit_digit<kB2, 1>(h, us.k_eff - d1.above, scan, &dg);
+    const Digit d2 = unit_digit<kB2, 1, NT>(h, us.k_eff - d1.above, scan, &dg);
     // level 3: bits [0, 10) of the keys with prefix (d1, d2)
     const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
-#pragma unroll
-    for (int i = 0; i < K; ++i)
-        if ((key[i] >> 10) == pre2) atomicAdd(&h[0][key[i] & (kB3 - 1)], 1);
+    run_hist<K>(h[0], [&](int i) { return (key[i] >> 10) == pre2 ? (int)(key[i] & (kB3 - 1)) : -1; });
     __syncthreads();
-    const Digit d3 = unit_digit<kB3, 1>(h, us.k_eff - d1.above - d2.above, scan, &dg);
+    const Digit d3 = unit_digit<kB3, 1, NT>(h, us.k_eff - d1.above - d2.above, scan, &dg);
     const uint32_t T = (pre2 << 10) | (uint32_t)d3.digit;
     const int ties = us.k_eff - d1.above - d2.above - d3.above;     // keys == T to take, lowest index first
 
-    // ordered write: one block scan of (keys > T, keys == T) per thread
+    // ordered write: block scans of the thread's keys > T and keys == T
     int gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -595,9 +605,9 @@ __global__ __launch_bounds__(kUnitThreads) void sel_unit_kernel(SelArgs a)
         eq += ok && key[i] == T;
     }
     int tot;
-    const int before = block_exclusive_scan(gt | (eq << 16), scan, &tot);
-    int eq_before = before >> 16;
-    int pos = (before & 0xffff) + min(ties, eq_before);
+    const int gt_before = block_exclusive_scan(gt, scan, &tot);
+    int eq_before = block_exclusive_scan(eq, scan, &tot);
+    int pos = gt_before + min(ties, eq_before);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         if (t0 + i >= us.C) break;
@@ -827,19 +837,22 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
     a.kpu = k_per_unit;
 
     const long c_max = (long)s_max - n_keep;
-    if (c_max <= 32768 && units >= dev.cus / 2) {
-        // every unit's candidates fit one work-group's registers, and the units fill the chip
+    if (c_max <= 16384 || (c_max <= 32768 && units >= dev.cus / 2)) {
+        // every unit's candidates fit one work-group's registers.  Past 16 keys per
+        // thread the LDS atomics of the histogram levels (one instruction per key slot
+        // and wave) outlast the chunked kernels, which spread a unit over many CUs,
+        // unless the units alone fill the chip
         const bool vec = s_max % 4 == 0 && ((uintptr_t)a.scores & 15) == 0;
-        const dim3 g1(units), b1(kUnitThreads);
+        const dim3 g1(units);
         if (c_max <= 8192) {
-            if (vec) hipLaunchKernelGGL((sel_unit_kernel<4, true>), g1, b1, 0, stream, a);
-            else hipLaunchKernelGGL((sel_unit_kernel<4, false>), g1, b1, 0, stream, a);
+            if (vec) hipLaunchKernelGGL((sel_unit_kernel<2, 1024, true>), g1, dim3(1024), 0, stream, a);
+            else hipLaunchKernelGGL((sel_unit_kernel<2, 1024, false>), g1, dim3(1024), 0, stream, a);
         } else if (c_max <= 16384) {
-            if (vec) hipLaunchKernelGGL((sel_unit_kernel<8, true>), g1, b1, 0, stream, a);
-            else hipLaunchKernelGGL((sel_unit_kernel<8, false>), g1, b1, 0, stream, a);
+            if (vec) hipLaunchKernelGGL((sel_unit_kernel<4, 1024, true>), g1, dim3(1024), 0, stream, a);
+            else hipLaunchKernelGGL((sel_unit_kernel<4, 1024, false>), g1, dim3(1024), 0, stream, a);
         } else {
-            if (vec) hipLaunchKernelGGL((sel_unit_kernel<16, true>), g1, b1, 0, stream, a);
-            else hipLaunchKernelGGL((sel_unit_kernel<16, false>), g1, b1, 0, stream, a);
+            if (vec) hipLaunchKernelGGL((sel_unit_kernel<16, 512, true>), g1, dim3(512), 0, stream, a);
+            else hipLaunchKernelGGL((sel_unit_kernel<16, 512, false>), g1, dim3(512), 0, stream, a);
         }
         return hipGetLastError();
     }

@@ -201,7 +201,7 @@ def test_select_bitexact_with_ties(s_max):
             _select_case(sc, sl, k, n_keep)
 
 
-@pytest.mark.parametrize("s_max", [4096, 131072])
+@pytest.mark.parametrize("s_max", [4096, 16000, 131072])
 def test_select_bitexact_continuous(s_max):
     _say("select continuous", s_max)
     rng = np.random.default_rng(3)
@@ -214,6 +214,11 @@ def test_select_bitexact_continuous(s_max):
     sc[0, 3] = (0.004 * (1.0 + 0.12 * rng.standard_normal(s_max))).astype(np.float32)
     sc[0, 3, rng.choice(s_max, s_max // 100, replace=False)] = 0.5
     sc[0, 4] = np.float32(0.004) + np.float32(2 ** -31) * rng.integers(0, 64, s_max).astype(np.float32)
+    # max-pooled (window 7) scores with planted heavy hitters of one value: runs of equal
+    # keys inside a thread's slots and the same key in many threads at once
+    x = rng.random(s_max + 6).astype(np.float32) ** 8
+    x[rng.choice(s_max, max(1, s_max // 50), replace=False) + 3] = 0.75
+    sc[0, 5] = np.lib.stride_tricks.sliding_window_view(x, 7).max(axis=1)
     sl = np.array([s_max], np.int32)
     for k in (1311, 2048, 7):
         _select_case(sc, sl, k, 32)
