@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--profile-call", choices=("score", "decode", "gather", "select"), default=None,
                     help="only replay one call of one headline layer (for rocprofv3 runs), then a 1 GiB elementwise kernel")
     ap.add_argument("--calls", type=int, default=10, help="replays of --profile-call")
+    ap.add_argument("--only", choices=("tiny_fp32", "llama3_8b_32k", "ctx_128k", "ragged_b16"), default=None,
+                    help="measure only this other workload and print its object (for rocprofv3 runs)")
     return ap.parse_args()
 
 
@@ -898,6 +900,13 @@ def main():
         profile_call(args, dev)
         return
     flush = Flusher(dev)
+    if args.only:
+        fn = {"tiny_fp32": lambda: measure_tiny(args, dev, flush),
+              "llama3_8b_32k": lambda: measure_folded("llama3_8b_32k", args, dev, flush, extras=True),
+              "ctx_128k": lambda: measure_folded("ctx_128k", args, dev, flush),
+              "ragged_b16": lambda: measure_ragged(args, dev, flush)}[args.only]
+        print(json.dumps({args.only: fn()}), flush=True)
+        return
     head, ctx = measure_headline(args, dev, flush)
     res = {"metric": METRIC, "value": head.pop("value"), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"), "higher_is_better": True,
