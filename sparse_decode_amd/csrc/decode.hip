@@ -10,8 +10,8 @@
 // Each lane group keeps an online softmax state (max m, sum l, output o); the groups
 // are folded in group order into the split's partial state.  The splits of a
 // (KV head, chunk) are folded in split order by whichever of its work-groups arrives
-// last (an arrival counter per chunk; up to kFuseSplits splits), or, for more splits,
-// by a second kernel.  Either way the result does not depend on scheduling.  Logits
+// last (an arrival counter per chunk; up to kFuseSplits splits, fewer for many heads
+// per work-group), or, for more splits, by a second kernel.  Either way the result does not depend on scheduling.  Logits
 // are kept in log2 units: q is pre-multiplied by scale * log2(e).  The arrival
 // counters open the workspace in a region of fixed size that no partial ever
 // overwrites; the last arrival returns its counter to zero, so one zero-filled
@@ -86,6 +86,51 @@ __device__ __forceinline__ void store_out(void *out, float *lse, size_t bh, int 
     else
         ((float *)out)[bh * D + d] = y;
     if (lse && d == 0) lse[bh] = (L > 0.f) ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+// Fold of a few splits (at most kFoldSmall) when a thread per (head, element) pair
+// fits the work-group: each thread loads every split's (max, sum) of its head and its
+// element of every split's output at once, forms the weights itself and adds the
+// splits in split order; no LDS, no barrier.
+constexpr int kFoldSmall = 16;
+
+template <bool BF16, int D, int RH>
+__device__ __forceinline__ void fold_small(const DecArgs &a, int unit, int hc, int heads)
+{
+    static_assert(RH * D <= kDecThreads, "a thread per pair");
+    const int tid = kvc_tid();
+    if (tid >= heads * D) return;
+    const int j = tid / D, d = tid - j * D;
+    const int NS = a.n_splits;
+    const size_t base = ((size_t)unit * a.r + hc * RH + j) * NS;   // slot of (head j, split 0)
+    const unsigned long long *ml = (const unsigned long long *)a.part_ml + base;
+    const float *po = a.part_o + base * D + d;
+    unsigned long long mlv[kFoldSmall];
+    float v[kFoldSmall];
+#pragma unroll
+    for (int q = 0; q < kFoldSmall; ++q) {
+        if (q < NS) {
+            mlv[q] = ld_dev(ml + q);
+            v[q] = ld_dev(po + (size_t)q * D);
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kFoldSmall; ++q)
+        if (q < NS) M = fmaxf(M, unpack_lo(mlv[q]));
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int q = 0; q < kFoldSmall; ++q) {
+        if (q < NS) {
+            const float m = unpack_lo(mlv[q]);
+            const float w = (M == -INFINITY || m == -INFINITY) ? 0.f : fast_exp2(m - M);
+            L = fmaf(w, unpack_hi(mlv[q]), L);
+            O = fmaf(w, v[q], O);
+        }
+    }
+    const int b = unit / a.n_kv;
+    const int g = unit - b * a.n_kv;
+    store_out<BF16>(a.out, a.lse, (size_t)b * a.n_h + g * a.r + hc * RH + j, D, d, M, L, O);
 }
 
 // Split-fold geometry of a chunk of RH heads of D elements: the kDecThreads threads
@@ -403,6 +448,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a)
     }
     __syncthreads();
     if (!sm_last) return;
+    if constexpr (RH * D <= kDecThreads) {
+        if (a.n_splits <= kFoldSmall) {
+            fold_small<BF16, D, RH>(a, unit, hc, heads);
+            return;
+        }
+    }
     fold_splits<BF16, D, RH>(a, unit, hc, heads, &sm_o[0][0][0], sm_M, &sm_w[0][0]);
 }
 
