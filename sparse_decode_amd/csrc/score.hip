@@ -845,6 +845,7 @@ constexpr int kSpWaves = kSpThreads / kWave;
 constexpr int kSpTiles = 16;                             // 16-token tiles per wave per item
 constexpr int kSpRing = 4;                               // K tiles in flight per wave
 constexpr int kSpItem = 16 * kSpTiles * kSpWaves;        // 1024 tokens
+constexpr int kSpFixGroups = 64;                          // work-groups of the follow-up kernel
 
 struct SpArgs {
     const uint16_t *q_win;
@@ -1445,7 +1446,9 @@ hipError_t launch_single(const SpArgs &a0, bool *done, hipStream_t stream)
     long G = cap < a.n_items ? cap : a.n_items;
     G = G / a.n_chunks * a.n_chunks;
     a.G = (int)G;
-    a.fix_g = (int)G;
+    // the follow-up kernel usually finds no deferred item: a small grid keeps its launch
+    // cheap, and its work-groups stride over whatever was deferred
+    a.fix_g = (int)(G < kSpFixGroups ? G : kSpFixGroups);
     hipLaunchKernelGGL((mfma_single_kernel<D, RT>), dim3((unsigned)G), dim3(kSpThreads), 0, stream, a);
     hipLaunchKernelGGL((mfma_single_fixup_kernel<D, RT>), dim3((unsigned)a.fix_g), dim3(kSpThreads), 0, stream, a);
     *done = true;
