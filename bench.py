@@ -204,7 +204,7 @@ def stored_traffic(workload):
     if h.hexdigest() != want:
         return None, "profiles/hbm_traffic_%s.md is stale (kernel sources changed): not reported" % workload
     return nbytes, ("stored: profiles/hbm_traffic_%s.md, two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                    "this build's sources, scaled by a 1 GiB copy" % workload)
+                    "this build's sources, scaled by a 1 GiB elementwise kernel" % workload)
 
 
 def cpu_model():
