@@ -934,6 +934,7 @@ def main():
     res["copy_probe"] = {"GBps": round(cgb, 1), "frac_of_peak": round(cgb / HBM_PEAK_GBPS, 4),
                          "what": "torch device copy of 1 GiB, read + write bytes / time (median of 5 cold copies)"}
     res["decode_frac_of_copy"] = round(res["value"] / cgb, 4)
+    res["roofline"]["frac_of_copy_probe"] = round(res["roofline"]["achieved"] / cgb, 4)
     # plain launch latency: a graph of 100 dependent one-element kernels
     t1 = torch.zeros(1, device=dev)
     g = graph_of(lambda: [t1.add_(1.0) for _ in range(100)])
