@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -158,9 +158,9 @@ const char *kvc_status_str(kvc_status status);
  * pooled     [B][n_kv][s_max] float, written (required)
  * flags      0, or KVC_SCORE_GENERIC and/or KVC_SCORE_DEFER_ALL
  * ws         at least kvc_score_window_workspace(dims, w, flags) bytes, 16-byte
- *            aligned, zero-filled before first use: per-item row statistics, and for
- *            the single-pass kernel per-KV-head arrival counters and a deferred-item
- *            count (returned to zero by each call that completes); calls with the same
+ *            aligned, zero-filled before first use: per-item row statistics, per-KV-head
+ *            arrival counters and, for the single-pass kernel, a deferred-item count
+ *            (returned to zero by each call that completes); calls with the same
  *            batch and n_kv may share one workspace without zero-filling it again
  * Arithmetic: fp32 logits (bf16 products are exact), fp32 exp2-based softmax with
  * the row sums accumulated per lane and merged in double; raw agrees with a
@@ -187,7 +187,11 @@ kvc_status kvc_score_window(const kvc_dims *dims, const void *q_win, const void 
  *           wait too long for the statistics (two such calls running at the same time
  *           on other streams, for instance) leave their items to a follow-up kernel
  *           that re-reads their K: slower, same results
- * out  int32[5], host memory.  Same argument checks as kvc_score_window_workspace.
+ *   out[5]  1 when the two-pass kernels merge the row statistics of a KV head's items
+ *           in the last of its first-pass work-groups to finish (at most 8 items per KV
+ *           head, all work-groups resident at once), 0 when a kernel of its own merges
+ *           them (or for the single-pass and portable kernels)
+ * out  int32[6], host memory.  Same argument checks as kvc_score_window_workspace.
  */
 kvc_status kvc_score_window_plan(const kvc_dims *dims, int32_t w, int32_t flags, int32_t *out);
 

@@ -120,6 +120,7 @@ KVC_EXPORT kvc_status kvc_score_window_plan(const kvc_dims *dims, int32_t w, int
     out[2] = p.mfma ? (p.single ? p.sp_item : p.chunk_tokens) : 0;
     out[3] = p.mfma ? (p.single ? p.sp_chunks : p.n_chunks) : 0;
     out[4] = p.single ? 1 : 0;
+    out[5] = p.mfma && !p.single && p.fold_merge ? 1 : 0;
     return KVC_OK;
 }
 

@@ -65,6 +65,8 @@ struct ScorePlan {
     int n_chunks = 0;
     int group_units = 0;       // KV-head units per pass-1/pass-2 launch pair
     int logit_rows = 0;        // MFMA path, R <= 16: logits kept per token between the passes
+    bool fold_merge = false;   // two-pass MFMA path: the last pass-1 work-group of a unit merges its
+                               // chunks' row statistics (else a merge kernel between the passes)
     size_t logits_off = 0;     // their place in the workspace
     // single-pass MFMA path (16 < R <= 32, S <= 131072): K read once, 1024-token items; its
     // zero-state words open the workspace and the two-pass region (a fallback when too

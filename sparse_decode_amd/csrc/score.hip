@@ -321,7 +321,9 @@ struct MfArgs {
     int s_max, n_h, n_kv, w, wic, R, unit0, n_chunks, chunk_tokens;
     float c;                 // scale * log2(e)
     float2 *part;            // pass 1 out: [group][chunk][RT*16] (m, l)
-    const float2 *fin;       // pass 2 in:  [group][RT*16] (-M*c, 1/L)
+    float2 *fin;             // merged row statistics, pass 2 in: [group][RT*16] (-M*c, 1/L)
+    int32_t *arrive;         // [group] chunk arrival counters (zero between calls) when the last
+                             // arriving pass-1 work-group merges its unit's chunks, else null
     float *raw;              // pass 2 out: [B*n_kv][s_max]
     float *logits;           // one row block only: pass 1 keeps its logits [B*n_kv][s_max][rs], or null
     int rs;                  // rows kept per token (R rounded up to 4)
@@ -523,6 +525,62 @@ __device__ __forceinline__ void stats_stage(const unsigned char *buf, int st0, i
     }
 }
 
+// Merges the chunk partials (m, l) of every row of unit ul in a fixed order, by the
+// unit's last arriving pass-1 work-group: thread (slice, row) folds chunks slice,
+// slice + slices, ... online (rescale factors in fp32, sums in double), and the slices
+// are then folded in slice order.  The partials were published with st_dev by the
+// work-groups of other XCDs, hence ld_dev.  buf: 3 KB of LDS.
+template <int RPAD>
+__device__ __forceinline__ void merge_chunks(const MfArgs &a, int ul, unsigned char *buf)
+{
+    constexpr int slices = kMfThreads / RPAD;
+    static_assert(slices * RPAD == kMfThreads, "rows must split the work-group evenly");
+    float *sm_M = (float *)buf;
+    double *sm_L = (double *)(buf + kMfThreads * sizeof(float));
+    const int row = kvc_tid() % RPAD;
+    const int slice = kvc_tid() / RPAD;
+    const unsigned long long *p = (const unsigned long long *)(a.part + (size_t)ul * a.n_chunks * RPAD) + row;
+    float Mx = -INFINITY;
+    double L = 0.0;
+    constexpr int kBatch = 8;               // chunk partials requested together per thread
+    for (int ch0 = slice; ch0 < a.n_chunks; ch0 += kBatch * slices) {
+        unsigned long long v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int ch = min(ch0 + q * slices, a.n_chunks - 1);    // unconditional: one round trip
+            v[q] = ld_dev(p + (size_t)ch * RPAD);
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            if (ch0 + q * slices >= a.n_chunks) continue;
+            const float vm = unpack_lo(v[q]), vl = unpack_hi(v[q]);
+            if (vm == -INFINITY) continue;
+            if (vm > Mx) {
+                L = L * (double)fast_exp2((Mx - vm) * a.c) + (double)vl;
+                Mx = vm;
+            } else {
+                L += (double)vl * (double)fast_exp2((vm - Mx) * a.c);
+            }
+        }
+    }
+    sm_M[kvc_tid()] = Mx;
+    sm_L[kvc_tid()] = L;
+    __syncthreads();
+    if (slice != 0) return;
+    float Mt = -INFINITY;
+    for (int s2 = 0; s2 < slices; ++s2) Mt = fmaxf(Mt, sm_M[s2 * RPAD + row]);
+    float2 res = make_float2(0.f, 0.f);
+    if (row < a.R && Mt != -INFINITY) {
+        double Lt = 0.0;
+        for (int s2 = 0; s2 < slices; ++s2) {
+            const float ms = sm_M[s2 * RPAD + row];
+            if (ms != -INFINITY) Lt += sm_L[s2 * RPAD + row] * (double)fast_exp2((ms - Mt) * a.c);
+        }
+        if (Lt > 0.0) res = make_float2(-Mt * a.c, (float)(1.0 / Lt));
+    }
+    a.fin[(size_t)ul * RPAD + row] = res;
+}
+
 template <int D, int RT>
 __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4))) void mfma_stats_kernel(MfArgs a)
 {
@@ -599,11 +657,27 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         float L = 0.f;
         if (Mx != -INFINITY)
             for (int t2 = 0; t2 < C::TG; ++t2) L += sm_l[t2][row] * fast_exp2((sm_m[t2][row] - Mx) * a.c);
-        a.part[((size_t)ul * a.n_chunks + chunk) * (RT * 16) + row] = make_float2(Mx, L);
+        float2 *dst = a.part + ((size_t)ul * a.n_chunks + chunk) * (RT * 16) + row;
+        if (a.arrive) st_dev((unsigned long long *)dst, pack2(Mx, L));
+        else *dst = make_float2(Mx, L);
     }
+    if (!a.arrive) return;                  // mfma_merge_kernel merges the chunks
+    // count this chunk's arrival once its partials have landed; the unit's last arrival
+    // merges every chunk (the K stage buffers are free by now and hold the merge's state)
+    stores_done();
+    __shared__ int sm_last;
+    __syncthreads();
+    if (kvc_tid() == 0) {
+        const int old = __hip_atomic_fetch_add(a.arrive + ul, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = old == a.n_chunks - 1;
+        if (sm_last) __hip_atomic_store(a.arrive + ul, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (sm_last) merge_chunks<RT * 16>(a, ul, lds);
 }
 
-// Merges the chunk partials of every row in a fixed order.  blockDim = 1024:
+// Merges the chunk partials of every row in a fixed order, as a kernel of its own
+// (launches with many chunks or work-group rounds).  blockDim = 1024:
 // thread (slice, row) folds chunks slice, slice + slices, ... online (rescale factors
 // in fp32, sums in double); the slices are then folded in slice order.
 constexpr int kMergeThreads = 1024;
@@ -1351,10 +1425,12 @@ void launch_mfma_group(const MfArgs &a, int group_units, hipStream_t stream)
 {
     using C = Sc<D, RT>;
     dim3 grid(a.n_chunks, group_units);
+    static_assert(C::LDS_BYTES >= kMfThreads * (sizeof(float) + sizeof(double)), "merge state fits the stages");
     hipLaunchKernelGGL((mfma_stats_kernel<D, RT>), grid, dim3(kMfThreads), C::LDS_BYTES, stream, a);
-    hipLaunchKernelGGL(mfma_merge_kernel, dim3(group_units), dim3(kMergeThreads), 0, stream,
-                       (const float2 *)a.part, a.n_chunks, RT * 16, a.R, a.c, a.mask ? a.mask + a.unit0 : nullptr,
-                       (float2 *)a.fin);
+    if (!a.arrive)
+        hipLaunchKernelGGL(mfma_merge_kernel, dim3(group_units), dim3(kMergeThreads), 0, stream,
+                           (const float2 *)a.part, a.n_chunks, RT * 16, a.R, a.c, a.mask ? a.mask + a.unit0 : nullptr,
+                           a.fin);
     if (RT == 1 && a.logits) {
         const dim3 lgrid((a.s_max + kLogitThreads - 1) / kLogitThreads, group_units);
         hipLaunchKernelGGL(logit_probsum_kernel, lgrid, dim3(kLogitThreads), 0, stream, (const float *)a.logits,
@@ -1482,8 +1558,16 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
         p.tiles_per_wave = 0;
         p.chunk_tokens = ct_tok;
         p.n_chunks = (s_max + ct_tok - 1) / ct_tok;
+        // a few chunks per unit in one round of work-groups: the unit's last arriving
+        // pass-1 work-group merges the chunks, one launch less.  With more chunks or
+        // rounds, publishing every work-group's partials device-coherently and waiting
+        // for its arrival count cost more than the merge kernel (measured: twice the
+        // pass-1 time at 128 chunks of a KV head, +15% over four rounds)
+        p.fold_merge = p.n_chunks <= 8 && (long)p.n_chunks * p.group_units <= 4L * cus;
+        // chunk partials, merged row statistics, chunk arrival counters (zero between calls)
         p.ws_bytes = align256((size_t)p.group_units * p.n_chunks * rpad * sizeof(float2)) +
-                     align256((size_t)p.group_units * rpad * sizeof(float2)) + 256;
+                     align256((size_t)p.group_units * rpad * sizeof(float2)) +
+                     align256((size_t)p.group_units * sizeof(int32_t)) + 256;
         // a single row block (R <= 16): pass 1 keeps its logits, 4 * rs bytes per token,
         // and pass 2 reads those instead of K's 2 * d_h bytes
         p.logit_rows = rt == 1 ? (p.R + 3) / 4 * 4 : 0;
@@ -1570,8 +1654,12 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         a.n_chunks = plan.n_chunks;
         a.chunk_tokens = plan.chunk_tokens;
         a.c = scale * kLog2e;
+        const size_t fin_off = align256((size_t)plan.group_units * plan.n_chunks * rpad * sizeof(float2));
         a.part = (float2 *)ws;
-        a.fin = (const float2 *)((char *)ws + align256((size_t)plan.group_units * plan.n_chunks * rpad * sizeof(float2)));
+        a.fin = (float2 *)((char *)ws + fin_off);
+        a.arrive = plan.fold_merge
+                       ? (int32_t *)((char *)ws + fin_off + align256((size_t)plan.group_units * rpad * sizeof(float2)))
+                       : nullptr;
         a.raw = raw;
         a.mask = unit_mask;
         a.rs = plan.logit_rows;

@@ -177,10 +177,10 @@ def score_window_workspace(dims: Dims, w: int, flags: int = 0) -> int:
 
 def score_window_plan(dims: Dims, w: int, flags: int = 0) -> dict:
     """kvc_score_window_plan: the launch configuration of kvc_score_window for dims."""
-    out = (ctypes.c_int32 * 5)()
+    out = (ctypes.c_int32 * 6)()
     _check(lib().kvc_score_window_plan(ctypes.byref(dims), int(w), int(flags), out), "kvc_score_window_plan")
     return {"mfma": bool(out[0]), "rt": int(out[1]), "chunk_tokens": int(out[2]), "chunks_per_unit": int(out[3]),
-            "single_pass": bool(out[4])}
+            "single_pass": bool(out[4]), "folded_merge": bool(out[5])}
 
 
 @on_stream

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvc.lib().kvc_abi_version() == 3
+    assert kvc.lib().kvc_abi_version() == 4
     seen = set()
     for s in range(5):
         txt = kvc.status_str(s)
@@ -273,24 +273,30 @@ def test_score_plan_query():
     # the launch configuration depends on the shapes only (host logic, no GPU)
     E = kvc.KVC_ERR_INVALID_ARG
     cfg2_fold = kvc.score_window_plan(_dims(batch=32, s_max=32768), 32)
-    assert cfg2_fold == {"mfma": True, "rt": 8, "chunk_tokens": 2048, "chunks_per_unit": 16, "single_pass": False}
+    assert cfg2_fold == {"mfma": True, "rt": 8, "chunk_tokens": 2048, "chunks_per_unit": 16, "single_pass": False,
+                         "folded_merge": False}
     one_layer = kvc.score_window_plan(_dims(batch=1, s_max=32768), 32)
     assert one_layer["rt"] == 8 and one_layer["chunk_tokens"] == 256 and one_layer["chunks_per_unit"] == 128
-    assert not one_layer["single_pass"]
+    assert not one_layer["single_pass"] and not one_layer["folded_merge"]
     # 17..32 rows per KV head, up to 131072 tokens: K read once, 1024-token items
     mha = kvc.score_window_plan(_dims(batch=2, s_max=65536, n_h=32, n_kv=32), 32)
-    assert mha == {"mfma": True, "rt": 2, "chunk_tokens": 1024, "chunks_per_unit": 64, "single_pass": True}
+    assert mha == {"mfma": True, "rt": 2, "chunk_tokens": 1024, "chunks_per_unit": 64, "single_pass": True,
+                   "folded_merge": False}
     mha_after = kvc.score_window_plan(_dims(batch=2, s_max=13140, n_h=32, n_kv=32), 32)
     assert mha_after["single_pass"] and mha_after["chunks_per_unit"] == 13
     assert kvc.score_window_plan(_dims(batch=2, s_max=131072, n_h=32, n_kv=32), 32)["single_pass"]
     assert not kvc.score_window_plan(_dims(batch=2, s_max=131073, n_h=32, n_kv=32), 32)["single_pass"]
     assert not kvc.score_window_plan(_dims(batch=2, s_max=4096, n_h=32, n_kv=32), 16)["single_pass"]   # R = 16
+    # one query per head over 16 sequences: 8 items per KV head in one round of
+    # work-groups, merged by the last first-pass work-group of each
     one_query = kvc.score_window_plan(_dims(batch=16, s_max=16384), 1)
-    assert one_query["rt"] == 1 and not one_query["single_pass"]
+    assert one_query["rt"] == 1 and not one_query["single_pass"] and one_query["chunks_per_unit"] == 8
+    assert one_query["folded_merge"]
+    assert not kvc.score_window_plan(_dims(batch=16, s_max=16385), 1)["folded_merge"]      # 9 items
     assert kvc.score_window_plan(_dims(dtype_code=kvc.KVC_F32), 32)["mfma"] is False
     assert kvc.score_window_plan(_dims(), 32, kvc.KVC_SCORE_GENERIC)["mfma"] is False
     assert kvc.score_window_plan(_dims(), 32, kvc.KVC_SCORE_DEFER_ALL) == kvc.score_window_plan(_dims(), 32)
-    out = (ctypes.c_int32 * 5)()
+    out = (ctypes.c_int32 * 6)()
     assert kvc.lib().kvc_score_window_plan(None, 32, 0, out) == E
     assert kvc.lib().kvc_score_window_plan(ctypes.byref(_dims()), 0, 0, out) == E
     assert kvc.lib().kvc_score_window_plan(ctypes.byref(_dims()), 32, 0, None) == E

@@ -157,13 +157,14 @@ def test_cfg2_all_layers_folded_as_timed():
     # work-groups over 8 blocks of 16 window rows
     wl = synth.WORKLOADS[2]
     _folded_parity(wl, list(range(wl.layers)), (0, 15, 31),
-                   {"mfma": True, "rt": 8, "chunk_tokens": 2048, "chunks_per_unit": 16, "single_pass": False})
+                   {"mfma": True, "rt": 8, "chunk_tokens": 2048, "chunks_per_unit": 16, "single_pass": False,
+                    "folded_merge": False})
 
 
 def test_cfg3_layers_folded():
     wl = synth.WORKLOADS[3]
     _folded_parity(wl, [0, 31], (0, 31), {"mfma": True, "rt": 8, "chunk_tokens": 2048, "chunks_per_unit": 64,
-                                          "single_pass": False})
+                                          "single_pass": False, "folded_merge": False})
 
 
 def test_cfg3_ctx_128k():

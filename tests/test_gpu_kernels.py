@@ -422,6 +422,41 @@ def _plan(B, n_h, n_kv, d, s_max, w):
     return kvc.score_window_plan(kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16), w)
 
 
+@pytest.mark.parametrize("shape", [(3, 16, 4, 2000, 1, False), (2, 8, 1, 1800, 16, True)])
+def test_score_folded_merge_mask_and_reuse(shape):
+    # at most 8 items per KV head, all work-groups resident: the last first-pass
+    # work-group of a KV head merges its items' row statistics.  Its arrival counters
+    # return to zero, so one workspace serves full, masked and repeated calls.
+    # R = 4 (logits kept between the passes) and R = 128 (K read twice).
+    B, n_h, n_kv, s_max, w, wic = shape
+    d = 128
+    plan = _plan(B, n_h, n_kv, d, s_max, w)
+    assert plan["folded_merge"] and not plan["single_pass"] and plan["chunks_per_unit"] == 8, plan
+    sl = np.array([s_max, 1500, 77][:B], np.int32)
+    _say("score folded merge", B, n_h, n_kv, d, s_max, w, list(sl), plan)
+    q = _randn((B, n_h, w, d), 310)
+    k = _randn((B, n_kv, s_max, d), 311)
+    dims = kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16)
+    ws = torch.zeros(kvc.score_window_workspace(dims, w), dtype=torch.uint8, device=DEV)
+    args = dict(seq_lens=sl, window_in_cache=wic, n_keep=32, pool=7, ws=ws)
+    raw, pooled = kvc.score_window(q, k, w, **args)
+    torch.cuda.synchronize()
+    rraw, rpooled = oracle.score_window(host(q), host(k), w, seq_lens=sl, window_in_cache=wic, n_keep=32, pool=7)
+    assert_scores_close(raw, rraw, "raw")
+    assert_scores_close(pooled, rpooled, "pooled")
+    mask = torch.from_numpy(np.random.default_rng(4).integers(0, 2, (B, n_kv)).astype(np.int32)).to(DEV)
+    mask.view(-1)[0] = 1
+    raw_m = torch.full((B, n_kv, s_max), -7.0, device=DEV)
+    pooled_m = torch.full((B, n_kv, s_max), -9.0, device=DEV)
+    kvc.score_window(q, k, w, raw=raw_m, pooled=pooled_m, unit_mask=mask, **args)
+    raw2, pooled2 = kvc.score_window(q, k, w, **args)
+    torch.cuda.synchronize()
+    on = mask.bool()
+    assert torch.equal(raw_m[on], raw[on]) and torch.equal(pooled_m[on], pooled[on])
+    assert bool((raw_m[~on] == -7.0).all()) and bool((pooled_m[~on] == -9.0).all())
+    assert torch.equal(raw, raw2) and torch.equal(pooled, pooled2)
+
+
 def test_score_single_pass_shapes():
     # 17..32 rows per KV head read K once (1024-token items exchanging row statistics)
     cases = [
