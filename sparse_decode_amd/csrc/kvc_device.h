@@ -116,15 +116,29 @@ __device__ __forceinline__ unsigned long long pack2(float a, float b)
 __device__ __forceinline__ float unpack_lo(unsigned long long v) { return __uint_as_float((uint32_t)v); }
 __device__ __forceinline__ float unpack_hi(unsigned long long v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
-// Inclusive prefix sum across one 64-lane wave.
+// v from another lane by a DPP operand modifier, for the rows of 16 lanes in ROW_MASK;
+// 0 in lanes with no source lane and in the other rows.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 to rows 2 and 3
+
+// Inclusive prefix sum across one 64-lane wave (every lane active), in VALU operand
+// modifiers: shifts by 1, 2, 4 and 8 lanes give the scan inside each row of 16; then
+// rows 1 and 3 add the last lane of the row before, and rows 2 and 3 add lane 31, by
+// then the total of rows 0 and 1.
 __device__ __forceinline__ int wave_inclusive_scan(int v)
 {
-    const int lane = kvc_tid() & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int u = __shfl_up(v, o, kWave);
-        if (lane >= o) v += u;
-    }
+    v += dpp_i<kDppRowShr1, 0xf>(v);
+    v += dpp_i<kDppRowShr2, 0xf>(v);
+    v += dpp_i<kDppRowShr4, 0xf>(v);
+    v += dpp_i<kDppRowShr8, 0xf>(v);
+    v += dpp_i<kDppRowBcast15, 0xa>(v);
+    v += dpp_i<kDppRowBcast31, 0xc>(v);
     return v;
 }
 
@@ -151,6 +165,32 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *to
     *total = tot;
     __syncthreads();
     return pre + inc - v;
+}
+
+// Exclusive prefix sums of two values across the work-group with the barriers of one
+// scan; `scratch` holds at least 32 ints of LDS.  Same conditions as above.
+__device__ __forceinline__ int2 block_exclusive_scan2(int a, int b, int *scratch)
+{
+    const int lane = kvc_tid() & (kWave - 1);
+    const int wid = kvc_tid() >> 6;
+    const int nw = kvc_bdim_x() >> 6;
+    const int ia = wave_inclusive_scan(a);
+    const int ib = wave_inclusive_scan(b);
+    if (lane == kWave - 1) {
+        scratch[wid] = ia;
+        scratch[16 + wid] = ib;
+    }
+    __syncthreads();
+    int pa = 0, pb = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i < wid && i < nw) {
+            pa += scratch[i];
+            pb += scratch[16 + i];
+        }
+    }
+    __syncthreads();
+    return make_int2(pa + ia - a, pb + ib - b);
 }
 
 }  // namespace kvc

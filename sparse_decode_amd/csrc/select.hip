@@ -534,7 +534,7 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
 {
     constexpr int K = 4 * NQ;
     __shared__ int h[kCopies][kB1];
-    __shared__ int scan[16];
+    __shared__ int scan[32];
     __shared__ Digit dg;
     const int u = kvc_bid_x();
     const int tid = kvc_tid();
@@ -604,9 +604,9 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
         gt += ok && key[i] > T;
         eq += ok && key[i] == T;
     }
-    int tot;
-    const int gt_before = block_exclusive_scan(gt, scan, &tot);
-    int eq_before = block_exclusive_scan(eq, scan, &tot);
+    const int2 before = block_exclusive_scan2(gt, eq, scan);
+    const int gt_before = before.x;
+    int eq_before = before.y;
     int pos = gt_before + min(ties, eq_before);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
