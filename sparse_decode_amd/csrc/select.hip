@@ -150,26 +150,42 @@ __device__ __forceinline__ void load_bins(const int32_t *__restrict__ g, int (&c
 }
 
 // The bin that holds the k_rem-th largest key (counting from the top bin) and the
-// number of keys in the bins above it, from the counts load_bins gave every thread.
-template <int NB>
-__device__ __forceinline__ Digit find_digit(const int (&c)[NB / kThreads], int k_rem, int *scan, Digit *out)
+// number of keys in the bins above it, from every thread's counts c[p] of bins top - p
+// (a thread's bins lie above those of the threads after it).  Exactly one thread finds
+// the bin (0 < k_rem <= the keys counted).  Two barriers: the wave totals, then the
+// result; the next call writes scan and *out only after its first barrier, when every
+// thread has read them.
+template <int PER>
+__device__ __forceinline__ Digit locate_digit(const int (&c)[PER], int top, int k_rem, int *scan, Digit *out)
 {
-    constexpr int per = NB / kThreads;
-    const int top = NB - 1 - (int)kvc_tid() * per;
+    const int lane = kvc_tid() & (kWave - 1);
+    const int wid = kvc_tid() >> 6;
+    const int nw = kvc_bdim_x() >> 6;
     int cnt = 0;
 #pragma unroll
-    for (int p = 0; p < per; ++p) cnt += c[p];
-    int tot;
-    int above = block_exclusive_scan(cnt, scan, &tot);
+    for (int p = 0; p < PER; ++p) cnt += c[p];
+    const int inc = wave_inclusive_scan(cnt);
+    if (lane == kWave - 1) scan[wid] = inc;
+    __syncthreads();
+    int above = inc - cnt;
 #pragma unroll
-    for (int p = 0; p < per; ++p) {
+    for (int i = 0; i < 16; ++i)
+        if (i < wid && i < nw) above += scan[i];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
         if (above < k_rem && above + c[p] >= k_rem) *out = Digit{top - p, above};
         above += c[p];
     }
     __syncthreads();
-    const Digit d = *out;
-    __syncthreads();
-    return d;
+    return *out;
+}
+
+// locate_digit over the counts load_bins gave every thread.
+template <int NB>
+__device__ __forceinline__ Digit find_digit(const int (&c)[NB / kThreads], int k_rem, int *scan, Digit *out)
+{
+    constexpr int per = NB / kThreads;
+    return locate_digit<per>(c, NB - 1 - (int)kvc_tid() * per, k_rem, scan, out);
 }
 
 // A chunk is KPT * kThreads consecutive candidates; thread i holds keys
@@ -471,41 +487,30 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
 // A unit of at most 16384 candidates (32768 when the units fill the chip) is selected
 // by one work-group of NT threads (1024, or 512 with 64 keys each) that holds all of
 // them in registers (16-byte loads, every load in flight at once) and runs the three
-// radix levels and the ordered write in LDS: one launch, every key read once.  Thread i holds K consecutive candidates, so equal keys, which come in
-// runs (plateaus of the max-pooled scores, repeated heavy-hitter scores), meet in one
-// thread: a histogram level adds a run of one bin with one LDS atomic, and the level-1
-// histogram is split over kCopies copies against conflicts between lanes.  The levels,
-// the tie rule and the output are those of the chunked kernels above.
-// Bin of the k_rem-th largest key of an LDS histogram (summed over its first NC
-// copies) and the number of keys above that bin; thread i owns bins NB-1-i*per down to
-// NB-per-i*per.
+// radix levels and the ordered write in LDS: one launch, every key read once.  Thread
+// i holds K consecutive candidates, so equal keys, which come in runs (plateaus of the
+// max-pooled scores, repeated heavy-hitter scores), meet in one thread: a histogram
+// level adds a run of one bin with one LDS atomic, and the level-1 histogram is split
+// over kCopies copies against conflicts between lanes.  The levels, the tie rule and
+// the output are those of the chunked kernels above.
+
+// Bin of the k_rem-th largest key of an LDS histogram (the sum of its NC copies of NB
+// bins, copy c at h + c NB) and the number of keys above that bin; thread i owns bins
+// NB-1-i*per down to NB-per-i*per.
 template <int NB, int NC, int NT>
-__device__ __forceinline__ Digit unit_digit(int (*h)[kB1], int k_rem, int *scan, Digit *out)
+__device__ __forceinline__ Digit unit_digit(const int *h, int k_rem, int *scan, Digit *out)
 {
     constexpr int per = NB / NT;
     const int top = NB - 1 - (int)kvc_tid() * per;
-    int c[per], cnt = 0;
+    int c[per];
 #pragma unroll
     for (int p = 0; p < per; ++p) {
         int s = 0;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) s += h[cc][top - p];
+        for (int cc = 0; cc < NC; ++cc) s += h[cc * NB + top - p];
         c[p] = s;
-        cnt += s;
     }
-    int tot;
-    int above = block_exclusive_scan(cnt, scan, &tot);
-#pragma unroll
-    for (int p = 0; p < per; ++p) {
-        if (above < k_rem && above + c[p] >= k_rem) *out = Digit{top - p, above};
-        above += c[p];
-    }
-    __syncthreads();
-    const Digit d = *out;
-    // the histogram is free again: clear the copy the next levels use
-    for (int i = kvc_tid(); i < kB1 / 4; i += NT) reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
-    __syncthreads();
-    return d;
+    return locate_digit<per>(c, top, k_rem, scan, out);
 }
 
 // Adds the thread's keys to an LDS histogram, a run of equal bins with one atomic:
@@ -533,7 +538,8 @@ template <int NQ, int NT, bool VEC>
 __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
 {
     constexpr int K = 4 * NQ;
-    __shared__ int h[kCopies][kB1];
+    // one histogram per level, all cleared up front: no clearing between the levels
+    __shared__ int h1[kCopies * kB1], h2[kB2], h3[kB3];
     __shared__ int scan[32];
     __shared__ Digit dg;
     const int u = kvc_bid_x();
@@ -574,25 +580,26 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
     // the counts above its bins do not change; the write checks validity
 #pragma unroll
     for (int i = 0; i < K; ++i) key[i] = t0 + i < us.C ? order_key(__uint_as_float(key[i])) : 0u;
-    for (int i = tid; i < kCopies * kB1 / 4; i += NT)
-        reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
+    for (int i = tid; i < kCopies * kB1 / 4; i += NT) reinterpret_cast<int4 *>(h1)[i] = make_int4(0, 0, 0, 0);
+    for (int i = tid; i < kB2 / 4; i += NT) reinterpret_cast<int4 *>(h2)[i] = make_int4(0, 0, 0, 0);
+    for (int i = tid; i < kB3 / 4; i += NT) reinterpret_cast<int4 *>(h3)[i] = make_int4(0, 0, 0, 0);
     __syncthreads();
 
     // level 1: key bits [21, 32), into the thread's histogram copy
-    run_hist<K>(h[tid & (kCopies - 1)], [&](int i) { return (int)(key[i] >> 21); });
+    run_hist<K>(h1 + (tid & (kCopies - 1)) * kB1, [&](int i) { return (int)(key[i] >> 21); });
     __syncthreads();
-    const Digit d1 = unit_digit<kB1, kCopies, NT>(h, us.k_eff, scan, &dg);
+    const Digit d1 = unit_digit<kB1, kCopies, NT>(h1, us.k_eff, scan, &dg);
     // level 2: bits [10, 21) of the keys in bin d1
-    run_hist<K>(h[0], [&](int i) {
+    run_hist<K>(h2, [&](int i) {
         return (int)(key[i] >> 21) == d1.digit ? (int)((key[i] >> 10) & (kB2 - 1)) : -1;
     });
     __syncthreads();
-    const Digit d2 = unit_digit<kB2, 1, NT>(h, us.k_eff - d1.above, scan, &dg);
+    const Digit d2 = unit_digit<kB2, 1, NT>(h2, us.k_eff - d1.above, scan, &dg);
     // level 3: bits [0, 10) of the keys with prefix (d1, d2)
     const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
-    run_hist<K>(h[0], [&](int i) { return (key[i] >> 10) == pre2 ? (int)(key[i] & (kB3 - 1)) : -1; });
+    run_hist<K>(h3, [&](int i) { return (key[i] >> 10) == pre2 ? (int)(key[i] & (kB3 - 1)) : -1; });
     __syncthreads();
-    const Digit d3 = unit_digit<kB3, 1, NT>(h, us.k_eff - d1.above - d2.above, scan, &dg);
+    const Digit d3 = unit_digit<kB3, 1, NT>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
     const uint32_t T = (pre2 << 10) | (uint32_t)d3.digit;
     const int ties = us.k_eff - d1.above - d2.above - d3.above;     // keys == T to take, lowest index first
 
