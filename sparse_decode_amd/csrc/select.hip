@@ -310,9 +310,8 @@ __global__ __launch_bounds__(kThreads) void sel_level3_kernel(SelArgs a)
         above += k22 > pre2;
         if (k22 == pre2) hist_add(hc, h[0], (int)(ck.key[q] & (kB3 - 1)));
     }
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) above += shfl_xor_i(above, o);
-    if (lane == 0) wave_above[tid >> 6] = above;
+    above = wave_inclusive_scan(above);
+    if (lane == kWave - 1) wave_above[tid >> 6] = above;
     __syncthreads();
     flush_hist<kB3>(h, a.hist + (size_t)u * kHistInts + kB1 + kB2);
     // suffix sums of the chunk's own level-3 histogram: sfx[b] = keys with low bits >= b
@@ -351,6 +350,7 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     __shared__ Digit dg;
     __shared__ int wave_gt[kWaves], wave_eq[kWaves];
     __shared__ int chunk_take, is_last;
+    __shared__ int stage[kChunk];           // the chunk's selected indices, in order
     const int u = kvc_bid_y();
     const int j = kvc_bid_x();
     const int tid = kvc_tid();
@@ -448,12 +448,9 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
         gt += ok && key[q] > T;
         eq += ok && key[q] == T;
     }
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        gt += shfl_xor_i(gt, o);
-        eq += shfl_xor_i(eq, o);
-    }
-    if (lane == 0) {
+    gt = wave_inclusive_scan(gt);
+    eq = wave_inclusive_scan(eq);
+    if (lane == kWave - 1) {
         wave_gt[wid] = gt;
         wave_eq[wid] = eq;
     }
@@ -477,10 +474,16 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
         const bool sel = is_gt || (is_eq && rank < take_j);
         const unsigned long long m_sel = __ballot(sel);
         const int p = pos + __popcll(m_sel & below);
-        if (sel && p < us.k_eff) out[p] = t;                     // never past the budget
+        if (sel && p < us.k_eff) stage[p - base] = t;            // never past the budget
         pos += __popcll(m_sel);
         eq_seen += __popcll(m_eq);
     }
+    // the chunk's selection leaves LDS in coalesced stores
+    __syncthreads();
+    int n_sel = take_j;
+    for (int w = 0; w < kWaves; ++w) n_sel += wave_gt[w];
+    for (int i = tid; i < n_sel; i += kThreads)
+        if (base + i < us.k_eff) out[base + i] = stage[i];
 }
 
 // ------------------------------------------------------------- one work-group per unit
@@ -615,15 +618,27 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
     const int gt_before = before.x;
     int eq_before = before.y;
     int pos = gt_before + min(ties, eq_before);
+    // the selection lands in LDS first (the level-1 histogram is free by now) when it
+    // fits, and leaves in coalesced stores: a store per key slot straight to global
+    // memory, with a few lanes of a wave active, costs more than the rest of the write
+    auto write_sel = [&](auto store) {
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        if (t0 + i >= us.C) break;
-        bool sel = key[i] > T;
-        if (key[i] == T) sel = eq_before++ < ties;
-        if (sel) {
-            if (pos < us.k_eff) out[pos] = t0 + i;                    // never past the budget
-            ++pos;
+        for (int i = 0; i < K; ++i) {
+            if (t0 + i >= us.C) break;
+            bool sel = key[i] > T;
+            if (key[i] == T) sel = eq_before++ < ties;
+            if (sel) {
+                if (pos < us.k_eff) store(pos, t0 + i);               // never past the budget
+                ++pos;
+            }
         }
+    };
+    if (us.k_eff <= kCopies * kB1) {
+        write_sel([&](int p, int t) { h1[p] = t; });
+        __syncthreads();
+        for (int i = tid; i < us.k_eff; i += NT) out[i] = h1[i];
+    } else {
+        write_sel([&](int p, int t) { out[p] = t; });
     }
 }
 
