@@ -63,6 +63,8 @@ struct ScorePlan {
     int tiles_per_wave = 1;    // MFMA path: 32-token tiles per wave per chunk
     int chunk_tokens = 0;      // MFMA path: tokens per work-group
     int n_chunks = 0;
+    int n_parts = 0;           // MFMA two-pass path: row partials per unit (per chunk, or per
+                               // 256-token block with one row block)
     int group_units = 0;       // KV-head units per pass-1/pass-2 launch pair
     int logit_rows = 0;        // MFMA path, R <= 16: logits kept per token between the passes
     bool fold_merge = false;   // two-pass MFMA path: the last pass-1 work-group of a unit merges its

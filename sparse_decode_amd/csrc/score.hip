@@ -10,8 +10,9 @@
 // the keys it sees and the probabilities are summed per key over all R rows.  The
 // row normalisers (max M_r, sum L_r) depend on every key, so the score takes two
 // passes over K:
-//   pass 1  logits -> per-row (max, sum of exp) for one chunk of tokens
-//   merge   chunk partials -> (M_r, 1/L_r) per row, in chunk order, in double
+//   pass 1  logits -> per-row (max, sum of exp) for one chunk of tokens (for one
+//           block of 16 rows: per 256-token block of the chunk)
+//   merge   partials -> (M_r, 1/L_r) per row, in token order, in double
 //   pass 2  logits again -> sum_r exp(x - M_r) / L_r per token
 //   pool    centred max over the candidate region
 // All units go into one launch of each kernel.  Both passes stream K from HBM; on
@@ -295,6 +296,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfThreads = 256;
+constexpr int kStatBlock = 256;     // tokens per row partial of the one-row-block statistics
+constexpr int kMaxChunk = 2048;     // tokens per work-group of the two-pass kernels at most
 constexpr int kMfWaves = kMfThreads / kWave;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -320,7 +323,8 @@ struct MfArgs {
     const int32_t *seq_lens;
     int s_max, n_h, n_kv, w, wic, R, unit0, n_chunks, chunk_tokens;
     float c;                 // scale * log2(e)
-    float2 *part;            // pass 1 out: [group][chunk][RT*16] (m, l)
+    int n_parts;             // row partials per unit: one per chunk, or per 256-token block (RT = 1)
+    float2 *part;            // pass 1 out: [group][n_parts][RT*16] (m, l)
     float2 *fin;             // merged row statistics, pass 2 in: [group][RT*16] (-M*c, 1/L)
     int32_t *arrive;         // [group] chunk arrival counters (zero between calls) when the last
                              // arriving pass-1 work-group merges its unit's chunks, else null
@@ -525,11 +529,12 @@ __device__ __forceinline__ void stats_stage(const unsigned char *buf, int st0, i
     }
 }
 
-// Merges the chunk partials (m, l) of every row of unit ul in a fixed order, by the
-// unit's last arriving pass-1 work-group: thread (slice, row) folds chunks slice,
+// Merges the partials (m, l) of every row of unit ul in a fixed order, by the unit's
+// last arriving pass-1 work-group or by mfma_merge_parts_kernel (kMfThreads threads
+// either way, so both give the same bits): thread (slice, row) folds partials slice,
 // slice + slices, ... online (rescale factors in fp32, sums in double), and the slices
-// are then folded in slice order.  The partials were published with st_dev by the
-// work-groups of other XCDs, hence ld_dev.  buf: 3 KB of LDS.
+// are then folded in slice order.  The partials may have been published with st_dev by
+// the work-groups of other XCDs, hence ld_dev.  buf: 3 KB of LDS.
 template <int RPAD>
 __device__ __forceinline__ void merge_chunks(const MfArgs &a, int ul, unsigned char *buf)
 {
@@ -539,20 +544,20 @@ __device__ __forceinline__ void merge_chunks(const MfArgs &a, int ul, unsigned c
     double *sm_L = (double *)(buf + kMfThreads * sizeof(float));
     const int row = kvc_tid() % RPAD;
     const int slice = kvc_tid() / RPAD;
-    const unsigned long long *p = (const unsigned long long *)(a.part + (size_t)ul * a.n_chunks * RPAD) + row;
+    const unsigned long long *p = (const unsigned long long *)(a.part + (size_t)ul * a.n_parts * RPAD) + row;
     float Mx = -INFINITY;
     double L = 0.0;
-    constexpr int kBatch = 8;               // chunk partials requested together per thread
-    for (int ch0 = slice; ch0 < a.n_chunks; ch0 += kBatch * slices) {
+    constexpr int kBatch = 8;               // partials requested together per thread
+    for (int ch0 = slice; ch0 < a.n_parts; ch0 += kBatch * slices) {
         unsigned long long v[kBatch];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-            const int ch = min(ch0 + q * slices, a.n_chunks - 1);    // unconditional: one round trip
+            const int ch = min(ch0 + q * slices, a.n_parts - 1);    // unconditional: one round trip
             v[q] = ld_dev(p + (size_t)ch * RPAD);
         }
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-            if (ch0 + q * slices >= a.n_chunks) continue;
+            if (ch0 + q * slices >= a.n_parts) continue;
             const float vm = unpack_lo(v[q]), vl = unpack_hi(v[q]);
             if (vm == -INFINITY) continue;
             if (vm > Mx) {
@@ -590,6 +595,17 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     unsigned char *kbuf = lds;                           // 2 stages
     __shared__ float sm_m[C::TG][RT * 16];
     __shared__ float sm_l[C::TG][RT * 16];
+    // One row block (RT = 1): a partial per 256-token block rather than per chunk, so
+    // the statistics do not depend on how the tokens are cut into chunks (a call that
+    // scores a few KV heads cuts them finer and gets the same bits).  At a block's last
+    // stage each wave merges a row's four lane groups with lane swaps (VALU only),
+    // keeps the result in LDS per (block, token group) and starts afresh; after the
+    // loop the token groups of every block are merged in order.
+    constexpr bool kBlocks = RT == 1;
+    constexpr int kBlkSt = kStatBlock / C::ST;           // stages per block
+    constexpr int kMaxBlk = kMaxChunk / kStatBlock;      // blocks per chunk at most
+    static_assert(!kBlocks || (kStatBlock % C::ST == 0 && C::CPW == 1), "a block is whole stages");
+    __shared__ float sm_bm[kBlocks ? kMaxBlk : 1][C::TG][16], sm_bl[kBlocks ? kMaxBlk : 1][C::TG][16];
 
     const int chunk = kvc_bid_x();
     const int ul = kvc_bid_y();
@@ -623,6 +639,46 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
         m[cb] = -INFINITY;
         l[cb] = 0.0;
     }
+    auto store_partial = [&](float Mx, float L, int idx, int row) {
+        float2 *dst = a.part + ((size_t)ul * a.n_parts + idx) * (RT * 16) + row;
+        if (a.arrive) st_dev((unsigned long long *)dst, pack2(Mx, L));
+        else *dst = make_float2(Mx, L);
+    };
+    auto block_end = [&](int st) { return st % kBlkSt == kBlkSt - 1 || st == n_st - 1; };
+    // (m, l) merged with the lane l ^ 32, then l ^ 16 (a symmetric expression: both
+    // lanes of a pair get the same bits)
+    auto lane_merge = [&](float &mm, double &ll) {
+#pragma unroll
+        for (int sw = 0; sw < 2; ++sw) {
+            const uint32_t mb = __float_as_uint(mm);
+            const uint32_t lo = (uint32_t)__double_as_longlong(ll), hi = (uint32_t)(__double_as_longlong(ll) >> 32);
+            uint32_t pm, plo, phi;
+            if (sw == 0) {
+                const bool low = (kvc_tid() & 63) < 32;
+                const auto x = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+                const auto y = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+                const auto z = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+                pm = low ? x[1] : x[0];
+                plo = low ? y[1] : y[0];
+                phi = low ? z[1] : z[0];
+            } else {
+                const bool even = ((kvc_tid() >> 4) & 1) == 0;
+                const auto x = __builtin_amdgcn_permlane16_swap(mb, mb, false, false);
+                const auto y = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+                const auto z = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+                pm = even ? x[1] : x[0];
+                plo = even ? y[1] : y[0];
+                phi = even ? z[1] : z[0];
+            }
+            const float m2 = __uint_as_float(pm);
+            const double l2 = __longlong_as_double((long long)(((unsigned long long)phi << 32) | plo));
+            const float Mx = fmaxf(mm, m2);
+            if (Mx != -INFINITY) {
+                ll = ll * (double)fast_exp2((mm - Mx) * a.c) + l2 * (double)fast_exp2((m2 - Mx) * a.c);
+                mm = Mx;
+            }
+        }
+    };
     stream_stages<D, RT, true>(kunit, ch0, n_st, kbuf,
         [&](const unsigned char *cur, int st) {
             const int st0 = ch0 + st * C::ST;
@@ -630,38 +686,67 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
                 stats_stage<D, RT, false>(cur, st0, tg, n, kg, qb, last, a.c, m, l, lg, a.rs, S);
             else
                 stats_stage<D, RT, true>(cur, st0, tg, n, kg, qb, last, a.c, m, l, lg, a.rs, S);
+            if constexpr (kBlocks) {
+                if (block_end(st)) {
+                    lane_merge(m[0], l[0]);
+                    const int bl = (st0 - ch0) / kStatBlock;
+                    if (kg == 0) {
+                        sm_bm[bl][tg][n] = m[0];
+                        sm_bl[bl][tg][n] = (float)l[0];
+                    }
+                    m[0] = -INFINITY;
+                    l[0] = 0.0;
+                }
+            }
         },
         [&](int) {});
-    // merge the four lane groups of a row (lanes n, n+16, n+32, n+48), then the token groups
+    if constexpr (kBlocks) {
+        // every block of the chunk: its token groups in order; blocks past the
+        // sequence hold no token
+        const int nb = (n_st * C::ST + kStatBlock - 1) / kStatBlock;      // blocks with stages
+        const int b1 = min(a.chunk_tokens / kStatBlock, a.n_parts - ch0 / kStatBlock);
+        __syncthreads();
+        for (int i = kvc_tid(); i < b1 * 16; i += kMfThreads) {
+            const int bl = i / 16, row = i % 16;
+            float Mx = -INFINITY, L = 0.f;
+            if (bl < nb) {
+                for (int t2 = 0; t2 < C::TG; ++t2) Mx = fmaxf(Mx, sm_bm[bl][t2][row]);
+                if (Mx != -INFINITY)
+                    for (int t2 = 0; t2 < C::TG; ++t2) L += sm_bl[bl][t2][row] * fast_exp2((sm_bm[bl][t2][row] - Mx) * a.c);
+            }
+            store_partial(Mx, L, ch0 / kStatBlock + bl, row);
+        }
+    } else {
+        // merge the four lane groups of a row (lanes n, n+16, n+32, n+48), then the
+        // token groups
 #pragma unroll
-    for (int cb = 0; cb < C::CPW; ++cb) {
+        for (int cb = 0; cb < C::CPW; ++cb) {
 #pragma unroll
-        for (int off = 16; off < 64; off <<= 1) {
-            const float m2 = shfl_xor_f(m[cb], off);
-            const double l2 = __shfl_xor(l[cb], off, kWave);
-            const float Mx = fmaxf(m[cb], m2);
-            if (Mx != -INFINITY) {
-                l[cb] = l[cb] * (double)fast_exp2((m[cb] - Mx) * a.c) + l2 * (double)fast_exp2((m2 - Mx) * a.c);
-                m[cb] = Mx;
+            for (int off = 16; off < 64; off <<= 1) {
+                const float m2 = shfl_xor_f(m[cb], off);
+                const double l2 = __shfl_xor(l[cb], off, kWave);
+                const float Mx = fmaxf(m[cb], m2);
+                if (Mx != -INFINITY) {
+                    l[cb] = l[cb] * (double)fast_exp2((m[cb] - Mx) * a.c) + l2 * (double)fast_exp2((m2 - Mx) * a.c);
+                    m[cb] = Mx;
+                }
+            }
+            if (kg == 0) {
+                sm_m[tg][(wr * C::CPW + cb) * 16 + n] = m[cb];
+                sm_l[tg][(wr * C::CPW + cb) * 16 + n] = (float)l[cb];
             }
         }
-        if (kg == 0) {
-            sm_m[tg][(wr * C::CPW + cb) * 16 + n] = m[cb];
-            sm_l[tg][(wr * C::CPW + cb) * 16 + n] = (float)l[cb];
+        __syncthreads();
+        for (int row = kvc_tid(); row < RT * 16; row += kMfThreads) {
+            float Mx = -INFINITY;
+            for (int t2 = 0; t2 < C::TG; ++t2) Mx = fmaxf(Mx, sm_m[t2][row]);
+            float L = 0.f;
+            if (Mx != -INFINITY)
+                for (int t2 = 0; t2 < C::TG; ++t2) L += sm_l[t2][row] * fast_exp2((sm_m[t2][row] - Mx) * a.c);
+            store_partial(Mx, L, chunk, row);
         }
     }
-    __syncthreads();
-    for (int row = kvc_tid(); row < RT * 16; row += kMfThreads) {
-        float Mx = -INFINITY;
-        for (int t2 = 0; t2 < C::TG; ++t2) Mx = fmaxf(Mx, sm_m[t2][row]);
-        float L = 0.f;
-        if (Mx != -INFINITY)
-            for (int t2 = 0; t2 < C::TG; ++t2) L += sm_l[t2][row] * fast_exp2((sm_m[t2][row] - Mx) * a.c);
-        float2 *dst = a.part + ((size_t)ul * a.n_chunks + chunk) * (RT * 16) + row;
-        if (a.arrive) st_dev((unsigned long long *)dst, pack2(Mx, L));
-        else *dst = make_float2(Mx, L);
-    }
-    if (!a.arrive) return;                  // mfma_merge_kernel merges the chunks
+    if (!a.arrive) return;                  // a merge kernel merges the partials
     // count this chunk's arrival once its partials have landed; the unit's last arrival
     // merges every chunk (the K stage buffers are free by now and hold the merge's state)
     stores_done();
@@ -674,6 +759,17 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
     __syncthreads();
     if (sm_last) merge_chunks<RT * 16>(a, ul, lds);
+}
+
+// The merge of one row block's partials as a kernel of its own: the arithmetic of the
+// merge in the last pass-1 work-group.
+template <int RPAD>
+__global__ __launch_bounds__(kMfThreads) void mfma_merge_parts_kernel(MfArgs a)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char buf[kMfThreads * (sizeof(float) + sizeof(double))];
+    const int ul = kvc_bid_x();
+    if (a.mask && !ld_uniform(a.mask, a.unit0 + ul)) return;
+    merge_chunks<RPAD>(a, ul, buf);
 }
 
 // Merges the chunk partials of every row in a fixed order, as a kernel of its own
@@ -1427,10 +1523,14 @@ void launch_mfma_group(const MfArgs &a, int group_units, hipStream_t stream)
     dim3 grid(a.n_chunks, group_units);
     static_assert(C::LDS_BYTES >= kMfThreads * (sizeof(float) + sizeof(double)), "merge state fits the stages");
     hipLaunchKernelGGL((mfma_stats_kernel<D, RT>), grid, dim3(kMfThreads), C::LDS_BYTES, stream, a);
-    if (!a.arrive)
-        hipLaunchKernelGGL(mfma_merge_kernel, dim3(group_units), dim3(kMergeThreads), 0, stream,
-                           (const float2 *)a.part, a.n_chunks, RT * 16, a.R, a.c, a.mask ? a.mask + a.unit0 : nullptr,
-                           a.fin);
+    if (!a.arrive) {
+        if constexpr (RT == 1)
+            hipLaunchKernelGGL((mfma_merge_parts_kernel<RT * 16>), dim3(group_units), dim3(kMfThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(mfma_merge_kernel, dim3(group_units), dim3(kMergeThreads), 0, stream,
+                               (const float2 *)a.part, a.n_parts, RT * 16, a.R, a.c,
+                               a.mask ? a.mask + a.unit0 : nullptr, a.fin);
+    }
     if (RT == 1 && a.logits) {
         const dim3 lgrid((a.s_max + kLogitThreads - 1) / kLogitThreads, group_units);
         hipLaunchKernelGGL(logit_probsum_kernel, lgrid, dim3(kLogitThreads), 0, stream, (const float *)a.logits,
@@ -1549,7 +1649,7 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
         p.group_units = units;
         // tokens per work-group: the largest of 2048, 1024, 512, 256 that still gives
         // at least four work-groups per CU (a multiple of every stage size)
-        int ct_tok = 2048;
+        int ct_tok = kMaxChunk;
         while (ct_tok > 256) {
             const long chunks = (s_max + ct_tok - 1) / ct_tok;
             if (chunks * p.group_units >= 4L * cus) break;
@@ -1558,14 +1658,15 @@ ScorePlan plan_score(int batch, int s_max, int n_h, int n_kv, int d_h, bool bf16
         p.tiles_per_wave = 0;
         p.chunk_tokens = ct_tok;
         p.n_chunks = (s_max + ct_tok - 1) / ct_tok;
+        p.n_parts = rt == 1 ? (s_max + kStatBlock - 1) / kStatBlock : p.n_chunks;
         // a few chunks per unit in one round of work-groups: the unit's last arriving
         // pass-1 work-group merges the chunks, one launch less.  With more chunks or
         // rounds, publishing every work-group's partials device-coherently and waiting
         // for its arrival count cost more than the merge kernel (measured: twice the
         // pass-1 time at 128 chunks of a KV head, +15% over four rounds)
         p.fold_merge = p.n_chunks <= 8 && (long)p.n_chunks * p.group_units <= 4L * cus;
-        // chunk partials, merged row statistics, chunk arrival counters (zero between calls)
-        p.ws_bytes = align256((size_t)p.group_units * p.n_chunks * rpad * sizeof(float2)) +
+        // row partials, merged row statistics, chunk arrival counters (zero between calls)
+        p.ws_bytes = align256((size_t)p.group_units * p.n_parts * rpad * sizeof(float2)) +
                      align256((size_t)p.group_units * rpad * sizeof(float2)) +
                      align256((size_t)p.group_units * sizeof(int32_t)) + 256;
         // a single row block (R <= 16): pass 1 keeps its logits, 4 * rs bytes per token,
@@ -1653,13 +1754,21 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         a.R = plan.R;
         a.n_chunks = plan.n_chunks;
         a.chunk_tokens = plan.chunk_tokens;
+        a.n_parts = plan.n_parts;
         a.c = scale * kLog2e;
-        const size_t fin_off = align256((size_t)plan.group_units * plan.n_chunks * rpad * sizeof(float2));
+        const size_t fin_off = align256((size_t)plan.group_units * plan.n_parts * rpad * sizeof(float2));
         a.part = (float2 *)ws;
         a.fin = (float2 *)((char *)ws + fin_off);
-        a.arrive = plan.fold_merge
-                       ? (int32_t *)((char *)ws + fin_off + align256((size_t)plan.group_units * rpad * sizeof(float2)))
-                       : nullptr;
+        int32_t *arrive = (int32_t *)((char *)ws + fin_off + align256((size_t)plan.group_units * rpad * sizeof(float2)));
+        a.arrive = plan.fold_merge ? arrive : nullptr;
+        if (rt == 1 && unit_mask) {
+            // a call for some KV heads (a correction): work-groups of one 256-token block,
+            // so a KV head is spread over many CUs, and the last one merges.  The
+            // partials are per block whatever the chunks: the same bits as a full call
+            a.chunk_tokens = kStatBlock;
+            a.n_chunks = (s_max + kStatBlock - 1) / kStatBlock;
+            a.arrive = arrive;
+        }
         a.raw = raw;
         a.mask = unit_mask;
         a.rs = plan.logit_rows;

@@ -422,6 +422,48 @@ def _plan(B, n_h, n_kv, d, s_max, w):
     return kvc.score_window_plan(kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16), w)
 
 
+@pytest.mark.parametrize("s_max", [16384, 9000])
+def test_score_one_row_block_masked_call_matches_full(s_max):
+    # one query per head over 16 ragged sequences (R = 4): a masked call cuts the
+    # tokens into 256-token work-groups whatever the full call's chunks (2048 tokens
+    # merged in the last work-group at 16384, 1024 tokens merged by a kernel at 9000),
+    # and its scores are the same bits, the row partials being per 256-token block
+    B, n_h, n_kv, d, w = 16, 32, 8, 128, 1
+    plan = _plan(B, n_h, n_kv, d, s_max, w)
+    assert plan["rt"] == 1 and plan["chunk_tokens"] >= 1024, plan
+    rng = np.random.default_rng(7)
+    sl = rng.integers(s_max // 4, s_max + 1, B).astype(np.int32)
+    sl[0] = s_max
+    sl[1] = 257
+    _say("score one row block masked", B, n_h, n_kv, d, s_max, w, plan)
+    q = _randn((B, n_h, w, d), 320)
+    k = _randn((B, n_kv, s_max, d), 321)
+    dims = kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16)
+    ws = torch.zeros(kvc.score_window_workspace(dims, w), dtype=torch.uint8, device=DEV)
+    args = dict(seq_lens=sl, window_in_cache=False, n_keep=32, pool=7, ws=ws)
+    raw, pooled = kvc.score_window(q, k, w, **args)
+    for frac in (0.05, 0.5):
+        mask_np = (rng.random((B, n_kv)) < frac).astype(np.int32)
+        mask_np[0, 0] = 1
+        mask_np[1, 1] = 1
+        mask = torch.from_numpy(mask_np).to(DEV)
+        raw_m = torch.full((B, n_kv, s_max), -7.0, device=DEV)
+        pooled_m = torch.full((B, n_kv, s_max), -9.0, device=DEV)
+        kvc.score_window(q, k, w, raw=raw_m, pooled=pooled_m, unit_mask=mask, **args)
+        torch.cuda.synchronize()
+        on = mask.bool()
+        assert torch.equal(raw_m[on], raw[on]) and torch.equal(pooled_m[on], pooled[on]), frac
+        assert bool((raw_m[~on] == -7.0).all()) and bool((pooled_m[~on] == -9.0).all())
+    raw2, pooled2 = kvc.score_window(q, k, w, **args)
+    assert torch.equal(raw, raw2) and torch.equal(pooled, pooled2)
+    # two sequences against the oracle
+    idx = [0, 1]
+    rraw, rpooled = oracle.score_window(host(q)[idx], host(k)[idx], w, seq_lens=sl[idx], window_in_cache=False,
+                                        n_keep=32, pool=7)
+    assert_scores_close(raw[idx], rraw, "raw")
+    assert_scores_close(pooled[idx], rpooled, "pooled")
+
+
 @pytest.mark.parametrize("shape", [(3, 16, 4, 2000, 1, False), (2, 8, 1, 1800, 16, True)])
 def test_score_folded_merge_mask_and_reuse(shape):
     # at most 8 items per KV head, all work-groups resident: the last first-pass
