@@ -194,50 +194,12 @@ __device__ __forceinline__ float pool_at(const float *tile, int base, int t, int
     return t < S ? tile[t - base] : 0.f;
 }
 
-// One work-group per kPoolTile tokens of a unit: the tile and its halo are staged in
-// LDS once (coalesced), then each output is the max over its window.  Each thread
-// owns 4 consecutive tokens (one 16-byte load and store when a row is a multiple of 4
-// floats).  HALF >= 0 is the half-width known at compile time: where the 4 windows
-// lie inside [0, C), the thread reads the 4 + 2 HALF values once into registers and
-// takes the 4 maxima there; elsewhere, and for HALF < 0, every window is walked.
+// The pooled outputs of one tile: tile[i] holds raw[base + i] for the kPoolTile tokens
+// from t0 and their halo; this thread's 4 tokens start at t = t0 + 4 tid.
 template <bool VEC, int HALF>
-__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restrict__ raw,
-                                                            const int32_t *__restrict__ seq_lens, int s_max,
-                                                            int n_kv, int n_keep, int half,
-                                                            const int32_t *__restrict__ mask,
-                                                            float *__restrict__ pooled, int32_t *reset, int n_reset)
+__device__ __forceinline__ void pool_tile(const float *tile, int base, int t, int s_max, int half, int C, int S,
+                                          float *__restrict__ out)
 {
-    // the single-pass kernels' counters go back to zero here, after their last use
-    if (reset && kvc_bid_x() == 0 && kvc_bid_y() == 0)
-        for (int i = kvc_tid(); i < n_reset; i += kPoolThreads) reset[i] = 0;
-    // 2 kMaxHalf + 2 slots (left halo, then 16-byte alignment), the body, the right halo
-    __shared__ __attribute__((aligned(16))) float tile[2 * kMaxHalf + 2 + kPoolTile + kMaxHalf + 1];
-    if constexpr (HALF >= 0) half = HALF;
-    const int u = kvc_bid_y();
-    if (mask && !ld_uniform(mask, u)) return;
-    const int S = clamp_len(seq_lens, u / n_kv, s_max);
-    const int C = S - n_keep > 0 ? S - n_keep : 0;
-    const int t0 = kvc_bid_x() * kPoolTile;
-    const float *rw = raw + (size_t)u * s_max;
-    float *out = pooled + (size_t)u * s_max;
-    const int tid = kvc_tid();
-    const int base = t0 - (2 * kMaxHalf + 2);               // tile[i] holds raw[base + i]
-    float *body = tile + 2 * kMaxHalf + 2;                  // 16-byte aligned: 64 floats in
-    const int t = t0 + 4 * tid;                             // this thread's 4 tokens
-    if constexpr (VEC) {
-        *(float4 *)(body + 4 * tid) = t < s_max ? *(const float4 *)(rw + t) : make_float4(0.f, 0.f, 0.f, 0.f);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) body[4 * tid + k] = t + k < s_max ? rw[t + k] : 0.f;
-    }
-    if (tid < half) {
-        const int th = t0 - half + tid;
-        tile[th - base] = th >= 0 ? rw[th] : 0.f;
-    } else if (tid < 2 * half) {
-        const int th = t0 + kPoolTile + (tid - half);
-        tile[th - base] = th < s_max ? rw[th] : 0.f;
-    }
-    __syncthreads();
     if (t >= s_max) return;
     float o[4];
     if (HALF >= 0 && t - HALF >= 0 && t + 3 + HALF <= C - 1) {
@@ -264,6 +226,55 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restr
         for (int k = 0; k < 4; ++k)
             if (t + k < s_max) out[t + k] = o[k];
     }
+}
+
+// LDS tile of the pooling kernels: 2 kMaxHalf + 2 slots (left halo, then 16-byte
+// alignment), the body, the right halo
+constexpr int kPoolLds = 2 * kMaxHalf + 2 + kPoolTile + kMaxHalf + 1;
+
+// One work-group per kPoolTile tokens of a unit: the tile and its halo are staged in
+// LDS once (coalesced), then each output is the max over its window.  Each thread
+// owns 4 consecutive tokens (one 16-byte load and store when a row is a multiple of 4
+// floats).  HALF >= 0 is the half-width known at compile time: where the 4 windows
+// lie inside [0, C), the thread reads the 4 + 2 HALF values once into registers and
+// takes the 4 maxima there; elsewhere, and for HALF < 0, every window is walked.
+template <bool VEC, int HALF>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restrict__ raw,
+                                                            const int32_t *__restrict__ seq_lens, int s_max,
+                                                            int n_kv, int n_keep, int half,
+                                                            const int32_t *__restrict__ mask,
+                                                            float *__restrict__ pooled, int32_t *reset, int n_reset)
+{
+    // the single-pass kernels' counters go back to zero here, after their last use
+    if (reset && kvc_bid_x() == 0 && kvc_bid_y() == 0)
+        for (int i = kvc_tid(); i < n_reset; i += kPoolThreads) reset[i] = 0;
+    __shared__ __attribute__((aligned(16))) float tile[kPoolLds];
+    if constexpr (HALF >= 0) half = HALF;
+    const int u = kvc_bid_y();
+    if (mask && !ld_uniform(mask, u)) return;
+    const int S = clamp_len(seq_lens, u / n_kv, s_max);
+    const int C = S - n_keep > 0 ? S - n_keep : 0;
+    const int t0 = kvc_bid_x() * kPoolTile;
+    const float *rw = raw + (size_t)u * s_max;
+    const int tid = kvc_tid();
+    const int base = t0 - (2 * kMaxHalf + 2);               // tile[i] holds raw[base + i]
+    float *body = tile + 2 * kMaxHalf + 2;                  // 16-byte aligned: 64 floats in
+    const int t = t0 + 4 * tid;                             // this thread's 4 tokens
+    if constexpr (VEC) {
+        *(float4 *)(body + 4 * tid) = t < s_max ? *(const float4 *)(rw + t) : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) body[4 * tid + k] = t + k < s_max ? rw[t + k] : 0.f;
+    }
+    if (tid < half) {
+        const int th = t0 - half + tid;
+        tile[th - base] = th >= 0 ? rw[th] : 0.f;
+    } else if (tid < 2 * half) {
+        const int th = t0 + kPoolTile + (tid - half);
+        tile[th - base] = th < s_max ? rw[th] : 0.f;
+    }
+    __syncthreads();
+    pool_tile<VEC, HALF>(tile, base, t, s_max, half, C, S, pooled + (size_t)u * s_max);
 }
 
 template <bool VEC>
@@ -329,6 +340,8 @@ struct MfArgs {
     int32_t *arrive;         // [group] chunk arrival counters (zero between calls) when the last
                              // arriving pass-1 work-group merges its unit's chunks, else null
     float *raw;              // pass 2 out: [B*n_kv][s_max]
+    float *pooled;           // one row block: pooled out of the fused pass 2 [B*n_kv][s_max]
+    int n_keep, half;        // its pooling: trailing tokens kept, half-width
     float *logits;           // one row block only: pass 1 keeps its logits [B*n_kv][s_max][rs], or null
     int rs;                  // rows kept per token (R rounded up to 4)
     const int32_t *mask;     // [B*n_kv] or null: units with 0 are skipped
@@ -942,44 +955,82 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
 }
 
-// Pass 2 from the logits pass 1 kept (a single row block of at most 16 rows): per
-// token, raw = sum over rows, in row order, of exp2(x c - M c) / L.  Each thread reads
-// one token's rs consecutive logits; no K is read again.
-constexpr int kLogitThreads = 256;
-
-__global__ __launch_bounds__(kLogitThreads) void logit_probsum_kernel(const float *__restrict__ logits,
-                                                                      const float2 *__restrict__ fin,
-                                                                      const int32_t *__restrict__ seq_lens,
-                                                                      int s_max, int n_kv, int R, int rs, int rpad,
-                                                                      int unit0, float c,
-                                                                      const int32_t *__restrict__ mask,
-                                                                      float *__restrict__ raw)
+// One row block (R <= 16): pass 2, from the logits pass 1 kept (no K is read again),
+// and the pooling in one kernel.  A work-group takes kPoolTile tokens of a unit and
+// the pooling halo around them, scores each token from its rs consecutive logits (sum
+// over rows, in row order, of exp2(x c - M c) / L), writes the tile's scores and pools
+// them from LDS as pool_kernel does.
+template <bool VEC, int HALF>
+__global__ __launch_bounds__(kPoolThreads) void logit_pool_kernel(MfArgs a)
 {
     __shared__ float2 f[16];
+    __shared__ __attribute__((aligned(16))) float tile[kPoolLds];
+    int half = a.half;
+    if constexpr (HALF >= 0) half = HALF;
     const int ul = kvc_bid_y();
-    const int u = unit0 + ul;
-    if (mask && !ld_uniform(mask, u)) return;
-    if (kvc_tid() < 16) f[kvc_tid()] = kvc_tid() < R ? fin[(size_t)ul * rpad + kvc_tid()] : make_float2(0.f, 0.f);
+    const int u = a.unit0 + ul;
+    if (a.mask && !ld_uniform(a.mask, u)) return;
+    const int tid = kvc_tid();
+    if (tid < 16) f[tid] = tid < a.R ? a.fin[(size_t)ul * 16 + tid] : make_float2(0.f, 0.f);
     __syncthreads();
-    const int S = clamp_len(seq_lens, u / n_kv, s_max);
-    const int t = kvc_bid_x() * kLogitThreads + kvc_tid();
-    if (t >= s_max) return;
-    float acc = 0.f;
-    if (t < S) {
-        const float4 *x4 = (const float4 *)(logits + ((size_t)u * s_max + t) * rs);
-        float x[16];
+    const int S = clamp_len(a.seq_lens, u / a.n_kv, a.s_max);
+    const int C = S - a.n_keep > 0 ? S - a.n_keep : 0;
+    const float *lg = a.logits + (size_t)u * a.s_max * a.rs;
+    auto score = [&](int t) {               // 0 outside [0, S)
+        float acc = 0.f;
+        if (t >= 0 && t < S) {
+            const float4 *x4 = (const float4 *)(lg + (size_t)t * a.rs);
+            float x[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (4 * q < rs) {
-                const float4 v = x4[q];
-                x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+            for (int q = 0; q < 4; ++q) {
+                if (4 * q < a.rs) {
+                    const float4 v = x4[q];
+                    x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+                }
             }
-        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (r < R) acc = fmaf(fast_exp2(fmaf(x[r], c, f[r].x)), f[r].y, acc);
+            for (int r = 0; r < 16; ++r)
+                if (r < a.R) acc = fmaf(fast_exp2(fmaf(x[r], a.c, f[r].x)), f[r].y, acc);
+        }
+        return acc;
+    };
+    const int t0 = kvc_bid_x() * kPoolTile;
+    const int base = t0 - (2 * kMaxHalf + 2);               // tile[i] holds raw[base + i]
+    float *body = tile + 2 * kMaxHalf + 2;
+    const int t = t0 + 4 * tid;                             // this thread's 4 tokens
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = score(t + k);
+    *(float4 *)(body + 4 * tid) = make_float4(v[0], v[1], v[2], v[3]);
+    float *rw = a.raw + (size_t)u * a.s_max;
+    if constexpr (VEC) {
+        if (t < a.s_max) *(float4 *)(rw + t) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (t + k < a.s_max) rw[t + k] = v[k];
     }
-    raw[(size_t)u * s_max + t] = acc;
+    if (tid < half) {
+        const int th = t0 - half + tid;
+        tile[th - base] = score(th);
+    } else if (tid < 2 * half) {
+        const int th = t0 + kPoolTile + (tid - half);
+        tile[th - base] = score(th);                        // 0 past S, so past s_max
+    }
+    __syncthreads();
+    pool_tile<VEC, HALF>(tile, base, t, a.s_max, half, C, S, a.pooled + (size_t)u * a.s_max);
+}
+
+template <bool VEC>
+void launch_logit_pool(dim3 grid, const MfArgs &a, hipStream_t stream)
+{
+    switch (a.half) {
+    case 0: hipLaunchKernelGGL((logit_pool_kernel<VEC, 0>), grid, dim3(kPoolThreads), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((logit_pool_kernel<VEC, 1>), grid, dim3(kPoolThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((logit_pool_kernel<VEC, 2>), grid, dim3(kPoolThreads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((logit_pool_kernel<VEC, 3>), grid, dim3(kPoolThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((logit_pool_kernel<VEC, -1>), grid, dim3(kPoolThreads), 0, stream, a); break;
+    }
 }
 
 // ====================================================================================
@@ -1532,9 +1583,12 @@ void launch_mfma_group(const MfArgs &a, int group_units, hipStream_t stream)
                                a.mask ? a.mask + a.unit0 : nullptr, a.fin);
     }
     if (RT == 1 && a.logits) {
-        const dim3 lgrid((a.s_max + kLogitThreads - 1) / kLogitThreads, group_units);
-        hipLaunchKernelGGL(logit_probsum_kernel, lgrid, dim3(kLogitThreads), 0, stream, (const float *)a.logits,
-                           a.fin, a.seq_lens, a.s_max, a.n_kv, a.R, a.rs, RT * 16, a.unit0, a.c, a.mask, a.raw);
+        // pass 2 fused with the pooling
+        const dim3 pgrid((a.s_max + kPoolTile - 1) / kPoolTile, group_units);
+        if (a.s_max % 4 == 0 && ((uintptr_t)a.raw & 15) == 0 && ((uintptr_t)a.pooled & 15) == 0)
+            launch_logit_pool<true>(pgrid, a, stream);
+        else
+            launch_logit_pool<false>(pgrid, a, stream);
     } else {
         hipLaunchKernelGGL((mfma_probsum_kernel<D, RT>), grid, dim3(kMfThreads),
                            C::LDS_BYTES + (size_t)a.chunk_tokens * sizeof(float), stream, a);
@@ -1770,6 +1824,9 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
             a.arrive = arrive;
         }
         a.raw = raw;
+        a.pooled = pooled;
+        a.n_keep = n_keep;
+        a.half = pool / 2;
         a.mask = unit_mask;
         a.rs = plan.logit_rows;
         a.logits = plan.logit_rows ? (float *)((char *)ws + plan.logits_off - plan.two_pass_off) : nullptr;
@@ -1799,6 +1856,8 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // the two-pass kernels of one row block pool in their second pass
+    if (plan.mfma && !single_done && plan.logit_rows) return hipGetLastError();
     // after the single-pass kernels the pooling kernel zeroes their arrival counters and
     // deferred count (laid out first in the workspace: units + 1 words)
     int32_t *reset = single_done ? (int32_t *)ws_base : nullptr;
