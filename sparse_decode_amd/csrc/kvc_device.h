@@ -168,8 +168,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *to
 }
 
 // Exclusive prefix sums of two values across the work-group with the barriers of one
-// scan; `scratch` holds at least 32 ints of LDS.  Same conditions as above.
-__device__ __forceinline__ int2 block_exclusive_scan2(int a, int b, int *scratch)
+// scan; `scratch` holds at least 32 ints of LDS.  Same conditions as above; the group
+// totals go to *total when it is not null.
+__device__ __forceinline__ int2 block_exclusive_scan2(int a, int b, int *scratch, int2 *total = nullptr)
 {
     const int lane = kvc_tid() & (kWave - 1);
     const int wid = kvc_tid() >> 6;
@@ -181,14 +182,20 @@ __device__ __forceinline__ int2 block_exclusive_scan2(int a, int b, int *scratch
         scratch[16 + wid] = ib;
     }
     __syncthreads();
-    int pa = 0, pb = 0;
+    int pa = 0, pb = 0, ta = 0, tb = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        if (i < wid && i < nw) {
-            pa += scratch[i];
-            pb += scratch[16 + i];
+        if (i < nw) {
+            const int sa = scratch[i], sb = scratch[16 + i];
+            if (i < wid) {
+                pa += sa;
+                pb += sb;
+            }
+            ta += sa;
+            tb += sb;
         }
     }
+    if (total) *total = make_int2(ta, tb);
     __syncthreads();
     return make_int2(pa + ia - a, pb + ib - b);
 }

@@ -346,10 +346,10 @@ template <int KPT>
 __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
 {
     constexpr int kChunk = KPT * kThreads;
-    __shared__ int scan[16];
+    __shared__ int scan[32];
     __shared__ Digit dg;
     __shared__ int wave_gt[kWaves], wave_eq[kWaves];
-    __shared__ int chunk_take, is_last;
+    __shared__ int chunk_take, chunk_base, is_last;
     __shared__ int stage[kChunk];           // the chunk's selected indices, in order
     const int u = kvc_bid_y();
     const int j = kvc_bid_x();
@@ -398,24 +398,17 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     const Digit d3 = find_digit<kB3>(c3, us.k_eff - d1.above - d2.above, scan, &dg);
     const uint32_t T = ((uint32_t)d1.digit << 21) | ((uint32_t)d2.digit << 10) | (uint32_t)d3.digit;
     const int ties = us.k_eff - d1.above - d2.above - d3.above;     // keys == T to take, lowest index first
-    // the last of the unit's work-groups to get here (all others have read H) returns
-    // the histograms and the counter to zero for the next call
-    if (tid == 0) {
-        const int n_wg = (us.C + kChunk - 1) / kChunk;
-        is_last = atomicAdd(&a.done[u], 1) == n_wg - 1;
-    }
-    __syncthreads();
-    if (is_last) {
-        int4 *h4 = reinterpret_cast<int4 *>(a.hist + (size_t)u * kHistInts);
-        for (int i = tid; i < kHistInts / 4; i += kThreads) h4[i] = make_int4(0, 0, 0, 0);
-        if (tid == 0) a.done[u] = 0;
-    }
-    __syncthreads();
+    // this work-group is past its reads of H: count it.  The last of the unit's
+    // work-groups returns the histograms and the counter to zero for the next call, at
+    // the end, so the atomic's round trip overlaps the rest
+    int done_before = 0;
+    if (tid == 0) done_before = atomicAdd(&a.done[u], 1);
 
     // output offset of this chunk: the chunks before it contribute their keys above T
-    // and, lowest chunk first, their keys equal to T until `ties` are taken.  Thread i
-    // of each block of kThreads chunks holds one chunk.
-    int base = 0, eq_run = 0;
+    // and, lowest chunk first, their keys equal to T until `ties` are taken, so the
+    // takes before chunk j add up to min(ties, their keys equal to T).  Thread i of each
+    // block of kThreads chunks holds one chunk.
+    int gt_run = 0, eq_run = 0;
     for (int jb = 0; jb <= j; jb += kThreads) {
         const int jj = jb + tid;
         int gt = 0, eq = 0;
@@ -425,20 +418,20 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
             gt = a.above12[(size_t)u * a.n_chunks + jj] + s_hi;
             eq = s_at - s_hi;
         }
-        int eq_tot;
-        const int eq_before = eq_run + block_exclusive_scan(eq, scan, &eq_tot);
-        int take = ties - eq_before;
-        take = take < 0 ? 0 : (take > eq ? eq : take);
+        int2 tot;
+        const int2 before = block_exclusive_scan2(gt, eq, scan, &tot);
         if (jj == j) {
-            chunk_take = take;
+            const int eq_before = eq_run + before.y;
+            int take = ties - eq_before;
+            chunk_take = take < 0 ? 0 : (take > eq ? eq : take);
+            chunk_base = gt_run + before.x + min(ties, eq_before);
         }
-        int sel_tot;
-        block_exclusive_scan(jj < j ? gt + take : 0, scan, &sel_tot);
-        base += sel_tot;
-        eq_run += eq_tot;
+        gt_run += tot.x;
+        eq_run += tot.y;
     }
     __syncthreads();
     const int take_j = chunk_take;
+    const int base = chunk_base;
 
     // ordered compaction: per-wave counts, then ballots give in-wave prefix counts
     int gt = 0, eq = 0;
@@ -484,6 +477,13 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
     for (int w = 0; w < kWaves; ++w) n_sel += wave_gt[w];
     for (int i = tid; i < n_sel; i += kThreads)
         if (base + i < us.k_eff) out[base + i] = stage[i];
+    if (tid == 0) is_last = done_before == (us.C + kChunk - 1) / kChunk - 1;
+    __syncthreads();
+    if (is_last) {
+        int4 *h4 = reinterpret_cast<int4 *>(a.hist + (size_t)u * kHistInts);
+        for (int i = tid; i < kHistInts / 4; i += kThreads) h4[i] = make_int4(0, 0, 0, 0);
+        if (tid == 0) a.done[u] = 0;
+    }
 }
 
 // ------------------------------------------------------------- one work-group per unit
