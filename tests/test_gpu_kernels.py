@@ -422,15 +422,16 @@ def _plan(B, n_h, n_kv, d, s_max, w):
     return kvc.score_window_plan(kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16), w)
 
 
-@pytest.mark.parametrize("s_max", [16384, 9000])
-def test_score_one_row_block_masked_call_matches_full(s_max):
+@pytest.mark.parametrize("s_max, d", [(16384, 128), (9000, 128), (5000, 64)])
+def test_score_one_row_block_masked_call_matches_full(s_max, d):
     # one query per head over 16 ragged sequences (R = 4): a masked call cuts the
     # tokens into 256-token work-groups whatever the full call's chunks (2048 tokens
-    # merged in the last work-group at 16384, 1024 tokens merged by a kernel at 9000),
-    # and its scores are the same bits, the row partials being per 256-token block
-    B, n_h, n_kv, d, w = 16, 32, 8, 128, 1
+    # merged in the last work-group at 16384, 1024 tokens merged by a kernel at 9000,
+    # 512 tokens at 5000 with d_h = 64), and its scores are the same bits, the row
+    # partials being per 256-token block
+    B, n_h, n_kv, w = 16, 32, 8, 1
     plan = _plan(B, n_h, n_kv, d, s_max, w)
-    assert plan["rt"] == 1 and plan["chunk_tokens"] >= 1024, plan
+    assert plan["rt"] == 1 and plan["chunk_tokens"] >= 512, plan
     rng = np.random.default_rng(7)
     sl = rng.integers(s_max // 4, s_max + 1, B).astype(np.int32)
     sl[0] = s_max
