@@ -26,9 +26,14 @@
 //           order (ballots give in-wave prefix counts); chunk 0 also writes the
 //           window, the padding and the count
 //
+// With the 8192-key chunks, levels 2, 3 and the write are one kernel instead
+// (sel_cand_kernel, below): every work-group lists its chunk's keys in the bins at or
+// above d1, and the unit's last work-group selects among those candidates in LDS.
+//
 // The unit histograms and a per-unit counter live in the workspace, which must be
-// zero when a call starts: the last write work-group of each unit clears them again.
-// Every figure is an integer count, so the result does not depend on scheduling.
+// zero when a call starts: the last write (or candidate) work-group of each unit
+// clears them again.  Every figure is an integer count, so the result does not depend
+// on scheduling.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -79,6 +84,8 @@ struct SelArgs {
     int32_t *done;            // [units]: write work-groups past their histogram reads (zero between calls)
     int32_t *above12;         // [units][n_chunks]: chunk keys above prefix (d1, d2)
     int32_t *sfx3;            // [units][n_chunks][kSfx]: suffix sums of the chunk's H3 part
+    unsigned long long *cand; // [units][n_chunks][chunk keys]: candidate lists, (index << 32) | key
+    int32_t *cand_n;          // [units][n_chunks]: their lengths
     int32_t *idx;             // [units][cap]
     int32_t *count;           // [units]
     const int32_t *mask;      // [units] or null: units with 0 are skipped by every kernel
@@ -642,6 +649,299 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
     }
 }
 
+// ------------------------------------------- candidate lists: long units in two launches
+// After level 1, every key that can be selected lies in H1's bin d1 (the bin of the
+// k_eff-th largest key) or above.  sel_cand_kernel's work-groups each find d1, write
+// their chunk's keys in bins >= d1 with their indices, in index order, to the chunk's
+// list in the workspace, and count their arrival; the unit's last work-group gathers
+// every chunk's list into LDS (the chunks in order: index order) and runs levels 2 and
+// 3 and the ordered write there.  The levels, the tie rule and the output are those of
+// the kernels above.  A unit with more candidates than LDS holds (long runs of equal
+// scores around the threshold) is finished by that work-group from the unit's scores
+// instead: levels 2 and 3 and the write streamed from the caches.
+constexpr int kCandLds = 6144;                  // candidates the last work-group holds in LDS
+constexpr int kCandPer = kCandLds / kThreads;   // per thread
+
+// Calls f(key) for every candidate t < C of a unit's row: coalesced loads, kCandPer in
+// flight per thread.
+template <typename F>
+__device__ __forceinline__ void stream_keys(const float *__restrict__ sc, int C, F f)
+{
+    constexpr int kStep = kThreads * kCandPer;
+    for (int t0 = (int)kvc_tid(); t0 < C; t0 += kStep) {
+        float x[kCandPer];
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+            const int t = t0 + q * kThreads;
+            x[q] = t < C ? sc[t] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q)
+            if (t0 + q * kThreads < C) f(order_key(x[q]));
+    }
+}
+
+// Calls f(t, key) for the candidates of this wave's range [r0, r1) in index order, 64
+// consecutive candidates per step (lane l holds t = s + l; lanes past the range get
+// t = -1 and key 0), every lane of the wave taking part in every step.
+template <typename F>
+__device__ __forceinline__ void walk_keys(const float *__restrict__ sc, int r0, int r1, F f)
+{
+    const int lane = kvc_tid() & (kWave - 1);
+    for (int s0 = r0; s0 < r1; s0 += kWave * kCandPer) {
+        float x[kCandPer];
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+            const int t = s0 + q * kWave + lane;
+            x[q] = t < r1 ? sc[t] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+            const int t = s0 + q * kWave + lane;
+            if (s0 + q * kWave < r1) f(t < r1 ? t : -1, t < r1 ? order_key(x[q]) : 0u);
+        }
+    }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
+{
+    constexpr int kChunk = KPT * kThreads;
+    __shared__ int scan[32];
+    __shared__ Digit dg;
+    __shared__ int wave_n[kWaves], wave_eq[kWaves];
+    __shared__ int sh_last;
+    __shared__ int offs[kThreads + 1];
+    __shared__ uint32_t c_key[kCandLds];
+    __shared__ int32_t c_idx[kCandLds];
+    __shared__ uint16_t c_chunk[kCandLds];
+    __shared__ int h2[kB2], h3[kB3];
+    const int u = kvc_bid_y();
+    const int j = kvc_bid_x();
+    const int tid = kvc_tid();
+    const int lane = tid & (kWave - 1);
+    const int wid = tid >> 6;
+    if (a.mask && !ld_uniform(a.mask, u)) return;
+    const UnitShape us = unit_shape(a.seq_lens, u / a.H, a.s_max, unit_budget(a, u), a.n_keep);
+    int32_t *out = a.idx + (size_t)u * a.cap;
+    if (j == 0) {
+        // the always-kept trailing tokens, the -1 padding and the count
+        const int nw = us.S - us.C;
+        for (int i = tid; i < nw; i += kThreads) out[us.k_eff + i] = us.C + i;
+        for (int i = us.k_eff + nw + tid; i < a.cap; i += kThreads) out[i] = -1;
+        if (tid == 0) a.count[u] = us.k_eff + nw;
+    }
+    const int t0 = j * kChunk;
+    if (us.k_eff == 0 || t0 >= us.C) return;
+    const int t1 = min(us.C, t0 + kChunk);
+    if (us.k_eff == us.C) {
+        for (int t = t0 + tid; t < t1; t += kThreads) out[t] = t;
+        return;
+    }
+    const int n_wg = (us.C + kChunk - 1) / kChunk;   // work-groups of this unit that get here
+
+    // ---- every work-group: d1, then the chunk's candidates in index order.  Wave w
+    // owns the contiguous quarter [w0, w0 + kChunk/4) of the chunk; lane l holds keys
+    // w0 + l + 64 q
+    const int w0 = t0 + wid * (kChunk / kWaves);
+    const float *sc = a.scores + (size_t)u * a.s_max;
+    int32_t *H = a.hist + (size_t)u * kHistInts;
+    int c1[kB1 / kThreads];
+    load_bins<kB1>(H, c1);
+    uint32_t key[KPT];
+    {
+        float v[KPT];
+#pragma unroll
+        for (int q = 0; q < KPT; ++q) {
+            const int t = w0 + lane + q * kWave;
+            v[q] = t < t1 ? sc[t] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < KPT; ++q) key[q] = order_key(v[q]);
+    }
+    const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
+    const uint32_t lo = (uint32_t)d1.digit << 21;         // candidates: key >= lo
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) cnt += w0 + lane + q * kWave < t1 && key[q] >= lo;
+    cnt = wave_inclusive_scan(cnt);
+    if (lane == kWave - 1) wave_n[wid] = cnt;
+    __syncthreads();
+    int pos = 0, n_c = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        pos += w < wid ? wave_n[w] : 0;
+        n_c += wave_n[w];
+    }
+    unsigned long long *list = a.cand + ((size_t)u * a.n_chunks + j) * kChunk;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+        const int t = w0 + lane + q * kWave;
+        const bool ok = t < t1 && key[q] >= lo;
+        const unsigned long long m = __ballot(ok);
+        if (ok) st_dev(list + pos + __popcll(m & below), ((unsigned long long)(uint32_t)t << 32) | key[q]);
+        pos += __popcll(m);
+    }
+    if (tid == 0) st_dev(a.cand_n + (size_t)u * a.n_chunks + j, n_c);
+    // count this chunk's arrival once its list has landed
+    stores_done();
+    __syncthreads();
+    if (tid == 0) sh_last = atomicAdd(&a.done[u], 1) == n_wg - 1;
+    __syncthreads();
+    if (!sh_last) return;
+
+    // ---- the unit's last work-group.  Every chunk has read H1 and published its list:
+    // H1 and the counter go back to zero for the next call
+    for (int i = tid; i < kB1 / 4; i += kThreads) reinterpret_cast<int4 *>(H)[i] = make_int4(0, 0, 0, 0);
+    if (tid == 0) a.done[u] = 0;
+    for (int i = tid; i < kB2; i += kThreads) h2[i] = 0;
+    for (int i = tid; i < kB3; i += kThreads) h3[i] = 0;
+    int total;
+    const int nc_t = tid < n_wg ? ld_dev(a.cand_n + (size_t)u * a.n_chunks + tid) : 0;
+    const int off_t = block_exclusive_scan(nc_t, scan, &total);
+    if (tid < n_wg) offs[tid] = off_t;
+    if (tid == 0) offs[n_wg < kThreads ? n_wg : kThreads] = total;
+    const bool in_lds = n_wg <= kThreads && total <= kCandLds;
+    __syncthreads();
+    int ties = 0;
+    uint32_t T = 0;
+    if (in_lds) {
+        // the lists, chunk after chunk: index order.  c_chunk[e]: the chunk of candidate e
+        for (int c = 0; c < n_wg; ++c)
+            for (int e = offs[c] + tid; e < offs[c + 1]; e += kThreads) c_chunk[e] = (uint16_t)c;
+        __syncthreads();
+        unsigned long long v[kCandPer];
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+            const int e = tid + q * kThreads;
+            v[q] = 0ull;
+            if (e < total) {
+                const int c = c_chunk[e];
+                v[q] = ld_dev(a.cand + ((size_t)u * a.n_chunks + c) * kChunk + (e - offs[c]));
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+            const int e = tid + q * kThreads;
+            if (e < total) {
+                c_key[e] = (uint32_t)v[q];
+                c_idx[e] = (int32_t)(v[q] >> 32);
+            }
+        }
+        __syncthreads();
+        // thread i takes the consecutive candidates [e0, e1): equal keys come in runs
+        const int per = (total + kThreads - 1) / kThreads;
+        const int e0 = min(tid * per, total), e1 = min(e0 + per, total);
+        auto runs = [&](int *h, auto bin_of) {
+            int cur = -1, rn = 0;
+            for (int e = e0; e < e1; ++e) {
+                const int b = bin_of(c_key[e]);
+                if (b != cur) {
+                    if (rn) atomicAdd(&h[cur], rn);
+                    cur = b;
+                    rn = 0;
+                }
+                rn += b >= 0;
+            }
+            if (rn) atomicAdd(&h[cur], rn);
+        };
+        runs(h2, [&](uint32_t k) { return (int)(k >> 21) == d1.digit ? (int)((k >> 10) & (kB2 - 1)) : -1; });
+        __syncthreads();
+        const Digit d2 = unit_digit<kB2, 1, kThreads>(h2, us.k_eff - d1.above, scan, &dg);
+        const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
+        runs(h3, [&](uint32_t k) { return (k >> 10) == pre2 ? (int)(k & (kB3 - 1)) : -1; });
+        __syncthreads();
+        const Digit d3 = unit_digit<kB3, 1, kThreads>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
+        T = (pre2 << 10) | (uint32_t)d3.digit;
+        ties = us.k_eff - d1.above - d2.above - d3.above;
+        // ordered write: the thread's selected indices to registers, then to LDS in
+        // output order (over the candidates' indices, free by then), then out
+        int gt = 0, eq = 0;
+        for (int e = e0; e < e1; ++e) {
+            gt += c_key[e] > T;
+            eq += c_key[e] == T;
+        }
+        const int2 before = block_exclusive_scan2(gt, eq, scan);
+        int p = before.x + min(ties, before.y);
+        int eq_seen = before.y;
+        int sel[kCandPer];
+        int n_sel = 0;
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+            const int e = e0 + q;
+            sel[q] = -1;
+            if (e < e1) {
+                const uint32_t k = c_key[e];
+                bool take = k > T;
+                if (k == T) take = eq_seen++ < ties;
+                if (take) sel[q] = c_idx[e];
+                n_sel += take;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+            if (sel[q] >= 0) {
+                if (p < us.k_eff) c_idx[p] = sel[q];                  // never past the budget
+                ++p;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < us.k_eff; i += kThreads) out[i] = c_idx[i];
+        return;
+    }
+
+    // ---- more candidates than LDS holds: levels 2 and 3 and the write from the scores
+    stream_keys(sc, us.C, [&](uint32_t k) {
+        if ((int)(k >> 21) == d1.digit) hist_add(h2, h2, (int)((k >> 10) & (kB2 - 1)));
+    });
+    __syncthreads();
+    const Digit d2 = unit_digit<kB2, 1, kThreads>(h2, us.k_eff - d1.above, scan, &dg);
+    const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
+    stream_keys(sc, us.C, [&](uint32_t k) {
+        if ((k >> 10) == pre2) hist_add(h3, h3, (int)(k & (kB3 - 1)));
+    });
+    __syncthreads();
+    const Digit d3 = unit_digit<kB3, 1, kThreads>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
+    T = (pre2 << 10) | (uint32_t)d3.digit;
+    ties = us.k_eff - d1.above - d2.above - d3.above;
+    // wave w owns the candidates [w R, w R + R), R a multiple of 64
+    const int R = ((us.C + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
+    const int r0 = min(wid * R, us.C), r1 = min(r0 + R, us.C);
+    int gt = 0, eq = 0;
+    walk_keys(sc, r0, r1, [&](int t, uint32_t k) {
+        gt += t >= 0 && k > T;
+        eq += t >= 0 && k == T;
+    });
+    gt = wave_inclusive_scan(gt);
+    eq = wave_inclusive_scan(eq);
+    if (lane == kWave - 1) {
+        wave_n[wid] = gt;
+        wave_eq[wid] = eq;
+    }
+    __syncthreads();
+    int p = 0, eq_seen = 0;
+    for (int w = 0; w < wid; ++w) {
+        int take = ties - eq_seen;
+        take = take < 0 ? 0 : (take > wave_eq[w] ? wave_eq[w] : take);
+        p += wave_n[w] + take;
+        eq_seen += wave_eq[w];
+    }
+    walk_keys(sc, r0, r1, [&](int t, uint32_t k) {
+        const bool is_gt = t >= 0 && k > T;
+        const bool is_eq = t >= 0 && k == T;
+        const unsigned long long m_eq = __ballot(is_eq);
+        const int rank = eq_seen + __popcll(m_eq & below);
+        const bool take = is_gt || (is_eq && rank < ties);
+        const unsigned long long m_sel = __ballot(take);
+        const int q = p + __popcll(m_sel & below);
+        if (take && q < us.k_eff) out[q] = t;                    // never past the budget
+        p += __popcll(m_sel);
+        eq_seen += __popcll(m_eq);
+    });
+}
+
 // TSP score: the sum over KV heads (one selection per sequence), added in double and
 // rounded to float once, so the selection key is the exact sum correctly rounded.
 __global__ __launch_bounds__(256) void head_sum_kernel(const float *__restrict__ scores, int n_kv, int s_max,
@@ -732,7 +1032,7 @@ __global__ __launch_bounds__(256) void core_budget_kernel(const int32_t *__restr
 struct SelLayout {
     int kpt;                  // keys per thread of the chunked kernels
     int n_chunks;
-    size_t sum_off, hist_off, done_off, above_off, sfx_off, bytes;
+    size_t sum_off, hist_off, done_off, above_off, sfx_off, cand_off, cand_n_off, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -761,6 +1061,10 @@ SelLayout sel_layout(int batch, int n_kv, int s_max, int n_keep, bool shared)
     off += align256((size_t)units * L.n_chunks * sizeof(int32_t));
     L.sfx_off = off;
     off += align256((size_t)units * L.n_chunks * kSfx * sizeof(int32_t));
+    L.cand_off = off;                         // candidate lists: the large-chunk path only
+    if (L.kpt == kKptLarge) off += align256((size_t)units * L.n_chunks * chunk * sizeof(unsigned long long));
+    L.cand_n_off = off;
+    off += align256((size_t)units * L.n_chunks * sizeof(int32_t));
     L.bytes = off;
     return L;
 }
@@ -853,6 +1157,8 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
     a.done = (int32_t *)(w + L.done_off);
     a.above12 = (int32_t *)(w + L.above_off);
     a.sfx3 = (int32_t *)(w + L.sfx_off);
+    a.cand = (unsigned long long *)(w + L.cand_off);
+    a.cand_n = (int32_t *)(w + L.cand_n_off);
     a.idx = idx;
     a.count = count;
     a.mask = shared ? nullptr : unit_mask;
@@ -880,11 +1186,14 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
     }
     const dim3 grid(L.n_chunks, units);
     if (L.kpt == kKptLarge) {
+        // few large chunks per unit: level 1, then the candidate lists and their last
+        // work-group (one launch for levels 2, 3 and the write)
         hipLaunchKernelGGL(sel_level1_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
-        hipLaunchKernelGGL(sel_level2_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
-        hipLaunchKernelGGL(sel_level3_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
-        hipLaunchKernelGGL(sel_write_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_cand_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
     } else {
+        // many small chunks per unit: the last work-group's gather and levels would
+        // outlast three chunked kernels (measured), so levels 2 and 3 and the write
+        // stay spread over the chunks
         hipLaunchKernelGGL(sel_level1_kernel<kKptSmall>, grid, dim3(kThreads), 0, stream, a);
         hipLaunchKernelGGL(sel_level2_kernel<kKptSmall>, grid, dim3(kThreads), 0, stream, a);
         hipLaunchKernelGGL(sel_level3_kernel<kKptSmall>, grid, dim3(kThreads), 0, stream, a);
