@@ -775,13 +775,29 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
     }
     unsigned long long *list = a.cand + ((size_t)u * a.n_chunks + j) * kChunk;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // the list goes through LDS (free until the last work-group needs it) when it fits,
+    // and out in coalesced stores
+    const bool staged = n_c <= kCandLds;
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
         const int t = w0 + lane + q * kWave;
         const bool ok = t < t1 && key[q] >= lo;
         const unsigned long long m = __ballot(ok);
-        if (ok) st_dev(list + pos + __popcll(m & below), ((unsigned long long)(uint32_t)t << 32) | key[q]);
+        const int e = pos + __popcll(m & below);
+        if (ok) {
+            if (staged) {
+                c_key[e] = key[q];
+                c_idx[e] = t;
+            } else {
+                st_dev(list + e, ((unsigned long long)(uint32_t)t << 32) | key[q]);
+            }
+        }
         pos += __popcll(m);
+    }
+    if (staged) {
+        __syncthreads();
+        for (int e = tid; e < n_c; e += kThreads)
+            st_dev(list + e, ((unsigned long long)(uint32_t)c_idx[e] << 32) | c_key[e]);
     }
     if (tid == 0) st_dev(a.cand_n + (size_t)u * a.n_chunks + j, n_c);
     // count this chunk's arrival once its list has landed
@@ -830,27 +846,22 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
             }
         }
         __syncthreads();
-        // thread i takes the consecutive candidates [e0, e1): equal keys come in runs
+        // thread i takes the consecutive candidates [e0, e1), to registers: equal keys
+        // come in runs
         const int per = (total + kThreads - 1) / kThreads;
         const int e0 = min(tid * per, total), e1 = min(e0 + per, total);
-        auto runs = [&](int *h, auto bin_of) {
-            int cur = -1, rn = 0;
-            for (int e = e0; e < e1; ++e) {
-                const int b = bin_of(c_key[e]);
-                if (b != cur) {
-                    if (rn) atomicAdd(&h[cur], rn);
-                    cur = b;
-                    rn = 0;
-                }
-                rn += b >= 0;
-            }
-            if (rn) atomicAdd(&h[cur], rn);
-        };
-        runs(h2, [&](uint32_t k) { return (int)(k >> 21) == d1.digit ? (int)((k >> 10) & (kB2 - 1)) : -1; });
+        uint32_t ck[kCandPer];
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) ck[q] = e0 + q < e1 ? c_key[e0 + q] : 0u;
+        run_hist<kCandPer>(h2, [&](int q) {
+            return e0 + q < e1 && (int)(ck[q] >> 21) == d1.digit ? (int)((ck[q] >> 10) & (kB2 - 1)) : -1;
+        });
         __syncthreads();
         const Digit d2 = unit_digit<kB2, 1, kThreads>(h2, us.k_eff - d1.above, scan, &dg);
         const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
-        runs(h3, [&](uint32_t k) { return (k >> 10) == pre2 ? (int)(k & (kB3 - 1)) : -1; });
+        run_hist<kCandPer>(h3, [&](int q) {
+            return e0 + q < e1 && (ck[q] >> 10) == pre2 ? (int)(ck[q] & (kB3 - 1)) : -1;
+        });
         __syncthreads();
         const Digit d3 = unit_digit<kB3, 1, kThreads>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
         T = (pre2 << 10) | (uint32_t)d3.digit;
@@ -858,9 +869,10 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
         // ordered write: the thread's selected indices to registers, then to LDS in
         // output order (over the candidates' indices, free by then), then out
         int gt = 0, eq = 0;
-        for (int e = e0; e < e1; ++e) {
-            gt += c_key[e] > T;
-            eq += c_key[e] == T;
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+            gt += e0 + q < e1 && ck[q] > T;
+            eq += e0 + q < e1 && ck[q] == T;
         }
         const int2 before = block_exclusive_scan2(gt, eq, scan);
         int p = before.x + min(ties, before.y);
@@ -872,7 +884,7 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
             const int e = e0 + q;
             sel[q] = -1;
             if (e < e1) {
-                const uint32_t k = c_key[e];
+                const uint32_t k = ck[q];
                 bool take = k > T;
                 if (k == T) take = eq_seen++ < ties;
                 if (take) sel[q] = c_idx[e];
