@@ -122,12 +122,14 @@ def seed_for(cfg_id: int, layer: int, stream: int, step: int = 0) -> int:
 
 
 def seq_lens(wl: Workload, s_max: int | None = None) -> np.ndarray:
+    """Per-sequence lengths: s_max each, or for a ragged workload its seeded lengths,
+    none above s_max (a smaller s_max cuts the longer sequences at s_max)."""
     s_max = wl.s_max if s_max is None else s_max
     if wl.ragged is None:
         return np.full(wl.batch, s_max, np.int32)
     lo, hi = wl.ragged
     rng = np.random.Generator(np.random.PCG64([wl.cfg_id, 0x6C656E73]))
-    return rng.integers(lo, hi + 1, size=wl.batch).astype(np.int32)
+    return np.minimum(rng.integers(lo, hi + 1, size=wl.batch), s_max).astype(np.int32)
 
 
 def planted_positions(wl: Workload, b: int, s_b: int, n_keep: int | None = None) -> np.ndarray:
