@@ -335,6 +335,8 @@ struct MfArgs {
     int s_max, n_h, n_kv, w, wic, R, unit0, n_chunks, chunk_tokens;
     float c;                 // scale * log2(e)
     int n_parts;             // row partials per unit: one per chunk, or per 256-token block (RT = 1)
+    int compact_batch;       // one row block, ragged lengths: B, the work-groups of the valid (KV head,
+                             // chunk) pairs first (see mfma_stats_kernel); 0: one work-group per pair
     float2 *part;            // pass 1 out: [group][n_parts][RT*16] (m, l)
     float2 *fin;             // merged row statistics, pass 2 in: [group][RT*16] (-M*c, 1/L)
     int32_t *arrive;         // [group] chunk arrival counters (zero between calls) when the last
@@ -548,6 +550,15 @@ __device__ __forceinline__ void stats_stage(const unsigned char *buf, int st0, i
 // slice + slices, ... online (rescale factors in fp32, sums in double), and the slices
 // are then folded in slice order.  The partials may have been published with st_dev by
 // the work-groups of other XCDs, hence ld_dev.  buf: 3 KB of LDS.
+// Chunks of a unit with S tokens that pass 1 visits: every chunk, or with compact_batch
+// only those holding tokens (at least one, so a unit with no token still publishes).
+__device__ __forceinline__ int chunks_of(const MfArgs &a, int S)
+{
+    if (!a.compact_batch) return a.n_chunks;
+    const int n = (S + a.chunk_tokens - 1) / a.chunk_tokens;
+    return n < 1 ? 1 : n;
+}
+
 template <int RPAD>
 __device__ __forceinline__ void merge_chunks(const MfArgs &a, int ul, unsigned char *buf)
 {
@@ -558,19 +569,25 @@ __device__ __forceinline__ void merge_chunks(const MfArgs &a, int ul, unsigned c
     const int row = kvc_tid() % RPAD;
     const int slice = kvc_tid() / RPAD;
     const unsigned long long *p = (const unsigned long long *)(a.part + (size_t)ul * a.n_parts * RPAD) + row;
+    // the partials written by this call: those of the chunks pass 1 visited
+    int n_parts = a.n_parts;
+    if (a.compact_batch) {
+        const int S = clamp_len(a.seq_lens, (a.unit0 + ul) / a.n_kv, a.s_max);
+        n_parts = min(n_parts, chunks_of(a, S) * (RPAD == 16 ? a.chunk_tokens / kStatBlock : 1));
+    }
     float Mx = -INFINITY;
     double L = 0.0;
     constexpr int kBatch = 8;               // partials requested together per thread
-    for (int ch0 = slice; ch0 < a.n_parts; ch0 += kBatch * slices) {
+    for (int ch0 = slice; ch0 < n_parts; ch0 += kBatch * slices) {
         unsigned long long v[kBatch];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-            const int ch = min(ch0 + q * slices, a.n_parts - 1);    // unconditional: one round trip
+            const int ch = min(ch0 + q * slices, n_parts - 1);    // unconditional: one round trip
             v[q] = ld_dev(p + (size_t)ch * RPAD);
         }
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
-            if (ch0 + q * slices >= a.n_parts) continue;
+            if (ch0 + q * slices >= n_parts) continue;
             const float vm = unpack_lo(v[q]), vl = unpack_hi(v[q]);
             if (vm == -INFINITY) continue;
             if (vm > Mx) {
@@ -620,8 +637,28 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     static_assert(!kBlocks || (kStatBlock % C::ST == 0 && C::CPW == 1), "a block is whole stages");
     __shared__ float sm_bm[kBlocks ? kMaxBlk : 1][C::TG][16], sm_bl[kBlocks ? kMaxBlk : 1][C::TG][16];
 
-    const int chunk = kvc_bid_x();
-    const int ul = kvc_bid_y();
+    int chunk = kvc_bid_x();
+    int ul = kvc_bid_y();
+    if (RT == 1 && a.compact_batch) {
+        // ragged lengths: work-group L of the grid takes the L-th (KV head, chunk) pair
+        // holding tokens, KV heads in order, and the ones past the last pair exit; the
+        // work that exists then fills the first work-groups, which the dispatcher spreads
+        // evenly over the CUs (a pair per work-group in grid order left whole CUs with
+        // four long chunks and others with four empty ones)
+        int L = (int)kvc_bid_y() * a.n_chunks + (int)kvc_bid_x();
+        bool found = false;
+        for (int bb = 0; bb < a.compact_batch; ++bb) {
+            const int nch = chunks_of(a, clamp_len(a.seq_lens, bb, a.s_max));
+            if (L < nch * a.n_kv) {
+                ul = bb * a.n_kv + L / nch;
+                chunk = L % nch;
+                found = true;
+                break;
+            }
+            L -= nch * a.n_kv;
+        }
+        if (!found) return;
+    }
     const int u = a.unit0 + ul;
     if (a.mask && !ld_uniform(a.mask, u)) return;
     const int b = u / a.n_kv;
@@ -767,7 +804,7 @@ __global__ __launch_bounds__(kMfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     __syncthreads();
     if (kvc_tid() == 0) {
         const int old = __hip_atomic_fetch_add(a.arrive + ul, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = old == a.n_chunks - 1;
+        sm_last = old == chunks_of(a, S) - 1;
         if (sm_last) __hip_atomic_store(a.arrive + ul, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
@@ -1809,6 +1846,10 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         a.n_chunks = plan.n_chunks;
         a.chunk_tokens = plan.chunk_tokens;
         a.n_parts = plan.n_parts;
+        // ragged lengths with one row block: the valid chunks first (units in one group).
+        // Not for a masked call, whose work-groups mostly exit at their first load: the
+        // mapping's walk over the lengths would delay every one of them
+        a.compact_batch = rt == 1 && seq_lens && !unit_mask && batch <= 64 && plan.group_units == units ? batch : 0;
         a.c = scale * kLog2e;
         const size_t fin_off = align256((size_t)plan.group_units * plan.n_parts * rpad * sizeof(float2));
         a.part = (float2 *)ws;
