@@ -160,8 +160,10 @@ const char *kvc_status_str(kvc_status status);
  * ws         at least kvc_score_window_workspace(dims, w, flags) bytes, 16-byte
  *            aligned, zero-filled before first use: per-item row statistics, per-KV-head
  *            arrival counters and, for the single-pass kernel, a deferred-item count
- *            (returned to zero by each call that completes); calls with the same
- *            batch and n_kv may share one workspace without zero-filling it again
+ *            (returned to zero by each call that completes) and a call tag (advanced
+ *            by each call; the final row statistics carry it); calls with the same
+ *            dims (seq_lens and unit_mask aside), w and flags may share one workspace
+ *            without zero-filling it again
  * Arithmetic: fp32 logits (bf16 products are exact), fp32 exp2-based softmax with
  * the row sums accumulated per lane and merged in double; raw agrees with a
  * double-precision evaluation to about 1e-6 relative.  Probabilities below the

@@ -245,9 +245,12 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const float *__restr
                                                             const int32_t *__restrict__ mask,
                                                             float *__restrict__ pooled, int32_t *reset, int n_reset)
 {
-    // the single-pass kernels' counters go back to zero here, after their last use
-    if (reset && kvc_bid_x() == 0 && kvc_bid_y() == 0)
+    // the single-pass kernels' counters go back to zero here, after their last use, and
+    // the tag word that follows them advances to this call's tag
+    if (reset && kvc_bid_x() == 0 && kvc_bid_y() == 0) {
         for (int i = kvc_tid(); i < n_reset; i += kPoolThreads) reset[i] = 0;
+        if (kvc_tid() == 0) reset[n_reset] += 1;
+    }
     __shared__ __attribute__((aligned(16))) float tile[kPoolLds];
     if constexpr (HALF >= 0) half = HALF;
     const int u = kvc_bid_y();
@@ -1094,9 +1097,13 @@ void launch_logit_pool(dim3 grid, const MfArgs &a, hipStream_t stream)
 // deadlock while all of it is resident.  A wait that does not end within a bounded
 // time (a work-group not resident, for instance) puts the item on a deferred list; a
 // follow-up kernel recomputes those items from K once every record is written.
-// Records and arrival counters are written and read with device-scope atomics
-// (coherent across the XCDs' L2 caches); a writer waits for its record stores to
-// complete before the arrival that announces them.
+// Records, final statistics and arrival counters are written and read with
+// device-scope atomics (coherent across the XCDs' L2 caches); a writer waits for its
+// record stores to complete before the arrival that announces them.  Every final
+// statistic word carries the call's tag (one more than a word of the workspace that
+// the pooling kernel advances after each call), so a waiting work-group polls the
+// final statistics themselves: the merging work-group neither waits for their stores
+// nor raises a separate flag, and the waiter needs no second load.
 // ====================================================================================
 constexpr int kSpThreads = 256;
 constexpr int kSpWaves = kSpThreads / kWave;
@@ -1117,11 +1124,18 @@ struct SpArgs {
     float *raw;               // [units][s_max]
     int32_t *arrive;          // [units] items that published their record (zero between calls)
     int32_t *defer_n;         // deferred items (zero between calls)
-    int32_t *gen;             // [units] bumped once per call when the unit's statistics are final
+    const int32_t *tag;       // the previous call's tag (advanced by the pooling kernel)
     int32_t *defer;           // [n_items]
     unsigned long long *rec;  // [units][n_chunks][16 RT] packed (m, l) per item and row
-    unsigned long long *fin;  // [units][16 RT] packed final (-M c, 1/L)
+    unsigned long long *fin;  // [units][16 RT][2] tagged final -M c, 1/L
 };
+
+// A record word: the value's bits low, the call's tag high.
+__device__ __forceinline__ unsigned long long tagged(float v, uint32_t tag)
+{
+    return (unsigned long long)__float_as_uint(v) | ((unsigned long long)tag << 32);
+}
+__device__ __forceinline__ uint32_t tag_of(unsigned long long w) { return (uint32_t)(w >> 32); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float v)
@@ -1228,26 +1242,24 @@ struct Sp {
         for (int v = 0; v < QV; ++v) {
             const int i = (int)kvc_tid() + v * kSpThreads;
             const int row = i / VPR, col = i - row * VPR;
-            if (i < ROWS * VPR) *(u32x4 *)(q_lds + row * QROWB + col * 16) = qr[v];
+            if ((ROWS * VPR) % kSpThreads == 0 || i < ROWS * VPR) *(u32x4 *)(q_lds + row * QROWB + col * 16) = qr[v];
         }
     }
 
-    // Last visible token of each of this lane's rows (cb*16 + 4 kg + jj); -1 for rows >= R.
-    __device__ static void last_of(const SpArgs &a, const SpItem &it, int kg, int (*last)[4])
-    {
-#pragma unroll
-        for (int cb = 0; cb < RT; ++cb)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = cb * 16 + 4 * kg + jj;
-                last[cb][jj] = r >= a.R ? -1 : (a.wic ? min(it.S - a.w + r % a.w, it.S - 1) : it.S - 1);
-            }
-    }
+    // Which (row, token) pairs are visible: row r < R sees token t when t <= last(r)
+    // (the causal window mask); every row r < R sees every token t <= lo.
+    struct Vis {
+        int R, S, w, wic, lo;
+        __device__ Vis(const SpArgs &a, const SpItem &it)
+            : R(a.R), S(it.S), w(a.w), wic(a.wic), lo(a.wic ? it.S - a.w : it.S - 1) {}
+        __device__ int last(int r) const { return r >= R ? -1 : (wic ? min(S - w + r % w, S - 1) : S - 1); }
+    };
 
     // Logits of one tile from its LDS slot: lane (kg, n) holds token t = tb + n for rows
-    // cb*16 + 4 kg + jj; invisible (row, token) pairs are -inf.
+    // cb*16 + 4 kg + jj; invisible (row, token) pairs are -inf.  Tiles wholly at or before
+    // vis.lo mask only rows >= R; the others (the window's tail) evaluate the mask per row.
     __device__ static void tile_logits(const unsigned char *slot, const unsigned char *q_lds, int tb, int n, int kg,
-                                       const int (*last)[4], float (*lg)[4])
+                                       const Vis &vis, float (*lg)[4])
     {
         u32x4 kb[KS];
 #pragma unroll
@@ -1262,8 +1274,13 @@ struct Sp {
                 const u32x4 qv = *(const u32x4 *)(q_lds + (cb * 16 + n) * QROWB + (4 * s + kg) * 16);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qv), as_bf16x8(kb[s]), acc, 0, 0, 0);
             }
+            if (tb + 15 <= vis.lo) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) lg[cb][jj] = t <= last[cb][jj] ? acc[jj] : -INFINITY;
+                for (int jj = 0; jj < 4; ++jj) lg[cb][jj] = cb * 16 + 4 * kg + jj < vis.R ? acc[jj] : -INFINITY;
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) lg[cb][jj] = t <= vis.last(cb * 16 + 4 * kg + jj) ? acc[jj] : -INFINITY;
+            }
         }
     }
 
@@ -1364,19 +1381,19 @@ __device__ __forceinline__ void sp_merge(const SpArgs &a, int u, int n_u, bool d
 // returned, its slot is refilled with tile P + 4.
 template <int D, int RT, int P>
 __device__ __forceinline__ void sp_tiles(__amdgpu_buffer_rsrc_t rs, unsigned char *const *slot,
-                                         const unsigned char *q_lds, int tw, int n, int kg, const int (*last)[4],
-                                         float (*lg)[RT][4])
+                                         const unsigned char *q_lds, int tw, int n, int kg,
+                                         const typename Sp<D, RT>::Vis &vis, float (*lg)[RT][4])
 {
     if constexpr (P < kSpTiles) {
         using S = Sp<D, RT>;
         constexpr int later = (P + kSpRing < kSpTiles ? P + kSpRing : kSpTiles) - (P + 1);
         vm_wait<S::KS * later>();
-        S::tile_logits(slot[P % kSpRing], q_lds, tw + 16 * P, n, kg, last, lg[P]);
+        S::tile_logits(slot[P % kSpRing], q_lds, tw + 16 * P, n, kg, vis, lg[P]);
         if constexpr (P + kSpRing < kSpTiles) {
             lds_reads_done();
             S::load_tile(rs, tw + 16 * (P + kSpRing), n, kg, slot[P % kSpRing]);
         }
-        sp_tiles<D, RT, P + 1>(rs, slot, q_lds, tw, n, kg, last, lg);
+        sp_tiles<D, RT, P + 1>(rs, slot, q_lds, tw, n, kg, vis, lg);
     }
 }
 
@@ -1409,7 +1426,8 @@ __global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     u32x4 qr[P::QV];
     SpItem prev;
     prev.active = false;
-    int prev_g0 = 0;          // thread 0: the generation the previous item waits past
+    // this call's tag: the pooling kernel advances the word after every call
+    const uint32_t tag = (uint32_t)ld_uniform(a.tag, 0) + 1u;
 
     // an item's query rows (to registers) and first ring of K tiles, issued ahead of it;
     // issued for every item (an inactive one reads unit 0's queries and no K: an empty
@@ -1437,33 +1455,36 @@ __global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
         // ---- B: the previous item, once its unit's statistics are final
         if (prev.active) {
-            if (tid == 0) {
-                // wait at most a.spin ticks of the 100 MHz real-time counter
+            if (wv == 0) {
+                // lane l < 2 ROWS polls word l of the unit's final statistics until every
+                // word carries this call's tag, for at most a.spin ticks of the 100 MHz
+                // real-time counter
+                const bool mine = lane < 2 * ROWS;
+                const unsigned long long *fp = a.fin + (size_t)prev.u * ROWS * 2 + (mine ? lane : 0);
+                unsigned long long f = 0;
                 int ok = 0;
-                const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + (uint64_t)a.spin;
-                for (bool first = true; first || __builtin_amdgcn_s_memrealtime() < t_end; first = false) {
-                    if (a.spin &&
-                        __hip_atomic_load(a.gen + prev.u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != prev_g0) {
-                        ok = 1;
-                        break;
+                if (a.spin) {
+                    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + (uint64_t)a.spin;
+                    for (;;) {
+                        f = ld_dev(fp);
+                        if (__builtin_amdgcn_ballot_w64(mine && tag_of(f) != tag) == 0) {
+                            ok = 1;
+                            break;
+                        }
+                        if (__builtin_amdgcn_s_memrealtime() >= t_end) break;
+                        __builtin_amdgcn_s_sleep(1);
                     }
-                    __builtin_amdgcn_s_sleep(1);
                 }
-                if (!ok) {
+                if (ok) {
+                    if (mine) reinterpret_cast<float *>(sh_fin)[lane] = __uint_as_float((uint32_t)f);
+                } else if (lane == 0) {
                     const int slot_i = __hip_atomic_fetch_add(a.defer_n, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     a.defer[slot_i] = (int)(prev.u * a.n_chunks + prev.ch);
                 }
-                sh_int[0] = ok;
+                if (lane == 0) sh_int[0] = ok;
             }
             lds_barrier();
-            if (sh_int[0]) {
-                if (tid < ROWS) {
-                    const unsigned long long f = ld_dev(a.fin + (size_t)prev.u * ROWS + tid);
-                    sh_fin[tid] = make_float2(unpack_lo(f), unpack_hi(f));
-                }
-                lds_barrier();
-                P::finish(a, prev, lg, sh_fin, wv, n, kg);
-            }
+            if (sh_int[0]) P::finish(a, prev, lg, sh_fin, wv, n, kg);
         }
         if (!have) break;
         if (it.zero) {
@@ -1486,11 +1507,10 @@ __global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         lds_barrier();                   // no wave still reads the previous item's queries
         P::store_q(qr, q_lds);
         lds_barrier();
-        int last[RT][4];
-        P::last_of(a, it, kg, last);
         {
+            const typename P::Vis vis(a, it);
             const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.k + (size_t)it.u * a.s_max * D, it.S * (2 * D));
-            sp_tiles<D, RT, 0>(rs, slot, q_lds, P::wave_t0(it, wv), n, kg, last, lg);
+            sp_tiles<D, RT, 0>(rs, slot, q_lds, P::wave_t0(it, wv), n, kg, vis, lg);
         }
 #pragma unroll
         for (int cb = 0; cb < RT; ++cb)
@@ -1530,33 +1550,24 @@ __global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             float l = 0.f;
             for (int x = 0; x < kSpWaves; ++x) l += sm_l[x][tid];
             st_dev(a.rec + ((size_t)it.u * a.n_chunks + it.ch) * ROWS + tid, pack2(m, l));
-            stores_done();               // nothing else is in flight here
+            stores_done();               // the record lands before the arrival announces it
         }
         lds_barrier();
         const int n_u = (it.S + kSpItem - 1) / kSpItem;
-        int g0 = 0, old = 0;
-        if (tid == 0) {
-            // the generation before this item arrives (only the unit's last arrival bumps it)
-            g0 = __hip_atomic_load(a.gen + it.u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            old = __hip_atomic_fetch_add(a.arrive + it.u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        int old = 0;
+        if (tid == 0) old = __hip_atomic_fetch_add(a.arrive + it.u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // the next item's queries and first K tiles fly from here on, across the previous
         // item's wait and finish
         prefetch(nx);
-        if (tid == 0) {
-            prev_g0 = g0;
-            sh_int[1] = old == n_u - 1;
-        }
+        if (tid == 0) sh_int[1] = old == n_u - 1;
         lds_barrier();
         if (sh_int[1]) {
-            // the unit's last item: merge the records, publish the final statistics
+            // the unit's last item: merge the records, publish the tagged final statistics
             sp_merge<ROWS>(a, it.u, n_u, true, mg_m, mg_l, sh_fin);
-            if (tid < ROWS) {
-                st_dev(a.fin + (size_t)it.u * ROWS + tid, pack2(sh_fin[tid].x, sh_fin[tid].y));
-                stores_done();
+            if (tid < 2 * ROWS) {
+                const float2 f = sh_fin[tid >> 1];
+                st_dev(a.fin + ((size_t)it.u * ROWS + (tid >> 1)) * 2 + (tid & 1), tagged((tid & 1) ? f.y : f.x, tag));
             }
-            __syncthreads();
-            if (tid == 0) __hip_atomic_fetch_add(a.gen + it.u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         it = nx;
     }
@@ -1590,14 +1601,13 @@ __global__ __launch_bounds__(kSpThreads) void mfma_single_fixup_kernel(SpArgs a)
         P::fetch_q(a, it, qr);
         P::store_q(qr, q_lds);
         sp_merge<ROWS>(a, it.u, (it.S + kSpItem - 1) / kSpItem, false, mg_m, mg_l, sh_fin);   // orders q_lds too
-        int last[RT][4];
-        P::last_of(a, it, kg, last);
+        const typename P::Vis vis(a, it);
 #pragma unroll
         for (int p = 0; p < kSpTiles; ++p) {
             lds_reads_done();
             P::load_tile(rs, tw + 16 * p, n, kg, slot);
             vm_wait<0>();
-            P::tile_logits(slot, q_lds, tw + 16 * p, n, kg, last, lg[p]);
+            P::tile_logits(slot, q_lds, tw + 16 * p, n, kg, vis, lg[p]);
         }
         P::finish(a, it, lg, sh_fin, wv, n, kg);
         __syncthreads();
@@ -1648,11 +1658,12 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Workspace of the single-pass path: the words that must be zero between calls come
 // first and depend on the unit count only.
 struct SpLayout {
-    size_t arrive_off, defer_n_off, gen_off, defer_off, rec_off, fin_off, bytes;
+    size_t arrive_off, defer_n_off, tag_off, defer_off, rec_off, fin_off, bytes;
 };
 
 // The arrival counters and the deferred count (units + 1 words, zero between calls)
-// open the workspace; the generation words (any value) follow.
+// open the workspace; the tag word follows (zero before first use, advanced by the
+// pooling kernel after every call).  Final statistics are two tagged words per row.
 SpLayout sp_layout(int units, int n_chunks, int rows)
 {
     SpLayout L;
@@ -1661,14 +1672,14 @@ SpLayout sp_layout(int units, int n_chunks, int rows)
     off += (size_t)units * sizeof(int32_t);
     L.defer_n_off = off;
     off += sizeof(int32_t);
-    L.gen_off = off;
-    off = align256(off + (size_t)units * sizeof(int32_t));
+    L.tag_off = off;
+    off = align256(off + sizeof(int32_t));
     L.defer_off = off;
     off = align256(off + (size_t)units * n_chunks * sizeof(int32_t));
     L.rec_off = off;
     off = align256(off + (size_t)units * n_chunks * rows * sizeof(unsigned long long));
     L.fin_off = off;
-    off = align256(off + (size_t)units * rows * sizeof(unsigned long long));
+    off = align256(off + (size_t)units * rows * 2 * sizeof(unsigned long long));
     L.bytes = off;
     return L;
 }
@@ -1818,7 +1829,7 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
         a.raw = raw;
         a.arrive = (int32_t *)(w8 + L.arrive_off);
         a.defer_n = (int32_t *)(w8 + L.defer_n_off);
-        a.gen = (int32_t *)(w8 + L.gen_off);
+        a.tag = (const int32_t *)(w8 + L.tag_off);
         a.fin = (unsigned long long *)(w8 + L.fin_off);
         a.defer = (int32_t *)(w8 + L.defer_off);
         a.rec = (unsigned long long *)(w8 + L.rec_off);
@@ -1900,7 +1911,8 @@ hipError_t launch_score(int batch, int s_max, const int32_t *seq_lens, int n_h, 
     // the two-pass kernels of one row block pool in their second pass
     if (plan.mfma && !single_done && plan.logit_rows) return hipGetLastError();
     // after the single-pass kernels the pooling kernel zeroes their arrival counters and
-    // deferred count (laid out first in the workspace: units + 1 words)
+    // deferred count (laid out first in the workspace: units + 1 words) and advances the
+    // tag word after them
     int32_t *reset = single_done ? (int32_t *)ws_base : nullptr;
     launch_pool(raw, seq_lens, s_max, units, n_kv, n_keep, pool / 2, unit_mask, pooled, reset, units + 1, stream);
     return hipGetLastError();
