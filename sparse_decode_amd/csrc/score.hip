@@ -1074,8 +1074,8 @@ void launch_logit_pool(dim3 grid, const MfArgs &a, hipStream_t stream)
 }
 
 // ====================================================================================
-// Single-pass MFMA path for R <= 32 rows per KV head (MHA or small groups, and the
-// one-query re-scoring of batched decode): K is read once.
+// Single-pass MFMA path for 17..32 rows per KV head (MHA windows, small groups): K is
+// read once.
 //
 // An item is 1024 consecutive tokens of one unit; each of the four waves of a
 // work-group takes 256 of them (16 tiles of 16 tokens).  K reaches LDS by direct
@@ -1088,11 +1088,12 @@ void launch_logit_pool(dim3 grid, const MfArgs &a, hipStream_t stream)
 // G a multiple of the items per unit, so all items of a unit fall in one round and
 // every work-group of a round is resident at once.  For its item a work-group
 //   A  computes the logits, reduces them to the item's per-row (max, sum of exp),
-//      publishes that record and counts the unit's arrival;
-//   B  one round later, once the next item's first K tiles are in flight, waits
-//      until every item of the unit has arrived, merges the unit's records in item
-//      order into the final per-row (M, 1/L), and turns the logits still in registers
-//      into the probability sums of the item's tokens.
+//      publishes that record and counts the unit's arrival; the unit's last arrival
+//      merges the unit's records in item order into the final per-row (M, 1/L) and
+//      publishes them;
+//   B  one round later, once the next item's first K tiles are in flight, waits for
+//      the unit's final statistics and turns the logits still in registers into the
+//      probability sums of the item's tokens.
 // A never waits and B waits only for items of an earlier round, so the grid cannot
 // deadlock while all of it is resident.  A wait that does not end within a bounded
 // time (a work-group not resident, for instance) puts the item on a deferred list; a
