@@ -561,6 +561,31 @@ def test_score_single_pass_unit_mask_and_reuse():
         assert_scores_close(full_raw, rraw, "raw")
 
 
+def test_score_single_pass_rounds_ragged_reuse():
+    # two rounds of the persistent grid (30 items per KV head, 32 KV heads), a
+    # short sequence whose later items only write zeros, and one workspace reused by a
+    # call of other lengths: the second call must not take the first call's final
+    # statistics (their words carry the earlier call's tag)
+    B, n_h, n_kv, d, s_max, w = 2, 16, 16, 128, 30000, 32
+    plan = _plan(B, n_h, n_kv, d, s_max, w)
+    assert plan["single_pass"] and plan["chunks_per_unit"] == 30, plan
+    q = _randn((B, n_h, w, d), 330)
+    k = _randn((B, n_kv, s_max, d), 331)
+    rng = np.random.default_rng(33)
+    pos = torch.from_numpy(rng.choice(s_max - w, 12, replace=False)).to(DEV)
+    k[:, :, pos, :] = (3.0 * _randn((1, n_kv, 1, d), 332)).to(k.dtype)
+    dims = kvc.make_dims(B, s_max, n_h, n_kv, d, kvc.KVC_BF16)
+    ws = torch.zeros(kvc.score_window_workspace(dims, w), dtype=torch.uint8, device=DEV)
+    for sl in ([30000, 17777], [21000, 30000]):
+        sl = np.array(sl, np.int32)
+        _say("score single pass rounds", list(sl))
+        raw, pooled = kvc.score_window(q, k, w, seq_lens=sl, n_keep=w, pool=7, ws=ws)
+        torch.cuda.synchronize()
+        rraw, rpooled = oracle.score_window(host(q), host(k), w, seq_lens=sl, n_keep=w, pool=7)
+        assert_scores_close(raw, rraw, "raw")
+        assert_scores_close(pooled, rpooled, "pooled")
+
+
 @pytest.mark.parametrize("s_max", [2999, 3000])
 def test_pool_kernel_widths(s_max):
     # every compiled window (pool 1, 3, 5, 7 specialised, 9 and 63 walked), rows of a
