@@ -54,6 +54,10 @@ constexpr int kKptSmall = 8;
 constexpr int kKptLarge = 32;
 constexpr int kCoreChunk = 2048;    // tokens per work-group of the core-mask kernel
 constexpr int kCopies = 4;          // LDS histogram copies, picked by lane & 3
+// Copy c of an LDS histogram starts 8 banks after copy c - 1 (32 banks of 4 bytes), so
+// the copies of one bin lie in different banks and lanes that add to neighbouring
+// bins of different copies do not wait on one bank.
+constexpr int kCopyStride = kB1 + 8;
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -116,15 +120,15 @@ __device__ __forceinline__ void hist_add(int *h_copy, int *h_lead, int bin)
     }
 }
 
-__device__ __forceinline__ void lds_clear(int (*h)[kB1])
+__device__ __forceinline__ void lds_clear(int (*h)[kCopyStride])
 {
-    for (int i = kvc_tid(); i < kCopies * kB1 / 4; i += kThreads)
+    for (int i = kvc_tid(); i < kCopies * kCopyStride / 4; i += kThreads)
         reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
 }
 
 // Adds the non-zero bins of the LDS histogram copies into the global histogram g.
 template <int NB>
-__device__ __forceinline__ void flush_hist(int (*h)[kB1], int32_t *g)
+__device__ __forceinline__ void flush_hist(int (*h)[kCopyStride], int32_t *g)
 {
     for (int b = kvc_tid(); b < NB; b += kThreads) {
         int s = 0;
@@ -241,7 +245,7 @@ __device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t
 template <int KPT>
 __global__ __launch_bounds__(kThreads) void sel_level1_kernel(SelArgs a)
 {
-    __shared__ int h[kCopies][kB1];
+    __shared__ int h[kCopies][kCopyStride];
     const int u = kvc_bid_y();
     UnitShape us;
     int t0, t1;
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void sel_level1_kernel(SelArgs a)
 template <int KPT>
 __global__ __launch_bounds__(kThreads) void sel_level2_kernel(SelArgs a)
 {
-    __shared__ int h[kCopies][kB1];
+    __shared__ int h[kCopies][kCopyStride];
     __shared__ int scan[16];
     __shared__ Digit dg;
     const int u = kvc_bid_y();
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void sel_level2_kernel(SelArgs a)
 template <int KPT>
 __global__ __launch_bounds__(kThreads) void sel_level3_kernel(SelArgs a)
 {
-    __shared__ int h[kCopies][kB1];
+    __shared__ int h[kCopies][kCopyStride];
     __shared__ int scan[16];
     __shared__ int wave_above[kWaves];
     __shared__ Digit dg;
@@ -505,9 +509,9 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelArgs a)
 // the output are those of the chunked kernels above.
 
 // Bin of the k_rem-th largest key of an LDS histogram (the sum of its NC copies of NB
-// bins, copy c at h + c NB) and the number of keys above that bin; thread i owns bins
+// bins, copy c at h + c STRIDE) and the number of keys above that bin; thread i owns bins
 // NB-1-i*per down to NB-per-i*per.
-template <int NB, int NC, int NT>
+template <int NB, int NC, int NT, int STRIDE = NB>
 __device__ __forceinline__ Digit unit_digit(const int *h, int k_rem, int *scan, Digit *out)
 {
     constexpr int per = NB / NT;
@@ -517,7 +521,7 @@ __device__ __forceinline__ Digit unit_digit(const int *h, int k_rem, int *scan, 
     for (int p = 0; p < per; ++p) {
         int s = 0;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) s += h[cc * NB + top - p];
+        for (int cc = 0; cc < NC; ++cc) s += h[cc * STRIDE + top - p];
         c[p] = s;
     }
     return locate_digit<per>(c, top, k_rem, scan, out);
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
 {
     constexpr int K = 4 * NQ;
     // one histogram per level, all cleared up front: no clearing between the levels
-    __shared__ int h1[kCopies * kB1], h2[kB2], h3[kB3];
+    __shared__ int h1[kCopies * kCopyStride], h2[kB2], h3[kB3];
     __shared__ int scan[32];
     __shared__ Digit dg;
     const int u = kvc_bid_x();
@@ -590,15 +594,15 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
     // the counts above its bins do not change; the write checks validity
 #pragma unroll
     for (int i = 0; i < K; ++i) key[i] = t0 + i < us.C ? order_key(__uint_as_float(key[i])) : 0u;
-    for (int i = tid; i < kCopies * kB1 / 4; i += NT) reinterpret_cast<int4 *>(h1)[i] = make_int4(0, 0, 0, 0);
+    for (int i = tid; i < kCopies * kCopyStride / 4; i += NT) reinterpret_cast<int4 *>(h1)[i] = make_int4(0, 0, 0, 0);
     for (int i = tid; i < kB2 / 4; i += NT) reinterpret_cast<int4 *>(h2)[i] = make_int4(0, 0, 0, 0);
     for (int i = tid; i < kB3 / 4; i += NT) reinterpret_cast<int4 *>(h3)[i] = make_int4(0, 0, 0, 0);
     __syncthreads();
 
     // level 1: key bits [21, 32), into the thread's histogram copy
-    run_hist<K>(h1 + (tid & (kCopies - 1)) * kB1, [&](int i) { return (int)(key[i] >> 21); });
+    run_hist<K>(h1 + (tid & (kCopies - 1)) * kCopyStride, [&](int i) { return (int)(key[i] >> 21); });
     __syncthreads();
-    const Digit d1 = unit_digit<kB1, kCopies, NT>(h1, us.k_eff, scan, &dg);
+    const Digit d1 = unit_digit<kB1, kCopies, NT, kCopyStride>(h1, us.k_eff, scan, &dg);
     // level 2: bits [10, 21) of the keys in bin d1
     run_hist<K>(h2, [&](int i) {
         return (int)(key[i] >> 21) == d1.digit ? (int)((key[i] >> 10) & (kB2 - 1)) : -1;
