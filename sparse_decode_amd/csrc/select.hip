@@ -603,27 +603,32 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
     run_hist<K>(h1 + (tid & (kCopies - 1)) * kCopyStride, [&](int i) { return (int)(key[i] >> 21); });
     __syncthreads();
     const Digit d1 = unit_digit<kB1, kCopies, NT, kCopyStride>(h1, us.k_eff, scan, &dg);
-    // level 2: bits [10, 21) of the keys in bin d1
-    run_hist<K>(h2, [&](int i) {
-        return (int)(key[i] >> 21) == d1.digit ? (int)((key[i] >> 10) & (kB2 - 1)) : -1;
-    });
+    // level 2: bits [10, 21) of the keys in bin d1.  Few keys take part, so each adds
+    // itself: a key slot that no lane of the wave needs costs a compare and a skipped
+    // branch, where the run aggregation of level 1 would cost several instructions
+    const uint32_t dg1 = (uint32_t)d1.digit;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        if ((key[i] >> 21) == dg1) atomicAdd(&h2[(key[i] >> 10) & (kB2 - 1)], 1);
     __syncthreads();
     const Digit d2 = unit_digit<kB2, 1, NT>(h2, us.k_eff - d1.above, scan, &dg);
     // level 3: bits [0, 10) of the keys with prefix (d1, d2)
-    const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
-    run_hist<K>(h3, [&](int i) { return (key[i] >> 10) == pre2 ? (int)(key[i] & (kB3 - 1)) : -1; });
+    const uint32_t pre2 = (dg1 << 11) | (uint32_t)d2.digit;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        if ((key[i] >> 10) == pre2) atomicAdd(&h3[key[i] & (kB3 - 1)], 1);
     __syncthreads();
     const Digit d3 = unit_digit<kB3, 1, NT>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
     const uint32_t T = (pre2 << 10) | (uint32_t)d3.digit;
     const int ties = us.k_eff - d1.above - d2.above - d3.above;     // keys == T to take, lowest index first
 
-    // ordered write: block scans of the thread's keys > T and keys == T
+    // ordered write: block scans of the thread's keys > T and keys == T.  A slot past
+    // the candidates holds key 0, which is never above T; it equals T only if T is 0
     int gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-        const bool ok = t0 + i < us.C;
-        gt += ok && key[i] > T;
-        eq += ok && key[i] == T;
+        gt += key[i] > T;
+        eq += key[i] == T && t0 + i < us.C;
     }
     const int2 before = block_exclusive_scan2(gt, eq, scan);
     const int gt_before = before.x;
@@ -635,12 +640,12 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
     auto write_sel = [&](auto store) {
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-            if (t0 + i >= us.C) break;
-            bool sel = key[i] > T;
-            if (key[i] == T) sel = eq_before++ < ties;
-            if (sel) {
-                if (pos < us.k_eff) store(pos, t0 + i);               // never past the budget
-                ++pos;
+            if (key[i] > T || (key[i] == T && t0 + i < us.C)) {      // few slots: one test each
+                const bool sel = key[i] > T || eq_before++ < ties;
+                if (sel) {
+                    if (pos < us.k_eff) store(pos, t0 + i);           // never past the budget
+                    ++pos;
+                }
             }
         }
     };
