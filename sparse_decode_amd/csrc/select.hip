@@ -144,19 +144,26 @@ struct Digit {
 
 // Thread i owns bins NB-1-i*per down to NB-per-i*per of a histogram; c[p] receives
 // the count of bin (NB-1-i*per) - p.  Two 16-byte loads per 8 bins.
-template <int NB>
-__device__ __forceinline__ void load_bins(const int32_t *__restrict__ g, int (&c)[NB / kThreads])
+template <int NB, int NT = kThreads>
+__device__ __forceinline__ void load_bins(const int32_t *__restrict__ g, int (&c)[NB / NT])
 {
-    constexpr int per = NB / kThreads;
+    constexpr int per = NB / NT;
     const int top = NB - 1 - (int)kvc_tid() * per;
-    const int4 *g4 = reinterpret_cast<const int4 *>(g + top - per + 1);
+    if constexpr (per % 4 == 0) {
+        const int4 *g4 = reinterpret_cast<const int4 *>(g + top - per + 1);
 #pragma unroll
-    for (int v = 0; v < per / 4; ++v) {
-        const int4 x = g4[v];                            // bins top-per+1+4v .. top-per+4+4v
-        c[per - 1 - 4 * v] = x.x;
-        c[per - 2 - 4 * v] = x.y;
-        c[per - 3 - 4 * v] = x.z;
-        c[per - 4 - 4 * v] = x.w;
+        for (int v = 0; v < per / 4; ++v) {
+            const int4 x = g4[v];                        // bins top-per+1+4v .. top-per+4+4v
+            c[per - 1 - 4 * v] = x.x;
+            c[per - 2 - 4 * v] = x.y;
+            c[per - 3 - 4 * v] = x.z;
+            c[per - 4 - 4 * v] = x.w;
+        }
+    } else {
+        static_assert(per == 2, "two bins per thread");   // (1024 threads)
+        const int2 x = *reinterpret_cast<const int2 *>(g + top - 1);   // bins top-1, top
+        c[0] = x.y;
+        c[1] = x.x;
     }
 }
 
@@ -192,10 +199,10 @@ __device__ __forceinline__ Digit locate_digit(const int (&c)[PER], int top, int 
 }
 
 // locate_digit over the counts load_bins gave every thread.
-template <int NB>
-__device__ __forceinline__ Digit find_digit(const int (&c)[NB / kThreads], int k_rem, int *scan, Digit *out)
+template <int NB, int NT = kThreads>
+__device__ __forceinline__ Digit find_digit(const int (&c)[NB / NT], int k_rem, int *scan, Digit *out)
 {
-    constexpr int per = NB / kThreads;
+    constexpr int per = NB / NT;
     return locate_digit<per>(c, NB - 1 - (int)kvc_tid() * per, k_rem, scan, out);
 }
 
@@ -669,58 +676,63 @@ __global__ __launch_bounds__(NT) void sel_unit_kernel(SelArgs a)
 // scores around the threshold) is finished by that work-group from the unit's scores
 // instead: levels 2 and 3 and the write streamed from the caches.
 constexpr int kCandLds = 6144;                  // candidates the last work-group holds in LDS
-constexpr int kCandPer = kCandLds / kThreads;   // per thread
 
 // Calls f(key) for every candidate t < C of a unit's row: coalesced loads, kCandPer in
 // flight per thread.
-template <typename F>
+template <int NT, typename F>
 __device__ __forceinline__ void stream_keys(const float *__restrict__ sc, int C, F f)
 {
-    constexpr int kStep = kThreads * kCandPer;
+    constexpr int CP = kCandLds / NT;
+    constexpr int kStep = NT * CP;
     for (int t0 = (int)kvc_tid(); t0 < C; t0 += kStep) {
-        float x[kCandPer];
+        float x[CP];
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) {
-            const int t = t0 + q * kThreads;
+        for (int q = 0; q < CP; ++q) {
+            const int t = t0 + q * NT;
             x[q] = t < C ? sc[t] : 0.f;
         }
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q)
-            if (t0 + q * kThreads < C) f(order_key(x[q]));
+        for (int q = 0; q < CP; ++q)
+            if (t0 + q * NT < C) f(order_key(x[q]));
     }
 }
 
 // Calls f(t, key) for the candidates of this wave's range [r0, r1) in index order, 64
 // consecutive candidates per step (lane l holds t = s + l; lanes past the range get
 // t = -1 and key 0), every lane of the wave taking part in every step.
-template <typename F>
+template <int CP, typename F>
 __device__ __forceinline__ void walk_keys(const float *__restrict__ sc, int r0, int r1, F f)
 {
     const int lane = kvc_tid() & (kWave - 1);
-    for (int s0 = r0; s0 < r1; s0 += kWave * kCandPer) {
-        float x[kCandPer];
+    for (int s0 = r0; s0 < r1; s0 += kWave * CP) {
+        float x[CP];
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) {
+        for (int q = 0; q < CP; ++q) {
             const int t = s0 + q * kWave + lane;
             x[q] = t < r1 ? sc[t] : 0.f;
         }
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) {
+        for (int q = 0; q < CP; ++q) {
             const int t = s0 + q * kWave + lane;
             if (s0 + q * kWave < r1) f(t < r1 ? t : -1, t < r1 ? order_key(x[q]) : 0u);
         }
     }
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
+// NT / 128 waves per SIMD: two work-groups per CU, as many as the LDS allows (left to
+// itself the compiler gave the 512-thread kernel 242 VGPRs, one work-group per CU and
+// spills).
+template <int KPT, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 128))) void sel_cand_kernel(SelArgs a)
 {
-    constexpr int kChunk = KPT * kThreads;
+    constexpr int NW = NT / kWave;
+    constexpr int CP = kCandLds / NT;      // candidates per thread of the last work-group
+    constexpr int kChunk = KPT * NT;
     __shared__ int scan[32];
     __shared__ Digit dg;
-    __shared__ int wave_n[kWaves], wave_eq[kWaves];
+    __shared__ int wave_n[NW], wave_eq[NW];
     __shared__ int sh_last;
-    __shared__ int offs[kThreads + 1];
+    __shared__ int offs[NT + 1];
     __shared__ uint32_t c_key[kCandLds];
     __shared__ int32_t c_idx[kCandLds];
     __shared__ uint16_t c_chunk[kCandLds];
@@ -736,15 +748,15 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
     if (j == 0) {
         // the always-kept trailing tokens, the -1 padding and the count
         const int nw = us.S - us.C;
-        for (int i = tid; i < nw; i += kThreads) out[us.k_eff + i] = us.C + i;
-        for (int i = us.k_eff + nw + tid; i < a.cap; i += kThreads) out[i] = -1;
+        for (int i = tid; i < nw; i += NT) out[us.k_eff + i] = us.C + i;
+        for (int i = us.k_eff + nw + tid; i < a.cap; i += NT) out[i] = -1;
         if (tid == 0) a.count[u] = us.k_eff + nw;
     }
     const int t0 = j * kChunk;
     if (us.k_eff == 0 || t0 >= us.C) return;
     const int t1 = min(us.C, t0 + kChunk);
     if (us.k_eff == us.C) {
-        for (int t = t0 + tid; t < t1; t += kThreads) out[t] = t;
+        for (int t = t0 + tid; t < t1; t += NT) out[t] = t;
         return;
     }
     const int n_wg = (us.C + kChunk - 1) / kChunk;   // work-groups of this unit that get here
@@ -752,11 +764,11 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
     // ---- every work-group: d1, then the chunk's candidates in index order.  Wave w
     // owns the contiguous quarter [w0, w0 + kChunk/4) of the chunk; lane l holds keys
     // w0 + l + 64 q
-    const int w0 = t0 + wid * (kChunk / kWaves);
+    const int w0 = t0 + wid * (kChunk / NW);
     const float *sc = a.scores + (size_t)u * a.s_max;
     int32_t *H = a.hist + (size_t)u * kHistInts;
-    int c1[kB1 / kThreads];
-    load_bins<kB1>(H, c1);
+    int c1[kB1 / NT];
+    load_bins<kB1, NT>(H, c1);
     uint32_t key[KPT];
     {
         float v[KPT];
@@ -768,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
 #pragma unroll
         for (int q = 0; q < KPT; ++q) key[q] = order_key(v[q]);
     }
-    const Digit d1 = find_digit<kB1>(c1, us.k_eff, scan, &dg);
+    const Digit d1 = find_digit<kB1, NT>(c1, us.k_eff, scan, &dg);
     const uint32_t lo = (uint32_t)d1.digit << 21;         // candidates: key >= lo
     int cnt = 0;
 #pragma unroll
@@ -778,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
     __syncthreads();
     int pos = 0, n_c = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         pos += w < wid ? wave_n[w] : 0;
         n_c += wave_n[w];
     }
@@ -805,7 +817,7 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
     }
     if (staged) {
         __syncthreads();
-        for (int e = tid; e < n_c; e += kThreads)
+        for (int e = tid; e < n_c; e += NT)
             st_dev(list + e, ((unsigned long long)(uint32_t)c_idx[e] << 32) | c_key[e]);
     }
     if (tid == 0) st_dev(a.cand_n + (size_t)u * a.n_chunks + j, n_c);
@@ -818,28 +830,28 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
 
     // ---- the unit's last work-group.  Every chunk has read H1 and published its list:
     // H1 and the counter go back to zero for the next call
-    for (int i = tid; i < kB1 / 4; i += kThreads) reinterpret_cast<int4 *>(H)[i] = make_int4(0, 0, 0, 0);
+    for (int i = tid; i < kB1 / 4; i += NT) reinterpret_cast<int4 *>(H)[i] = make_int4(0, 0, 0, 0);
     if (tid == 0) a.done[u] = 0;
-    for (int i = tid; i < kB2; i += kThreads) h2[i] = 0;
-    for (int i = tid; i < kB3; i += kThreads) h3[i] = 0;
+    for (int i = tid; i < kB2; i += NT) h2[i] = 0;
+    for (int i = tid; i < kB3; i += NT) h3[i] = 0;
     int total;
     const int nc_t = tid < n_wg ? ld_dev(a.cand_n + (size_t)u * a.n_chunks + tid) : 0;
     const int off_t = block_exclusive_scan(nc_t, scan, &total);
     if (tid < n_wg) offs[tid] = off_t;
-    if (tid == 0) offs[n_wg < kThreads ? n_wg : kThreads] = total;
-    const bool in_lds = n_wg <= kThreads && total <= kCandLds;
+    if (tid == 0) offs[n_wg < NT ? n_wg : NT] = total;
+    const bool in_lds = n_wg <= NT && total <= kCandLds;
     __syncthreads();
     int ties = 0;
     uint32_t T = 0;
     if (in_lds) {
         // the lists, chunk after chunk: index order.  c_chunk[e]: the chunk of candidate e
         for (int c = 0; c < n_wg; ++c)
-            for (int e = offs[c] + tid; e < offs[c + 1]; e += kThreads) c_chunk[e] = (uint16_t)c;
+            for (int e = offs[c] + tid; e < offs[c + 1]; e += NT) c_chunk[e] = (uint16_t)c;
         __syncthreads();
-        unsigned long long v[kCandPer];
+        unsigned long long v[CP];
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) {
-            const int e = tid + q * kThreads;
+        for (int q = 0; q < CP; ++q) {
+            const int e = tid + q * NT;
             v[q] = 0ull;
             if (e < total) {
                 const int c = c_chunk[e];
@@ -847,8 +859,8 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
             }
         }
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) {
-            const int e = tid + q * kThreads;
+        for (int q = 0; q < CP; ++q) {
+            const int e = tid + q * NT;
             if (e < total) {
                 c_key[e] = (uint32_t)v[q];
                 c_idx[e] = (int32_t)(v[q] >> 32);
@@ -857,39 +869,39 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
         __syncthreads();
         // thread i takes the consecutive candidates [e0, e1), to registers: equal keys
         // come in runs
-        const int per = (total + kThreads - 1) / kThreads;
+        const int per = (total + NT - 1) / NT;
         const int e0 = min(tid * per, total), e1 = min(e0 + per, total);
-        uint32_t ck[kCandPer];
+        uint32_t ck[CP];
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) ck[q] = e0 + q < e1 ? c_key[e0 + q] : 0u;
-        run_hist<kCandPer>(h2, [&](int q) {
+        for (int q = 0; q < CP; ++q) ck[q] = e0 + q < e1 ? c_key[e0 + q] : 0u;
+        run_hist<CP>(h2, [&](int q) {
             return e0 + q < e1 && (int)(ck[q] >> 21) == d1.digit ? (int)((ck[q] >> 10) & (kB2 - 1)) : -1;
         });
         __syncthreads();
-        const Digit d2 = unit_digit<kB2, 1, kThreads>(h2, us.k_eff - d1.above, scan, &dg);
+        const Digit d2 = unit_digit<kB2, 1, NT>(h2, us.k_eff - d1.above, scan, &dg);
         const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
-        run_hist<kCandPer>(h3, [&](int q) {
+        run_hist<CP>(h3, [&](int q) {
             return e0 + q < e1 && (ck[q] >> 10) == pre2 ? (int)(ck[q] & (kB3 - 1)) : -1;
         });
         __syncthreads();
-        const Digit d3 = unit_digit<kB3, 1, kThreads>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
+        const Digit d3 = unit_digit<kB3, 1, NT>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
         T = (pre2 << 10) | (uint32_t)d3.digit;
         ties = us.k_eff - d1.above - d2.above - d3.above;
         // ordered write: the thread's selected indices to registers, then to LDS in
         // output order (over the candidates' indices, free by then), then out
         int gt = 0, eq = 0;
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) {
+        for (int q = 0; q < CP; ++q) {
             gt += e0 + q < e1 && ck[q] > T;
             eq += e0 + q < e1 && ck[q] == T;
         }
         const int2 before = block_exclusive_scan2(gt, eq, scan);
         int p = before.x + min(ties, before.y);
         int eq_seen = before.y;
-        int sel[kCandPer];
+        int sel[CP];
         int n_sel = 0;
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) {
+        for (int q = 0; q < CP; ++q) {
             const int e = e0 + q;
             sel[q] = -1;
             if (e < e1) {
@@ -902,36 +914,36 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
         }
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < kCandPer; ++q) {
+        for (int q = 0; q < CP; ++q) {
             if (sel[q] >= 0) {
                 if (p < us.k_eff) c_idx[p] = sel[q];                  // never past the budget
                 ++p;
             }
         }
         __syncthreads();
-        for (int i = tid; i < us.k_eff; i += kThreads) out[i] = c_idx[i];
+        for (int i = tid; i < us.k_eff; i += NT) out[i] = c_idx[i];
         return;
     }
 
     // ---- more candidates than LDS holds: levels 2 and 3 and the write from the scores
-    stream_keys(sc, us.C, [&](uint32_t k) {
+    stream_keys<NT>(sc, us.C, [&](uint32_t k) {
         if ((int)(k >> 21) == d1.digit) hist_add(h2, h2, (int)((k >> 10) & (kB2 - 1)));
     });
     __syncthreads();
-    const Digit d2 = unit_digit<kB2, 1, kThreads>(h2, us.k_eff - d1.above, scan, &dg);
+    const Digit d2 = unit_digit<kB2, 1, NT>(h2, us.k_eff - d1.above, scan, &dg);
     const uint32_t pre2 = ((uint32_t)d1.digit << 11) | (uint32_t)d2.digit;
-    stream_keys(sc, us.C, [&](uint32_t k) {
+    stream_keys<NT>(sc, us.C, [&](uint32_t k) {
         if ((k >> 10) == pre2) hist_add(h3, h3, (int)(k & (kB3 - 1)));
     });
     __syncthreads();
-    const Digit d3 = unit_digit<kB3, 1, kThreads>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
+    const Digit d3 = unit_digit<kB3, 1, NT>(h3, us.k_eff - d1.above - d2.above, scan, &dg);
     T = (pre2 << 10) | (uint32_t)d3.digit;
     ties = us.k_eff - d1.above - d2.above - d3.above;
     // wave w owns the candidates [w R, w R + R), R a multiple of 64
-    const int R = ((us.C + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
+    const int R = ((us.C + NW - 1) / NW + kWave - 1) / kWave * kWave;
     const int r0 = min(wid * R, us.C), r1 = min(r0 + R, us.C);
     int gt = 0, eq = 0;
-    walk_keys(sc, r0, r1, [&](int t, uint32_t k) {
+    walk_keys<CP>(sc, r0, r1, [&](int t, uint32_t k) {
         gt += t >= 0 && k > T;
         eq += t >= 0 && k == T;
     });
@@ -949,7 +961,7 @@ __global__ __launch_bounds__(kThreads) void sel_cand_kernel(SelArgs a)
         p += wave_n[w] + take;
         eq_seen += wave_eq[w];
     }
-    walk_keys(sc, r0, r1, [&](int t, uint32_t k) {
+    walk_keys<CP>(sc, r0, r1, [&](int t, uint32_t k) {
         const bool is_gt = t >= 0 && k > T;
         const bool is_eq = t >= 0 && k == T;
         const unsigned long long m_eq = __ballot(is_eq);
@@ -1210,7 +1222,9 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
         // few large chunks per unit: level 1, then the candidate lists and their last
         // work-group (one launch for levels 2, 3 and the write)
         hipLaunchKernelGGL(sel_level1_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
-        hipLaunchKernelGGL(sel_cand_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
+        // (512 threads: the same 8192-key chunks, twice the threads for the last
+        // work-group's gather, levels and write, and still two work-groups per CU)
+        hipLaunchKernelGGL((sel_cand_kernel<kKptLarge * kThreads / 512, 512>), grid, dim3(512), 0, stream, a);
     } else {
         // many small chunks per unit: the last work-group's gather and levels would
         // outlast three chunked kernels (measured), so levels 2 and 3 and the write
