@@ -59,8 +59,11 @@ __global__ __launch_bounds__(kBlkThreads) void block_landmarks_kernel(const u32x
 // One thread per (unit, block): scale * sum over the group's query heads, then over d,
 // of q * landmark, in double, for the candidate blocks j < floor((S_b - n_keep) / block);
 // 0 elsewhere.  Unit (b, 0)'s block-0 thread also writes the candidate block count.
+// Two waves per SIMD: a thread holds its 512-byte landmark row in registers, and
+// without the bound the compiler's allocation left one wave per SIMD (a few registers
+// spill instead).
 template <bool BF16, int D>
-__global__ __launch_bounds__(kBlkThreads) void block_scores_kernel(const void *__restrict__ q,
+__global__ __launch_bounds__(kBlkThreads) __attribute__((amdgpu_waves_per_eu(2))) void block_scores_kernel(const void *__restrict__ q,
                                                                    const float *__restrict__ landmarks,
                                                                    const int32_t *__restrict__ seq_lens,
                                                                    int n_h, int n_kv, int d_h, int s_max, int block,
