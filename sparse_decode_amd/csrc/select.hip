@@ -120,17 +120,18 @@ __device__ __forceinline__ void hist_add(int *h_copy, int *h_lead, int bin)
     }
 }
 
+template <int NT = kThreads>
 __device__ __forceinline__ void lds_clear(int (*h)[kCopyStride])
 {
-    for (int i = kvc_tid(); i < kCopies * kCopyStride / 4; i += kThreads)
+    for (int i = kvc_tid(); i < kCopies * kCopyStride / 4; i += NT)
         reinterpret_cast<int4 *>(&h[0][0])[i] = make_int4(0, 0, 0, 0);
 }
 
 // Adds the non-zero bins of the LDS histogram copies into the global histogram g.
-template <int NB>
+template <int NB, int NT = kThreads>
 __device__ __forceinline__ void flush_hist(int (*h)[kCopyStride], int32_t *g)
 {
-    for (int b = kvc_tid(); b < NB; b += kThreads) {
+    for (int b = kvc_tid(); b < NB; b += NT) {
         int s = 0;
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) s += h[c][b];
@@ -215,7 +216,7 @@ struct ChunkKeys {
     int t0, t1;
 };
 
-template <int KPT>
+template <int KPT, int NT = kThreads>
 __device__ __forceinline__ void load_chunk(const float *__restrict__ sc, int t0, int t1, ChunkKeys<KPT> &ck)
 {
     ck.t0 = t0;
@@ -223,25 +224,25 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ sc, int t0,
     float v[KPT];
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-        const int t = t0 + (int)kvc_tid() + q * kThreads;
+        const int t = t0 + (int)kvc_tid() + q * NT;
         v[q] = t < t1 ? sc[t] : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < KPT; ++q) ck.key[q] = order_key(v[q]);
 }
 
-template <int KPT>
+template <int KPT, int NT = kThreads>
 __device__ __forceinline__ bool chunk_valid(const ChunkKeys<KPT> &ck, int q)
 {
-    return ck.t0 + (int)kvc_tid() + q * kThreads < ck.t1;
+    return ck.t0 + (int)kvc_tid() + q * NT < ck.t1;
 }
 
 // ------------------------------------------------------------------------------ kernels
 // The work-group's unit and chunk; false when the chunk has nothing to histogram.
-template <int KPT>
+template <int KPT, int NT = kThreads>
 __device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t0, int &t1)
 {
-    constexpr int kChunk = KPT * kThreads;
+    constexpr int kChunk = KPT * NT;
     us = unit_shape(a.seq_lens, (int)kvc_bid_y() / a.H, a.s_max, unit_budget(a, kvc_bid_y()), a.n_keep);
     t0 = (int)kvc_bid_x() * kChunk;
     t1 = min(us.C, t0 + kChunk);
@@ -249,24 +250,24 @@ __device__ __forceinline__ bool chunk_of(const SelArgs &a, UnitShape &us, int &t
     return us.k_eff > 0 && us.k_eff < us.C && t0 < us.C;
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void sel_level1_kernel(SelArgs a)
+template <int KPT, int NT = kThreads>
+__global__ __launch_bounds__(NT) void sel_level1_kernel(SelArgs a)
 {
     __shared__ int h[kCopies][kCopyStride];
     const int u = kvc_bid_y();
     UnitShape us;
     int t0, t1;
-    if (!chunk_of<KPT>(a, us, t0, t1)) return;
+    if (!chunk_of<KPT, NT>(a, us, t0, t1)) return;
     ChunkKeys<KPT> ck;
-    load_chunk(a.scores + (size_t)u * a.s_max, t0, t1, ck);
-    lds_clear(h);
+    load_chunk<KPT, NT>(a.scores + (size_t)u * a.s_max, t0, t1, ck);
+    lds_clear<NT>(h);
     __syncthreads();
     int *hc = h[kvc_tid() & (kCopies - 1)];
 #pragma unroll
     for (int q = 0; q < KPT; ++q)
-        if (chunk_valid(ck, q)) hist_add(hc, h[0], (int)(ck.key[q] >> 21));
+        if (chunk_valid<KPT, NT>(ck, q)) hist_add(hc, h[0], (int)(ck.key[q] >> 21));
     __syncthreads();
-    flush_hist<kB1>(h, a.hist + (size_t)u * kHistInts);
+    flush_hist<kB1, NT>(h, a.hist + (size_t)u * kHistInts);
 }
 
 template <int KPT>
@@ -1221,7 +1222,7 @@ hipError_t launch_select(int batch, int n_kv, int s_max, const int32_t *seq_lens
     if (L.kpt == kKptLarge) {
         // few large chunks per unit: level 1, then the candidate lists and their last
         // work-group (one launch for levels 2, 3 and the write)
-        hipLaunchKernelGGL(sel_level1_kernel<kKptLarge>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((sel_level1_kernel<kKptLarge * kThreads / 512, 512>), grid, dim3(512), 0, stream, a);
         // (512 threads: the same 8192-key chunks, twice the threads for the last
         // work-group's gather, levels and write, and still two work-groups per CU)
         hipLaunchKernelGGL((sel_cand_kernel<kKptLarge * kThreads / 512, 512>), grid, dim3(512), 0, stream, a);
