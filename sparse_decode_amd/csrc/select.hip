@@ -9,9 +9,10 @@
 // the selected set is every key > T plus the lowest-indexed keys == T, written in
 // index order.  One work-group alone streams a unit's keys far below the chip's
 // bandwidth (a CU keeps only so many cache lines in flight), so every pass is spread
-// over the unit's chunks of 2048 keys, or 8192 when the call has at least 512 such
-// larger chunks (one work-group each, every key loaded once into registers), and the
-// levels meet through per-unit histograms in global memory:
+// over the unit's chunks of 2048 keys, or 8192 when the call has at least 32 such
+// larger chunks (512 for the head-summed selection; one work-group each, every key
+// loaded once into registers), and the levels meet through per-unit histograms in
+// global memory:
 //
 //   level1  grid (chunks, units): histogram of the top 11 bits of the chunk's keys,
 //           added into the unit histogram H1
@@ -1081,7 +1082,12 @@ SelLayout sel_layout(int batch, int n_kv, int s_max, int n_keep, bool shared)
     const long units = shared ? batch : (long)batch * n_kv;
     const long c_max = s_max - n_keep > 1 ? (long)s_max - n_keep : 1;
     const long big = kKptLarge * kThreads;
-    L.kpt = units * ((c_max + big - 1) / big) >= 512 ? kKptLarge : kKptSmall;
+    // 8192-key chunks (level 1, then the candidate lists) when the call has at least 32
+    // of them: a KV head's last work-group then gathers a few long lists.  The shared
+    // (head-summed) selection keeps 2048-key chunks below 512 of them: its budget, a
+    // rate of the sequence, is more than the candidate LDS holds
+    const long n_big = units * ((c_max + big - 1) / big);
+    L.kpt = (n_big >= 512 || (!shared && n_big >= 32)) ? kKptLarge : kKptSmall;
     const long chunk = (long)L.kpt * kThreads;
     L.n_chunks = (int)((c_max + chunk - 1) / chunk);
     size_t off = 0;
