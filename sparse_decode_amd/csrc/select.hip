@@ -150,22 +150,16 @@ template <int NB, int NT = kThreads>
 __device__ __forceinline__ void load_bins(const int32_t *__restrict__ g, int (&c)[NB / NT])
 {
     constexpr int per = NB / NT;
+    static_assert(per % 4 == 0, "whole 16-byte groups of bins per thread");
     const int top = NB - 1 - (int)kvc_tid() * per;
-    if constexpr (per % 4 == 0) {
-        const int4 *g4 = reinterpret_cast<const int4 *>(g + top - per + 1);
+    const int4 *g4 = reinterpret_cast<const int4 *>(g + top - per + 1);
 #pragma unroll
-        for (int v = 0; v < per / 4; ++v) {
-            const int4 x = g4[v];                        // bins top-per+1+4v .. top-per+4+4v
-            c[per - 1 - 4 * v] = x.x;
-            c[per - 2 - 4 * v] = x.y;
-            c[per - 3 - 4 * v] = x.z;
-            c[per - 4 - 4 * v] = x.w;
-        }
-    } else {
-        static_assert(per == 2, "two bins per thread");   // (1024 threads)
-        const int2 x = *reinterpret_cast<const int2 *>(g + top - 1);   // bins top-1, top
-        c[0] = x.y;
-        c[1] = x.x;
+    for (int v = 0; v < per / 4; ++v) {
+        const int4 x = g4[v];                            // bins top-per+1+4v .. top-per+4+4v
+        c[per - 1 - 4 * v] = x.x;
+        c[per - 2 - 4 * v] = x.y;
+        c[per - 3 - 4 * v] = x.z;
+        c[per - 4 - 4 * v] = x.w;
     }
 }
 
